@@ -1,0 +1,495 @@
+"""Pins of the CPU oracle to things other than itself: exact rational
+arithmetic, library routines, closed forms and symmetry reductions.
+
+Each test is chosen so that a plausible slip in the oracle (a dropped term, a
+transposed comb, a wrong divisor, eps in the wrong place, a double rounding)
+fails at least one of them.
+"""
+import math
+import os
+import struct
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from mhc_hyper_connection_boundary_amd import workloads as WL
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+PARAMS = dict(rms_eps=1e-6, pre_eps=1e-6, post_mult=2.0, sinkhorn_eps=1e-6,
+              sinkhorn_iters=20, norm_eps=1e-6)
+
+
+# ---- exact-arithmetic helpers (independent of the oracle) -------------------
+
+def f32_of_bits(u):
+    return struct.unpack("<f", struct.pack("<I", u))[0]
+
+
+def bits_of_f32(x):
+    return struct.unpack("<I", struct.pack("<f", x))[0]
+
+
+def round_sig(v: Fraction, bits: int, ties_away=False) -> Fraction:
+    """Round a rational to `bits` significant bits (normal range), nearest,
+    ties to even or away from zero."""
+    if v == 0:
+        return Fraction(0)
+    sign = -1 if v < 0 else 1
+    a = abs(v)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    ulp = Fraction(2) ** (e - bits + 1)
+    q = a / ulp
+    fl = q.numerator // q.denominator
+    rem = q - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and (ties_away or fl % 2 == 1)):
+        fl += 1
+    return sign * fl * ulp
+
+
+def rf32(v: Fraction) -> Fraction:
+    return round_sig(v, 24)
+
+
+def rbf16(v: Fraction) -> Fraction:
+    return round_sig(v, 8)
+
+
+def fr(x) -> Fraction:
+    return Fraction(float(x))
+
+
+def bf16_vals(bits):
+    return WL.bf16_bits_to_f32(np.asarray(bits, np.uint16))
+
+
+def bf16_of(x: float) -> int:
+    return bits_of_f32(x) >> 16  # only for values exactly representable in bf16
+
+
+# ---- TF32 rounding and the hi/lo split ---------------------------------------
+
+def _read_golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split()[:2])
+    return rows
+
+
+def test_tf32_golden_cases(oracle):
+    for a, b in _read_golden("tf32_ties_away.txt"):
+        assert oracle.tf32_bits(int(a, 16)) == int(b, 16), a
+
+
+def test_tf32_ties_away_exhaustive_low_bits(oracle):
+    """All 2^13 dropped-bit patterns under several kept parts, against rounding
+    of the exact value to 11 significant bits with ties away from zero."""
+    highs = [0x3F800000, 0x3FFFE000, 0x40490000, 0xC2F6A000, 0x00800000, 0x3E2AA000,
+             0xBF7FE000, 0x7E000000]
+    bits = np.array([h | low for h in highs for low in range(1 << 13)], dtype=np.uint32)
+    t, _, _ = oracle.split_weight(bits.view(np.float32))
+    got = t.view(np.uint32)
+    for u, g in zip(bits[::7].tolist(), got[::7].tolist()):
+        exact = round_sig(fr(f32_of_bits(u)), 11, ties_away=True)
+        assert g == bits_of_f32(float(exact)), hex(u)
+    assert np.all(got & 0x1FFF == 0)
+
+
+def test_hi_lo_split_is_exact(oracle):
+    inp = WL.make_inputs("decode", T=1)
+    w = np.concatenate([inp.W.ravel(), np.array([1.0, -1.0, 3.0e-30, 6.5e37, 1.0 + 2 ** -11],
+                                                np.float32)])
+    t, hi, lo = oracle.split_weight(w)
+    hs, ls = bf16_vals(hi), bf16_vals(lo)
+    assert np.array_equal((hs + ls).view(np.uint32), t.view(np.uint32))
+    # hi is the bf16 rounding of tf32(w): |lo| is at most half a bf16 ulp of hi
+    nz = hs != 0
+    assert np.all(np.abs(ls[nz]) <= np.abs(hs[nz]) * 2.0 ** -8)
+    # and torch's bf16 cast of tf32(w) is hi
+    th = torch.from_numpy(t).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(th, hi)
+
+
+def test_bf16_from_f32_matches_torch(oracle):
+    rng = np.random.default_rng(11)
+    vals = np.concatenate([
+        rng.standard_normal(4000).astype(np.float32) * np.float32(10.0) ** rng.integers(-20, 20, 4000),
+        # exact ties at several exponents, both kept-bit parities
+        np.array([f32_of_bits(0x3F808000), f32_of_bits(0x3F818000), f32_of_bits(0xC0808000),
+                  f32_of_bits(0x3F807FFF), f32_of_bits(0x3F808001)], np.float32)])
+    ref = torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([oracle.bf16_from_f32(float(v)) for v in vals], np.uint16)
+    assert np.array_equal(got, ref)
+
+
+def test_bf16_from_f64_single_rounding(oracle):
+    for expr, b in _read_golden("bf16_single_rounding.txt"):
+        v = eval(expr, {"__builtins__": {}})
+        assert oracle.bf16_from_f64(v) == int(b, 16), expr
+    rng = np.random.default_rng(12)
+    for v in (rng.standard_normal(3000) * 10.0 ** rng.integers(-30, 30, 3000)).tolist():
+        want = rbf16(Fraction(v))
+        assert oracle.bf16_from_f64(v) == bits_of_f32(float(want)) >> 16, v
+
+
+# ---- prepared weight: the documented layout contracts to the right mixes -----
+
+def test_prepared_weight_contracts_like_the_mixes(oracle):
+    """Emulate the 16x16x32 matrix-core contraction straight from the layout's
+    lane description (A row = lane % 16, k group = lane / 16; C rows 4*(lane/16)+i)
+    and compare with tf32(W) @ flat(X') in exact arithmetic."""
+    d, ntok = 64, 16
+    rng = np.random.default_rng(5)
+    W = rng.standard_normal((24, 4 * d)).astype(np.float32)
+    prep = oracle.prepare_weight(W).view(np.uint16)
+    A = bf16_vals(prep).astype(np.float64).reshape(d // 32, 4, 3, 4, 16, 8)  # step,s,m,g,r,e
+    Xp = bf16_vals(WL.to_bf16_bits(rng.standard_normal((ntok, 4, d)).astype(np.float32)))
+    B = Xp.astype(np.float64).reshape(ntok, 4, d // 32, 4, 8)                # n,s,step,g,e
+    C = np.einsum("asmgre,nsage->mrn", A, B)                                 # [3,16,ntok]
+    mixes = np.zeros((ntok, 24))
+    for m in range(3):
+        for q in range(4):
+            for j in range(2):
+                mixes[:, 8 * m + 2 * q + j] = C[m, 4 * q + j] + C[m, 4 * q + j + 2]
+    t, _, _ = oracle.split_weight(W)
+    ref = Xp.reshape(ntok, 4 * d).astype(np.float64) @ t.astype(np.float64).T
+    np.testing.assert_allclose(mixes, ref, rtol=0, atol=1e-12)
+    # every prepared element is used exactly once per (mix, column, part)
+    assert prep.size == 192 * d
+
+
+# ---- residual update, collapse: special cases and exact brute force ----------
+
+def _tiny(T=4, d=256, seed=0):
+    inp = WL.make_inputs(WL.Config("t", d=d, T=T, seed=seed, norm="noisy"))
+    return inp
+
+
+def test_update_identity_and_pure_x(oracle):
+    inp = _tiny()
+    inp.comb_prev[:] = np.eye(4, dtype=np.float32)
+    inp.post_prev[:] = 0.0
+    r = oracle.boundary(inp)
+    assert np.array_equal(r["xn"], inp.X)
+    inp.comb_prev[:] = 0.0
+    inp.post_prev[:] = 1.0
+    r = oracle.boundary(inp)
+    for s in range(4):
+        assert np.array_equal(r["xn"][:, s], inp.x)
+    inp.post_prev[:] = 2.0
+    r = oracle.boundary(inp)
+    assert np.array_equal(bf16_vals(r["xn"][:, 1]), 2.0 * bf16_vals(inp.x))
+
+
+def test_update_comb_orientation(oracle):
+    """comb[j][s] routes source stream j to destination stream s."""
+    inp = _tiny()
+    perm = [2, 0, 3, 1]                      # j -> s, not an involution
+    inp.comb_prev[:] = 0.0
+    for j, s in enumerate(perm):
+        inp.comb_prev[:, j, s] = 1.0
+    inp.post_prev[:] = 0.0
+    r = oracle.boundary(inp)
+    for j, s in enumerate(perm):
+        assert np.array_equal(r["xn"][:, s], inp.X[:, j])
+
+
+def test_collapse_unit_pre(oracle):
+    inp = _tiny()
+    r0 = oracle.boundary(inp, use_norm=False)
+    for j in range(4):
+        inp.pre_lag[:] = 0.0
+        inp.pre_lag[:, j] = 1.0
+        r = oracle.boundary(inp, use_norm=False)
+        assert np.array_equal(r["li"], r0["xn"][:, j])
+        assert np.array_equal(r["layer_input"], r["li"])            # no norm: li itself
+        v = bf16_vals(r0["xn"][:, j]).astype(np.float64)
+        np.testing.assert_allclose(r["ssq_li"], (v * v).sum(1), rtol=1e-15)
+
+
+def test_bruteforce_d8_exact(oracle):
+    """d=8, T=3: every rounding point redone in exact rational arithmetic."""
+    d, T = 8, 3
+    rng = np.random.default_rng(8)
+    X = WL.to_bf16_bits(rng.standard_normal((T, 4, d)).astype(np.float32))
+    x = WL.to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32))
+    post = rng.uniform(0, 2, (T, 4)).astype(np.float32)
+    comb = rng.uniform(0, 1, (T, 4, 4)).astype(np.float32)
+    pre = rng.uniform(0, 1, (T, 4)).astype(np.float32)
+    W = rng.standard_normal((24, 4 * d)).astype(np.float32)
+    scale = np.array([0.3, 0.2, 0.1], np.float32)
+    base = rng.standard_normal(24).astype(np.float32)
+    r = oracle.run(True, X, x, post, comb, pre, W, scale, base, None, PARAMS)
+    tw, _, _ = oracle.split_weight(W)
+    Xv, xv = bf16_vals(X), bf16_vals(x)
+    for t in range(T):
+        xn = [[None] * d for _ in range(4)]
+        for h in range(d):
+            for s in range(4):
+                nu = rf32(fr(post[t, s]) * fr(xv[t, h]))
+                for j in range(4):
+                    nu = rf32(fr(comb[t, j, s]) * fr(Xv[t, j, h]) + nu)
+                xn[s][h] = rbf16(nu)
+                assert float(xn[s][h]) == float(bf16_vals(r["xn"][t, s, h])), (t, s, h)
+        ssq = sum(v * v for row in xn for v in row)
+        assert float(ssq) == r["ssq"][t]
+        ssq_li = Fraction(0)
+        for h in range(d):
+            acc = Fraction(0)
+            for j in range(4):
+                acc = rf32(fr(pre[t, j]) * xn[j][h] + acc)
+            li = rbf16(acc)
+            assert float(li) == float(bf16_vals(r["li"][t, h]))
+            ssq_li += li * li
+        assert float(ssq_li) == r["ssq_li"][t]
+        flat = [v for row in xn for v in row]
+        for n in range(24):
+            exact = sum(fr(tw[n, k]) * flat[k] for k in range(4 * d))
+            assert abs(float(exact) - r["mixes"][t, n]) <= 1e-15 * max(1.0, abs(float(exact)))
+
+
+# ---- mixes ---------------------------------------------------------------------
+
+def test_mixes_within_fp64_bound_of_exact_sum(oracle):
+    """Products tf32 x bf16 are exact in FP64, so math.fsum gives the correctly
+    rounded exact sum; the oracle's plain sum must lie within K*u*sum|terms|."""
+    inp = WL.make_inputs("tiny")
+    r = oracle.boundary(inp)
+    tw, _, _ = oracle.split_weight(inp.W)
+    xn = bf16_vals(r["xn"]).reshape(inp.T, -1).astype(np.float64)
+    K = xn.shape[1]
+    for t in range(inp.T):
+        for n in range(24):
+            terms = tw[n].astype(np.float64) * xn[t]
+            exact = math.fsum(terms.tolist())
+            bound = K * 2.0 ** -53 * np.abs(terms).sum()
+            assert abs(r["mixes"][t, n] - exact) <= bound
+
+
+def test_fused_projection_equals_three(oracle):
+    """One fused [24, 4d] projection equals the pre / post / comb projections."""
+    inp = WL.make_inputs("tiny")
+    fused = oracle.boundary(inp)["mixes"]
+    parts = np.zeros_like(fused)
+    for rows in (slice(0, 4), slice(4, 8), slice(8, 24)):
+        W = np.zeros_like(inp.W)
+        W[rows] = inp.W[rows]
+        one = oracle.run(True, inp.X, inp.x, inp.post_prev, inp.comb_prev, inp.pre_lag, W,
+                         inp.scale, inp.base, inp.norm_w, inp.params())["mixes"]
+        assert np.all(np.delete(one, np.arange(24)[rows], axis=1) == 0.0)
+        parts += one
+    assert np.array_equal(parts, fused)
+
+
+# ---- rstd / pre / post ------------------------------------------------------------
+
+def _constant_xn(inp, c):
+    """Inputs whose updated residual is the constant c everywhere."""
+    inp.comb_prev[:] = 0.0
+    inp.post_prev[:] = 1.0
+    inp.x[:] = bf16_of(c)
+    return inp
+
+
+def test_constant_residual_closed_forms(oracle):
+    """X' = c everywhere: ssq = 4 d c^2, rstd = 1/sqrt(c^2 + eps), and with
+    rms eps 0 the logits are sign(c) * rowsum(tf32 W) * scale + base."""
+    c = -1.5
+    inp = _constant_xn(_tiny(T=2), c)
+    d = inp.d
+    p = dict(PARAMS, rms_eps=0.0)
+    r = oracle.run(True, inp.X, inp.x, inp.post_prev, inp.comb_prev, inp.pre_lag, inp.W,
+                   inp.scale, inp.base, None, p)
+    assert np.all(r["ssq"] == 4 * d * c * c)
+    np.testing.assert_allclose(r["rstd"], 1.0 / abs(c), rtol=1e-15)
+    tw, _, _ = oracle.split_weight(inp.W)
+    rowsum = np.array([math.fsum(tw[n].astype(np.float64).tolist()) for n in range(24)])
+    logit = -rowsum * inp.scale.astype(np.float64)[[0] * 4 + [1] * 4 + [2] * 16] + inp.base
+    sig = 1.0 / (1.0 + np.exp(-logit))
+    np.testing.assert_allclose(r["pre"][0], sig[:4] + float(np.float32(1e-6)), rtol=1e-13)
+    np.testing.assert_allclose(r["post"][0], 2.0 * sig[4:8], rtol=1e-13)
+
+
+def test_pre_post_closed_form_at_zero_scale(oracle):
+    """scale = 0: pre = sigmoid(base) + eps, post = 2 sigmoid(base), independent of X.
+    sigmoid(0) = 1/2 and sigmoid(ln 3) = 3/4 exactly."""
+    inp = _tiny(T=3)
+    inp.scale[:] = 0.0
+    inp.base[:4] = [0.0, math.log(3.0), -math.log(3.0), 0.0]
+    inp.base[4:8] = [0.0, math.log(3.0), 0.0, -math.log(3.0)]
+    r = oracle.boundary(inp)
+    eps = float(np.float32(1e-6))
+    want_pre = np.array([0.5, 0.75, 0.25, 0.5]) + eps
+    want_post = np.array([1.0, 1.5, 1.0, 0.5])
+    for t in range(inp.T):
+        np.testing.assert_allclose(r["pre"][t], want_pre, atol=1e-7)   # ln 3 is rounded to fp32
+        np.testing.assert_allclose(r["post"][t], want_post, atol=2e-7)
+    assert r["pre"][0][0] == 0.5 + eps and r["post"][0][0] == 1.0
+
+
+def test_rms_invariance(oracle):
+    """Scaling X and x by 2^k scales X' by 2^k exactly; with both eps 0 the
+    coefficients and the normalised layer input do not move."""
+    inp = _tiny(T=3)
+    p = dict(PARAMS, rms_eps=0.0, norm_eps=0.0)
+    args = lambda X, x: (True, X, x, inp.post_prev, inp.comb_prev, inp.pre_lag, inp.W,
+                         inp.scale, inp.base, inp.norm_w, p)
+    r0 = oracle.run(*args(inp.X, inp.x))
+    X8 = WL.to_bf16_bits(bf16_vals(inp.X) * np.float32(8.0))
+    x8 = WL.to_bf16_bits(bf16_vals(inp.x) * np.float32(8.0))
+    r1 = oracle.run(*args(X8, x8))
+    assert np.array_equal(bf16_vals(r1["xn"]), 8.0 * bf16_vals(r0["xn"]))
+    for key in ("pre", "post", "comb"):
+        np.testing.assert_allclose(r1[key], r0[key], rtol=1e-13, atol=1e-15)
+    assert np.array_equal(r1["layer_input"], r0["layer_input"])
+
+
+def test_pre_post_ranges(oracle):
+    inp = WL.make_inputs("stress", T=300)
+    r = oracle.boundary(inp)
+    eps = float(np.float32(1e-6))
+    assert np.all(r["pre"] > eps) and np.all(r["pre"] < 1 + eps)
+    assert np.all(r["post"] > 0) and np.all(r["post"] < 2)
+
+
+# ---- Sinkhorn ----------------------------------------------------------------------
+
+def _scalar_recurrence(a, rowsum, eps, iters):
+    """Every entry equals lam * a where all row and column sums are equal:
+    one column pass, then (iters - 1) x (row, column)."""
+    lam = 1.0
+    lam = lam / (lam * rowsum + eps)
+    for _ in range(iters - 1):
+        lam = lam / (lam * rowsum + eps)
+        lam = lam / (lam * rowsum + eps)
+    return lam * a
+
+
+def test_sinkhorn_constant_logits(oracle):
+    eps = 1e-3
+    for iters in (1, 2, 7, 20):
+        out = oracle.sinkhorn(np.full(16, 0.7), eps, iters)
+        a = 0.25 + eps
+        want = _scalar_recurrence(a, 4 * a, eps, iters)
+        np.testing.assert_allclose(out, want, rtol=1e-14)
+        assert np.all(out == out[0, 0])
+
+
+def test_sinkhorn_circulant_logits(oracle):
+    """Circulant logits give a circulant softmax: all row and column sums are
+    equal at every pass, so the result is the softmax (+eps) times a scalar."""
+    eps = 1e-2
+    f = np.array([0.3, -1.2, 2.0, 0.5])
+    logits = np.array([[f[(k - i) % 4] for k in range(4)] for i in range(4)])
+    e = np.exp(f - f.max())
+    row = e / e.sum() + eps
+    soft = np.array([[row[(k - i) % 4] for k in range(4)] for i in range(4)])
+    out = oracle.sinkhorn(logits, eps, 20)
+    lam = _scalar_recurrence(1.0, row.sum(), eps, 20)
+    np.testing.assert_allclose(out, soft * lam, rtol=1e-13)
+
+
+def _doubly_stochastic_scaling(A):
+    """diag(e^u) A diag(e^v) with unit row and column sums, solved as a root
+    of the scaling equations (v_0 = 0 fixes the free constant)."""
+    from scipy.optimize import root
+
+    def eqs(z):
+        u, v = z[:4], np.concatenate([[0.0], z[4:]])
+        P = np.exp(u)[:, None] * A * np.exp(v)[None, :]
+        return np.concatenate([P.sum(1) - 1.0, P.sum(0)[1:] - 1.0])
+
+    sol = root(eqs, np.zeros(7), method="lm", tol=1e-14)
+    assert np.abs(eqs(sol.x)).max() < 1e-12
+    u, v = sol.x[:4], np.concatenate([[0.0], sol.x[4:]])
+    return np.exp(u)[:, None] * A * np.exp(v)[None, :]
+
+
+def test_sinkhorn_limit_and_orientation(oracle):
+    """With eps 0 and many passes the iteration reaches the doubly stochastic
+    scaling of exp(logits) (Sinkhorn's theorem), with logit (i, k) at row i,
+    column k: for non-symmetric logits a transposed reading lands on the
+    transpose."""
+    rng = np.random.default_rng(21)
+    for _ in range(5):
+        B = rng.standard_normal((4, 4)) * 1.5
+        out = oracle.sinkhorn(B, 0.0, 3000)
+        want = _doubly_stochastic_scaling(np.exp(B))
+        np.testing.assert_allclose(out, want, atol=1e-9)
+        assert np.abs(want - want.T).max() > 1e-3
+
+
+def test_sinkhorn_softmax_runs_along_rows(oracle):
+    """iters = 1, eps 0: a row softmax then one column normalisation.  Columns
+    sum to 1, and the result is not the column softmax (which a softmax along
+    columns would leave unchanged)."""
+    B = np.array([[0.0, 1.0, 2.0, 3.0], [3.0, 0.5, -1.0, 0.0],
+                  [1.0, 1.0, -2.0, 0.5], [-1.0, 2.5, 0.0, 1.0]])
+    out = oracle.sinkhorn(B, 0.0, 1)
+    np.testing.assert_allclose(out.sum(0), 1.0, rtol=1e-15)
+    col_soft = np.exp(B) / np.exp(B).sum(0, keepdims=True)
+    assert np.abs(out - col_soft).max() > 1e-2
+    # ratios within a column are those of the row softmax: exp(B_ik - B_jk) Z_j / Z_i
+    Z = np.exp(B).sum(1)
+    for k in range(4):
+        np.testing.assert_allclose(out[:, k] / out[0, k],
+                                   np.exp(B[:, k] - B[0, k]) * Z[0] / Z, rtol=1e-13)
+
+
+def test_sinkhorn_final_column_sums(oracle):
+    """After the final column pass every column sums to S/(S+eps) < 1 with S
+    about 1; rows are close to 1 for the near-uniform logits of the configs."""
+    rng = np.random.default_rng(3)
+    eps = 1e-6
+    for _ in range(50):
+        out = oracle.sinkhorn(rng.standard_normal(16) * 0.3, eps, 20)
+        cs = out.sum(0)
+        assert np.all(cs < 1.0) and np.all(cs > 1.0 - 3 * eps)
+        assert np.all(np.abs(out.sum(1) - 1.0) < 1e-4)
+        assert np.all(out > 0)
+    # iters = 1: the column pass follows the softmax; with S_k the column sums of
+    # softmax + eps, the final column sums are S_k / (S_k + eps)
+    B = rng.standard_normal((4, 4)) * 3.0
+    out = oracle.sinkhorn(B, eps, 1)
+    S = (np.exp(B) / np.exp(B).sum(1, keepdims=True) + eps).sum(0)
+    np.testing.assert_allclose(out.sum(0), S / (S + eps), rtol=1e-14)
+
+
+# ---- layer input ------------------------------------------------------------------
+
+def test_layer_input_closed_form(oracle):
+    """li = c everywhere: rstd_li = 1/sqrt(c^2 + eps); with eps 0 the layer input
+    is bf16(sign(c) * norm_w) = sign(c) * norm_w exactly."""
+    c = 0.375
+    inp = _constant_xn(_tiny(T=2), c)
+    inp.pre_lag[:] = 0.0
+    inp.pre_lag[:, 2] = 1.0
+    r = oracle.run(True, inp.X, inp.x, inp.post_prev, inp.comb_prev, inp.pre_lag, inp.W,
+                   inp.scale, inp.base, inp.norm_w, dict(PARAMS, norm_eps=0.0))
+    assert np.all(bf16_vals(r["li"]) == c)
+    assert np.array_equal(r["layer_input"], np.broadcast_to(inp.norm_w, r["layer_input"].shape))
+    eps = float(np.float32(1e-6))
+    r = oracle.run(True, inp.X, inp.x, inp.post_prev, inp.comb_prev, inp.pre_lag, inp.W,
+                   inp.scale, inp.base, inp.norm_w, dict(PARAMS, norm_eps=eps))
+    k = Fraction(c) / Fraction(math.sqrt(c * c + eps))
+    for h in range(0, inp.d, 17):
+        want = rbf16(k * fr(bf16_vals(inp.norm_w[h])))
+        assert float(bf16_vals(r["layer_input"][0, h])) == float(want)
+
+
+def test_non_shifted_pre_collapses_with_fresh_pre(oracle):
+    """scale = 0 and bases (40, -200, -200, -200) with pre eps 0 give the fresh
+    pre (1, 0, 0, 0) in FP32, so the non-shifted layer input is stream 0 of X."""
+    inp = _tiny(T=3)
+    inp.scale[:] = 0.0
+    inp.base[:4] = [-200.0, 40.0, -200.0, -200.0]
+    r = oracle.run(False, inp.X, None, None, None, None, inp.W, inp.scale, inp.base, None,
+                   dict(PARAMS, pre_eps=0.0))
+    assert np.array_equal(r["layer_input"], inp.X[:, 1])
+    assert np.array_equal(r["xn"], inp.X)
