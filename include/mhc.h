@@ -1,0 +1,166 @@
+/*
+ * mhc.h -- C ABI of the MI355X (gfx950) mHC layer-boundary library.
+ *
+ * The manifold-constrained hyper-connection (mHC) boundary works on a residual
+ * of n_hc = 4 BF16 streams per token.  Per token t (streams s, j in 0..3,
+ * hidden h in 0..d-1, flat index k = s*d + h):
+ *
+ *   X'[s][h]  = bf16( FMA chain over j = 0..3 of comb[j][s]*X[j][h], started
+ *                     from post[s]*x[h] in FP32 )
+ *   mix[n]    = sum_k tf32(W)[n][k] * X'[k]                 (n = 0..23)
+ *   rstd      = 1 / sqrt( sum_k X'[k]^2 / (4d) + rms_eps )
+ *   pre[j]    = sigmoid( mix[j]*rstd*scale[0] + base[j] ) + pre_eps
+ *   post[j]   = post_mult * sigmoid( mix[4+j]*rstd*scale[1] + base[4+j] )
+ *   comb[i][k]= Sinkhorn of the logits mix[8+4i+k]*rstd*scale[2] + base[8+4i+k]:
+ *               row softmax + eps, one column normalisation, then
+ *               (sinkhorn_iters - 1) x (row, column) normalisations,
+ *               each normalisation dividing by (sum + sinkhorn_eps)
+ *   li[h]     = bf16( FMA chain over j = 0..3 of pre_lag[j]*X'[j][h], from 0 )
+ *   layer_input[h] = bf16( li[h] * rstd_li * norm_w[h] ),
+ *               rstd_li = 1 / sqrt( sum_h li[h]^2 / d + norm_eps );
+ *               layer_input = li when norm_w is NULL.
+ *
+ * Sources: the vLLM page "DeepSeek-V4.1 shifted mHC boundary for decode-size
+ * batches" (module description; residual_update; lagged_collapse;
+ * coefficients; sinkhorn; col_normalize; layer_input_words;
+ * prepare_boundary_weight; mhc_shifted_post_pre_boundary) and the blog "The
+ * Hyper Connection Preprocessing GPU Kernel Study" (Table 1 variable map;
+ * "square sum and RMSNorm"; "computing A_l", "computing C_l", "computing B_l";
+ * "computing layer_input A_l X_l"; "memory layout assumptions").
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers on the current HIP device, contiguous,
+ *     row-major, 16-byte aligned.  BF16 tensors are passed as uint16_t bit
+ *     patterns.  The caller allocates and owns every buffer and keeps it alive
+ *     until the work on `stream` has completed.  The library keeps no pointer
+ *     after it returns and allocates no device memory.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
+ *     asynchronously; the library never synchronises.
+ *   - Arguments are validated on the host before anything is enqueued; on any
+ *     error nothing is launched and no output is written.  Execution faults
+ *     surface at the caller's next synchronisation.
+ *   - Results are deterministic: every reduction runs in a fixed order, so
+ *     equal inputs give bitwise-equal outputs from call to call.
+ */
+#ifndef MHC_H
+#define MHC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MHC_ABI_VERSION 1
+#define MHC_N_HC 4          /* residual streams (the pages' hc_mult / kHc4) */
+#define MHC_MIXES 24        /* 4 pre + 4 post + 16 comb (the pages' kMixHc4) */
+#define MHC_MAX_TOKENS (1 << 20)
+#define MHC_MIN_HIDDEN 256
+#define MHC_MAX_HIDDEN 16384
+
+typedef enum {
+    MHC_OK = 0,
+    MHC_ERR_INVALID_ARGUMENT = 1, /* tokens <= 0, NULL required pointer, iters < 1, eps < 0 */
+    MHC_ERR_UNSUPPORTED_SHAPE = 2,/* hidden % 256 != 0, hidden outside [256, 16384], tokens > MHC_MAX_TOKENS */
+    MHC_ERR_MISALIGNED = 3,       /* a pointer not 16-byte aligned */
+    MHC_ERR_ALIASING = 4,         /* an output overlaps another output or an input */
+    MHC_ERR_WORKSPACE = 5,        /* workspace NULL or smaller than mhc_workspace_bytes() */
+    MHC_ERR_DEVICE = 6            /* a HIP call or kernel launch failed */
+} mhc_status;
+
+/* Scheduling choice for mhc_boundary (results are identical up to the
+ * accumulation order of the FP32 sums; each choice is deterministic). */
+typedef enum {
+    MHC_SCHEDULE_AUTO = 0,        /* pick by token count */
+    MHC_SCHEDULE_SPLIT = 1,       /* hidden split over many workgroups + finishing kernel */
+    MHC_SCHEDULE_FUSED = 2        /* one workgroup per 16-token tile owns all of hidden */
+} mhc_schedule;
+
+/* Runtime scalars (the pages pass them as kernel arguments). */
+typedef struct {
+    float rms_eps;        /* eps of the mix RMS (hc_norm_eps) */
+    float pre_eps;        /* added to sigmoid for pre (hc_pre_eps) */
+    float post_mult;      /* post scale (hc_post_scale), usually 2 */
+    float sinkhorn_eps;   /* softmax floor and normalisation eps */
+    int sinkhorn_iters;   /* >= 1: column passes; row passes = iters - 1 */
+    float norm_eps;       /* eps of the layer-input RMSNorm */
+    int schedule;         /* mhc_schedule; mhc_pre ignores it */
+} mhc_params;
+
+/* Bytes of the prepared weight for `hidden`: 384 * hidden (0 if unsupported).
+ *
+ * Layout (uint16 BF16 elements).  Element (step, s, m, l, e) with
+ * step in [0, hidden/32), s in [0,4), m in [0,3), l in [0,64), e in [0,8) sits at
+ *     ((((step*4 + s)*3 + m)*64 + l)*8 + e)
+ * and holds part P of mix n at column k of W, where
+ *     k = s*hidden + 32*step + 8*(l/16) + e,   r = l % 16,
+ *     n = 8*m + 2*(r/4) + (r % 2),   P = high if (r % 4) < 2 else low,
+ *     high = bf16(t), low = bf16(t - high), t = tf32(W[n][k]) (ties away).
+ * The 64 x 8 block of one (step, s, m) is the A operand of one
+ * 16x16x32 BF16 matrix-core product (row = l % 16, k group = l / 16): the
+ * result rows 4q+0 / 4q+2 hold the high / low products of mix 8m+2q and rows
+ * 4q+1 / 4q+3 those of mix 8m+2q+1.  high + low == t exactly, and every
+ * BF16 x BF16 product is exact in FP32, so the projection equals the TF32 one. */
+size_t mhc_prepared_weight_bytes(int hidden);
+
+/* Device workspace bytes that mhc_pre / mhc_boundary need for `tokens`
+ * tokens of `hidden` (partial sums of the split schedule). */
+size_t mhc_workspace_bytes(int tokens, int hidden);
+
+/* Round W to TF32, split it into BF16 high/low parts and write them in the
+ * layout above.  (prepare_boundary_weight on the vLLM page.)
+ *   w           [24, 4*hidden] FP32, rows = 4 pre | 4 post | 16 comb (row-major 4x4)
+ *   w_prepared  mhc_prepared_weight_bytes(hidden) bytes, written
+ * Errors: INVALID_ARGUMENT (NULL), UNSUPPORTED_SHAPE, MISALIGNED, ALIASING, DEVICE. */
+mhc_status mhc_prepare_weight(const float* w, int hidden, void* w_prepared, void* stream);
+
+/* Non-shifted mHC pre (the blog's mhc_pre_big_fuse, with the projection and
+ * the sum of squares computed here): X' = X, pre/post/comb from the mixes of
+ * X, and layer_input = bf16(FMA chain of the FRESH pre[j]*X[j]), then the
+ * optional RMSNorm with norm_w.
+ *   residual    [T, 4, hidden] BF16            (read)
+ *   w_prepared  from mhc_prepare_weight         (read)
+ *   scale [3], base [24] FP32                   (read)
+ *   norm_w      [hidden] BF16 or NULL           (read)
+ *   layer_input [T, hidden] BF16                (written)
+ *   pre, post   [T, 4] FP32; comb [T, 4, 4] FP32 (written; comb row i = source stream)
+ *   mixes       [T, 24] FP32 or NULL; rstd [T] FP32 or NULL (debug outputs)
+ *   workspace   >= mhc_workspace_bytes(T, hidden) bytes (scratch) */
+mhc_status mhc_pre(int tokens, int hidden, const uint16_t* residual, const void* w_prepared,
+                   const float* scale, const float* base, const uint16_t* norm_w,
+                   const mhc_params* params, uint16_t* layer_input, float* pre, float* post,
+                   float* comb, float* mixes, float* rstd, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/* Shifted mHC boundary (mhc_shifted_post_pre_boundary on the vLLM page):
+ * residual update with the previous layer's post/comb, projection, new
+ * pre/post/comb, and the layer input collapsed with the LAGGED pre.
+ *   x           [T, hidden] BF16 block output    (read)
+ *   residual    [T, 4, hidden] BF16              (read)
+ *   post_prev   [T, 4] FP32; comb_prev [T, 4, 4] FP32 (row j = source stream,
+ *               column s = destination stream); pre_lag [T, 4] FP32   (read)
+ *   w_prepared, scale, base, norm_w              as for mhc_pre
+ *   residual_out [T, 4, hidden] BF16 = X'        (written)
+ *   layer_input  [T, hidden] BF16                (written)
+ *   pre_out, post_out [T, 4]; comb_out [T, 4, 4] FP32 (written)
+ *   mixes, rstd, workspace                       as for mhc_pre */
+mhc_status mhc_boundary(int tokens, int hidden, const uint16_t* x, const uint16_t* residual,
+                        const float* post_prev, const float* comb_prev, const float* pre_lag,
+                        const void* w_prepared, const float* scale, const float* base,
+                        const uint16_t* norm_w, const mhc_params* params,
+                        uint16_t* residual_out, uint16_t* layer_input, float* pre_out,
+                        float* post_out, float* comb_out, float* mixes, float* rstd,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static text for a status code. */
+const char* mhc_status_string(mhc_status status);
+
+/* MHC_ABI_VERSION of the loaded library. */
+int mhc_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MHC_H */

@@ -1,0 +1,157 @@
+"""Python binding of libmhc.so (ctypes).  Argument marshalling only: every step
+of the boundary runs in the HIP kernels behind the C ABI.  torch supplies
+device memory and the current stream.  There is no fallback: if the library is
+missing, loading raises."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmhc.so")
+ABI_VERSION = 1
+
+SCHEDULES = {"auto": 0, "split": 1, "fused": 2}
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape", 3: "misaligned",
+          4: "aliasing", 5: "workspace", 6: "device"}
+
+
+class MhcError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: status {status} ({STATUS.get(status, '?')})")
+        self.status = status
+
+
+class Params(ctypes.Structure):
+    _fields_ = [("rms_eps", ctypes.c_float), ("pre_eps", ctypes.c_float),
+                ("post_mult", ctypes.c_float), ("sinkhorn_eps", ctypes.c_float),
+                ("sinkhorn_iters", ctypes.c_int), ("norm_eps", ctypes.c_float),
+                ("schedule", ctypes.c_int)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C ABI.  Raises if libmhc.so has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it first "
+                               "(python -m mhc_hyper_connection_boundary_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        L.mhc_abi_version.restype = I
+        L.mhc_abi_version.argtypes = []
+        L.mhc_status_string.restype = ctypes.c_char_p
+        L.mhc_status_string.argtypes = [I]
+        L.mhc_prepared_weight_bytes.restype = Z
+        L.mhc_prepared_weight_bytes.argtypes = [I]
+        L.mhc_workspace_bytes.restype = Z
+        L.mhc_workspace_bytes.argtypes = [I, I]
+        L.mhc_prepare_weight.restype = I
+        L.mhc_prepare_weight.argtypes = [P, I, P, P]
+        L.mhc_pre.restype = I
+        L.mhc_pre.argtypes = [I, I, P, P, P, P, P, P, P, P, P, P, P, P, P, Z, P]
+        L.mhc_boundary.restype = I
+        L.mhc_boundary.argtypes = [I, I, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, Z, P]
+        if L.mhc_abi_version() != ABI_VERSION:
+            raise RuntimeError("libmhc.so ABI version mismatch")
+        _lib = L
+    return _lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def params(rms_eps=1e-6, pre_eps=1e-6, post_mult=2.0, sinkhorn_eps=1e-6, sinkhorn_iters=20,
+           norm_eps=1e-6, schedule="auto") -> Params:
+    return Params(rms_eps, pre_eps, post_mult, sinkhorn_eps, sinkhorn_iters, norm_eps,
+                  SCHEDULES[schedule])
+
+
+def _check(fn, status):
+    if status != 0:
+        raise MhcError(fn, status)
+
+
+def prepared_weight_bytes(hidden: int) -> int:
+    return lib().mhc_prepared_weight_bytes(hidden)
+
+
+def workspace_bytes(tokens: int, hidden: int) -> int:
+    return lib().mhc_workspace_bytes(tokens, hidden)
+
+
+def workspace(tokens: int, hidden: int, device=None) -> torch.Tensor:
+    n = max(workspace_bytes(tokens, hidden), 16)
+    return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
+
+
+def prepare_weight(w: torch.Tensor) -> torch.Tensor:
+    """W [24, 4*hidden] FP32 (device) -> prepared uint8 tensor (384*hidden bytes)."""
+    hidden = w.shape[1] // 4
+    out = torch.empty(prepared_weight_bytes(hidden), dtype=torch.uint8, device=w.device)
+    _check("mhc_prepare_weight", lib().mhc_prepare_weight(_ptr(w), hidden, _ptr(out), _stream()))
+    return out
+
+
+def boundary(x, residual, post_prev, comb_prev, pre_lag, w_prepared, scale, base, norm_w=None,
+             *, prm: Params | None = None, debug: bool = False, ws: torch.Tensor | None = None,
+             out: dict | None = None):
+    """Shifted mHC boundary.  Returns (new_residual, new_post [T,4,1], new_comb [T,4,4],
+    layer_input, new_pre), plus (mixes, rstd) when debug=True."""
+    T, _, hidden = residual.shape
+    dev = residual.device
+    prm = prm or params()
+    o = out if out is not None else {}
+    nres = o.get("residual_out")
+    if nres is None:
+        nres = torch.empty_like(residual)
+    li = o.get("layer_input")
+    if li is None:
+        li = torch.empty(T, hidden, dtype=torch.bfloat16, device=dev)
+    pre = torch.empty(T, 4, dtype=torch.float32, device=dev) if "pre" not in o else o["pre"]
+    post = torch.empty(T, 4, 1, dtype=torch.float32, device=dev) if "post" not in o else o["post"]
+    comb = torch.empty(T, 4, 4, dtype=torch.float32, device=dev) if "comb" not in o else o["comb"]
+    mixes = torch.empty(T, 24, dtype=torch.float32, device=dev) if debug else None
+    rstd = torch.empty(T, dtype=torch.float32, device=dev) if debug else None
+    if ws is None:
+        ws = workspace(T, hidden, dev)
+    _check("mhc_boundary", lib().mhc_boundary(
+        T, hidden, _ptr(x), _ptr(residual), _ptr(post_prev), _ptr(comb_prev), _ptr(pre_lag),
+        _ptr(w_prepared), _ptr(scale), _ptr(base), _ptr(norm_w), ctypes.byref(prm),
+        _ptr(nres), _ptr(li), _ptr(pre), _ptr(post), _ptr(comb), _ptr(mixes), _ptr(rstd),
+        _ptr(ws), ws.numel(), _stream()))
+    res = (nres, post, comb, li, pre)
+    return res + (mixes, rstd) if debug else res
+
+
+def pre(residual, w_prepared, scale, base, norm_w=None, *, prm: Params | None = None,
+        debug: bool = False, ws: torch.Tensor | None = None):
+    """Non-shifted mHC pre.  Returns (layer_input, pre, post [T,4,1], comb [T,4,4]),
+    plus (mixes, rstd) when debug=True."""
+    T, _, hidden = residual.shape
+    dev = residual.device
+    prm = prm or params()
+    li = torch.empty(T, hidden, dtype=torch.bfloat16, device=dev)
+    pr = torch.empty(T, 4, dtype=torch.float32, device=dev)
+    post = torch.empty(T, 4, 1, dtype=torch.float32, device=dev)
+    comb = torch.empty(T, 4, 4, dtype=torch.float32, device=dev)
+    mixes = torch.empty(T, 24, dtype=torch.float32, device=dev) if debug else None
+    rstd = torch.empty(T, dtype=torch.float32, device=dev) if debug else None
+    if ws is None:
+        ws = workspace(T, hidden, dev)
+    _check("mhc_pre", lib().mhc_pre(
+        T, hidden, _ptr(residual), _ptr(w_prepared), _ptr(scale), _ptr(base), _ptr(norm_w),
+        ctypes.byref(prm), _ptr(li), _ptr(pr), _ptr(post), _ptr(comb), _ptr(mixes), _ptr(rstd),
+        _ptr(ws), ws.numel(), _stream()))
+    res = (li, pr, post, comb)
+    return res + (mixes, rstd) if debug else res

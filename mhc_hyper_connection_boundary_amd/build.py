@@ -1,0 +1,43 @@
+"""Builds libmhc.so (the HIP kernels and the C ABI) for gfx950 with hipcc."""
+from __future__ import annotations
+
+import os
+import subprocess
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIB = os.path.join(PKG, "libmhc.so")
+SOURCES = ["mhc_api.hip", "mhc_kernels.hip"]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-ffp-contract=off",
+    # packed FP32 instructions stay off (v_pk_fma_f32 and friends are not used)
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+]
+
+
+def build(verbose: bool = False, resource_usage: bool = False) -> str:
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), *srcs, "-o", LIB + ".tmp"]
+    if resource_usage:
+        cmd.insert(1, "-Rpass-analysis=kernel-resource-usage")
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
+                     if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed:\n{msgs}")
+    if verbose and msgs.strip():
+        print(msgs)
+    os.replace(LIB + ".tmp", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    import sys
+    build(verbose=True, resource_usage="--resources" in sys.argv)

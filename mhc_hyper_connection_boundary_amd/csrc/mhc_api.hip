@@ -1,0 +1,218 @@
+// C ABI of the mHC boundary library: host-side validation, scheduling and
+// launches.  Validation is pure host code that makes no HIP call, so every
+// refusal happens before anything is enqueued.
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "../../include/mhc.h"
+#include "mhc_device.h"
+#include "mhc_launch.h"
+
+namespace mhc {
+
+namespace {
+
+constexpr long kTargetWaves = 2048;  // waves of k_partial work to aim for
+constexpr int kFinishTarget = 512;   // k_finish workgroups to aim for
+
+int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
+
+bool shape_ok(int hidden) {
+    return hidden >= MHC_MIN_HIDDEN && hidden <= MHC_MAX_HIDDEN && hidden % 256 == 0;
+}
+
+bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Span {
+    const void* p;
+    size_t bytes;
+};
+
+bool overlap(const Span& a, const Span& b) {
+    if (!a.p || !b.p || !a.bytes || !b.bytes) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+    return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+// Each output must be disjoint from every other output and every input.
+bool any_alias(const Span* outs, int n_out, const Span* ins, int n_in) {
+    for (int i = 0; i < n_out; ++i) {
+        for (int j = i + 1; j < n_out; ++j)
+            if (overlap(outs[i], outs[j])) return true;
+        for (int j = 0; j < n_in; ++j)
+            if (overlap(outs[i], ins[j])) return true;
+    }
+    return false;
+}
+
+mhc_status check_params(const mhc_params* p) {
+    if (!p) return MHC_ERR_INVALID_ARGUMENT;
+    if (p->sinkhorn_iters < 1) return MHC_ERR_INVALID_ARGUMENT;
+    if (!(p->rms_eps >= 0.f) || !(p->pre_eps >= 0.f) || !(p->sinkhorn_eps >= 0.f) ||
+        !(p->norm_eps >= 0.f) || !(p->post_mult == p->post_mult))
+        return MHC_ERR_INVALID_ARGUMENT;
+    if (p->schedule < MHC_SCHEDULE_AUTO || p->schedule > MHC_SCHEDULE_FUSED)
+        return MHC_ERR_INVALID_ARGUMENT;
+    return MHC_OK;
+}
+
+Scalars scalars(const mhc_params* p) {
+    Scalars s;
+    s.rms_eps = p->rms_eps;
+    s.pre_eps = p->pre_eps;
+    s.post_mult = p->post_mult;
+    s.sinkhorn_eps = p->sinkhorn_eps;
+    s.sinkhorn_iters = p->sinkhorn_iters;
+    s.norm_eps = p->norm_eps;
+    return s;
+}
+
+}  // namespace
+
+SplitPlan split_plan(int T, int hidden) {
+    SplitPlan plan;
+    const int nsteps = hidden / kStep;
+    const int tiles = ceil_div(T, kTile);
+    const long wave_steps = (long)tiles * nsteps;
+    int spw = (int)std::max<long>(1, wave_steps / kTargetWaves);
+    spw = std::min(spw, ceil_div(nsteps, 4));
+    plan.steps_per_wave = spw;
+    plan.slices = ceil_div(nsteps, 4L * spw);
+    int fs = std::max(1, std::min(ceil_div(kFinishTarget, tiles), hidden / 256));
+    plan.finish_width = ceil_div(ceil_div(hidden, fs), 8) * 8;
+    plan.finish_slices = ceil_div(hidden, plan.finish_width);
+    return plan;
+}
+
+size_t split_workspace_bytes(int T, int hidden) {
+    return (size_t)T * split_plan(T, hidden).slices * kPart * sizeof(float);
+}
+
+}  // namespace mhc
+
+using namespace mhc;
+
+extern "C" {
+
+int mhc_abi_version(void) { return MHC_ABI_VERSION; }
+
+const char* mhc_status_string(mhc_status s) {
+    switch (s) {
+        case MHC_OK: return "ok";
+        case MHC_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case MHC_ERR_UNSUPPORTED_SHAPE: return "unsupported shape";
+        case MHC_ERR_MISALIGNED: return "pointer not 16-byte aligned";
+        case MHC_ERR_ALIASING: return "output overlaps another buffer";
+        case MHC_ERR_WORKSPACE: return "workspace missing or too small";
+        case MHC_ERR_DEVICE: return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+size_t mhc_prepared_weight_bytes(int hidden) {
+    return shape_ok(hidden) ? (size_t)384 * hidden : 0;
+}
+
+size_t mhc_workspace_bytes(int tokens, int hidden) {
+    if (tokens <= 0 || tokens > MHC_MAX_TOKENS || !shape_ok(hidden)) return 0;
+    return split_workspace_bytes(tokens, hidden);
+}
+
+mhc_status mhc_prepare_weight(const float* w, int hidden, void* w_prepared, void* stream) {
+    if (!w || !w_prepared) return MHC_ERR_INVALID_ARGUMENT;
+    if (!shape_ok(hidden)) return MHC_ERR_UNSUPPORTED_SHAPE;
+    if (!aligned(w) || !aligned(w_prepared)) return MHC_ERR_MISALIGNED;
+    const Span out{w_prepared, mhc_prepared_weight_bytes(hidden)};
+    const Span in{w, (size_t)24 * 4 * hidden * sizeof(float)};
+    if (overlap(out, in)) return MHC_ERR_ALIASING;
+    if (launch_prepare_weight(w, hidden, w_prepared, (hipStream_t)stream) != hipSuccess)
+        return MHC_ERR_DEVICE;
+    return MHC_OK;
+}
+
+mhc_status mhc_pre(int tokens, int hidden, const uint16_t* residual, const void* w_prepared,
+                   const float* scale, const float* base, const uint16_t* norm_w,
+                   const mhc_params* params, uint16_t* layer_input, float* pre, float* post,
+                   float* comb, float* mixes, float* rstd, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+    mhc_status st = check_params(params);
+    if (st != MHC_OK) return st;
+    if (tokens <= 0) return MHC_ERR_INVALID_ARGUMENT;
+    if (!residual || !w_prepared || !scale || !base || !layer_input || !pre || !post || !comb)
+        return MHC_ERR_INVALID_ARGUMENT;
+    if (tokens > MHC_MAX_TOKENS || !shape_ok(hidden)) return MHC_ERR_UNSUPPORTED_SHAPE;
+    const void* ptrs[] = {residual, w_prepared, scale, base, norm_w, layer_input, pre, post,
+                          comb, mixes, rstd, workspace};
+    for (const void* q : ptrs)
+        if (q && !aligned(q)) return MHC_ERR_MISALIGNED;
+    const size_t T = tokens, d = hidden;
+    const size_t need = mhc_workspace_bytes(tokens, hidden);
+    const Span outs[] = {{layer_input, T * d * 2}, {pre, T * 16}, {post, T * 16}, {comb, T * 64},
+                         {mixes, mixes ? T * 96 : 0}, {rstd, rstd ? T * 4 : 0},
+                         {workspace, need}};
+    const Span ins[] = {{residual, T * 4 * d * 2}, {w_prepared, 384 * d}, {scale, 12},
+                        {base, 96}, {norm_w, norm_w ? d * 2 : 0}};
+    if (any_alias(outs, 7, ins, 5)) return MHC_ERR_ALIASING;
+    if (!workspace || workspace_bytes < need) return MHC_ERR_WORKSPACE;
+
+    const SplitPlan plan = split_plan(tokens, hidden);
+    const Scalars s = scalars(params);
+    hipStream_t hs = (hipStream_t)stream;
+    float* part = static_cast<float*>(workspace);
+    if (launch_partial(false, plan, tokens, hidden, nullptr, residual, nullptr, nullptr, nullptr,
+                       w_prepared, nullptr, nullptr, part, hs) != hipSuccess)
+        return MHC_ERR_DEVICE;
+    if (launch_pre_finish(plan, tokens, hidden, residual, part, scale, base, norm_w, s,
+                          layer_input, pre, post, comb, mixes, rstd, hs) != hipSuccess)
+        return MHC_ERR_DEVICE;
+    return MHC_OK;
+}
+
+mhc_status mhc_boundary(int tokens, int hidden, const uint16_t* x, const uint16_t* residual,
+                        const float* post_prev, const float* comb_prev, const float* pre_lag,
+                        const void* w_prepared, const float* scale, const float* base,
+                        const uint16_t* norm_w, const mhc_params* params,
+                        uint16_t* residual_out, uint16_t* layer_input, float* pre_out,
+                        float* post_out, float* comb_out, float* mixes, float* rstd,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+    mhc_status st = check_params(params);
+    if (st != MHC_OK) return st;
+    if (tokens <= 0) return MHC_ERR_INVALID_ARGUMENT;
+    if (!x || !residual || !post_prev || !comb_prev || !pre_lag || !w_prepared || !scale ||
+        !base || !residual_out || !layer_input || !pre_out || !post_out || !comb_out)
+        return MHC_ERR_INVALID_ARGUMENT;
+    if (tokens > MHC_MAX_TOKENS || !shape_ok(hidden)) return MHC_ERR_UNSUPPORTED_SHAPE;
+    const void* ptrs[] = {x, residual, post_prev, comb_prev, pre_lag, w_prepared, scale, base,
+                          norm_w, residual_out, layer_input, pre_out, post_out, comb_out,
+                          mixes, rstd, workspace};
+    for (const void* q : ptrs)
+        if (q && !aligned(q)) return MHC_ERR_MISALIGNED;
+    const size_t T = tokens, d = hidden;
+    const size_t need = mhc_workspace_bytes(tokens, hidden);
+    const Span outs[] = {{residual_out, T * 4 * d * 2}, {layer_input, T * d * 2},
+                         {pre_out, T * 16}, {post_out, T * 16}, {comb_out, T * 64},
+                         {mixes, mixes ? T * 96 : 0}, {rstd, rstd ? T * 4 : 0},
+                         {workspace, need}};
+    const Span ins[] = {{x, T * d * 2}, {residual, T * 4 * d * 2}, {post_prev, T * 16},
+                        {comb_prev, T * 64}, {pre_lag, T * 16}, {w_prepared, 384 * d},
+                        {scale, 12}, {base, 96}, {norm_w, norm_w ? d * 2 : 0}};
+    if (any_alias(outs, 8, ins, 9)) return MHC_ERR_ALIASING;
+    if (!workspace || workspace_bytes < need) return MHC_ERR_WORKSPACE;
+
+    const SplitPlan plan = split_plan(tokens, hidden);
+    const Scalars s = scalars(params);
+    hipStream_t hs = (hipStream_t)stream;
+    float* part = static_cast<float*>(workspace);
+    // layer_input first receives li; the finishing kernel rescales it in place.
+    if (launch_partial(true, plan, tokens, hidden, x, residual, post_prev, comb_prev, pre_lag,
+                       w_prepared, residual_out, layer_input, part, hs) != hipSuccess)
+        return MHC_ERR_DEVICE;
+    if (launch_finish(plan, tokens, hidden, part, scale, base, norm_w, s, layer_input, pre_out,
+                      post_out, comb_out, mixes, rstd, hs) != hipSuccess)
+        return MHC_ERR_DEVICE;
+    return MHC_OK;
+}
+
+}  // extern "C"

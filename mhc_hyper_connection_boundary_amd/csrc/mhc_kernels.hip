@@ -1,0 +1,370 @@
+// gfx950 kernels of the mHC boundary and their host-side launchers.
+//
+// Split schedule (any token count):
+//   k_partial   one workgroup = 4 waves on one 16-token tile and a contiguous
+//               run of hidden steps.  Each wave streams its steps: 16-byte
+//               loads of X and x, residual update, lagged collapse, stores of
+//               X' and li, sums of squares, and the projection on the matrix
+//               cores.  The 4 waves' partials are combined in LDS in a fixed
+//               order and written as one record per (token, slice).
+//   k_finish    one workgroup per (tile, hidden slice): sums the records of
+//               its tokens over the slices in slice order, forms rstd_li and
+//               rescales li into the layer input; the slice-0 workgroup also
+//               computes pre / post / Sinkhorn comb (one quad per token).
+//   k_pre_finish (non-shifted pre) one workgroup per token: coefficients
+//               first, then the collapse with the fresh pre and the RMSNorm.
+// Weight preparation: k_prepare_weight.
+#include "mhc_device.h"
+#include "mhc_launch.h"
+
+namespace mhc {
+namespace {
+
+// ---------------------------------------------------------------------------
+// Weight preparation: one thread per 16-byte A-operand word (8 BF16).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float tf32_ties_away(float w) {
+    return __uint_as_float((__float_as_uint(w) + 0x1000u) & 0xFFFFE000u);
+}
+
+__global__ __launch_bounds__(256) void k_prepare_weight(const float* __restrict__ w, int hidden,
+                                                        uint4* __restrict__ out, int n_words) {
+    const int o = blockIdx.x * blockDim.x + threadIdx.x;
+    if (o >= n_words) return;
+    const int l = o % 64;
+    const int m = (o / 64) % 3;
+    const int s = (o / 192) % 4;
+    const int step = o / 768;
+    const int r = l % 16;
+    const int mix = 8 * m + 2 * (r / 4) + (r % 2);
+    const bool high = (r % 4) < 2;
+    const size_t k = (size_t)s * hidden + 32 * step + 8 * (l / 16);
+    const float* src = w + (size_t)mix * 4 * hidden + k;
+    uint32_t words[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        float part[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const float t = tf32_ties_away(src[2 * p + e]);
+            const float hi = bf_lo((uint32_t)(pack_bf16(t, 0.0f) & 0xFFFFu));
+            part[e] = high ? hi : t - hi;
+        }
+        words[p] = pack_bf16(part[0], part[1]);
+    }
+    out[o] = make_uint4(words[0], words[1], words[2], words[3]);
+}
+
+// ---------------------------------------------------------------------------
+// Split schedule, kernel 1: partial sums over a run of hidden steps.
+// ---------------------------------------------------------------------------
+template <bool SHIFTED>
+__global__ __launch_bounds__(256) void k_partial(
+    int T, int hidden, int steps_per_wave, int slices, const uint16_t* __restrict__ x,
+    const uint16_t* __restrict__ X, const float* __restrict__ post_prev,
+    const float* __restrict__ comb_prev, const float* __restrict__ pre_lag,
+    const uint4* __restrict__ wprep, uint16_t* __restrict__ xn_out,
+    uint16_t* __restrict__ li_out, float* __restrict__ part) {
+    __shared__ float red[4][kTile][24];
+    __shared__ float sq[4][4][kTile][2];
+
+    const int tile = blockIdx.x;
+    const int slice = blockIdx.y;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 15;
+    const int g = lane >> 4;
+    const int t = tile * kTile + n;
+    const bool valid = t < T;
+    const size_t tc = valid ? (size_t)t : (size_t)(T - 1);
+
+    PrevCoef c;
+    if (SHIFTED) load_prev(c, post_prev, comb_prev, pre_lag, tc);
+
+    const int nsteps = hidden / kStep;
+    const int s0 = (slice * 4 + wave) * steps_per_wave;
+    const int s1 = min(s0 + steps_per_wave, nsteps);
+
+    f32x4_t acc[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    float ssq = 0.0f, ssq_li = 0.0f;
+    const uint16_t* Xrow = X + tc * 4 * hidden;
+    const uint16_t* xrow = SHIFTED ? x + tc * hidden : nullptr;
+
+    for (int step = s0; step < s1; ++step) {
+        const int h = step * kStep + g * 8;
+        uint4 Xv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            Xv[j] = *reinterpret_cast<const uint4*>(Xrow + (size_t)j * hidden + h);
+        uint4 xv = make_uint4(0, 0, 0, 0);
+        if (SHIFTED) xv = *reinterpret_cast<const uint4*>(xrow + h);
+        uint4 A[kFragsPerStep];
+        const uint4* wp = wprep + (size_t)step * kFragsPerStep * 64 + lane;
+#pragma unroll
+        for (int i = 0; i < kFragsPerStep; ++i) A[i] = wp[i * 64];
+
+        uint4 Xn[4];
+        if (SHIFTED) {
+            uint4 li;
+            update_collapse(Xv, xv, c, Xn, li, ssq, ssq_li);
+            if (valid) {
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    *reinterpret_cast<uint4*>(xn_out + (tc * 4 + s) * hidden + h) = Xn[s];
+                *reinterpret_cast<uint4*>(li_out + tc * hidden + h) = li;
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) Xn[s] = Xv[s];
+            square_sum(Xv, ssq);
+        }
+        mfma_step(A, Xn, acc);
+    }
+
+    // Combine the 4 waves in a fixed order: waves ascending, lane groups ascending.
+#pragma unroll
+    for (int m = 0; m < 3; ++m)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) red[wave][n][8 * m + 2 * g + j] = mix_of(acc, m, j);
+    sq[wave][g][n][0] = ssq;
+    sq[wave][g][n][1] = ssq_li;
+    __syncthreads();
+    for (int i = threadIdx.x; i < kTile * 26; i += blockDim.x) {
+        const int tn = i / 26, v = i % 26;
+        float sum;
+        if (v < 24) {
+            sum = ((red[0][tn][v] + red[1][tn][v]) + red[2][tn][v]) + red[3][tn][v];
+        } else {
+            sum = 0.0f;
+            for (int w = 0; w < 4; ++w)
+                for (int q = 0; q < 4; ++q) sum += sq[w][q][tn][v - 24];
+        }
+        const int tt = tile * kTile + tn;
+        if (tt < T) part[((size_t)tt * slices + slice) * kPart + v] = sum;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Split schedule, kernel 2: totals, coefficients, layer input.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_finish(
+    int T, int hidden, int slices, int slice_width, const float* __restrict__ part,
+    const float* __restrict__ scale, const float* __restrict__ base,
+    const uint16_t* __restrict__ norm_w, Scalars p, uint16_t* __restrict__ layer_input,
+    float* __restrict__ pre_out, float* __restrict__ post_out, float* __restrict__ comb_out,
+    float* __restrict__ mixes_out, float* __restrict__ rstd_out) {
+    __shared__ float tot[kTile][26];
+    __shared__ float rli[kTile];
+
+    const int tile = blockIdx.x;
+    const int hs = blockIdx.y;
+    const int tid = threadIdx.x;
+    const bool coef_wg = hs == 0;
+
+    for (int i = tid; i < kTile * 26; i += blockDim.x) {
+        const int tn = i / 26, v = i % 26;
+        if (!coef_wg && v != 25) continue;
+        const int t = tile * kTile + tn;
+        float sum = 0.0f;
+        if (t < T) {
+            const float* src = part + (size_t)t * slices * kPart + v;
+            for (int q = 0; q < slices; ++q) sum += src[(size_t)q * kPart];
+        }
+        tot[tn][v] = sum;
+    }
+    __syncthreads();
+    if (tid < kTile) rli[tid] = 1.0f / sqrtf(tot[tid][25] / (float)hidden + p.norm_eps);
+    __syncthreads();
+
+    if (coef_wg && tid < 64) {
+        const int tn = tid >> 2, i = tid & 3;
+        const int t = tile * kTile + tn;
+        const TokenCoef o = coefficients(tot[tn], i, hidden, scale, base, p);
+        if (t < T) {
+            pre_out[(size_t)t * 4 + i] = o.pre;
+            post_out[(size_t)t * 4 + i] = o.post;
+            *reinterpret_cast<float4*>(comb_out + (size_t)t * 16 + 4 * i) =
+                make_float4(o.row[0], o.row[1], o.row[2], o.row[3]);
+            if (mixes_out)
+                for (int k = 0; k < 6; ++k) mixes_out[(size_t)t * 24 + 6 * i + k] = tot[tn][6 * i + k];
+            if (rstd_out && i == 0) rstd_out[t] = o.rstd;
+        }
+        return;
+    }
+    if (!norm_w) return;  // layer_input already holds li
+    const int h0 = hs * slice_width;
+    const int width = min(slice_width, hidden - h0);
+    if (width <= 0) return;
+    const int chunks = width / 8;
+    const int first = coef_wg ? tid - 64 : tid;
+    const int stride = coef_wg ? (int)blockDim.x - 64 : (int)blockDim.x;
+    for (int u = first; u < kTile * chunks; u += stride) {
+        const int tn = u / chunks, cidx = u % chunks;
+        const int t = tile * kTile + tn;
+        if (t >= T) break;
+        const int h = h0 + cidx * 8;
+        uint4* dst = reinterpret_cast<uint4*>(layer_input + (size_t)t * hidden + h);
+        const uint4 li = *dst;
+        const uint4 nw = *reinterpret_cast<const uint4*>(norm_w + h);
+        const float r = rli[tn];
+        uint4 out;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t a = word(li, q), b = word(nw, q);
+            set_word(out, q, pack_bf16((bf_lo(a) * r) * bf_lo(b), (bf_hi(a) * r) * bf_hi(b)));
+        }
+        *dst = out;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Non-shifted pre, kernel 2: one workgroup (256 threads) per token.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_pre_finish(
+    int T, int hidden, int slices, const uint16_t* __restrict__ X, const float* __restrict__ part,
+    const float* __restrict__ scale, const float* __restrict__ base,
+    const uint16_t* __restrict__ norm_w, Scalars p, uint16_t* __restrict__ layer_input,
+    float* __restrict__ pre_out, float* __restrict__ post_out, float* __restrict__ comb_out,
+    float* __restrict__ mixes_out, float* __restrict__ rstd_out) {
+    extern __shared__ uint4 li_s[];  // [hidden / 8] when norm_w is given
+    __shared__ float tot[26];
+    __shared__ float pre_s[4];
+    __shared__ float red[192];
+    __shared__ float rli;
+
+    const int t = blockIdx.x;
+    const int tid = threadIdx.x;
+    if (tid < 25) {
+        const float* src = part + (size_t)t * slices * kPart + tid;
+        float sum = 0.0f;
+        for (int q = 0; q < slices; ++q) sum += src[(size_t)q * kPart];
+        tot[tid] = sum;
+    }
+    __syncthreads();
+    TokenCoef o;
+    if (tid < 4) {
+        o = coefficients(tot, tid, hidden, scale, base, p);
+        pre_s[tid] = o.pre;
+    }
+    __syncthreads();  // only pre is needed by the collapse
+    if (tid < 64) {
+        if (tid < 4) {
+            pre_out[(size_t)t * 4 + tid] = o.pre;
+            post_out[(size_t)t * 4 + tid] = o.post;
+            *reinterpret_cast<float4*>(comb_out + (size_t)t * 16 + 4 * tid) =
+                make_float4(o.row[0], o.row[1], o.row[2], o.row[3]);
+            if (mixes_out)
+                for (int k = 0; k < 6; ++k) mixes_out[(size_t)t * 24 + 6 * tid + k] = tot[6 * tid + k];
+            if (rstd_out && tid == 0) rstd_out[t] = o.rstd;
+        }
+    } else {
+        const int u0 = tid - 64;
+        const float pr[4] = {pre_s[0], pre_s[1], pre_s[2], pre_s[3]};
+        const uint16_t* Xrow = X + (size_t)t * 4 * hidden;
+        float ssq_li = 0.0f;
+        for (int cidx = u0; cidx < hidden / 8; cidx += 192) {
+            const int h = cidx * 8;
+            uint4 Xv[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                Xv[j] = *reinterpret_cast<const uint4*>(Xrow + (size_t)j * hidden + h);
+            uint4 li;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float acc[2];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    acc[e] = 0.0f;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t w = word(Xv[j], q);
+                        acc[e] = __builtin_fmaf(pr[j], e ? bf_hi(w) : bf_lo(w), acc[e]);
+                    }
+                }
+                const uint32_t lw = pack_bf16(acc[0], acc[1]);
+                set_word(li, q, lw);
+                ssq_li = __builtin_fmaf(bf_lo(lw), bf_lo(lw), ssq_li);
+                ssq_li = __builtin_fmaf(bf_hi(lw), bf_hi(lw), ssq_li);
+            }
+            if (norm_w) li_s[cidx] = li;
+            else *reinterpret_cast<uint4*>(layer_input + (size_t)t * hidden + h) = li;
+        }
+        red[u0] = ssq_li;
+    }
+    if (!norm_w) return;
+    __syncthreads();
+    if (tid == 0) {
+        float s = 0.0f;
+        for (int i = 0; i < 192; ++i) s += red[i];
+        rli = 1.0f / sqrtf(s / (float)hidden + p.norm_eps);
+    }
+    __syncthreads();
+    const float r = rli;
+    for (int cidx = tid; cidx < hidden / 8; cidx += blockDim.x) {
+        const int h = cidx * 8;
+        const uint4 li = li_s[cidx];
+        const uint4 nw = *reinterpret_cast<const uint4*>(norm_w + h);
+        uint4 out;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t a = word(li, q), b = word(nw, q);
+            set_word(out, q, pack_bf16((bf_lo(a) * r) * bf_lo(b), (bf_hi(a) * r) * bf_hi(b)));
+        }
+        *reinterpret_cast<uint4*>(layer_input + (size_t)t * hidden + h) = out;
+    }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Launchers (host).  Shapes were validated by the caller.
+// ---------------------------------------------------------------------------
+hipError_t launch_prepare_weight(const float* w, int hidden, void* out, hipStream_t stream) {
+    const int n_words = (hidden / kStep) * kFragsPerStep * 64;
+    hipLaunchKernelGGL(k_prepare_weight, dim3((n_words + 255) / 256), dim3(256), 0, stream, w,
+                       hidden, reinterpret_cast<uint4*>(out), n_words);
+    return hipGetLastError();
+}
+
+hipError_t launch_partial(bool shifted, const SplitPlan& plan, int T, int hidden,
+                          const uint16_t* x, const uint16_t* X, const float* post_prev,
+                          const float* comb_prev, const float* pre_lag, const void* wprep,
+                          uint16_t* xn_out, uint16_t* li_out, float* part, hipStream_t stream) {
+    const dim3 grid((T + kTile - 1) / kTile, plan.slices);
+    const uint4* w = reinterpret_cast<const uint4*>(wprep);
+    if (shifted)
+        hipLaunchKernelGGL(k_partial<true>, grid, dim3(256), 0, stream, T, hidden,
+                           plan.steps_per_wave, plan.slices, x, X, post_prev, comb_prev, pre_lag,
+                           w, xn_out, li_out, part);
+    else
+        hipLaunchKernelGGL(k_partial<false>, grid, dim3(256), 0, stream, T, hidden,
+                           plan.steps_per_wave, plan.slices, nullptr, X, nullptr, nullptr,
+                           nullptr, w, nullptr, nullptr, part);
+    return hipGetLastError();
+}
+
+hipError_t launch_finish(const SplitPlan& plan, int T, int hidden, const float* part,
+                         const float* scale, const float* base, const uint16_t* norm_w,
+                         const Scalars& p, uint16_t* layer_input, float* pre_out,
+                         float* post_out, float* comb_out, float* mixes, float* rstd,
+                         hipStream_t stream) {
+    const dim3 grid((T + kTile - 1) / kTile, plan.finish_slices);
+    hipLaunchKernelGGL(k_finish, grid, dim3(256), 0, stream, T, hidden, plan.slices,
+                       plan.finish_width, part, scale, base, norm_w, p, layer_input, pre_out,
+                       post_out, comb_out, mixes, rstd);
+    return hipGetLastError();
+}
+
+hipError_t launch_pre_finish(const SplitPlan& plan, int T, int hidden, const uint16_t* X,
+                             const float* part, const float* scale, const float* base,
+                             const uint16_t* norm_w, const Scalars& p, uint16_t* layer_input,
+                             float* pre_out, float* post_out, float* comb_out, float* mixes,
+                             float* rstd, hipStream_t stream) {
+    const size_t lds = norm_w ? (size_t)hidden * 2 : 0;
+    hipLaunchKernelGGL(k_pre_finish, dim3(T), dim3(256), lds, stream, T, hidden, plan.slices, X,
+                       part, scale, base, norm_w, p, layer_input, pre_out, post_out, comb_out,
+                       mixes, rstd);
+    return hipGetLastError();
+}
+
+}  // namespace mhc

@@ -1,0 +1,46 @@
+// Host-side launch interface between the C ABI and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mhc {
+
+struct Scalars;
+
+// Work split of the split schedule for (T, hidden):
+//   k_partial: grid (tiles, slices); wave w of slice q covers hidden steps
+//              [(4q + w) * steps_per_wave, ... + steps_per_wave) of 32 elements.
+//   k_finish:  grid (tiles, finish_slices); workgroup q rescales hidden
+//              [q * finish_width, (q + 1) * finish_width).
+struct SplitPlan {
+    int steps_per_wave;
+    int slices;
+    int finish_slices;
+    int finish_width;
+};
+
+SplitPlan split_plan(int T, int hidden);
+size_t split_workspace_bytes(int T, int hidden);
+
+hipError_t launch_prepare_weight(const float* w, int hidden, void* out, hipStream_t stream);
+
+hipError_t launch_partial(bool shifted, const SplitPlan& plan, int T, int hidden,
+                          const uint16_t* x, const uint16_t* X, const float* post_prev,
+                          const float* comb_prev, const float* pre_lag, const void* wprep,
+                          uint16_t* xn_out, uint16_t* li_out, float* part, hipStream_t stream);
+
+hipError_t launch_finish(const SplitPlan& plan, int T, int hidden, const float* part,
+                         const float* scale, const float* base, const uint16_t* norm_w,
+                         const Scalars& p, uint16_t* layer_input, float* pre_out,
+                         float* post_out, float* comb_out, float* mixes, float* rstd,
+                         hipStream_t stream);
+
+hipError_t launch_pre_finish(const SplitPlan& plan, int T, int hidden, const uint16_t* X,
+                             const float* part, const float* scale, const float* base,
+                             const uint16_t* norm_w, const Scalars& p, uint16_t* layer_input,
+                             float* pre_out, float* post_out, float* comb_out, float* mixes,
+                             float* rstd, hipStream_t stream);
+
+}  // namespace mhc

@@ -1,0 +1,126 @@
+"""The C ABI on the host: the library loads, exports every entry point that
+include/mhc.h declares, and refuses bad arguments before any HIP call (these
+tests pass fake, never-dereferenced device addresses and run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mhc_hyper_connection_boundary_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mhc.h")
+
+OK, INVALID, SHAPE, MISALIGNED, ALIASING, WORKSPACE = 0, 1, 2, 3, 4, 5
+T, D = 32, 1024
+GB = 1 << 30
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mhc_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return api.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert {"mhc_prepare_weight", "mhc_pre", "mhc_boundary"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.mhc_abi_version() == 1
+    assert L.mhc_status_string(3) == b"pointer not 16-byte aligned"
+
+
+def test_size_queries(L):
+    assert L.mhc_prepared_weight_bytes(7168) == 384 * 7168 == 2752512
+    assert L.mhc_prepared_weight_bytes(7000) == 0
+    assert L.mhc_workspace_bytes(32, 7168) > 0
+    assert L.mhc_workspace_bytes(0, 7168) == 0
+    assert L.mhc_workspace_bytes(32, 100) == 0
+
+
+class Buffers:
+    """Disjoint fake device addresses, 16-byte aligned, for one boundary call."""
+
+    def __init__(self, L, T=T, d=D):
+        self.T, self.d = T, d
+        sizes = dict(x=T * d * 2, residual=T * 4 * d * 2, post=T * 16, comb=T * 64, pre_lag=T * 16,
+                     w=384 * d, scale=16, base=96, norm_w=d * 2, res_out=T * 4 * d * 2,
+                     li=T * d * 2, pre_out=T * 16, post_out=T * 16, comb_out=T * 64,
+                     mixes=T * 96, rstd=T * 4, ws=max(L.mhc_workspace_bytes(T, d), 16))
+        self.addr = {}
+        a = GB
+        for k, n in sizes.items():
+            self.addr[k] = a
+            a += (n + 4095) // 4096 * 4096 + 4096
+        self.ws_bytes = sizes["ws"]
+
+    def args(self, **over):
+        a = dict(self.addr)
+        a.update(over)
+        P = lambda k: ctypes.c_void_p(a[k]) if a[k] else None
+        return [a.get("T", self.T), a.get("d", self.d), P("x"), P("residual"), P("post"),
+                P("comb"), P("pre_lag"), P("w"), P("scale"), P("base"), P("norm_w"),
+                a.get("prm", ctypes.byref(api.params())), P("res_out"), P("li"), P("pre_out"),
+                P("post_out"), P("comb_out"), P("mixes"), P("rstd"), P("ws"),
+                a.get("ws_bytes", self.ws_bytes), None]
+
+
+def call(L, b, **over):
+    return L.mhc_boundary(*b.args(**over))
+
+
+def test_boundary_refusals(L):
+    b = Buffers(L)
+    assert call(L, b, T=0) == INVALID
+    assert call(L, b, T=-3) == INVALID
+    assert call(L, b, x=0) == INVALID
+    assert call(L, b, li=0) == INVALID
+    assert call(L, b, prm=None) == INVALID
+    assert call(L, b, prm=ctypes.byref(api.params(sinkhorn_iters=0))) == INVALID
+    assert call(L, b, prm=ctypes.byref(api.params(rms_eps=-1.0))) == INVALID
+    assert call(L, b, prm=ctypes.byref(api.params(norm_eps=float("nan")))) == INVALID
+    assert call(L, b, d=1000) == SHAPE
+    assert call(L, b, d=128) == SHAPE
+    assert call(L, b, T=(1 << 20) + 1) == SHAPE
+    assert call(L, b, residual=b.addr["residual"] + 2) == MISALIGNED
+    assert call(L, b, comb_out=b.addr["comb_out"] + 8) == MISALIGNED
+    assert call(L, b, li=b.addr["res_out"] + 64) == ALIASING            # output in output
+    assert call(L, b, res_out=b.addr["residual"]) == ALIASING           # in place is refused
+    assert call(L, b, ws=b.addr["x"]) == ALIASING                       # workspace over input
+    assert call(L, b, ws=0) == WORKSPACE
+    assert call(L, b, ws_bytes=b.ws_bytes - 16) == WORKSPACE
+
+
+def test_pre_refusals(L):
+    b = Buffers(L)
+    a = b.addr
+    P = ctypes.c_void_p
+    prm = ctypes.byref(api.params())
+
+    def pre(T=T, d=D, residual=a["residual"], li=a["li"], ws=a["ws"], wsb=b.ws_bytes, prm=prm):
+        return L.mhc_pre(T, d, P(residual) if residual else None, P(a["w"]), P(a["scale"]),
+                         P(a["base"]), None, prm, P(li) if li else None, P(a["pre_out"]),
+                         P(a["post_out"]), P(a["comb_out"]), None, None,
+                         P(ws) if ws else None, wsb, None)
+    assert pre(T=0) == INVALID
+    assert pre(residual=0) == INVALID
+    assert pre(d=300) == SHAPE
+    assert pre(li=a["li"] + 4) == MISALIGNED
+    assert pre(li=a["residual"]) == ALIASING
+    assert pre(ws=0) == WORKSPACE
+    assert pre(prm=ctypes.byref(api.params(sinkhorn_iters=0))) == INVALID
+
+
+def test_prepare_weight_refusals(L):
+    P = ctypes.c_void_p
+    assert L.mhc_prepare_weight(None, 1024, P(GB), None) == INVALID
+    assert L.mhc_prepare_weight(P(GB), 1000, P(2 * GB), None) == SHAPE
+    assert L.mhc_prepare_weight(P(GB + 4), 1024, P(2 * GB), None) == MISALIGNED
+    assert L.mhc_prepare_weight(P(GB), 1024, P(GB + 4096), None) == ALIASING

@@ -1,0 +1,217 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.
+
+Bars: prepared weight bit-exact; X' bit-exact (same FP32 FMA chain); layer input
+within 1 BF16 ulp; mixes relative error <= 2e-5 against max(|o|, rms of the
+token's mixes); rstd relative error <= 2e-5; pre / post / comb absolute error
+<= 1e-5.  Full-size configurations compare sampled tokens (the oracle is per
+token) on the full GPU launch.
+"""
+import numpy as np
+import pytest
+import torch
+
+from mhc_hyper_connection_boundary_amd import api
+from mhc_hyper_connection_boundary_amd import workloads as WL
+
+pytestmark = pytest.mark.gpu
+
+MIX_TOL = 2e-5
+COEF_TOL = 1e-5
+
+
+def say(msg):
+    print(f"[parity] {msg}", flush=True)
+
+
+def dev_bf16(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def dev_f32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def host_bits(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+class Dev:
+    def __init__(self, inp: WL.Inputs):
+        self.inp = inp
+        self.X, self.x = dev_bf16(inp.X), dev_bf16(inp.x)
+        self.post, self.comb, self.pre_lag = dev_f32(inp.post_prev), dev_f32(inp.comb_prev), dev_f32(inp.pre_lag)
+        self.W, self.scale, self.base = dev_f32(inp.W), dev_f32(inp.scale), dev_f32(inp.base)
+        self.norm_w = dev_bf16(inp.norm_w)
+        self.wp = api.prepare_weight(self.W)
+
+    def prm(self, **kw):
+        p = dict(self.inp.params())
+        p.update(kw)
+        return api.params(**p)
+
+    def boundary(self, norm=True, schedule="auto", **kw):
+        r = api.boundary(self.x, self.X, self.post, self.comb, self.pre_lag, self.wp, self.scale,
+                         self.base, self.norm_w if norm else None,
+                         prm=self.prm(schedule=schedule, **kw), debug=True)
+        torch.cuda.synchronize()
+        nres, post, comb, li, pre, mixes, rstd = r
+        return dict(xn=host_bits(nres), post=post.cpu().numpy().reshape(-1, 4),
+                    comb=comb.cpu().numpy(), layer_input=host_bits(li), pre=pre.cpu().numpy(),
+                    mixes=mixes.cpu().numpy(), rstd=rstd.cpu().numpy())
+
+    def pre(self, norm=False, **kw):
+        r = api.pre(self.X, self.wp, self.scale, self.base, self.norm_w if norm else None,
+                    prm=self.prm(**kw), debug=True)
+        torch.cuda.synchronize()
+        li, pre, post, comb, mixes, rstd = r
+        return dict(layer_input=host_bits(li), pre=pre.cpu().numpy(),
+                    post=post.cpu().numpy().reshape(-1, 4), comb=comb.cpu().numpy(),
+                    mixes=mixes.cpu().numpy(), rstd=rstd.cpu().numpy())
+
+
+def ulp_distance(a, b):
+    """Distance in BF16 ulps between bit patterns (sign-magnitude ordering)."""
+    def order(u):
+        u = u.astype(np.int64)
+        return np.where(u & 0x8000, -(u & 0x7FFF), u)
+    return np.abs(order(a) - order(b))
+
+
+def compare(g, o, tokens=None, xn=True, label=""):
+    """g: GPU outputs (all tokens); o: oracle outputs for `tokens`."""
+    sel = slice(None) if tokens is None else np.asarray(tokens)
+    if xn and "xn" in g:
+        gx = g["xn"][sel]
+        bad = gx != o["xn"]
+        assert not bad.any(), f"{label} X' differs at {np.argwhere(bad)[:5]}"
+    d = ulp_distance(g["layer_input"][sel], o["layer_input"])
+    assert d.max() <= 1, f"{label} layer_input ulp distance {d.max()}"
+    om = o["mixes"]
+    rms = np.sqrt((om ** 2).mean(axis=1, keepdims=True))
+    rel = np.abs(g["mixes"][sel] - om) / np.maximum(np.abs(om), rms)
+    assert rel.max() <= MIX_TOL, f"{label} mixes rel {rel.max():.3g}"
+    rr = np.abs(g["rstd"][sel] - o["rstd"]) / o["rstd"]
+    assert rr.max() <= MIX_TOL, f"{label} rstd rel {rr.max():.3g}"
+    for k in ("pre", "post", "comb"):
+        err = np.abs(g[k][sel].reshape(o[k].shape) - o[k]).max()
+        assert err <= COEF_TOL, f"{label} {k} abs {err:.3g}"
+    return dict(layer_input_exact=float((d == 0).mean()), mixes_rel=float(rel.max()))
+
+
+def sample_tokens(T, n=48, seed=0):
+    rng = np.random.default_rng(seed)
+    pick = set(rng.choice(T, size=min(n, T), replace=False).tolist())
+    pick |= {0, T - 1, min(15, T - 1), min(16, T - 1), (T // 16) * 16 - 1 if T >= 16 else 0}
+    return np.array(sorted(pick), dtype=np.int32)
+
+
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d", [256, 1024, 4096, 7168])
+def test_prepare_weight_bit_exact(oracle, d):
+    say(f"prepare_weight d={d}")
+    inp = WL.make_inputs(WL.Config("w", d=d, T=1, seed=d))
+    dv = Dev(inp)
+    got = dv.wp.cpu().numpy()
+    want = oracle.prepare_weight(inp.W)
+    assert got.shape == want.shape
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("T,d", [(8, 256), (37, 1024), (1, 512), (50, 2048)])
+def test_boundary_small_full(oracle, T, d):
+    say(f"boundary small T={T} d={d}")
+    inp = WL.make_inputs(WL.Config("s", d=d, T=T, seed=T * 7 + d))
+    g = Dev(inp).boundary()
+    o = oracle.boundary(inp)
+    compare(g, o, label=f"T={T} d={d}")
+
+
+def test_boundary_tiny_config(oracle):
+    say("boundary tiny config")
+    inp = WL.make_inputs("tiny")
+    g = Dev(inp).boundary()
+    compare(g, oracle.boundary(inp), label="tiny")
+
+
+def test_boundary_no_norm_is_li(oracle):
+    say("boundary without norm_w")
+    inp = WL.make_inputs(WL.Config("n", d=1024, T=20, seed=3))
+    g = Dev(inp).boundary(norm=False)
+    o = oracle.boundary(inp, use_norm=False)
+    assert np.array_equal(g["layer_input"], o["li"])
+    compare(g, o, label="no-norm")
+
+
+def test_boundary_special_cases(oracle):
+    say("boundary special cases")
+    inp = WL.make_inputs(WL.Config("sc", d=512, T=18, seed=9))
+    inp.comb_prev[:] = np.eye(4, dtype=np.float32)
+    inp.post_prev[:] = 0.0
+    g = Dev(inp).boundary()
+    assert np.array_equal(g["xn"], inp.X)
+    compare(g, oracle.boundary(inp), label="identity")
+    inp.scale[:] = 0.0
+    inp.base[:] = 0.0
+    g = Dev(inp).boundary()
+    eps = np.float32(1e-6)
+    assert np.all(g["pre"] == np.float32(0.5) + eps)
+    assert np.all(g["post"] == 1.0)
+    np.testing.assert_allclose(g["comb"], 0.25, atol=1e-6)
+
+
+@pytest.mark.parametrize("name", ["decode", "decode_wave"])
+def test_boundary_decode_configs(oracle, name):
+    say(f"boundary {name}")
+    inp = WL.make_inputs(name)
+    g = Dev(inp).boundary()
+    stats = compare(g, oracle.boundary(inp), label=name)
+    say(f"{name}: {stats}")
+
+
+@pytest.mark.parametrize("name", ["prefill", "stress"])
+def test_boundary_large_configs_sampled(oracle, name):
+    say(f"boundary {name} (sampled tokens)")
+    inp = WL.make_inputs(name)
+    dv = Dev(inp)
+    g = dv.boundary()
+    tok = sample_tokens(inp.T, seed=len(name))
+    stats = compare(g, oracle.boundary(inp, tokens=tok), tokens=tok, label=name)
+    say(f"{name}: {stats}")
+    if name == "stress":
+        # Sinkhorn on peaked logits: rows are reported, columns close to 1
+        cs = g["comb"].sum(axis=1)
+        assert np.all(np.abs(cs - 1) < 1e-4)
+        for rep in range(2):
+            say(f"stress determinism run {rep + 2}")
+            h = dv.boundary()
+            for k in g:
+                assert np.array_equal(g[k], h[k]), f"run-to-run difference in {k}"
+
+
+def test_pre_tiny(oracle):
+    say("pre tiny")
+    inp = WL.make_inputs("tiny")
+    dv = Dev(inp)
+    for norm in (False, True):
+        g = dv.pre(norm=norm)
+        o = oracle.pre(inp, use_norm=norm)
+        compare(g, o, xn=False, label=f"pre norm={norm}")
+
+
+def test_pre_ragged(oracle):
+    say("pre ragged")
+    inp = WL.make_inputs(WL.Config("p", d=2048, T=21, seed=5))
+    g = Dev(inp).pre(norm=True)
+    compare(g, oracle.pre(inp, use_norm=True), xn=False, label="pre ragged")
+
+
+def test_determinism_decode():
+    say("determinism decode")
+    dv = Dev(WL.make_inputs("decode"))
+    a = dv.boundary()
+    for _ in range(3):
+        b = dv.boundary()
+        for k in a:
+            assert np.array_equal(a[k], b[k]), k
