@@ -78,25 +78,49 @@ def time_calls(torch, fn, steps, warmup):
     return start.elapsed_time(stop) / steps, wall
 
 
+def graph_time(torch, calls, reps):
+    """Capture `calls` (a list of thunks) once into a HIP graph and time
+    `reps` replays: the per-call device time without host launch overhead."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for c in calls:
+            c()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for c in calls:
+            c()
+    g.replay()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        g.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / (reps * len(calls))
+
+
 def decode_numbers(steps, schedule):
     import torch
 
-    from mhc_hyper_connection_boundary_amd import api
-    from mhc_hyper_connection_boundary_amd import workloads as WL
-
     w = Workload("decode", schedule=schedule)
-    hot_ms, _ = time_calls(torch, lambda k: w.call(), steps, 20)
-    # cold: rotate through 64 copies of the inputs and weights (~320 MB in all,
-    # more than the 256 MB last-level cache), so every call reads from HBM
-    sets = [({k: v.clone() for k, v in w.t.items()}, w.wp.clone()) for _ in range(64)]
-    base_inp = w.inp
-    cold_ms, _ = time_calls(torch, lambda k: w.call(*sets[k % len(sets)]), max(steps, 128), 64)
-    T, d = base_inp.T, base_inp.d
+    T, d = w.inp.T, w.inp.d
     b = algorithmic_bytes(T, d)
-    return dict(workload="decode d=7168 T=32", us_per_call_hot=hot_ms * 1e3,
-                us_per_call_cold=cold_ms * 1e3, tokens_per_s_hot=T / (hot_ms * 1e-3),
-                tokens_per_s_cold=T / (cold_ms * 1e-3),
-                gbs_cold=b / (cold_ms * 1e-3) / 1e9, roofline_frac_cold=b / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
+    eager_ms, _ = time_calls(torch, lambda k: w.call(), steps, 20)
+    hot_ms = graph_time(torch, [w.call] * 20, max(1, steps // 20))
+    # cold: 64 copies of the inputs and weights (~320 MB in all, more than the
+    # 256 MB last-level cache), used in turn, so every call reads from HBM
+    sets = [({k: v.clone() for k, v in w.t.items()}, w.wp.clone()) for _ in range(64)]
+    cold_ms = graph_time(torch, [lambda t=t, wp=wp: w.call(t, wp) for t, wp in sets], 4)
+    return dict(workload="decode d=7168 T=32", timing="HIP graph replay",
+                us_per_call_hot=hot_ms * 1e3, us_per_call_cold=cold_ms * 1e3,
+                us_per_call_eager=eager_ms * 1e3,
+                tokens_per_s_hot=T / (hot_ms * 1e-3), tokens_per_s_cold=T / (cold_ms * 1e-3),
+                gbs_cold=b / (cold_ms * 1e-3) / 1e9,
+                roofline_frac_cold=b / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
 
 
 def cpu_baseline(inp, budget_s=10.0):

@@ -8,7 +8,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmhc.so")
-SOURCES = ["mhc_api.hip", "mhc_kernels.hip"]
+SOURCES = ["mhc_api.hip", "mhc_kernels.hip", "mhc_fused.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

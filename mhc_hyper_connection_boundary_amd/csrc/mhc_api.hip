@@ -6,7 +6,7 @@
 
 #include <algorithm>
 
-#include "../../include/mhc.h"
+#include "mhc.h"
 #include "mhc_device.h"
 #include "mhc_launch.h"
 
@@ -16,6 +16,7 @@ namespace {
 
 constexpr long kTargetWaves = 2048;  // waves of k_partial work to aim for
 constexpr int kFinishTarget = 512;   // k_finish workgroups to aim for
+constexpr int kFusedMinTokens = 2048; // automatic schedule: fused from this many tokens
 
 int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 
@@ -201,9 +202,23 @@ mhc_status mhc_boundary(int tokens, int hidden, const uint16_t* x, const uint16_
     if (any_alias(outs, 8, ins, 9)) return MHC_ERR_ALIASING;
     if (!workspace || workspace_bytes < need) return MHC_ERR_WORKSPACE;
 
-    const SplitPlan plan = split_plan(tokens, hidden);
     const Scalars s = scalars(params);
     hipStream_t hs = (hipStream_t)stream;
+    bool fused = false;
+    if (params->schedule == MHC_SCHEDULE_FUSED) {
+        if (!fused_supported(hidden)) return MHC_ERR_UNSUPPORTED_SHAPE;
+        fused = true;
+    } else if (params->schedule == MHC_SCHEDULE_AUTO) {
+        fused = fused_supported(hidden) && tokens >= kFusedMinTokens;
+    }
+    if (fused) {
+        if (launch_fused(tokens, hidden, x, residual, post_prev, comb_prev, pre_lag, w_prepared,
+                         scale, base, norm_w, s, residual_out, layer_input, pre_out, post_out,
+                         comb_out, mixes, rstd, hs) != hipSuccess)
+            return MHC_ERR_DEVICE;
+        return MHC_OK;
+    }
+    const SplitPlan plan = split_plan(tokens, hidden);
     float* part = static_cast<float*>(workspace);
     // layer_input first receives li; the finishing kernel rescales it in place.
     if (launch_partial(true, plan, tokens, hidden, x, residual, post_prev, comb_prev, pre_lag,

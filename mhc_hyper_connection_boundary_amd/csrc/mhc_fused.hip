@@ -1,0 +1,267 @@
+// Fused schedule of the mHC boundary: one workgroup of 8 waves owns a tile of
+// 16 tokens and all of hidden, so the partial sums never leave the chip.
+//
+// A wave step covers 64 hidden elements of the tile (two 32-element MFMA
+// k-blocks); wave w takes steps w, w+8, w+16, ...  Every lane reads both
+// 64-byte halves of each 128-byte line it touches back to back, and the 8
+// waves together sweep 1 KB of every row at a time, so HBM sees long runs.
+// While a wave computes step i (residual update, X' store, lagged collapse,
+// sums of squares) the activations of step i+1 are in flight; the weight
+// fragments of step i are fetched after that VALU work, then projected on
+// the matrix cores.
+//
+// The BF16 li of the tile (16 x hidden) must wait for rstd_li, which depends
+// on the whole row: the first 8 steps of every wave park it in LDS (128 KB),
+// later steps in the layer-input buffer itself, which the epilogue reads back
+// and overwrites with the normalised values.  After the loop the 8 waves'
+// partials are combined in LDS in a fixed order; wave 0 computes pre / post /
+// Sinkhorn comb (one quad per token) while the other waves already write the
+// layer input.
+#include "mhc_device.h"
+#include "mhc_launch.h"
+
+namespace mhc {
+namespace {
+
+constexpr int kWaves = 8;
+constexpr int kWide = 2 * kStep;  // hidden elements per wave step: two MFMA k-blocks
+
+template <int S>                  // S = hidden / (kWaves * kWide): steps per wave
+struct FusedShape {
+    static constexpr int kLiLds = S < 8 ? S : 8;  // steps whose li waits in LDS (16 KB each)
+};                                                // (later steps: layer_input)
+
+// Activations of one wave step.  Lane (n, g) holds, for token n, the 8 hidden
+// elements 64*step + 32*b + 8*g + [0, 8) of block b = 0, 1: the two 64-byte
+// halves of every 128-byte line of the step are read by the same lane group
+// with back-to-back loads, and block b is directly the B operand of MFMA
+// k-block 2*step + b.
+struct Act {
+    uint4 X[2][4];  // [block][stream]
+    uint4 x[2];
+};
+
+__device__ __forceinline__ uint4 load_stream(const uint16_t* p) {
+    return *reinterpret_cast<const uint4*>(p);
+}
+
+__device__ __forceinline__ void store_stream(uint16_t* p, const uint4& v) {
+    *reinterpret_cast<uint4*>(p) = v;
+}
+
+__device__ __forceinline__ void load_act(Act& a, const uint16_t* __restrict__ Xrow,
+                                         const uint16_t* __restrict__ xrow, int hidden, int h) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        a.X[0][j] = load_stream(Xrow + (size_t)j * hidden + h);
+        a.X[1][j] = load_stream(Xrow + (size_t)j * hidden + h + kStep);
+    }
+    a.x[0] = load_stream(xrow + h);
+    a.x[1] = load_stream(xrow + h + kStep);
+}
+
+__device__ __forceinline__ void load_frags(uint4 (&A)[kFragsPerStep], const uint4* __restrict__ wprep,
+                                           int kblock, int lane) {
+    const uint4* wp = wprep + (size_t)kblock * kFragsPerStep * 64 + lane;
+#pragma unroll
+    for (int i = 0; i < kFragsPerStep; ++i) A[i] = wp[i * 64];
+}
+
+template <int S>
+__global__ __launch_bounds__(512) void k_fused(
+    int T, const uint16_t* __restrict__ x, const uint16_t* __restrict__ X,
+    const float* __restrict__ post_prev, const float* __restrict__ comb_prev,
+    const float* __restrict__ pre_lag, const uint4* __restrict__ wprep,
+    const float* __restrict__ scale, const float* __restrict__ base,
+    const uint16_t* __restrict__ norm_w, Scalars p, uint16_t* __restrict__ xn_out,
+    uint16_t* __restrict__ layer_input, float* __restrict__ pre_out,
+    float* __restrict__ post_out, float* __restrict__ comb_out, float* __restrict__ mixes_out,
+    float* __restrict__ rstd_out) {
+    using Shape = FusedShape<S>;
+    constexpr int hidden = S * kWide * kWaves;
+    __shared__ uint4 li_lds[Shape::kLiLds > 0 ? Shape::kLiLds : 1][kWaves][2][64];
+    __shared__ float red[kWaves][kTile][24];
+    __shared__ float sq[kWaves][4][kTile][2];
+    __shared__ float tot[kTile][26];
+    __shared__ float rli[kTile];
+
+    const int tile = blockIdx.x;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 15;
+    const int g = lane >> 4;
+    const int t = tile * kTile + n;
+    const size_t tc = t < T ? (size_t)t : (size_t)(T - 1);
+
+    PrevCoef c;
+    load_prev(c, post_prev, comb_prev, pre_lag, tc);
+
+    const uint16_t* Xrow = X + tc * 4 * hidden;
+    const uint16_t* xrow = x + tc * hidden;
+    uint16_t* li_row = layer_input + tc * hidden;
+
+    f32x4_t acc[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    float ssq = 0.0f, ssq_li = 0.0f;
+
+    // Wave w takes steps w, w + 8, ...: at any moment the 8 waves cover 512
+    // contiguous hidden elements of every row of the tile.
+    Act cur;
+    load_act(cur, Xrow, xrow, hidden, wave * kWide + g * 8);
+#pragma unroll 1
+    for (int i = 0; i < S; ++i) {
+        const int step = i * kWaves + wave;
+        const int h = step * kWide + g * 8;
+        Act nxt;
+        if (i + 1 < S) load_act(nxt, Xrow, xrow, hidden, h + kWaves * kWide);
+        uint4 Xn[2][4], li[2];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) update_collapse(cur.X[b], cur.x[b], c, Xn[b], li[b], ssq, ssq_li);
+        // A lane past the last token works on token T-1 (tc), so it stores
+        // the same bytes as that token's own lane: no branch needed.
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            store_stream(xn_out + (tc * 4 + s) * hidden + h, Xn[0][s]);
+            store_stream(xn_out + (tc * 4 + s) * hidden + h + kStep, Xn[1][s]);
+        }
+        if (i < Shape::kLiLds) {
+            li_lds[i][wave][0][lane] = li[0];
+            li_lds[i][wave][1][lane] = li[1];
+        } else {
+            store_stream(li_row + h, li[0]);
+            store_stream(li_row + h + kStep, li[1]);
+        }
+        // The weight fragments (L2-resident) are fetched only now, so they hold
+        // no registers during the VALU work above; the other wave of the SIMD
+        // runs its VALU phase while this one waits for them.
+        __builtin_amdgcn_sched_barrier(0);
+        uint4 A0[kFragsPerStep], A1[kFragsPerStep];
+        load_frags(A0, wprep, 2 * step, lane);
+        load_frags(A1, wprep, 2 * step + 1, lane);
+        mfma_step(A0, Xn[0], acc);
+        mfma_step(A1, Xn[1], acc);
+        cur = nxt;
+    }
+
+    // Partials of the 8 waves, combined in a fixed order.
+#pragma unroll
+    for (int m = 0; m < 3; ++m)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) red[wave][n][8 * m + 2 * g + j] = mix_of(acc, m, j);
+    sq[wave][g][n][0] = ssq;
+    sq[wave][g][n][1] = ssq_li;
+    __syncthreads();
+    if (threadIdx.x < kTile * 26) {
+        const int tn = threadIdx.x / 26, v = threadIdx.x % 26;
+        float sum = 0.0f;
+        if (v < 24) {
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) sum += red[w][tn][v];
+        } else {
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) sum += sq[w][q][tn][v - 24];
+        }
+        tot[tn][v] = sum;
+        if (v == 25) rli[tn] = 1.0f / sqrtf(sum / (float)hidden + p.norm_eps);
+    }
+    __syncthreads();
+
+    if (wave == 0) {
+        const int tn = lane >> 2, i = lane & 3;
+        const int tt = tile * kTile + tn;
+        const TokenCoef o = coefficients(tot[tn], i, hidden, scale, base, p);
+        if (tt < T) {
+            pre_out[(size_t)tt * 4 + i] = o.pre;
+            post_out[(size_t)tt * 4 + i] = o.post;
+            *reinterpret_cast<float4*>(comb_out + (size_t)tt * 16 + 4 * i) =
+                make_float4(o.row[0], o.row[1], o.row[2], o.row[3]);
+            if (mixes_out)
+                for (int k = 0; k < 6; ++k) mixes_out[(size_t)tt * 24 + 6 * i + k] = tot[tn][6 * i + k];
+            if (rstd_out && i == 0) rstd_out[tt] = o.rstd;
+        }
+    }
+
+    // Layer input for this wave's steps: li from LDS, then li parked in the
+    // layer-input buffer (written by this same lane before the barrier above).
+    // Lanes past the last token rewrite token T-1's identical values.
+    const float r = rli[n];
+    auto emit = [&](int h, const uint4& li) {
+        uint4 out = li;
+        if (norm_w) {
+            const uint4 nw = *reinterpret_cast<const uint4*>(norm_w + h);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t a = word(li, q), b = word(nw, q);
+                set_word(out, q, pack_bf16((bf_lo(a) * r) * bf_lo(b), (bf_hi(a) * r) * bf_hi(b)));
+            }
+        }
+        store_stream(li_row + h, out);
+    };
+#pragma unroll 2
+    for (int i = 0; i < Shape::kLiLds; ++i) {
+        const int h = (i * kWaves + wave) * kWide + g * 8;
+        emit(h, li_lds[i][wave][0][lane]);
+        emit(h + kStep, li_lds[i][wave][1][lane]);
+    }
+#pragma unroll 2
+    for (int i = Shape::kLiLds; i < S; ++i) {
+        const int h = (i * kWaves + wave) * kWide + g * 8;
+        const uint4 l0 = *reinterpret_cast<const uint4*>(li_row + h);
+        const uint4 l1 = *reinterpret_cast<const uint4*>(li_row + h + kStep);
+        emit(h, l0);
+        emit(h + kStep, l1);
+    }
+}
+
+template <int S>
+hipError_t launch_s(int T, const uint16_t* x, const uint16_t* X, const float* post_prev,
+                    const float* comb_prev, const float* pre_lag, const void* wprep,
+                    const float* scale, const float* base, const uint16_t* norm_w,
+                    const Scalars& p, uint16_t* xn_out, uint16_t* layer_input, float* pre_out,
+                    float* post_out, float* comb_out, float* mixes, float* rstd,
+                    hipStream_t stream) {
+    hipLaunchKernelGGL(k_fused<S>, dim3((T + kTile - 1) / kTile), dim3(kWaves * 64), 0, stream,
+                       T, x, X, post_prev, comb_prev, pre_lag,
+                       reinterpret_cast<const uint4*>(wprep), scale, base, norm_w, p, xn_out,
+                       layer_input, pre_out, post_out, comb_out, mixes, rstd);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool fused_supported(int hidden) {
+    switch (hidden) {
+        case 1024: case 2048: case 4096: case 5120: case 6144: case 7168: case 8192:
+            return true;
+        default:
+            return false;
+    }
+}
+
+hipError_t launch_fused(int T, int hidden, const uint16_t* x, const uint16_t* X,
+                        const float* post_prev, const float* comb_prev, const float* pre_lag,
+                        const void* wprep, const float* scale, const float* base,
+                        const uint16_t* norm_w, const Scalars& p, uint16_t* xn_out,
+                        uint16_t* layer_input, float* pre_out, float* post_out, float* comb_out,
+                        float* mixes, float* rstd, hipStream_t stream) {
+#define MHC_FUSED_CASE(D)                                                                     \
+    case D:                                                                                   \
+        return launch_s<D / 512>(T, x, X, post_prev, comb_prev, pre_lag, wprep, scale, base,  \
+                                 norm_w, p, xn_out, layer_input, pre_out, post_out, comb_out, \
+                                 mixes, rstd, stream);
+    switch (hidden) {
+        MHC_FUSED_CASE(1024)
+        MHC_FUSED_CASE(2048)
+        MHC_FUSED_CASE(4096)
+        MHC_FUSED_CASE(5120)
+        MHC_FUSED_CASE(6144)
+        MHC_FUSED_CASE(7168)
+        MHC_FUSED_CASE(8192)
+        default:
+            return hipErrorInvalidValue;
+    }
+#undef MHC_FUSED_CASE
+}
+
+}  // namespace mhc

@@ -9,8 +9,8 @@
 //               order and written as one record per (token, slice).
 //   k_finish    one workgroup per (tile, hidden slice): sums the records of
 //               its tokens over the slices in slice order, forms rstd_li and
-//               rescales li into the layer input; the slice-0 workgroup also
-//               computes pre / post / Sinkhorn comb (one quad per token).
+//               rescales li into the layer input; its first wave computes
+//               pre / post / Sinkhorn comb of one or more of the tile's tokens.
 //   k_pre_finish (non-shifted pre) one workgroup per token: coefficients
 //               first, then the collapse with the fresh pre and the RMSNorm.
 // Weight preparation: k_prepare_weight.
@@ -81,16 +81,19 @@ __global__ __launch_bounds__(256) void k_partial(
     PrevCoef c;
     if (SHIFTED) load_prev(c, post_prev, comb_prev, pre_lag, tc);
 
+    // The slice covers steps [slice*4*spw, (slice+1)*4*spw); its 4 waves take
+    // them interleaved (wave w: first + w, first + 4 + w, ...) so the waves read
+    // adjacent pieces of each row at the same time.
     const int nsteps = hidden / kStep;
-    const int s0 = (slice * 4 + wave) * steps_per_wave;
-    const int s1 = min(s0 + steps_per_wave, nsteps);
+    const int first = slice * 4 * steps_per_wave;
+    const int last = min(first + 4 * steps_per_wave, nsteps);
 
     f32x4_t acc[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
     float ssq = 0.0f, ssq_li = 0.0f;
     const uint16_t* Xrow = X + tc * 4 * hidden;
     const uint16_t* xrow = SHIFTED ? x + tc * hidden : nullptr;
 
-    for (int step = s0; step < s1; ++step) {
+    for (int step = first + wave; step < last; step += 4) {
         const int h = step * kStep + g * 8;
         uint4 Xv[4];
 #pragma unroll
@@ -146,48 +149,89 @@ __global__ __launch_bounds__(256) void k_partial(
 
 // ---------------------------------------------------------------------------
 // Split schedule, kernel 2: totals, coefficients, layer input.
+//
+// Sum over slices q of part[t][q][v], q ascending.  The loads are issued in
+// batches of 8 so they overlap; the additions keep the slice order.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ float slice_sum(const float* __restrict__ src, int first, int stride,
+                                           int count) {
+    float sum = 0.0f;
+    for (int q0 = first; q0 < count; q0 += 8 * stride) {
+        float v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int q = q0 + k * stride;
+            v[k] = q < count ? src[(size_t)q * kPart] : 0.0f;
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            if (q0 + k * stride < count) sum += v[k];
+    }
+    return sum;
+}
+
+// Make the wave's LDS writes visible to its other lanes.
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Workgroup (tile, hs): rstd_li of the tile's 16 tokens; wave 0 computes the
+// coefficients of tokens hs, hs + finish_slices, ... of the tile; waves 1-3
+// rescale li into the layer input over hidden [hs*width, (hs+1)*width).
 __global__ __launch_bounds__(256) void k_finish(
-    int T, int hidden, int slices, int slice_width, const float* __restrict__ part,
-    const float* __restrict__ scale, const float* __restrict__ base,
-    const uint16_t* __restrict__ norm_w, Scalars p, uint16_t* __restrict__ layer_input,
-    float* __restrict__ pre_out, float* __restrict__ post_out, float* __restrict__ comb_out,
-    float* __restrict__ mixes_out, float* __restrict__ rstd_out) {
-    __shared__ float tot[kTile][26];
+    int T, int hidden, int slices, int finish_slices, int slice_width,
+    const float* __restrict__ part, const float* __restrict__ scale,
+    const float* __restrict__ base, const uint16_t* __restrict__ norm_w, Scalars p,
+    uint16_t* __restrict__ layer_input, float* __restrict__ pre_out,
+    float* __restrict__ post_out, float* __restrict__ comb_out, float* __restrict__ mixes_out,
+    float* __restrict__ rstd_out) {
+    __shared__ float lsum[kTile][16];
     __shared__ float rli[kTile];
+    __shared__ float cred[2][26];
+    __shared__ float ctot[26];
 
     const int tile = blockIdx.x;
     const int hs = blockIdx.y;
     const int tid = threadIdx.x;
-    const bool coef_wg = hs == 0;
 
-    for (int i = tid; i < kTile * 26; i += blockDim.x) {
-        const int tn = i / 26, v = i % 26;
-        if (!coef_wg && v != 25) continue;
+    {  // sums of li squares: thread (tn, group) adds slices group, group + 16, ...
+        const int tn = tid >> 4, grp = tid & 15;
         const int t = tile * kTile + tn;
-        float sum = 0.0f;
-        if (t < T) {
-            const float* src = part + (size_t)t * slices * kPart + v;
-            for (int q = 0; q < slices; ++q) sum += src[(size_t)q * kPart];
-        }
-        tot[tn][v] = sum;
+        lsum[tn][grp] = t < T ? slice_sum(part + (size_t)t * slices * kPart + 25, grp, 16, slices)
+                              : 0.0f;
     }
     __syncthreads();
-    if (tid < kTile) rli[tid] = 1.0f / sqrtf(tot[tid][25] / (float)hidden + p.norm_eps);
+    if (tid < kTile) {
+        float sum = 0.0f;
+        for (int grp = 0; grp < 16; ++grp) sum += lsum[tid][grp];
+        rli[tid] = 1.0f / sqrtf(sum / (float)hidden + p.norm_eps);
+    }
     __syncthreads();
 
-    if (coef_wg && tid < 64) {
-        const int tn = tid >> 2, i = tid & 3;
-        const int t = tile * kTile + tn;
-        const TokenCoef o = coefficients(tot[tn], i, hidden, scale, base, p);
-        if (t < T) {
-            pre_out[(size_t)t * 4 + i] = o.pre;
-            post_out[(size_t)t * 4 + i] = o.post;
-            *reinterpret_cast<float4*>(comb_out + (size_t)t * 16 + 4 * i) =
-                make_float4(o.row[0], o.row[1], o.row[2], o.row[3]);
-            if (mixes_out)
-                for (int k = 0; k < 6; ++k) mixes_out[(size_t)t * 24 + 6 * i + k] = tot[tn][6 * i + k];
-            if (rstd_out && i == 0) rstd_out[t] = o.rstd;
+    if (tid < 64) {
+        const int lane = tid;
+        for (int tn = hs; tn < kTile; tn += finish_slices) {
+            const int t = tile * kTile + tn;
+            if (t >= T) break;
+            const int v = lane & 31, half = lane >> 5;
+            if (v < 25)
+                cred[half][v] = slice_sum(part + (size_t)t * slices * kPart + v, half, 2, slices);
+            wave_sync();
+            if (lane < 25) ctot[lane] = cred[0][lane] + cred[1][lane];
+            wave_sync();
+            if (lane < 4) {
+                const TokenCoef o = coefficients(ctot, lane, hidden, scale, base, p);
+                pre_out[(size_t)t * 4 + lane] = o.pre;
+                post_out[(size_t)t * 4 + lane] = o.post;
+                *reinterpret_cast<float4*>(comb_out + (size_t)t * 16 + 4 * lane) =
+                    make_float4(o.row[0], o.row[1], o.row[2], o.row[3]);
+                if (mixes_out)
+                    for (int k = 0; k < 6; ++k) mixes_out[(size_t)t * 24 + 6 * lane + k] = ctot[6 * lane + k];
+                if (rstd_out && lane == 0) rstd_out[t] = o.rstd;
+            }
+            wave_sync();
         }
         return;
     }
@@ -196,9 +240,7 @@ __global__ __launch_bounds__(256) void k_finish(
     const int width = min(slice_width, hidden - h0);
     if (width <= 0) return;
     const int chunks = width / 8;
-    const int first = coef_wg ? tid - 64 : tid;
-    const int stride = coef_wg ? (int)blockDim.x - 64 : (int)blockDim.x;
-    for (int u = first; u < kTile * chunks; u += stride) {
+    for (int u = tid - 64; u < kTile * chunks; u += (int)blockDim.x - 64) {
         const int tn = u / chunks, cidx = u % chunks;
         const int t = tile * kTile + tn;
         if (t >= T) break;
@@ -234,12 +276,7 @@ __global__ __launch_bounds__(256) void k_pre_finish(
 
     const int t = blockIdx.x;
     const int tid = threadIdx.x;
-    if (tid < 25) {
-        const float* src = part + (size_t)t * slices * kPart + tid;
-        float sum = 0.0f;
-        for (int q = 0; q < slices; ++q) sum += src[(size_t)q * kPart];
-        tot[tid] = sum;
-    }
+    if (tid < 25) tot[tid] = slice_sum(part + (size_t)t * slices * kPart + tid, 0, 1, slices);
     __syncthreads();
     TokenCoef o;
     if (tid < 4) {
@@ -350,8 +387,8 @@ hipError_t launch_finish(const SplitPlan& plan, int T, int hidden, const float* 
                          hipStream_t stream) {
     const dim3 grid((T + kTile - 1) / kTile, plan.finish_slices);
     hipLaunchKernelGGL(k_finish, grid, dim3(256), 0, stream, T, hidden, plan.slices,
-                       plan.finish_width, part, scale, base, norm_w, p, layer_input, pre_out,
-                       post_out, comb_out, mixes, rstd);
+                       plan.finish_slices, plan.finish_width, part, scale, base, norm_w, p,
+                       layer_input, pre_out, post_out, comb_out, mixes, rstd);
     return hipGetLastError();
 }
 

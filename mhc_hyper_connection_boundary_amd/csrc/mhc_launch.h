@@ -10,8 +10,9 @@ namespace mhc {
 struct Scalars;
 
 // Work split of the split schedule for (T, hidden):
-//   k_partial: grid (tiles, slices); wave w of slice q covers hidden steps
-//              [(4q + w) * steps_per_wave, ... + steps_per_wave) of 32 elements.
+//   k_partial: grid (tiles, slices); slice q covers hidden steps
+//              [4q * steps_per_wave, 4(q + 1) * steps_per_wave) of 32 elements,
+//              interleaved over its 4 waves.
 //   k_finish:  grid (tiles, finish_slices); workgroup q rescales hidden
 //              [q * finish_width, (q + 1) * finish_width).
 struct SplitPlan {
@@ -42,5 +43,14 @@ hipError_t launch_pre_finish(const SplitPlan& plan, int T, int hidden, const uin
                              const uint16_t* norm_w, const Scalars& p, uint16_t* layer_input,
                              float* pre_out, float* post_out, float* comb_out, float* mixes,
                              float* rstd, hipStream_t stream);
+
+// Fused schedule: one 8-wave workgroup per 16-token tile over all of hidden.
+bool fused_supported(int hidden);
+hipError_t launch_fused(int T, int hidden, const uint16_t* x, const uint16_t* X,
+                        const float* post_prev, const float* comb_prev, const float* pre_lag,
+                        const void* wprep, const float* scale, const float* base,
+                        const uint16_t* norm_w, const Scalars& p, uint16_t* xn_out,
+                        uint16_t* layer_input, float* pre_out, float* post_out, float* comb_out,
+                        float* mixes, float* rstd, hipStream_t stream);
 
 }  // namespace mhc

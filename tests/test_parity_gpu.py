@@ -119,13 +119,37 @@ def test_prepare_weight_bit_exact(oracle, d):
     assert np.array_equal(got, want)
 
 
-@pytest.mark.parametrize("T,d", [(8, 256), (37, 1024), (1, 512), (50, 2048)])
-def test_boundary_small_full(oracle, T, d):
-    say(f"boundary small T={T} d={d}")
+FUSED_D = {1024, 2048, 4096, 5120, 6144, 7168, 8192}
+
+
+@pytest.mark.parametrize("schedule", ["split", "fused"])
+@pytest.mark.parametrize("T,d", [(8, 256), (37, 1024), (1, 512), (50, 2048), (3, 5120), (17, 6144),
+                                 (20, 8192)])
+def test_boundary_small_full(oracle, T, d, schedule):
+    if schedule == "fused" and d not in FUSED_D:
+        pytest.skip("no fused kernel for this width")
+    say(f"boundary small T={T} d={d} schedule={schedule}")
     inp = WL.make_inputs(WL.Config("s", d=d, T=T, seed=T * 7 + d))
-    g = Dev(inp).boundary()
+    g = Dev(inp).boundary(schedule=schedule)
     o = oracle.boundary(inp)
-    compare(g, o, label=f"T={T} d={d}")
+    compare(g, o, label=f"T={T} d={d} {schedule}")
+
+
+def test_fused_refuses_unsupported_width():
+    inp = WL.make_inputs(WL.Config("u", d=256, T=4, seed=1))
+    with pytest.raises(api.MhcError) as e:
+        Dev(inp).boundary(schedule="fused")
+    assert e.value.status == 2
+
+
+def test_schedules_agree_on_residual(oracle):
+    """Both schedules run the same FP32 chain for X': bitwise equal outputs."""
+    say("split vs fused X'")
+    inp = WL.make_inputs(WL.Config("x", d=7168, T=40, seed=11))
+    dv = Dev(inp)
+    a, b = dv.boundary(schedule="split"), dv.boundary(schedule="fused")
+    assert np.array_equal(a["xn"], b["xn"])
+    assert ulp_distance(a["layer_input"], b["layer_input"]).max() <= 1
 
 
 def test_boundary_tiny_config(oracle):
@@ -151,6 +175,10 @@ def test_boundary_special_cases(oracle):
     inp.post_prev[:] = 0.0
     g = Dev(inp).boundary()
     assert np.array_equal(g["xn"], inp.X)
+    inp2 = WL.make_inputs(WL.Config("sc2", d=1024, T=18, seed=9))
+    inp2.comb_prev[:] = np.eye(4, dtype=np.float32)
+    inp2.post_prev[:] = 0.0
+    assert np.array_equal(Dev(inp2).boundary(schedule="fused")["xn"], inp2.X)
     compare(g, oracle.boundary(inp), label="identity")
     inp.scale[:] = 0.0
     inp.base[:] = 0.0
@@ -161,31 +189,33 @@ def test_boundary_special_cases(oracle):
     np.testing.assert_allclose(g["comb"], 0.25, atol=1e-6)
 
 
+@pytest.mark.parametrize("schedule", ["auto", "fused"])
 @pytest.mark.parametrize("name", ["decode", "decode_wave"])
-def test_boundary_decode_configs(oracle, name):
-    say(f"boundary {name}")
+def test_boundary_decode_configs(oracle, name, schedule):
+    say(f"boundary {name} schedule={schedule}")
     inp = WL.make_inputs(name)
-    g = Dev(inp).boundary()
-    stats = compare(g, oracle.boundary(inp), label=name)
-    say(f"{name}: {stats}")
+    g = Dev(inp).boundary(schedule=schedule)
+    stats = compare(g, oracle.boundary(inp), label=f"{name} {schedule}")
+    say(f"{name} {schedule}: {stats}")
 
 
+@pytest.mark.parametrize("schedule", ["auto", "split"])
 @pytest.mark.parametrize("name", ["prefill", "stress"])
-def test_boundary_large_configs_sampled(oracle, name):
-    say(f"boundary {name} (sampled tokens)")
+def test_boundary_large_configs_sampled(oracle, name, schedule):
+    say(f"boundary {name} schedule={schedule} (sampled tokens)")
     inp = WL.make_inputs(name)
     dv = Dev(inp)
-    g = dv.boundary()
+    g = dv.boundary(schedule=schedule)
     tok = sample_tokens(inp.T, seed=len(name))
-    stats = compare(g, oracle.boundary(inp, tokens=tok), tokens=tok, label=name)
-    say(f"{name}: {stats}")
+    stats = compare(g, oracle.boundary(inp, tokens=tok), tokens=tok, label=f"{name} {schedule}")
+    say(f"{name} {schedule}: {stats}")
     if name == "stress":
-        # Sinkhorn on peaked logits: rows are reported, columns close to 1
+        # columns sum to 1 - eps/S after the final column pass, rows close to 1
         cs = g["comb"].sum(axis=1)
         assert np.all(np.abs(cs - 1) < 1e-4)
         for rep in range(2):
             say(f"stress determinism run {rep + 2}")
-            h = dv.boundary()
+            h = dv.boundary(schedule=schedule)
             for k in g:
                 assert np.array_equal(g[k], h[k]), f"run-to-run difference in {k}"
 
@@ -207,11 +237,12 @@ def test_pre_ragged(oracle):
     compare(g, oracle.pre(inp, use_norm=True), xn=False, label="pre ragged")
 
 
-def test_determinism_decode():
-    say("determinism decode")
+@pytest.mark.parametrize("schedule", ["split", "fused"])
+def test_determinism_decode(schedule):
+    say(f"determinism decode {schedule}")
     dv = Dev(WL.make_inputs("decode"))
-    a = dv.boundary()
+    a = dv.boundary(schedule=schedule)
     for _ in range(3):
-        b = dv.boundary()
+        b = dv.boundary(schedule=schedule)
         for k in a:
             assert np.array_equal(a[k], b[k]), k
