@@ -27,6 +27,34 @@ sys.path.insert(0, ROOT)
 
 METRIC = "mHC boundary tokens/s at d=7168 (decode T=32, prefill T=8192); % HBM roofline"
 HBM_PEAK_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_PROFILE = os.path.join(PROFILES, "k_fused_prefill_traffic.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "mhc_hyper_connection_boundary_amd", "csrc", f)
+                  for f in ("mhc_fused.hip", "mhc_device.h")]
+COPY_BYTES = 1 << 30
+
+
+def kernel_sources_sha256() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per call of the fused kernel from the committed counter
+    summary, if it was taken on the current kernel sources (else None)."""
+    try:
+        with open(TRAFFIC_PROFILE) as f:
+            kv = dict(l.split(":", 1) for l in f if ":" in l and not l.startswith(" "))
+    except OSError:
+        return None
+    if kv.get("sources_sha256", "").strip() != kernel_sources_sha256():
+        return None
+    return float(kv["traffic_bytes_per_call"])
 
 
 def algorithmic_bytes(T: int, d: int) -> int:
@@ -124,21 +152,89 @@ def decode_numbers(steps, schedule):
 
 
 def cpu_baseline(inp, budget_s=10.0):
+    """The oracle, as it stands, on tokens of the prefill batch: whole passes
+    over the batch until about budget_s seconds of wall time have run."""
     from oracle import oracle as O
 
     O.lib()
-    rng = np.random.default_rng(7)
-    probe = np.sort(rng.choice(inp.T, size=32, replace=False)).astype(np.int32)
     t0 = time.perf_counter()
-    O.boundary(inp, tokens=probe)
-    per_tok = (time.perf_counter() - t0) / len(probe)
-    n = int(min(inp.T, max(64, budget_s / max(per_tok, 1e-9))))
-    tok = np.sort(rng.choice(inp.T, size=n, replace=False)).astype(np.int32)
-    t0 = time.perf_counter()
-    O.boundary(inp, tokens=tok)
-    dt = time.perf_counter() - t0
-    return dict(value=n / dt, unit="tokens/s", cores=O.max_threads(), kind="oracle",
-                sample=f"{n} random tokens of the prefill batch (d={inp.d}), {dt:.1f} s wall")
+    passes, tokens = 0, 0
+    while True:
+        O.boundary(inp)
+        passes += 1
+        tokens += inp.T
+        dt = time.perf_counter() - t0
+        if dt >= budget_s:
+            break
+    return dict(value=tokens / dt, unit="tokens/s", cores=O.max_threads(), kind="oracle",
+                sample=f"{passes} pass(es) over the prefill batch (T={inp.T}, d={inp.d}), "
+                       f"{dt:.1f} s wall")
+
+
+def copy_calibration():
+    """A plain 1 GiB device copy: the box's practical streaming ceiling and the
+    reference reading for the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+
+    a = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    ms, _ = time_calls(torch, lambda k: b.copy_(a), 5, 3)
+    return dict(copy_bytes=COPY_BYTES, us=ms * 1e3, gbs_read_plus_write=2 * COPY_BYTES / (ms * 1e-3) / 1e9)
+
+
+def _counter_median(directory, counter, kernel_substr):
+    import csv
+    import glob
+
+    vals = []
+    for f in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter and kernel_substr in r["Kernel_Name"]:
+                vals.append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no {counter} rows for {kernel_substr} under {directory}")
+    vals.sort()
+    return vals[len(vals) // 2], len(vals)
+
+
+def write_traffic_profile(prof_dir):
+    """Summarises four rocprofv3 --pmc runs (see the command list written into
+    the summary) into profiles/k_fused_prefill_traffic.txt."""
+    f_k, nf = _counter_median(os.path.join(prof_dir, "fetch_boundary"), "FETCH_SIZE", "k_fused")
+    w_k, nw = _counter_median(os.path.join(prof_dir, "write_boundary"), "WRITE_SIZE", "k_fused")
+    f_c, _ = _counter_median(os.path.join(prof_dir, "fetch_copy"), "FETCH_SIZE", "copyBuffer")
+    w_c, _ = _counter_median(os.path.join(prof_dir, "write_copy"), "WRITE_SIZE", "copyBuffer")
+    f_scale = COPY_BYTES / (f_c * 1024)
+    w_scale = COPY_BYTES / (w_c * 1024)
+    traffic = f_k * 1024 * f_scale + w_k * 1024 * w_scale
+    T, d = 8192, 7168
+    lines = [
+        "k_fused prefill (d=7168, T=8192): HBM traffic per launch from rocprofv3 counters",
+        f"sources_sha256: {kernel_sources_sha256()}",
+        f"fetch_size_kib_per_dispatch: {f_k:.1f}",
+        f"write_size_kib_per_dispatch: {w_k:.1f}",
+        f"dispatches: {nf} / {nw}",
+        f"copy_1GiB_fetch_size_kib: {f_c:.1f}",
+        f"copy_1GiB_write_size_kib: {w_c:.1f}",
+        f"fetch_scale: {f_scale:.4f}",
+        f"write_scale: {w_scale:.4f}",
+        f"read_bytes_per_call: {f_k * 1024 * f_scale:.0f}",
+        f"written_bytes_per_call: {w_k * 1024 * w_scale:.0f}",
+        f"traffic_bytes_per_call: {traffic:.0f}",
+        f"algorithmic_bytes_per_call: {algorithmic_bytes(T, d)}",
+        f"traffic_over_algorithmic: {traffic / algorithmic_bytes(T, d):.3f}",
+        "commands (from the repository root, TMPDIR=/tmp):",
+        "  rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/fetch_boundary -o run -- python bench.py --steps 5 --warmup 2 --no-decode --no-cpu-baseline",
+        "  rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/write_boundary -o run -- python bench.py --steps 5 --warmup 2 --no-decode --no-cpu-baseline",
+        "  rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/fetch_copy -o run -- python bench.py --copy-calibration",
+        "  rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/write_copy -o run -- python bench.py --copy-calibration",
+        "  python bench.py --write-traffic-profile <dir>",
+    ]
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(TRAFFIC_PROFILE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def main():
@@ -149,11 +245,22 @@ def main():
     ap.add_argument("--schedule", default="auto", choices=["auto", "split", "fused"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="time a plain 1 GiB device copy and exit")
+    ap.add_argument("--write-traffic-profile", metavar="DIR",
+                    help="summarise rocprofv3 counter runs under DIR into profiles/")
     a = ap.parse_args()
+    if a.write_traffic_profile:
+        write_traffic_profile(a.write_traffic_profile)
+        return
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the boundary has "
               "no cross-GPU step to measure", file=sys.stderr)
         sys.exit(2)
+
+    if a.copy_calibration:
+        print(json.dumps(copy_calibration()), flush=True)
+        return
 
     import torch
 
@@ -164,6 +271,9 @@ def main():
     ms, wall = time_calls(torch, lambda k: w.call(), a.steps, a.warmup)
     b = algorithmic_bytes(T, d)
     gbs = b / (ms * 1e-3) / 1e9
+    fused = a.schedule == "fused" or (a.schedule == "auto" and T >= 2048)
+    kernel = f"k_fused<{d // 512}> (one launch per call)" if fused else "k_partial + k_finish"
+    traffic = recorded_traffic() if fused else None
     line = dict(
         metric=METRIC, value=T / (ms * 1e-3), unit="tokens/s", n_gpus=1, steps=a.steps,
         warmup=a.warmup, ms_per_step=ms, higher_is_better=True, scaling="weak",
@@ -171,8 +281,8 @@ def main():
         config=dict(workload="prefill d=7168 T=8192", d=d, T=T, n_hc=4, sinkhorn_iters=20,
                     schedule=a.schedule),
         roofline=dict(bound="hbm", achieved=gbs, peak=HBM_PEAK_GBS, unit="GB/s",
-                      frac=gbs / HBM_PEAK_GBS, traffic=None,
-                      bytes_per_call=b, kernel="mhc_boundary (whole call)"),
+                      frac=gbs / HBM_PEAK_GBS, traffic=traffic, bytes_per_call=b,
+                      kernel=kernel),
     )
     if not a.no_decode:
         print("[bench] decode T=32", file=sys.stderr, flush=True)
