@@ -175,11 +175,19 @@ __device__ __forceinline__ float quad_xor2(float v) {
 
 __device__ __forceinline__ float sigmoid(float v) { return 1.0f / (1.0f + expf(-v)); }
 
+// 1/x for a positive normal x: the hardware estimate (v_rcp_f32, within 1 ulp)
+// refined by one Newton-Raphson step r + r(1 - x r).  Used for the Sinkhorn
+// normalisations, whose sums lie in [eps, 4 + 5 eps].
+__device__ __forceinline__ float recip(float x) {
+    const float r = __builtin_amdgcn_rcpf(x);
+    return __builtin_fmaf(r, __builtin_fmaf(-x, r, 1.0f), r);
+}
+
 // Coefficients of one token, computed by the 4 lanes of a quad: lane i of the
 // quad owns row i of comb and pre[i], post[i].  tot points at the token's
 // reduced record (24 mixes, then the sum of squares).  Column sums use the
 // (r0 + r1) + (r2 + r3) order, row sums ((c0 + c1) + c2) + c3; each
-// normalisation multiplies by the IEEE reciprocal of (sum + eps).
+// normalisation multiplies by the reciprocal of (sum + eps) (see recip).
 struct TokenCoef {
     float rstd, pre, post;
     float row[4];
@@ -202,13 +210,13 @@ __device__ __forceinline__ TokenCoef coefficients(const float* tot, int i, int h
     float e[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) e[k] = expf(v[k] - mx);
-    const float inv = 1.0f / (((e[0] + e[1]) + e[2]) + e[3]);
+    const float inv = recip(((e[0] + e[1]) + e[2]) + e[3]);
     float c[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) c[k] = __builtin_fmaf(e[k], inv, p.sinkhorn_eps);
     for (int it = 0; it < p.sinkhorn_iters; ++it) {
         if (it > 0) {
-            const float rinv = 1.0f / ((((c[0] + c[1]) + c[2]) + c[3]) + p.sinkhorn_eps);
+            const float rinv = recip((((c[0] + c[1]) + c[2]) + c[3]) + p.sinkhorn_eps);
 #pragma unroll
             for (int k = 0; k < 4; ++k) c[k] *= rinv;
         }
@@ -216,7 +224,7 @@ __device__ __forceinline__ TokenCoef coefficients(const float* tot, int i, int h
         for (int k = 0; k < 4; ++k) {
             float s = c[k] + quad_xor1(c[k]);      // rows (0+1) and (2+3)
             s = s + quad_xor2(s);                   // (0+1) + (2+3)
-            c[k] *= 1.0f / (s + p.sinkhorn_eps);
+            c[k] *= recip(s + p.sinkhorn_eps);
         }
     }
 #pragma unroll

@@ -9,8 +9,8 @@
 //               order and written as one record per (token, slice).
 //   k_finish    one workgroup per (tile, hidden slice): sums the records of
 //               its tokens over the slices in slice order, forms rstd_li and
-//               rescales li into the layer input; its first wave computes
-//               pre / post / Sinkhorn comb of one or more of the tile's tokens.
+//               rescales li into the layer input; it also computes pre /
+//               post / Sinkhorn comb of one or more of the tile's tokens.
 //   k_pre_finish (non-shifted pre) one workgroup per token: coefficients
 //               first, then the collapse with the fresh pre and the RMSNorm.
 // Weight preparation: k_prepare_weight.
@@ -170,16 +170,48 @@ __device__ __forceinline__ float slice_sum(const float* __restrict__ src, int fi
     return sum;
 }
 
-// Make the wave's LDS writes visible to its other lanes.
-__device__ __forceinline__ void wave_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+// Remaining coefficient tokens of a workgroup (tokens hs + k*finish_slices,
+// k >= 1), when there are fewer than 16 rescale workgroups per tile.
+__device__ __forceinline__ void finish_more_coefficients(
+    int T, int hidden, int slices, int finish_slices, int tile, int hs, int tid,
+    const float* __restrict__ part, const float* __restrict__ scale,
+    const float* __restrict__ base, const Scalars& p, float (*cred)[26], float* ctot,
+    float* __restrict__ pre_out, float* __restrict__ post_out, float* __restrict__ comb_out,
+    float* __restrict__ mixes_out, float* __restrict__ rstd_out) {
+    for (int tn = hs + finish_slices; tn < kTile; tn += finish_slices) {
+        const int t = tile * kTile + tn;
+        if (t >= T) break;
+        __syncthreads();
+        if ((tid & 31) < 25)
+            cred[tid >> 5][tid & 31] =
+                slice_sum(part + (size_t)t * slices * kPart + (tid & 31), tid >> 5, 8, slices);
+        __syncthreads();
+        if (tid < 25) {
+            float sum = 0.0f;
+            for (int q = 0; q < 8; ++q) sum += cred[q][tid];
+            ctot[tid] = sum;
+        }
+        __syncthreads();
+        if (tid < 4) {
+            const TokenCoef o = coefficients(ctot, tid, hidden, scale, base, p);
+            pre_out[(size_t)t * 4 + tid] = o.pre;
+            post_out[(size_t)t * 4 + tid] = o.post;
+            *reinterpret_cast<float4*>(comb_out + (size_t)t * 16 + 4 * tid) =
+                make_float4(o.row[0], o.row[1], o.row[2], o.row[3]);
+            if (mixes_out)
+                for (int k = 0; k < 6; ++k) mixes_out[(size_t)t * 24 + 6 * tid + k] = ctot[6 * tid + k];
+            if (rstd_out && tid == 0) rstd_out[t] = o.rstd;
+        }
+    }
 }
 
-// Workgroup (tile, hs): rstd_li of the tile's 16 tokens; wave 0 computes the
-// coefficients of tokens hs, hs + finish_slices, ... of the tile; waves 1-3
-// rescale li into the layer input over hidden [hs*width, (hs+1)*width).
+// Workgroup (tile, hs): rstd_li of the tile's 16 tokens; the coefficients of
+// tokens hs, hs + finish_slices, ... of the tile; li -> layer input over hidden
+// [hs*width, (hs+1)*width).  Every reduction over slices is a fixed two-level
+// order: interleaved groups summed in slice order, then the groups in order.
+// The partial records, li and norm_w of the first coefficient token and of the
+// first two rescale chunks of every thread are all requested before the first
+// wait, so the kernel pays about one memory round trip.
 __global__ __launch_bounds__(256) void k_finish(
     int T, int hidden, int slices, int finish_slices, int slice_width,
     const float* __restrict__ part, const float* __restrict__ scale,
@@ -189,65 +221,73 @@ __global__ __launch_bounds__(256) void k_finish(
     float* __restrict__ rstd_out) {
     __shared__ float lsum[kTile][16];
     __shared__ float rli[kTile];
-    __shared__ float cred[2][26];
+    __shared__ float cred[8][26];
     __shared__ float ctot[26];
 
     const int tile = blockIdx.x;
     const int hs = blockIdx.y;
     const int tid = threadIdx.x;
+    const int h0 = hs * slice_width;
+    const int width = max(0, min(slice_width, hidden - h0));
+    const int chunks = width / 8;
 
-    {  // sums of li squares: thread (tn, group) adds slices group, group + 16, ...
+    // Rescale chunks u = tid and tid + 256 (the common case); their loads go first.
+    uint4 li_v[2], nw_v[2];
+    bool have[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int u = tid + k * (int)blockDim.x;
+        const int tn = chunks ? u / chunks : kTile, cidx = chunks ? u % chunks : 0;
+        have[k] = norm_w && u < kTile * chunks && tile * kTile + tn < T;
+        if (have[k]) {
+            const int h = h0 + cidx * 8;
+            li_v[k] = *reinterpret_cast<const uint4*>(layer_input + (size_t)(tile * kTile + tn) * hidden + h);
+            nw_v[k] = *reinterpret_cast<const uint4*>(norm_w + h);
+        }
+    }
+
+    // Phase 1: partial sums of li squares (thread (tn, group) adds slices
+    // group, group + 16, ...) and of the first coefficient token's 25 values
+    // (thread (v, group) adds slices group, group + 8, ...).
+    {
         const int tn = tid >> 4, grp = tid & 15;
         const int t = tile * kTile + tn;
         lsum[tn][grp] = t < T ? slice_sum(part + (size_t)t * slices * kPart + 25, grp, 16, slices)
                               : 0.0f;
     }
+    const int t_first = tile * kTile + hs;
+    const bool coef_first = hs < kTile && t_first < T;
+    if (coef_first && (tid & 31) < 25)
+        cred[tid >> 5][tid & 31] =
+            slice_sum(part + (size_t)t_first * slices * kPart + (tid & 31), tid >> 5, 8, slices);
     __syncthreads();
+    // Phase 2: totals.
     if (tid < kTile) {
         float sum = 0.0f;
         for (int grp = 0; grp < 16; ++grp) sum += lsum[tid][grp];
         rli[tid] = 1.0f / sqrtf(sum / (float)hidden + p.norm_eps);
+    } else if (tid >= 32 && tid < 32 + 25 && coef_first) {
+        float sum = 0.0f;
+        for (int q = 0; q < 8; ++q) sum += cred[q][tid - 32];
+        ctot[tid - 32] = sum;
     }
     __syncthreads();
+    // Phase 3: one quad of wave 0 runs the coefficients (Sinkhorn) of the
+    // first token while the other waves rescale li.
+    auto emit_coef = [&](int t) {
+        const TokenCoef o = coefficients(ctot, tid, hidden, scale, base, p);
+        pre_out[(size_t)t * 4 + tid] = o.pre;
+        post_out[(size_t)t * 4 + tid] = o.post;
+        *reinterpret_cast<float4*>(comb_out + (size_t)t * 16 + 4 * tid) =
+            make_float4(o.row[0], o.row[1], o.row[2], o.row[3]);
+        if (mixes_out)
+            for (int k = 0; k < 6; ++k) mixes_out[(size_t)t * 24 + 6 * tid + k] = ctot[6 * tid + k];
+        if (rstd_out && tid == 0) rstd_out[t] = o.rstd;
+    };
+    if (coef_first && tid < 4) emit_coef(t_first);
 
-    if (tid < 64) {
-        const int lane = tid;
-        for (int tn = hs; tn < kTile; tn += finish_slices) {
-            const int t = tile * kTile + tn;
-            if (t >= T) break;
-            const int v = lane & 31, half = lane >> 5;
-            if (v < 25)
-                cred[half][v] = slice_sum(part + (size_t)t * slices * kPart + v, half, 2, slices);
-            wave_sync();
-            if (lane < 25) ctot[lane] = cred[0][lane] + cred[1][lane];
-            wave_sync();
-            if (lane < 4) {
-                const TokenCoef o = coefficients(ctot, lane, hidden, scale, base, p);
-                pre_out[(size_t)t * 4 + lane] = o.pre;
-                post_out[(size_t)t * 4 + lane] = o.post;
-                *reinterpret_cast<float4*>(comb_out + (size_t)t * 16 + 4 * lane) =
-                    make_float4(o.row[0], o.row[1], o.row[2], o.row[3]);
-                if (mixes_out)
-                    for (int k = 0; k < 6; ++k) mixes_out[(size_t)t * 24 + 6 * lane + k] = ctot[6 * lane + k];
-                if (rstd_out && lane == 0) rstd_out[t] = o.rstd;
-            }
-            wave_sync();
-        }
-        return;
-    }
-    if (!norm_w) return;  // layer_input already holds li
-    const int h0 = hs * slice_width;
-    const int width = min(slice_width, hidden - h0);
-    if (width <= 0) return;
-    const int chunks = width / 8;
-    for (int u = tid - 64; u < kTile * chunks; u += (int)blockDim.x - 64) {
+    auto rescale = [&](int u, const uint4& li, const uint4& nw) {
         const int tn = u / chunks, cidx = u % chunks;
-        const int t = tile * kTile + tn;
-        if (t >= T) break;
-        const int h = h0 + cidx * 8;
-        uint4* dst = reinterpret_cast<uint4*>(layer_input + (size_t)t * hidden + h);
-        const uint4 li = *dst;
-        const uint4 nw = *reinterpret_cast<const uint4*>(norm_w + h);
         const float r = rli[tn];
         uint4 out;
 #pragma unroll
@@ -255,9 +295,24 @@ __global__ __launch_bounds__(256) void k_finish(
             const uint32_t a = word(li, q), b = word(nw, q);
             set_word(out, q, pack_bf16((bf_lo(a) * r) * bf_lo(b), (bf_hi(a) * r) * bf_hi(b)));
         }
-        *dst = out;
+        *reinterpret_cast<uint4*>(layer_input + (size_t)(tile * kTile + tn) * hidden + h0 + cidx * 8) = out;
+    };
+    if (norm_w) {  // (without norm_w, layer_input already holds li)
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+            if (have[k]) rescale(tid + k * (int)blockDim.x, li_v[k], nw_v[k]);
+        for (int u = tid + 2 * (int)blockDim.x; u < kTile * chunks; u += (int)blockDim.x) {
+            if (tile * kTile + u / chunks >= T) break;
+            const int h = h0 + (u % chunks) * 8;
+            const uint4 li = *reinterpret_cast<const uint4*>(layer_input + (size_t)(tile * kTile + u / chunks) * hidden + h);
+            rescale(u, li, *reinterpret_cast<const uint4*>(norm_w + h));
+        }
     }
+    if (finish_slices < kTile)
+        finish_more_coefficients(T, hidden, slices, finish_slices, tile, hs, tid, part, scale, base,
+                                 p, cred, ctot, pre_out, post_out, comb_out, mixes_out, rstd_out);
 }
+
 
 // ---------------------------------------------------------------------------
 // Non-shifted pre, kernel 2: one workgroup (256 threads) per token.
