@@ -153,6 +153,35 @@ mhc_status mhc_boundary(int tokens, int hidden, const uint16_t* x, const uint16_
                         float* post_out, float* comb_out, float* mixes, float* rstd,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* Non-shifted pre from a projection computed elsewhere (the blog's "pure" path:
+ * mhc_pre_big_fuse with precomputed dot_mix and sqrsum, optionally split-K):
+ *   dot_mix  [splits, T, 24] FP32  partial mixes, summed over splits in order
+ *   sqrsum   [splits, T] FP32      partial sums of squares of the residual, likewise
+ *   residual [T, 4, hidden] BF16; scale [3], base [24]; norm_w [hidden] BF16 or NULL
+ * rstd = 1/sqrt(sqrsum/(4*hidden) + rms_eps); pre / post / comb as in mhc_pre;
+ * layer_input = bf16(FMA chain of pre[j]*X[j]) then the optional RMSNorm.
+ *   splits in [1, 64].  Outputs layer_input [T, hidden] BF16, pre, post [T, 4],
+ *   comb [T, 4, 4] FP32.  ("square sum and RMSNorm", "explaining split-K" and
+ *   "computing layer_input" in the blog.)
+ * Errors: INVALID_ARGUMENT (incl. splits out of range), UNSUPPORTED_SHAPE,
+ * MISALIGNED, ALIASING, DEVICE. */
+mhc_status mhc_pre_mixes(int tokens, int hidden, int splits, const uint16_t* residual,
+                         const float* dot_mix, const float* sqrsum, const float* scale,
+                         const float* base, const uint16_t* norm_w, const mhc_params* params,
+                         uint16_t* layer_input, float* pre, float* post, float* comb,
+                         void* stream);
+
+/* Residual update alone (the "post" half of the boundary): X'[s] =
+ * bf16(FMA chain over j of comb_prev[j][s]*X[j], from post_prev[s]*x), the same
+ * bits as mhc_boundary's residual_out.  (residual_update on the vLLM page; the
+ * mhc_post kernel the blog mentions after "why this kernel is called pre".)
+ *   x [T, hidden] BF16, residual [T, 4, hidden] BF16, post_prev [T, 4] FP32,
+ *   comb_prev [T, 4, 4] FP32 (read); residual_out [T, 4, hidden] BF16 (written).
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED_SHAPE, MISALIGNED, ALIASING, DEVICE. */
+mhc_status mhc_post(int tokens, int hidden, const uint16_t* x, const uint16_t* residual,
+                    const float* post_prev, const float* comb_prev, uint16_t* residual_out,
+                    void* stream);
+
 /* Static text for a status code. */
 const char* mhc_status_string(mhc_status status);
 

@@ -55,6 +55,10 @@ def lib() -> ctypes.CDLL:
         L.mhc_prepare_weight.argtypes = [P, I, P, P]
         L.mhc_pre.restype = I
         L.mhc_pre.argtypes = [I, I, P, P, P, P, P, P, P, P, P, P, P, P, P, Z, P]
+        L.mhc_pre_mixes.restype = I
+        L.mhc_pre_mixes.argtypes = [I, I, I, P, P, P, P, P, P, P, P, P, P, P, P]
+        L.mhc_post.restype = I
+        L.mhc_post.argtypes = [I, I, P, P, P, P, P, P]
         L.mhc_boundary.restype = I
         L.mhc_boundary.argtypes = [I, I, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, Z, P]
         if L.mhc_abi_version() != ABI_VERSION:
@@ -134,6 +138,16 @@ def boundary(x, residual, post_prev, comb_prev, pre_lag, w_prepared, scale, base
     return res + (mixes, rstd) if debug else res
 
 
+def post(x, residual, post_prev, comb_prev, out: torch.Tensor | None = None):
+    """Residual update alone: returns X' [T, 4, hidden] (the bits of boundary's
+    new_residual)."""
+    T, _, hidden = residual.shape
+    nres = torch.empty_like(residual) if out is None else out
+    _check("mhc_post", lib().mhc_post(T, hidden, _ptr(x), _ptr(residual), _ptr(post_prev),
+                                      _ptr(comb_prev), _ptr(nres), _stream()))
+    return nres
+
+
 def pre(residual, w_prepared, scale, base, norm_w=None, *, prm: Params | None = None,
         debug: bool = False, ws: torch.Tensor | None = None):
     """Non-shifted mHC pre.  Returns (layer_input, pre, post [T,4,1], comb [T,4,4]),
@@ -155,3 +169,21 @@ def pre(residual, w_prepared, scale, base, norm_w=None, *, prm: Params | None = 
         _ptr(ws), ws.numel(), _stream()))
     res = (li, pr, post, comb)
     return res + (mixes, rstd) if debug else res
+
+
+def pre_mixes(residual, dot_mix, sqrsum, scale, base, norm_w=None, *, prm: Params | None = None):
+    """Non-shifted pre from projection partials made elsewhere: dot_mix
+    [splits, T, 24] and sqrsum [splits, T] FP32.  Returns (layer_input, pre,
+    post [T,4,1], comb [T,4,4])."""
+    T, _, hidden = residual.shape
+    splits = dot_mix.shape[0]
+    dev = residual.device
+    prm = prm or params()
+    li = torch.empty(T, hidden, dtype=torch.bfloat16, device=dev)
+    pr = torch.empty(T, 4, dtype=torch.float32, device=dev)
+    post = torch.empty(T, 4, 1, dtype=torch.float32, device=dev)
+    comb = torch.empty(T, 4, 4, dtype=torch.float32, device=dev)
+    _check("mhc_pre_mixes", lib().mhc_pre_mixes(
+        T, hidden, splits, _ptr(residual), _ptr(dot_mix), _ptr(sqrsum), _ptr(scale), _ptr(base),
+        _ptr(norm_w), ctypes.byref(prm), _ptr(li), _ptr(pr), _ptr(post), _ptr(comb), _stream()))
+    return li, pr, post, comb

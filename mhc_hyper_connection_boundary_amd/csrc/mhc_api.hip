@@ -133,6 +133,54 @@ mhc_status mhc_prepare_weight(const float* w, int hidden, void* w_prepared, void
     return MHC_OK;
 }
 
+mhc_status mhc_pre_mixes(int tokens, int hidden, int splits, const uint16_t* residual,
+                         const float* dot_mix, const float* sqrsum, const float* scale,
+                         const float* base, const uint16_t* norm_w, const mhc_params* params,
+                         uint16_t* layer_input, float* pre, float* post, float* comb,
+                         void* stream) {
+    mhc_status st = check_params(params);
+    if (st != MHC_OK) return st;
+    if (tokens <= 0 || splits < 1 || splits > 64) return MHC_ERR_INVALID_ARGUMENT;
+    if (!residual || !dot_mix || !sqrsum || !scale || !base || !layer_input || !pre || !post ||
+        !comb)
+        return MHC_ERR_INVALID_ARGUMENT;
+    if (tokens > MHC_MAX_TOKENS || !shape_ok(hidden)) return MHC_ERR_UNSUPPORTED_SHAPE;
+    const void* ptrs[] = {residual, dot_mix, sqrsum, scale, base, norm_w, layer_input, pre, post,
+                          comb};
+    for (const void* q : ptrs)
+        if (q && !aligned(q)) return MHC_ERR_MISALIGNED;
+    const size_t T = tokens, d = hidden, S = splits;
+    const Span outs[] = {{layer_input, T * d * 2}, {pre, T * 16}, {post, T * 16}, {comb, T * 64}};
+    const Span ins[] = {{residual, T * 4 * d * 2}, {dot_mix, S * T * 96}, {sqrsum, S * T * 4},
+                        {scale, 12}, {base, 96}, {norm_w, norm_w ? d * 2 : 0}};
+    if (any_alias(outs, 4, ins, 6)) return MHC_ERR_ALIASING;
+    if (launch_pre_mixes(tokens, hidden, splits, residual, dot_mix, sqrsum, scale, base, norm_w,
+                         scalars(params), layer_input, pre, post, comb,
+                         (hipStream_t)stream) != hipSuccess)
+        return MHC_ERR_DEVICE;
+    return MHC_OK;
+}
+
+mhc_status mhc_post(int tokens, int hidden, const uint16_t* x, const uint16_t* residual,
+                    const float* post_prev, const float* comb_prev, uint16_t* residual_out,
+                    void* stream) {
+    if (tokens <= 0 || !x || !residual || !post_prev || !comb_prev || !residual_out)
+        return MHC_ERR_INVALID_ARGUMENT;
+    if (tokens > MHC_MAX_TOKENS || !shape_ok(hidden)) return MHC_ERR_UNSUPPORTED_SHAPE;
+    const void* ptrs[] = {x, residual, post_prev, comb_prev, residual_out};
+    for (const void* q : ptrs)
+        if (!aligned(q)) return MHC_ERR_MISALIGNED;
+    const size_t T = tokens, d = hidden;
+    const Span outs[] = {{residual_out, T * 4 * d * 2}};
+    const Span ins[] = {{x, T * d * 2}, {residual, T * 4 * d * 2}, {post_prev, T * 16},
+                        {comb_prev, T * 64}};
+    if (any_alias(outs, 1, ins, 4)) return MHC_ERR_ALIASING;
+    if (launch_post(tokens, hidden, x, residual, post_prev, comb_prev, residual_out,
+                    (hipStream_t)stream) != hipSuccess)
+        return MHC_ERR_DEVICE;
+    return MHC_OK;
+}
+
 mhc_status mhc_pre(int tokens, int hidden, const uint16_t* residual, const void* w_prepared,
                    const float* scale, const float* base, const uint16_t* norm_w,
                    const mhc_params* params, uint16_t* layer_input, float* pre, float* post,

@@ -154,14 +154,14 @@ __global__ __launch_bounds__(256) void k_partial(
 // batches of 8 so they overlap; the additions keep the slice order.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float slice_sum(const float* __restrict__ src, int first, int stride,
-                                           int count) {
+                                           int count, size_t elem_stride = kPart) {
     float sum = 0.0f;
     for (int q0 = first; q0 < count; q0 += 8 * stride) {
         float v[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const int q = q0 + k * stride;
-            v[k] = q < count ? src[(size_t)q * kPart] : 0.0f;
+            v[k] = q < count ? src[(size_t)q * elem_stride] : 0.0f;
         }
 #pragma unroll
         for (int k = 0; k < 8; ++k)
@@ -317,8 +317,18 @@ __global__ __launch_bounds__(256) void k_finish(
 // ---------------------------------------------------------------------------
 // Non-shifted pre, kernel 2: one workgroup (256 threads) per token.
 // ---------------------------------------------------------------------------
+// Where the partial sums of the projection live: value v (24 mixes, then the
+// sum of squares) of token t in split q is
+//   mix:  mix[q*mix_split + t*mix_tok + v]      ssq: ssq[q*ssq_split + t*ssq_tok]
+struct PartialLayout {
+    const float* mix;
+    const float* ssq;
+    size_t mix_split, mix_tok, ssq_split, ssq_tok;
+    int splits;
+};
+
 __global__ __launch_bounds__(256) void k_pre_finish(
-    int T, int hidden, int slices, const uint16_t* __restrict__ X, const float* __restrict__ part,
+    int T, int hidden, PartialLayout pl, const uint16_t* __restrict__ X,
     const float* __restrict__ scale, const float* __restrict__ base,
     const uint16_t* __restrict__ norm_w, Scalars p, uint16_t* __restrict__ layer_input,
     float* __restrict__ pre_out, float* __restrict__ post_out, float* __restrict__ comb_out,
@@ -331,7 +341,10 @@ __global__ __launch_bounds__(256) void k_pre_finish(
 
     const int t = blockIdx.x;
     const int tid = threadIdx.x;
-    if (tid < 25) tot[tid] = slice_sum(part + (size_t)t * slices * kPart + tid, 0, 1, slices);
+    if (tid < 24)
+        tot[tid] = slice_sum(pl.mix + (size_t)t * pl.mix_tok + tid, 0, 1, pl.splits, pl.mix_split);
+    else if (tid == 24)
+        tot[24] = slice_sum(pl.ssq + (size_t)t * pl.ssq_tok, 0, 1, pl.splits, pl.ssq_split);
     __syncthreads();
     TokenCoef o;
     if (tid < 4) {
@@ -406,6 +419,33 @@ __global__ __launch_bounds__(256) void k_pre_finish(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Residual update alone.  Workgroup (token, chunk group): 256 threads, thread
+// i covers hidden [8*(blockIdx.y*256 + i), +8) of all four streams, so every
+// wave instruction reads or writes 1 KB of one row.  The token's coefficients
+// are workgroup-uniform (scalar loads).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_post(int hidden, const uint16_t* __restrict__ x,
+                                              const uint16_t* __restrict__ X,
+                                              const float* __restrict__ post_prev,
+                                              const float* __restrict__ comb_prev,
+                                              uint16_t* __restrict__ xn_out) {
+    const size_t t = blockIdx.x;
+    const int h = (blockIdx.y * blockDim.x + threadIdx.x) * 8;
+    if (h >= hidden) return;
+    PrevCoef c;
+    load_prev(c, post_prev, comb_prev, post_prev, t);  // (pre unused)
+    uint4 Xv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) Xv[j] = *reinterpret_cast<const uint4*>(X + (t * 4 + j) * hidden + h);
+    const uint4 xv = *reinterpret_cast<const uint4*>(x + t * hidden + h);
+    uint4 Xn[4], li;
+    float ssq = 0.0f, ssq_li = 0.0f;
+    update_collapse(Xv, xv, c, Xn, li, ssq, ssq_li);  // li and the sums are unused
+#pragma unroll
+    for (int s = 0; s < 4; ++s) *reinterpret_cast<uint4*>(xn_out + (t * 4 + s) * hidden + h) = Xn[s];
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -415,6 +455,15 @@ hipError_t launch_prepare_weight(const float* w, int hidden, void* out, hipStrea
     const int n_words = (hidden / kStep) * kFragsPerStep * 64;
     hipLaunchKernelGGL(k_prepare_weight, dim3((n_words + 255) / 256), dim3(256), 0, stream, w,
                        hidden, reinterpret_cast<uint4*>(out), n_words);
+    return hipGetLastError();
+}
+
+hipError_t launch_post(int T, int hidden, const uint16_t* x, const uint16_t* X,
+                       const float* post_prev, const float* comb_prev, uint16_t* xn_out,
+                       hipStream_t stream) {
+    const dim3 grid(T, (hidden / 8 + 255) / 256);
+    hipLaunchKernelGGL(k_post, grid, dim3(256), 0, stream, hidden, x, X, post_prev, comb_prev,
+                       xn_out);
     return hipGetLastError();
 }
 
@@ -447,16 +496,37 @@ hipError_t launch_finish(const SplitPlan& plan, int T, int hidden, const float* 
     return hipGetLastError();
 }
 
+static hipError_t launch_pre_finish_layout(int T, int hidden, const PartialLayout& pl,
+                                           const uint16_t* X, const float* scale,
+                                           const float* base, const uint16_t* norm_w,
+                                           const Scalars& p, uint16_t* layer_input,
+                                           float* pre_out, float* post_out, float* comb_out,
+                                           float* mixes, float* rstd, hipStream_t stream) {
+    const size_t lds = norm_w ? (size_t)hidden * 2 : 0;
+    hipLaunchKernelGGL(k_pre_finish, dim3(T), dim3(256), lds, stream, T, hidden, pl, X, scale,
+                       base, norm_w, p, layer_input, pre_out, post_out, comb_out, mixes, rstd);
+    return hipGetLastError();
+}
+
 hipError_t launch_pre_finish(const SplitPlan& plan, int T, int hidden, const uint16_t* X,
                              const float* part, const float* scale, const float* base,
                              const uint16_t* norm_w, const Scalars& p, uint16_t* layer_input,
                              float* pre_out, float* post_out, float* comb_out, float* mixes,
                              float* rstd, hipStream_t stream) {
-    const size_t lds = norm_w ? (size_t)hidden * 2 : 0;
-    hipLaunchKernelGGL(k_pre_finish, dim3(T), dim3(256), lds, stream, T, hidden, plan.slices, X,
-                       part, scale, base, norm_w, p, layer_input, pre_out, post_out, comb_out,
-                       mixes, rstd);
-    return hipGetLastError();
+    const size_t rec = (size_t)plan.slices * kPart;
+    const PartialLayout pl{part, part + 24, kPart, rec, kPart, rec, plan.slices};
+    return launch_pre_finish_layout(T, hidden, pl, X, scale, base, norm_w, p, layer_input,
+                                    pre_out, post_out, comb_out, mixes, rstd, stream);
+}
+
+hipError_t launch_pre_mixes(int T, int hidden, int splits, const uint16_t* X,
+                            const float* dot_mix, const float* sqrsum, const float* scale,
+                            const float* base, const uint16_t* norm_w, const Scalars& p,
+                            uint16_t* layer_input, float* pre_out, float* post_out,
+                            float* comb_out, hipStream_t stream) {
+    const PartialLayout pl{dot_mix, sqrsum, (size_t)T * 24, 24, (size_t)T, 1, splits};
+    return launch_pre_finish_layout(T, hidden, pl, X, scale, base, norm_w, p, layer_input,
+                                    pre_out, post_out, comb_out, nullptr, nullptr, stream);
 }
 
 }  // namespace mhc

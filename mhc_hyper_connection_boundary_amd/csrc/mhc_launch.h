@@ -27,6 +27,10 @@ size_t split_workspace_bytes(int T, int hidden);
 
 hipError_t launch_prepare_weight(const float* w, int hidden, void* out, hipStream_t stream);
 
+hipError_t launch_post(int T, int hidden, const uint16_t* x, const uint16_t* X,
+                       const float* post_prev, const float* comb_prev, uint16_t* xn_out,
+                       hipStream_t stream);
+
 hipError_t launch_partial(bool shifted, const SplitPlan& plan, int T, int hidden,
                           const uint16_t* x, const uint16_t* X, const float* post_prev,
                           const float* comb_prev, const float* pre_lag, const void* wprep,
@@ -43,6 +47,14 @@ hipError_t launch_pre_finish(const SplitPlan& plan, int T, int hidden, const uin
                              const uint16_t* norm_w, const Scalars& p, uint16_t* layer_input,
                              float* pre_out, float* post_out, float* comb_out, float* mixes,
                              float* rstd, hipStream_t stream);
+
+// Non-shifted pre from precomputed projection partials (dot_mix [splits, T, 24],
+// sqrsum [splits, T]).
+hipError_t launch_pre_mixes(int T, int hidden, int splits, const uint16_t* X,
+                            const float* dot_mix, const float* sqrsum, const float* scale,
+                            const float* base, const uint16_t* norm_w, const Scalars& p,
+                            uint16_t* layer_input, float* pre_out, float* post_out,
+                            float* comb_out, hipStream_t stream);
 
 // Fused schedule: one 8-wave workgroup per 16-token tile over all of hidden.
 bool fused_supported(int hidden);

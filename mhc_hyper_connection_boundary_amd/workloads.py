@@ -144,6 +144,19 @@ def make_inputs(cfg: Config | str, T: int | None = None) -> Inputs:
     return inp
 
 
+def make_partials(T: int, d: int, splits: int, seed: int):
+    """Projection partials as a split-K GEMM hands them over, drawn at random:
+    dot_mix [splits, T, 24] FP32 with N(0, 1/splits) entries (their sum has the
+    unit spread of the fused projection of unit-variance activations with the
+    1/sqrt(4d) weights above) and sqrsum [splits, T] FP32, each split's share of
+    a total near 4d (4d/splits times U(0.5, 1.5)).  A separate stream so that
+    the residual draws stay as they are."""
+    rng = np.random.default_rng(10_000 + seed)
+    dot_mix = (rng.standard_normal((splits, T, MIXES)) / np.sqrt(splits)).astype(np.float32)
+    sqrsum = (N_HC * d / splits * rng.uniform(0.5, 1.5, (splits, T))).astype(np.float32)
+    return dot_mix, sqrsum
+
+
 def _check_no_subnormals(inp: Inputs) -> None:
     """No input holds a nonzero value below 2^-126, so flush-to-zero and IEEE
     subnormal handling cannot differ on them."""

@@ -23,6 +23,8 @@
  *                          page P, "computing B_l"
  *   layer input RMSNorm    page B, kernel "totals in rank order" + layer_input_words
  *   non-shifted pre        page P, write_layer_input and "why this kernel is called pre"
+ *   precomputed mixes      page P, "square sum and RMSNorm" (path 1) and "explaining
+ *                          split-K": dot_mix and sqrsum summed over the splits
  *
  * Readings where the pages leave a step open are listed in the design notes;
  * the ones that matter here:
@@ -173,6 +175,33 @@ static void coefficients(const double mix[NMIX], double ssq, int d, const float*
     *rstd_out = rstd;
 }
 
+/* li = bf16(FMA chain over j of pc[j]*xn[j], from 0) in FP32; ssq_li = sum of
+ * li^2; rstd_li = 1/sqrt(ssq_li/d + norm_eps); layer_input = bf16(li*rstd_li*
+ * norm_w) with one rounding from FP64, or li without norm_w.  xn holds the four
+ * streams' values (as FP32) stream-major; li is scratch of d floats. */
+static void collapse(const float* xn, const float pc[4], int d, const uint16_t* norm_w,
+                     const oracle_params* p, float* li, double* ssq_li_out,
+                     double* rstd_li_out, uint16_t* li_out, uint16_t* layer_input) {
+    double ssq_li = 0.0;
+    for (int h = 0; h < d; ++h) {
+        float acc = 0.0f;
+        for (int j = 0; j < 4; ++j) acc = fmaf(pc[j], xn[(size_t)j * d + h], acc);
+        li[h] = bf16_to_f32(oracle_bf16_from_f32(acc));
+        ssq_li += (double)li[h] * (double)li[h];
+    }
+    double rstd_li = 1.0 / sqrt(ssq_li / (double)d + (double)p->norm_eps);
+    for (int h = 0; h < d; ++h) {
+        uint16_t lb = oracle_bf16_from_f32(li[h]);
+        if (li_out) li_out[h] = lb;
+        if (layer_input)
+            layer_input[h] = norm_w ? oracle_bf16_from_f64((double)li[h] * rstd_li *
+                                                           (double)bf16_to_f32(norm_w[h]))
+                                    : lb;
+    }
+    *ssq_li_out = ssq_li;
+    *rstd_li_out = rstd_li;
+}
+
 /*
  * The shifted boundary (shifted=1) or the non-shifted pre (shifted=0) for the
  * tokens listed in tok[0..n_tok).  Inputs are the full [T,...] arrays; outputs
@@ -243,32 +272,71 @@ int oracle_run(int shifted, int T, int d, const int* tok, int n_tok,
         /* collapse: lagged pre for the boundary, fresh pre for the non-shifted pre */
         float pc[4];
         for (int j = 0; j < 4; ++j) pc[j] = shifted ? pre_lag[t * 4 + j] : (float)pre[j];
-        double ssq_li = 0.0;
-        for (int h = 0; h < d; ++h) {
-            float acc = 0.0f;
-            for (int j = 0; j < 4; ++j) acc = fmaf(pc[j], xn[(size_t)j * d + h], acc);
-            li[h] = bf16_to_f32(oracle_bf16_from_f32(acc));
-            ssq_li += (double)li[h] * (double)li[h];
-        }
-        double rstd_li = 1.0 / sqrt(ssq_li / (double)d + (double)p->norm_eps);
+        double ssq_li, rstd_li;
+        collapse(xn, pc, d, norm_w, p, li, &ssq_li, &rstd_li,
+                 li_out ? &li_out[(size_t)ti * d] : NULL,
+                 layer_input ? &layer_input[(size_t)ti * d] : NULL);
 
         /* outputs */
         if (xn_out)
             for (size_t k = 0; k < K; ++k) xn_out[ti * K + k] = oracle_bf16_from_f32(xn[k]);
-        for (int h = 0; h < d; ++h) {
-            uint16_t lb = oracle_bf16_from_f32(li[h]);
-            if (li_out) li_out[(size_t)ti * d + h] = lb;
-            if (layer_input) {
-                layer_input[(size_t)ti * d + h] =
-                    norm_w ? oracle_bf16_from_f64((double)li[h] * rstd_li *
-                                                  (double)bf16_to_f32(norm_w[h]))
-                           : lb;
-            }
-        }
         if (mixes_out) memcpy(&mixes_out[(size_t)ti * NMIX], mix, sizeof mix);
         if (ssq_out) ssq_out[ti] = ssq;
         if (rstd_out) rstd_out[ti] = rstd;
         if (ssq_li_out) ssq_li_out[ti] = ssq_li;
+        if (rstd_li_out) rstd_li_out[ti] = rstd_li;
+        if (pre_out) memcpy(&pre_out[(size_t)ti * 4], pre, sizeof pre);
+        if (post_out) memcpy(&post_out[(size_t)ti * 4], post, sizeof post);
+        if (comb_out) memcpy(&comb_out[(size_t)ti * 16], comb, sizeof comb);
+        free(xn);
+        free(li);
+    }
+    return status;
+}
+
+/*
+ * The non-shifted pre from a projection computed elsewhere ("pure" path):
+ * mixes = sum over splits q (in order) of dot_mix[q][t][:], ssq likewise from
+ * sqrsum[q][t] (FP64), then the coefficients and the collapse of X with the fresh
+ * pre exactly as in oracle_run(shifted=0).  Outputs as in oracle_run (mixes_out
+ * and ssq_out receive the summed values).
+ */
+int oracle_pre_from_mixes(int T, int d, int splits, const int* tok, int n_tok,
+                          const uint16_t* X, const float* dot_mix, const float* sqrsum,
+                          const float* scale, const float* base, const uint16_t* norm_w,
+                          const oracle_params* p, uint16_t* layer_input, uint16_t* li_out,
+                          double* mixes_out, double* ssq_out, double* rstd_out,
+                          double* rstd_li_out, double* pre_out, double* post_out,
+                          double* comb_out) {
+    if (T <= 0 || d <= 0 || splits < 1 || n_tok < 0 || p->sinkhorn_iters < 1) return 1;
+    for (int i = 0; i < n_tok; ++i)
+        if (tok[i] < 0 || tok[i] >= T) return 2;
+    const size_t K = (size_t)NHC * d;
+    int status = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int ti = 0; ti < n_tok; ++ti) {
+        const size_t t = (size_t)tok[ti];
+        float* xn = (float*)malloc(sizeof(float) * K);
+        float* li = (float*)malloc(sizeof(float) * d);
+        if (!xn || !li) { free(xn); free(li); status = 3; continue; }
+        for (size_t k = 0; k < K; ++k) xn[k] = bf16_to_f32(X[t * K + k]);
+        double mix[NMIX], ssq = 0.0;
+        for (int n = 0; n < NMIX; ++n) mix[n] = 0.0;
+        for (int q = 0; q < splits; ++q) {
+            for (int n = 0; n < NMIX; ++n) mix[n] += (double)dot_mix[((size_t)q * T + t) * NMIX + n];
+            ssq += (double)sqrsum[(size_t)q * T + t];
+        }
+        double rstd, pre[4], post[4], comb[16];
+        coefficients(mix, ssq, d, scale, base, p, &rstd, pre, post, comb);
+        float pc[4];
+        for (int j = 0; j < 4; ++j) pc[j] = (float)pre[j];
+        double ssq_li, rstd_li;
+        collapse(xn, pc, d, norm_w, p, li, &ssq_li, &rstd_li,
+                 li_out ? &li_out[(size_t)ti * d] : NULL,
+                 layer_input ? &layer_input[(size_t)ti * d] : NULL);
+        if (mixes_out) memcpy(&mixes_out[(size_t)ti * NMIX], mix, sizeof mix);
+        if (ssq_out) ssq_out[ti] = ssq;
+        if (rstd_out) rstd_out[ti] = rstd;
         if (rstd_li_out) rstd_li_out[ti] = rstd_li;
         if (pre_out) memcpy(&pre_out[(size_t)ti * 4], pre, sizeof pre);
         if (post_out) memcpy(&post_out[(size_t)ti * 4], post, sizeof post);

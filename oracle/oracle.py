@@ -56,6 +56,8 @@ def lib():
         L.oracle_sinkhorn.argtypes = [P, ctypes.c_double, ctypes.c_int, P]
         L.oracle_run.restype = ctypes.c_int
         L.oracle_run.argtypes = [ctypes.c_int] * 3 + [P, ctypes.c_int] + [P] * 10 + [P] * 11
+        L.oracle_pre_from_mixes.restype = ctypes.c_int
+        L.oracle_pre_from_mixes.argtypes = [ctypes.c_int] * 3 + [P, ctypes.c_int] + [P] * 7 + [P] * 9
         L.oracle_max_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -159,3 +161,32 @@ def pre(inp, tokens=None, use_norm: bool = False) -> dict:
     """Non-shifted pre on a ``workloads.Inputs`` set (X as the residual)."""
     return run(False, inp.X, None, None, None, None, inp.W, inp.scale, inp.base,
                inp.norm_w if use_norm else None, inp.params(), tokens)
+
+
+def pre_from_mixes(X, dot_mix, sqrsum, scale, base, norm_w, params: dict, tokens=None) -> dict:
+    """Non-shifted pre from precomputed projection partials dot_mix [S,T,24] and
+    sqrsum [S,T] (summed over S in order)."""
+    X = np.ascontiguousarray(X, np.uint16)
+    T, _, d = X.shape
+    dot_mix = np.ascontiguousarray(dot_mix, np.float32)
+    sqrsum = np.ascontiguousarray(sqrsum, np.float32)
+    S = dot_mix.shape[0]
+    assert dot_mix.shape == (S, T, 24) and sqrsum.shape == (S, T)
+    tok = np.arange(T, dtype=np.int32) if tokens is None else np.ascontiguousarray(tokens, np.int32)
+    n = len(tok)
+    scale = np.ascontiguousarray(scale, np.float32)
+    base = np.ascontiguousarray(base, np.float32)
+    norm_w = None if norm_w is None else np.ascontiguousarray(norm_w, np.uint16)
+    out = dict(layer_input=np.empty((n, d), np.uint16), li=np.empty((n, d), np.uint16),
+               mixes=np.empty((n, 24)), ssq=np.empty(n), rstd=np.empty(n),
+               rstd_li=np.empty(n), pre=np.empty((n, 4)), post=np.empty((n, 4)),
+               comb=np.empty((n, 4, 4)))
+    prm = _params(params)
+    rc = lib().oracle_pre_from_mixes(
+        T, d, S, _p(tok), n, _p(X), _p(dot_mix), _p(sqrsum), _p(scale), _p(base), _p(norm_w),
+        ctypes.addressof(prm), _p(out["layer_input"]), _p(out["li"]), _p(out["mixes"]),
+        _p(out["ssq"]), _p(out["rstd"]), _p(out["rstd_li"]), _p(out["pre"]), _p(out["post"]),
+        _p(out["comb"]))
+    if rc:
+        raise ValueError(f"oracle_pre_from_mixes: status {rc}")
+    return out

@@ -124,3 +124,42 @@ def test_prepare_weight_refusals(L):
     assert L.mhc_prepare_weight(P(GB), 1000, P(2 * GB), None) == SHAPE
     assert L.mhc_prepare_weight(P(GB + 4), 1024, P(2 * GB), None) == MISALIGNED
     assert L.mhc_prepare_weight(P(GB), 1024, P(GB + 4096), None) == ALIASING
+
+
+def test_post_refusals(L):
+    P = ctypes.c_void_p
+    b = Buffers(L)
+    a = b.addr
+
+    def post(T=T, d=D, x=a["x"], res=a["residual"], out=a["res_out"]):
+        return L.mhc_post(T, d, P(x) if x else None, P(res), P(a["post"]), P(a["comb"]),
+                          P(out) if out else None, None)
+    assert post(T=0) == INVALID
+    assert post(x=0) == INVALID
+    assert post(out=0) == INVALID
+    assert post(d=1000) == SHAPE
+    assert post(x=a["x"] + 8) == MISALIGNED
+    assert post(out=a["residual"] + 4096) == ALIASING
+
+
+def test_pre_mixes_refusals(L):
+    P = ctypes.c_void_p
+    b = Buffers(L)
+    a = b.addr
+    S = 4
+    dm, sq = a["ws"], a["ws"] + S * T * 96 + 4096   # fake partial buffers past the others
+    prm = ctypes.byref(api.params())
+
+    def pm(T=T, d=D, S=S, res=a["residual"], dm=dm, sq=sq, li=a["li"], prm=prm):
+        return L.mhc_pre_mixes(T, d, S, P(res) if res else None, P(dm) if dm else None, P(sq),
+                               P(a["scale"]), P(a["base"]), None, prm, P(li), P(a["pre_out"]),
+                               P(a["post_out"]), P(a["comb_out"]), None)
+    assert pm(T=0) == INVALID
+    assert pm(S=0) == INVALID
+    assert pm(S=65) == INVALID
+    assert pm(dm=0) == INVALID
+    assert pm(prm=ctypes.byref(api.params(sinkhorn_iters=0))) == INVALID
+    assert pm(d=1000) == SHAPE
+    assert pm(dm=dm + 4) == MISALIGNED
+    assert pm(li=dm + 16) == ALIASING                     # output over the partials
+    assert pm(li=sq + (S - 1) * T * 4) == ALIASING       # ... over the last split of sqrsum

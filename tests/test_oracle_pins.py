@@ -493,3 +493,83 @@ def test_non_shifted_pre_collapses_with_fresh_pre(oracle):
                    dict(PARAMS, pre_eps=0.0))
     assert np.array_equal(r["layer_input"], inp.X[:, 1])
     assert np.array_equal(r["xn"], inp.X)
+
+
+# ---- the pre from precomputed projection partials ("pure" path) ------------------
+
+def _split_k_partials(inp, X, S):
+    """dot_mix [S, T, 24] and sqrsum [S, T]: the tf32(W) x X contraction and the
+    sum of squares over S contiguous column chunks, each in FP64 by numpy and
+    rounded to FP32 (how a split-K GEMM hands them over)."""
+    tw = (inp.W.view(np.uint32).astype(np.uint64) + 0x1000) & 0xFFFFE000
+    tw = tw.astype(np.uint32).view(np.float32).astype(np.float64)
+    xv = bf16_vals(X).reshape(X.shape[0], -1).astype(np.float64)
+    K = xv.shape[1]
+    bounds = np.linspace(0, K, S + 1).astype(int)
+    dm = np.stack([xv[:, a:b] @ tw[:, a:b].T for a, b in zip(bounds[:-1], bounds[1:])])
+    sq = np.stack([(xv[:, a:b] ** 2).sum(1) for a, b in zip(bounds[:-1], bounds[1:])])
+    return dm.astype(np.float32), sq.astype(np.float32)
+
+
+def test_pre_from_mixes_sums_splits_in_fp64(oracle):
+    """mixes and ssq are the FP64 sums of the FP32 partials: within the
+    S-term FP64 bound of math.fsum of the same partials."""
+    inp = _tiny(T=5)
+    dm, sq = _split_k_partials(inp, inp.X, 7)
+    r = oracle.pre_from_mixes(inp.X, dm, sq, inp.scale, inp.base, None, PARAMS)
+    for t in range(5):
+        for n in range(24):
+            terms = dm[:, t, n].astype(np.float64)
+            assert abs(r["mixes"][t, n] - math.fsum(terms.tolist())) <= \
+                7 * 2.0 ** -53 * np.abs(terms).sum()
+        assert abs(r["ssq"][t] - math.fsum(sq[:, t].astype(np.float64).tolist())) <= \
+            7 * 2.0 ** -53 * sq[:, t].sum()
+
+
+def test_pre_from_mixes_split_count_is_invisible(oracle):
+    """All of the projection in split 0 and zeros in the others gives the S=1
+    result bit for bit (index slip over the split axis fails this)."""
+    inp = _tiny(T=4)
+    dm, sq = _split_k_partials(inp, inp.X, 1)
+    one = oracle.pre_from_mixes(inp.X, dm, sq, inp.scale, inp.base, inp.norm_w, PARAMS)
+    for S, q in ((3, 0), (5, 4), (64, 17)):
+        dmS = np.zeros((S,) + dm.shape[1:], np.float32)
+        sqS = np.zeros((S,) + sq.shape[1:], np.float32)
+        dmS[q], sqS[q] = dm[0], sq[0]
+        r = oracle.pre_from_mixes(inp.X, dmS, sqS, inp.scale, inp.base, inp.norm_w, PARAMS)
+        for k in ("layer_input", "pre", "post", "comb", "mixes", "rstd"):
+            assert np.array_equal(r[k], one[k]), (S, q, k)
+
+
+def test_pre_from_mixes_matches_direct_pre(oracle):
+    """Split-K partials from numpy's FP64 GEMM reproduce the direct pre: the
+    coefficients within the FP32 hand-over's error, the layer input within one
+    BF16 step where the collapse lands near a rounding boundary."""
+    inp = _tiny(T=6)
+    dm, sq = _split_k_partials(inp, inp.X, 4)
+    r = oracle.pre_from_mixes(inp.X, dm, sq, inp.scale, inp.base, inp.norm_w, PARAMS)
+    ref = oracle.run(False, inp.X, None, None, None, None, inp.W, inp.scale, inp.base,
+                     inp.norm_w, PARAMS)
+    np.testing.assert_allclose(r["mixes"], ref["mixes"], rtol=1e-6, atol=1e-6)
+    np.testing.assert_allclose(r["rstd"], ref["rstd"], rtol=1e-6)
+    for k in ("pre", "post", "comb"):
+        np.testing.assert_allclose(r[k], ref[k], rtol=1e-5, atol=1e-6)
+    a = bf16_vals(r["layer_input"]).astype(np.float64)
+    b = bf16_vals(ref["layer_input"]).astype(np.float64)
+    assert np.all(np.abs(a - b) <= 2.0 ** -7 * np.abs(b) + 1e-30)
+    assert np.mean(a == b) > 0.95
+
+
+def test_pre_from_mixes_fresh_pre_selects_stream(oracle):
+    """scale = 0, one dominant pre base and pre eps 0: the fresh pre is the unit
+    vector, so the layer input is that stream of the residual, whatever the
+    partials hold."""
+    inp = _tiny(T=3)
+    rng = np.random.default_rng(5)
+    dm = rng.standard_normal((2, 3, 24)).astype(np.float32)
+    sq = rng.uniform(1, 2, (2, 3)).astype(np.float32)
+    scale = np.zeros(3, np.float32)
+    base = inp.base.copy()
+    base[:4] = [-200.0, -200.0, 40.0, -200.0]
+    r = oracle.pre_from_mixes(inp.X, dm, sq, scale, base, None, dict(PARAMS, pre_eps=0.0))
+    assert np.array_equal(r["layer_input"], inp.X[:, 2])

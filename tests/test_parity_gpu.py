@@ -2,10 +2,14 @@
 same seeded inputs.
 
 Bars: prepared weight bit-exact; X' bit-exact (same FP32 FMA chain); layer input
-within 1 BF16 ulp; mixes relative error <= 2e-5 against max(|o|, rms of the
-token's mixes); rstd relative error <= 2e-5; pre / post / comb absolute error
-<= 1e-5.  Full-size configurations compare sampled tokens (the oracle is per
-token) on the full GPU launch.
+of the shifted boundary within 1 BF16 ulp (it collapses with the input pre_lag,
+so both sides round the same FP32 chain); mixes relative error <= 2e-5 against
+max(|o|, rms of the token's mixes); rstd relative error <= 2e-5; pre / post /
+comb absolute error <= 1e-5.  The non-shifted pre collapses with the pre it has
+just computed, FP32 here and FP64 in the oracle: its layer input is held to the
+bound that this difference carries through the collapse (fresh_pre_bound).
+Full-size configurations compare sampled tokens (the oracle is per token) on the
+full GPU launch.
 """
 import numpy as np
 import pytest
@@ -78,15 +82,58 @@ def ulp_distance(a, b):
     return np.abs(order(a) - order(b))
 
 
-def compare(g, o, tokens=None, xn=True, label=""):
-    """g: GPU outputs (all tokens); o: oracle outputs for `tokens`."""
+def fresh_pre_bound(X_bits, g_pre, o, norm_w_bits):
+    """Per-element bound on |layer_input_gpu - layer_input_oracle| for a collapse
+    with a freshly computed pre.  With delta = max_j |pre_gpu[j] - fp32(pre_oracle[j])|
+    and A = sum_j |X_j|, the two exact collapses differ by at most delta*A; each
+    side's 4-term FP32 FMA chain adds at most 2^-21*A, and each BF16 rounding half
+    an ulp (an ulp is at most 2^-7 of the magnitude).  With norm_w the difference
+    scales by rstd_li*|norm_w| (rstd_li's own relative difference, far below 1e-4
+    here, is covered by a 1e-4 margin) before the final rounding."""
+    X = WL.bf16_bits_to_f32(X_bits).astype(np.float64)
+    A = np.abs(X).sum(axis=1)
+    delta = np.abs(g_pre.reshape(-1, 4) - o["pre"].astype(np.float32)).max(axis=1)[:, None]
+    li = np.abs(WL.bf16_bits_to_f32(o["li"]).astype(np.float64))
+    core = (delta + 2.0 ** -23) * A + 2.0 ** -21 * A
+    e_li = core + 2.0 ** -7 * (li + core)
+    if norm_w_bits is None:
+        return e_li
+    w = np.abs(WL.bf16_bits_to_f32(norm_w_bits).astype(np.float64))[None, :]
+    r = o["rstd_li"][:, None]
+    out = np.abs(WL.bf16_bits_to_f32(o["layer_input"]).astype(np.float64))
+    scaled = (e_li * (1 + 1e-4) + 1e-4 * li) * r * w
+    return scaled + 2.0 ** -7 * (out + scaled)
+
+
+def check_fresh_layer_input(g_li, g_pre, o, X_bits, norm_w_bits, label=""):
+    delta = np.abs(g_pre.reshape(-1, 4) - o["pre"]).max()
+    assert delta <= COEF_TOL, f"{label} pre abs {delta:.3g}"
+    a = WL.bf16_bits_to_f32(g_li).astype(np.float64)
+    b = WL.bf16_bits_to_f32(o["layer_input"]).astype(np.float64)
+    bound = fresh_pre_bound(X_bits, g_pre, o, norm_w_bits)
+    excess = np.abs(a - b) - bound
+    assert excess.max() <= 0, f"{label} layer_input off by {excess.max():.3g} beyond the bound"
+    exact = float((g_li == o["layer_input"]).mean())
+    assert exact >= 0.9, f"{label} only {exact:.3f} of the layer input is bit-identical"
+    return exact
+
+
+def compare(g, o, tokens=None, xn=True, label="", fresh=None):
+    """g: GPU outputs (all tokens); o: oracle outputs for `tokens`.  fresh =
+    (X bits, norm_w bits or None) for a collapse with the freshly computed pre."""
     sel = slice(None) if tokens is None else np.asarray(tokens)
     if xn and "xn" in g:
         gx = g["xn"][sel]
         bad = gx != o["xn"]
         assert not bad.any(), f"{label} X' differs at {np.argwhere(bad)[:5]}"
-    d = ulp_distance(g["layer_input"][sel], o["layer_input"])
-    assert d.max() <= 1, f"{label} layer_input ulp distance {d.max()}"
+    if fresh is None:
+        d = ulp_distance(g["layer_input"][sel], o["layer_input"])
+        assert d.max() <= 1, f"{label} layer_input ulp distance {d.max()}"
+    else:
+        Xb, nw = fresh
+        exact = check_fresh_layer_input(g["layer_input"][sel], g["pre"][sel], o, Xb[sel], nw,
+                                        label)
+        d = np.where(g["layer_input"][sel] == o["layer_input"], 0, 1)
     om = o["mixes"]
     rms = np.sqrt((om ** 2).mean(axis=1, keepdims=True))
     rel = np.abs(g["mixes"][sel] - om) / np.maximum(np.abs(om), rms)
@@ -227,14 +274,16 @@ def test_pre_tiny(oracle):
     for norm in (False, True):
         g = dv.pre(norm=norm)
         o = oracle.pre(inp, use_norm=norm)
-        compare(g, o, xn=False, label=f"pre norm={norm}")
+        compare(g, o, xn=False, label=f"pre norm={norm}",
+                fresh=(inp.X, inp.norm_w if norm else None))
 
 
 def test_pre_ragged(oracle):
     say("pre ragged")
     inp = WL.make_inputs(WL.Config("p", d=2048, T=21, seed=5))
     g = Dev(inp).pre(norm=True)
-    compare(g, oracle.pre(inp, use_norm=True), xn=False, label="pre ragged")
+    compare(g, oracle.pre(inp, use_norm=True), xn=False, label="pre ragged",
+            fresh=(inp.X, inp.norm_w))
 
 
 @pytest.mark.parametrize("schedule", ["split", "fused"])
@@ -246,3 +295,34 @@ def test_determinism_decode(schedule):
         b = dv.boundary(schedule=schedule)
         for k in a:
             assert np.array_equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("T,d", [(1, 256), (37, 1024), (300, 7168)])
+def test_post_matches_boundary_residual(oracle, T, d):
+    """The standalone residual update gives the oracle's X' bit for bit."""
+    say(f"post T={T} d={d}")
+    inp = WL.make_inputs(WL.Config("post", d=d, T=T, seed=T + d))
+    dv = Dev(inp)
+    got = host_bits(api.post(dv.x, dv.X, dv.post, dv.comb))
+    torch.cuda.synchronize()
+    tok = sample_tokens(T, seed=3) if T > 64 else None
+    o = oracle.boundary(inp, tokens=tok)
+    assert np.array_equal(got if tok is None else got[tok], o["xn"])
+
+
+@pytest.mark.parametrize("T,d,S", [(1, 256, 1), (37, 1024, 3), (200, 7168, 16), (64, 4096, 64)])
+def test_pre_mixes_against_oracle(oracle, T, d, S):
+    """The pre from precomputed partials: same bars as the direct pre."""
+    say(f"pre_mixes T={T} d={d} splits={S}")
+    inp = WL.make_inputs(WL.Config("pm", d=d, T=T, seed=7 * T + S))
+    dm, sq = WL.make_partials(T, d, S, seed=T + S)
+    dv = Dev(inp)
+    li, pre, post, comb = api.pre_mixes(dv.X, dev_f32(dm), dev_f32(sq), dv.scale, dv.base,
+                                        dv.norm_w, prm=dv.prm())
+    torch.cuda.synchronize()
+    o = oracle.pre_from_mixes(inp.X, dm, sq, inp.scale, inp.base, inp.norm_w, inp.params())
+    for k, g in (("pre", pre), ("post", post), ("comb", comb)):
+        err = np.abs(g.cpu().numpy().reshape(o[k].shape) - o[k]).max()
+        assert err <= COEF_TOL, f"{k} abs {err:.3g}"
+    check_fresh_layer_input(host_bits(li), pre.cpu().numpy(), o, inp.X, inp.norm_w,
+                            label="pre_mixes")
