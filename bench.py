@@ -151,6 +151,86 @@ def decode_numbers(steps, schedule):
                 roofline_frac_cold=b / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
 
 
+def cold_graph_time(torch, make_call, sets, reps=3, min_calls=24):
+    """Per-call device time of make_call(set) rotated over `sets` (distinct
+    buffers whose total exceeds the last-level cache), replayed from a HIP graph."""
+    calls = [make_call(st) for st in sets]
+    calls = calls * max(1, -(-min_calls // len(calls)))
+    return graph_time(torch, calls, reps)
+
+
+def _sets_for(bytes_per_set, cap=64, llc_bytes=256 << 20):
+    return max(2, min(cap, -(-2 * llc_bytes // max(1, bytes_per_set))))
+
+
+def entry_point_numbers():
+    """The other entry points, each on its own workloads, timed cold from HIP
+    graph replays against its algorithmic bytes:
+      mhc_pre_mixes (partials made elsewhere, no norm): T*(10d + 96 + 100*splits) + 108
+      mhc_pre (no norm):                                  T*(10d + 96) + 384d + 108
+      mhc_post:                                           T*(18d + 80)
+    (X read 8d, x read 2d, X' write 8d, layer input write 2d per token; 96 B of
+    coefficients written; 96+4 B of partials read per split.)"""
+    import torch
+
+    from mhc_hyper_connection_boundary_amd import api
+    from mhc_hyper_connection_boundary_amd import workloads as WL
+
+    dev = torch.device("cuda")
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    f = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+    out = {}
+
+    def record(name, T, d, nbytes, us, **extra):
+        gbs = nbytes / (us * 1e-6) / 1e9
+        out[name] = dict(T=T, d=d, us_per_call=us, tokens_per_s=T / (us * 1e-6),
+                         bytes_per_call=nbytes, gbs=gbs, roofline_frac=gbs / HBM_PEAK_GBS,
+                         timing="HIP graph replay, cold (rotating buffer sets)", **extra)
+        print(f"[bench] {name}: {us:.2f} us, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
+
+    for T, d, S in ((4096, 7168, 1), (4096, 4096, 1), (128, 7168, 1), (4096, 7168, 16)):
+        inp = WL.make_inputs(WL.Config("pm", d=d, T=T, seed=11))
+        dm, sq = WL.make_partials(T, d, S, seed=11)
+        base = dict(X=bf(inp.X), dm=f(dm), sq=f(sq), scale=f(inp.scale), base=f(inp.base))
+        nbytes = T * (10 * d + 96 + 100 * S) + 108
+        sets = [base] + [{k: v.clone() for k, v in base.items()}
+                         for _ in range(_sets_for(nbytes) - 1)]
+        prm = api.params(**inp.params())
+        mk = lambda st: (lambda: api.pre_mixes(st["X"], st["dm"], st["sq"], st["scale"],
+                                               st["base"], None, prm=prm))
+        us = cold_graph_time(torch, mk, sets) * 1e3
+        record(f"mhc_pre_mixes T={T} d={d} splits={S}", T, d, nbytes, us, splits=S)
+        del sets, base
+
+    for T, d in ((8192, 7168), (32, 7168)):
+        inp = WL.make_inputs("prefill" if T == 8192 else "decode")
+        base = dict(X=bf(inp.X), x=bf(inp.x), post=f(inp.post_prev), comb=f(inp.comb_prev),
+                    scale=f(inp.scale), base=f(inp.base))
+        W = f(inp.W)
+        prm = api.params(**inp.params())
+        nb_pre = T * (10 * d + 96) + 384 * d + 108
+        nb_post = T * (18 * d + 80)
+        n = _sets_for(min(nb_pre, nb_post))
+        sets = [dict(base, wp=api.prepare_weight(W), ws=api.workspace(T, d, dev))]
+        for _ in range(n - 1):
+            st = {k: v.clone() for k, v in base.items()}
+            st.update(wp=api.prepare_weight(W), ws=api.workspace(T, d, dev))
+            sets.append(st)
+        mk_pre = lambda st: (lambda: api.pre(st["X"], st["wp"], st["scale"], st["base"], None,
+                                             prm=prm, ws=st["ws"]))
+        us = cold_graph_time(torch, mk_pre, sets) * 1e3
+        record(f"mhc_pre T={T} d={d}", T, d, nb_pre, us)
+        for st in sets:
+            st["out"] = torch.empty_like(st["X"])
+        mk_post = lambda st: (lambda: api.post(st["x"], st["X"], st["post"], st["comb"],
+                                               out=st["out"]))
+        us = cold_graph_time(torch, mk_post, sets) * 1e3
+        record(f"mhc_post T={T} d={d}", T, d, nb_post, us)
+        del sets, base
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(inp, budget_s=10.0):
     """The oracle, as it stands, on tokens of the prefill batch: whole passes
     over the batch until about budget_s seconds of wall time have run."""
@@ -245,6 +325,8 @@ def main():
     ap.add_argument("--schedule", default="auto", choices=["auto", "split", "fused"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-entry-points", action="store_true",
+                    help="skip the mhc_pre / mhc_pre_mixes / mhc_post legs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain 1 GiB device copy and exit")
     ap.add_argument("--write-traffic-profile", metavar="DIR",
@@ -287,9 +369,19 @@ def main():
     if not a.no_decode:
         print("[bench] decode T=32", file=sys.stderr, flush=True)
         line["decode_t32"] = decode_numbers(200, a.schedule)
+    if not a.no_entry_points:
+        del w
+        torch.cuda.empty_cache()
+        line["entry_points"] = entry_point_numbers()
+        w = None
     if not a.no_cpu_baseline:
+        if w is None:
+            from mhc_hyper_connection_boundary_amd import workloads as WL
+            inp = WL.make_inputs("prefill")
+        else:
+            inp = w.inp
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(w.inp)
+        line["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(line), flush=True)
 
 

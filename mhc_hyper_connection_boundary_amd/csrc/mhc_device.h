@@ -193,15 +193,22 @@ struct TokenCoef {
     float row[4];
 };
 
-__device__ __forceinline__ TokenCoef coefficients(const float* tot, int i, int hidden,
-                                                  const float* __restrict__ scale,
-                                                  const float* __restrict__ base,
-                                                  const Scalars& p) {
-    TokenCoef o;
+// rstd, pre[i] and post[i] of a token: the cheap part of the coefficients,
+// which the collapse of the non-shifted pre waits for.
+__device__ __forceinline__ void pre_post(TokenCoef& o, const float* tot, int i, int hidden,
+                                         const float* __restrict__ scale,
+                                         const float* __restrict__ base, const Scalars& p) {
     o.rstd = 1.0f / sqrtf(tot[24] / (4.0f * (float)hidden) + p.rms_eps);
-    const float s0 = scale[0], s1 = scale[1], s2 = scale[2];
-    o.pre = sigmoid(__builtin_fmaf(tot[i] * o.rstd, s0, base[i])) + p.pre_eps;
-    o.post = sigmoid(__builtin_fmaf(tot[4 + i] * o.rstd, s1, base[4 + i])) * p.post_mult;
+    o.pre = sigmoid(__builtin_fmaf(tot[i] * o.rstd, scale[0], base[i])) + p.pre_eps;
+    o.post = sigmoid(__builtin_fmaf(tot[4 + i] * o.rstd, scale[1], base[4 + i])) * p.post_mult;
+}
+
+// Row i of the Sinkhorn comb (needs o.rstd from pre_post; all 4 lanes of the
+// quad must call it together).
+__device__ __forceinline__ void comb_row(TokenCoef& o, const float* tot, int i,
+                                         const float* __restrict__ scale,
+                                         const float* __restrict__ base, const Scalars& p) {
+    const float s2 = scale[2];
     float v[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k)
@@ -229,6 +236,15 @@ __device__ __forceinline__ TokenCoef coefficients(const float* tot, int i, int h
     }
 #pragma unroll
     for (int k = 0; k < 4; ++k) o.row[k] = c[k];
+}
+
+__device__ __forceinline__ TokenCoef coefficients(const float* tot, int i, int hidden,
+                                                  const float* __restrict__ scale,
+                                                  const float* __restrict__ base,
+                                                  const Scalars& p) {
+    TokenCoef o;
+    pre_post(o, tot, i, hidden, scale, base, p);
+    comb_row(o, tot, i, scale, base, p);
     return o;
 }
 

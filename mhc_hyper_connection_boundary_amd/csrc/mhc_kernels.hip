@@ -341,38 +341,46 @@ __global__ __launch_bounds__(256) void k_pre_finish(
 
     const int t = blockIdx.x;
     const int tid = threadIdx.x;
-    if (tid < 24)
-        tot[tid] = slice_sum(pl.mix + (size_t)t * pl.mix_tok + tid, 0, 1, pl.splits, pl.mix_split);
-    else if (tid == 24)
-        tot[24] = slice_sum(pl.ssq + (size_t)t * pl.ssq_tok, 0, 1, pl.splits, pl.ssq_split);
-    __syncthreads();
-    TokenCoef o;
-    if (tid < 4) {
-        o = coefficients(tot, tid, hidden, scale, base, p);
-        pre_s[tid] = o.pre;
-    }
-    __syncthreads();  // only pre is needed by the collapse
-    if (tid < 64) {
-        if (tid < 4) {
-            pre_out[(size_t)t * 4 + tid] = o.pre;
-            post_out[(size_t)t * 4 + tid] = o.post;
-            *reinterpret_cast<float4*>(comb_out + (size_t)t * 16 + 4 * tid) =
-                make_float4(o.row[0], o.row[1], o.row[2], o.row[3]);
-            if (mixes_out)
-                for (int k = 0; k < 6; ++k) mixes_out[(size_t)t * 24 + 6 * tid + k] = tot[6 * tid + k];
-            if (rstd_out && tid == 0) rstd_out[t] = o.rstd;
-        }
-    } else {
-        const int u0 = tid - 64;
-        const float pr[4] = {pre_s[0], pre_s[1], pre_s[2], pre_s[3]};
-        const uint16_t* Xrow = X + (size_t)t * 4 * hidden;
-        float ssq_li = 0.0f;
-        for (int cidx = u0; cidx < hidden / 8; cidx += 192) {
-            const int h = cidx * 8;
-            uint4 Xv[4];
+    const int nch = hidden / 8;             // 16-byte chunks of a row
+    const int u0 = tid - 64;                // collapse thread index (waves 1-3)
+    const uint16_t* Xrow = X + (size_t)t * 4 * hidden;
+
+    // Waves 1-3 request their first two chunks of X before anything waits;
+    // wave 0 gathers the token's projection record.
+    uint4 bufA[4], bufB[4];
+    auto load_chunk = [&](uint4 (&b)[4], int cidx) {
+        if (cidx < nch) {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                Xv[j] = *reinterpret_cast<const uint4*>(Xrow + (size_t)j * hidden + h);
+                b[j] = *reinterpret_cast<const uint4*>(Xrow + (size_t)j * hidden + cidx * 8);
+        }
+    };
+    if (tid >= 64) {
+        load_chunk(bufA, u0);
+        load_chunk(bufB, u0 + 192);
+    } else if (tid < 24) {
+        tot[tid] = slice_sum(pl.mix + (size_t)t * pl.mix_tok + tid, 0, 1, pl.splits, pl.mix_split);
+    } else if (tid == 24) {
+        tot[24] = slice_sum(pl.ssq + (size_t)t * pl.ssq_tok, 0, 1, pl.splits, pl.ssq_split);
+    }
+    __syncthreads();
+    // pre is published as soon as it exists: the collapse does not wait for
+    // the Sinkhorn iterations, which wave 0 runs at the end.
+    TokenCoef o;
+    if (tid < 4) {
+        pre_post(o, tot, tid, hidden, scale, base, p);
+        pre_s[tid] = o.pre;
+    }
+    __syncthreads();
+
+    if (tid >= 64) {
+        const float pr[4] = {pre_s[0], pre_s[1], pre_s[2], pre_s[3]};
+        float ssq_li = 0.0f;
+        auto collapse = [&](uint4 (&b)[4], int cidx) {
+            uint4 Xv[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) Xv[j] = b[j];
+            load_chunk(b, cidx + 384);          // two chunks ahead
             uint4 li;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -392,30 +400,49 @@ __global__ __launch_bounds__(256) void k_pre_finish(
                 ssq_li = __builtin_fmaf(bf_hi(lw), bf_hi(lw), ssq_li);
             }
             if (norm_w) li_s[cidx] = li;
-            else *reinterpret_cast<uint4*>(layer_input + (size_t)t * hidden + h) = li;
+            else *reinterpret_cast<uint4*>(layer_input + (size_t)t * hidden + cidx * 8) = li;
+        };
+        for (int cidx = u0; cidx < nch; cidx += 384) {
+            collapse(bufA, cidx);
+            if (cidx + 192 < nch) collapse(bufB, cidx + 192);
         }
         red[u0] = ssq_li;
     }
-    if (!norm_w) return;
-    __syncthreads();
-    if (tid == 0) {
-        float s = 0.0f;
-        for (int i = 0; i < 192; ++i) s += red[i];
-        rli = 1.0f / sqrtf(s / (float)hidden + p.norm_eps);
-    }
-    __syncthreads();
-    const float r = rli;
-    for (int cidx = tid; cidx < hidden / 8; cidx += blockDim.x) {
-        const int h = cidx * 8;
-        const uint4 li = li_s[cidx];
-        const uint4 nw = *reinterpret_cast<const uint4*>(norm_w + h);
-        uint4 out;
+    if (norm_w) {
+        __syncthreads();
+        if (tid >= 64 && tid < 128) {  // fixed-order reduction of the 192 partial sums
+            float v = (red[u0] + red[u0 + 64]) + red[u0 + 128];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const uint32_t a = word(li, q), b = word(nw, q);
-            set_word(out, q, pack_bf16((bf_lo(a) * r) * bf_lo(b), (bf_hi(a) * r) * bf_hi(b)));
+            for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+            if (u0 == 0) rli = 1.0f / sqrtf(v / (float)hidden + p.norm_eps);
         }
-        *reinterpret_cast<uint4*>(layer_input + (size_t)t * hidden + h) = out;
+        __syncthreads();
+        if (tid >= 64) {
+            const float r = rli;
+            for (int cidx = u0; cidx < nch; cidx += 192) {
+                const int h = cidx * 8;
+                const uint4 li = li_s[cidx];
+                const uint4 nw = *reinterpret_cast<const uint4*>(norm_w + h);
+                uint4 out;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t a = word(li, q), b = word(nw, q);
+                    set_word(out, q, pack_bf16((bf_lo(a) * r) * bf_lo(b), (bf_hi(a) * r) * bf_hi(b)));
+                }
+                *reinterpret_cast<uint4*>(layer_input + (size_t)t * hidden + h) = out;
+            }
+        }
+    }
+    // Wave 0: the Sinkhorn comb, overlapping the layer-input work above.
+    if (tid < 4) {
+        comb_row(o, tot, tid, scale, base, p);
+        pre_out[(size_t)t * 4 + tid] = o.pre;
+        post_out[(size_t)t * 4 + tid] = o.post;
+        *reinterpret_cast<float4*>(comb_out + (size_t)t * 16 + 4 * tid) =
+            make_float4(o.row[0], o.row[1], o.row[2], o.row[3]);
+        if (mixes_out)
+            for (int k = 0; k < 6; ++k) mixes_out[(size_t)t * 24 + 6 * tid + k] = tot[6 * tid + k];
+        if (rstd_out && tid == 0) rstd_out[t] = o.rstd;
     }
 }
 
