@@ -143,8 +143,34 @@ def decode_numbers(steps, schedule):
     # 256 MB last-level cache), used in turn, so every call reads from HBM
     sets = [({k: v.clone() for k, v in w.t.items()}, w.wp.clone()) for _ in range(64)]
     cold_ms = graph_time(torch, [lambda t=t, wp=wp: w.call(t, wp) for t, wp in sets], 4)
+    # With a stand-in producer of x (a 16 MB device copy, as the block before
+    # the boundary would be) in front of every call: the boundary alone, then
+    # with the weight prefetch on a forked stream overlapping the producer.
+    src = torch.empty(16 << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    side = torch.cuda.Stream()
+
+    def produced(t, wp, prefetch):
+        def run():
+            main = torch.cuda.current_stream()
+            if prefetch:
+                side.wait_stream(main)
+                with torch.cuda.stream(side):
+                    w.api.prefetch_weight(wp, d, side)
+            dst.copy_(src)
+            if prefetch:
+                main.wait_stream(side)
+            w.call(t, wp)
+        return run
+
+    prod_ms = graph_time(torch, [lambda: dst.copy_(src)] * 64, 4)
+    cold_prod_ms = graph_time(torch, [produced(t, wp, False) for t, wp in sets], 4)
+    cold_pref_ms = graph_time(torch, [produced(t, wp, True) for t, wp in sets], 4)
     return dict(workload="decode d=7168 T=32", timing="HIP graph replay",
                 us_per_call_hot=hot_ms * 1e3, us_per_call_cold=cold_ms * 1e3,
+                producer_us=prod_ms * 1e3,
+                us_per_call_cold_after_producer=(cold_prod_ms - prod_ms) * 1e3,
+                us_per_call_cold_after_producer_with_prefetch=(cold_pref_ms - prod_ms) * 1e3,
                 us_per_call_eager=eager_ms * 1e3,
                 tokens_per_s_hot=T / (hot_ms * 1e-3), tokens_per_s_cold=T / (cold_ms * 1e-3),
                 gbs_cold=b / (cold_ms * 1e-3) / 1e9,

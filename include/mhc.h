@@ -69,12 +69,24 @@ typedef enum {
     MHC_ERR_DEVICE = 6            /* a HIP call or kernel launch failed */
 } mhc_status;
 
-/* Scheduling choice for mhc_boundary (results are identical up to the
- * accumulation order of the FP32 sums; each choice is deterministic). */
+/* Scheduling choice for mhc_boundary and mhc_pre (results are identical up
+ * to the accumulation order of the FP32 sums; each choice is deterministic:
+ * the same call on the same inputs gives the same bits).  FUSED exists for
+ * hidden in {1024, 2048, 4096, 5120, 6144, 7168, 8192}; asked for any other
+ * width it returns MHC_ERR_UNSUPPORTED_SHAPE.
+ *
+ * INVARIANT is the batch-invariant mode (the vLLM page, module notes on the
+ * pinned reduction order of mhc_fused_hc): every FP32 sum of a token runs in
+ * an order fixed by hidden alone, so a token's outputs are bit-identical for
+ * any token count T and any position in the batch.  It runs the split kernels
+ * with one 32-element step per wave (the finest split).  AUTO and SPLIT pick
+ * that same split while ceil(T / 16) * hidden < 131072 (T <= 288 at hidden
+ * 7168), so small decode batches give the same bits under all three. */
 typedef enum {
-    MHC_SCHEDULE_AUTO = 0,        /* pick by token count */
+    MHC_SCHEDULE_AUTO = 0,        /* FUSED from 2048 tokens where it exists, else SPLIT */
     MHC_SCHEDULE_SPLIT = 1,       /* hidden split over many workgroups + finishing kernel */
-    MHC_SCHEDULE_FUSED = 2        /* one workgroup per 16-token tile owns all of hidden */
+    MHC_SCHEDULE_FUSED = 2,       /* one workgroup per 16-token tile owns all of hidden */
+    MHC_SCHEDULE_INVARIANT = 3    /* batch-invariant: split with an order fixed by hidden */
 } mhc_schedule;
 
 /* Runtime scalars (the pages pass them as kernel arguments). */
@@ -85,7 +97,7 @@ typedef struct {
     float sinkhorn_eps;   /* softmax floor and normalisation eps */
     int sinkhorn_iters;   /* >= 1: column passes; row passes = iters - 1 */
     float norm_eps;       /* eps of the layer-input RMSNorm */
-    int schedule;         /* mhc_schedule; mhc_pre ignores it */
+    int schedule;         /* mhc_schedule (mhc_boundary and mhc_pre) */
 } mhc_params;
 
 /* Bytes of the prepared weight for `hidden`: 384 * hidden (0 if unsupported).
@@ -105,7 +117,8 @@ typedef struct {
 size_t mhc_prepared_weight_bytes(int hidden);
 
 /* Device workspace bytes that mhc_pre / mhc_boundary need for `tokens`
- * tokens of `hidden` (partial sums of the split schedule). */
+ * tokens of `hidden` under every schedule (partial sums of the split kernels:
+ * 128 bytes per token per 128 elements of hidden, T * hidden bytes in all). */
 size_t mhc_workspace_bytes(int tokens, int hidden);
 
 /* Round W to TF32, split it into BF16 high/low parts and write them in the
@@ -181,6 +194,16 @@ mhc_status mhc_pre_mixes(int tokens, int hidden, int splits, const uint16_t* res
 mhc_status mhc_post(int tokens, int hidden, const uint16_t* x, const uint16_t* residual,
                     const float* post_prev, const float* comb_prev, uint16_t* residual_out,
                     void* stream);
+
+/* Weight prefetch: reads the prepared weight (384 * hidden bytes, read only)
+ * so that it is resident in the last-level cache when a following mhc_boundary
+ * or mhc_pre reads it.  ROCm has no programmatic dependent launch; the stand-in
+ * for the vLLM page's early weight loads (issued before the kernel waits on
+ * its producer) is to enqueue this on a stream forked from the caller's before
+ * the producer of x, joined back before mhc_boundary, so the weight fetch
+ * overlaps the producer instead of the boundary.  It writes nothing.
+ * Errors: INVALID_ARGUMENT (NULL), UNSUPPORTED_SHAPE, MISALIGNED, DEVICE. */
+mhc_status mhc_prefetch_weight(const void* w_prepared, int hidden, void* stream);
 
 /* Static text for a status code. */
 const char* mhc_status_string(mhc_status status);

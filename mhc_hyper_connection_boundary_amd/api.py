@@ -13,7 +13,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmhc.so")
 ABI_VERSION = 1
 
-SCHEDULES = {"auto": 0, "split": 1, "fused": 2}
+SCHEDULES = {"auto": 0, "split": 1, "fused": 2, "invariant": 3}
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape", 3: "misaligned",
           4: "aliasing", 5: "workspace", 6: "device"}
 
@@ -57,6 +57,8 @@ def lib() -> ctypes.CDLL:
         L.mhc_pre.argtypes = [I, I, P, P, P, P, P, P, P, P, P, P, P, P, P, Z, P]
         L.mhc_pre_mixes.restype = I
         L.mhc_pre_mixes.argtypes = [I, I, I, P, P, P, P, P, P, P, P, P, P, P, P]
+        L.mhc_prefetch_weight.restype = I
+        L.mhc_prefetch_weight.argtypes = [P, I, P]
         L.mhc_post.restype = I
         L.mhc_post.argtypes = [I, I, P, P, P, P, P, P]
         L.mhc_boundary.restype = I
@@ -136,6 +138,12 @@ def boundary(x, residual, post_prev, comb_prev, pre_lag, w_prepared, scale, base
         _ptr(ws), ws.numel(), _stream()))
     res = (nres, post, comb, li, pre)
     return res + (mixes, rstd) if debug else res
+
+
+def prefetch_weight(w_prepared: torch.Tensor, hidden: int, stream=None):
+    """Enqueue a read of the prepared weight (warms the last-level cache)."""
+    st = ctypes.c_void_p((stream or torch.cuda.current_stream()).cuda_stream)
+    _check("mhc_prefetch_weight", lib().mhc_prefetch_weight(_ptr(w_prepared), hidden, st))
 
 
 def post(x, residual, post_prev, comb_prev, out: torch.Tensor | None = None):

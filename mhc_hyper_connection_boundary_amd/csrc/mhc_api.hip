@@ -54,9 +54,16 @@ mhc_status check_params(const mhc_params* p) {
     if (!(p->rms_eps >= 0.f) || !(p->pre_eps >= 0.f) || !(p->sinkhorn_eps >= 0.f) ||
         !(p->norm_eps >= 0.f) || !(p->post_mult == p->post_mult))
         return MHC_ERR_INVALID_ARGUMENT;
-    if (p->schedule < MHC_SCHEDULE_AUTO || p->schedule > MHC_SCHEDULE_FUSED)
+    if (p->schedule < MHC_SCHEDULE_AUTO || p->schedule > MHC_SCHEDULE_INVARIANT)
         return MHC_ERR_INVALID_ARGUMENT;
     return MHC_OK;
+}
+
+// FUSED is honoured (the caller gets UNSUPPORTED_SHAPE where the width has no
+// fused kernel); AUTO takes the fused kernel from kFusedMinTokens tokens.
+bool use_fused(int schedule, int tokens, int hidden) {
+    if (schedule == MHC_SCHEDULE_FUSED) return true;
+    return schedule == MHC_SCHEDULE_AUTO && fused_supported(hidden) && tokens >= kFusedMinTokens;
 }
 
 Scalars scalars(const mhc_params* p) {
@@ -72,12 +79,14 @@ Scalars scalars(const mhc_params* p) {
 
 }  // namespace
 
-SplitPlan split_plan(int T, int hidden) {
+SplitPlan split_plan(int T, int hidden, bool invariant) {
     SplitPlan plan;
     const int nsteps = hidden / kStep;
     const int tiles = ceil_div(T, kTile);
     const long wave_steps = (long)tiles * nsteps;
-    int spw = (int)std::max<long>(1, wave_steps / kTargetWaves);
+    // Batch-invariant: one step per wave whatever T is, so every sum of a token
+    // has the same order for every batch.
+    int spw = invariant ? 1 : (int)std::max<long>(1, wave_steps / kTargetWaves);
     spw = std::min(spw, ceil_div(nsteps, 4));
     plan.steps_per_wave = spw;
     plan.slices = ceil_div(nsteps, 4L * spw);
@@ -87,8 +96,9 @@ SplitPlan split_plan(int T, int hidden) {
     return plan;
 }
 
+// The finest split (one step per wave) has the most slices: enough for every plan.
 size_t split_workspace_bytes(int T, int hidden) {
-    return (size_t)T * split_plan(T, hidden).slices * kPart * sizeof(float);
+    return (size_t)T * split_plan(T, hidden, true).slices * kPart * sizeof(float);
 }
 
 }  // namespace mhc
@@ -161,6 +171,15 @@ mhc_status mhc_pre_mixes(int tokens, int hidden, int splits, const uint16_t* res
     return MHC_OK;
 }
 
+mhc_status mhc_prefetch_weight(const void* w_prepared, int hidden, void* stream) {
+    if (!w_prepared) return MHC_ERR_INVALID_ARGUMENT;
+    if (!shape_ok(hidden)) return MHC_ERR_UNSUPPORTED_SHAPE;
+    if (!aligned(w_prepared)) return MHC_ERR_MISALIGNED;
+    if (launch_prefetch_weight(w_prepared, hidden, (hipStream_t)stream) != hipSuccess)
+        return MHC_ERR_DEVICE;
+    return MHC_OK;
+}
+
 mhc_status mhc_post(int tokens, int hidden, const uint16_t* x, const uint16_t* residual,
                     const float* post_prev, const float* comb_prev, uint16_t* residual_out,
                     void* stream) {
@@ -206,9 +225,17 @@ mhc_status mhc_pre(int tokens, int hidden, const uint16_t* residual, const void*
     if (any_alias(outs, 7, ins, 5)) return MHC_ERR_ALIASING;
     if (!workspace || workspace_bytes < need) return MHC_ERR_WORKSPACE;
 
-    const SplitPlan plan = split_plan(tokens, hidden);
     const Scalars s = scalars(params);
     hipStream_t hs = (hipStream_t)stream;
+    if (use_fused(params->schedule, tokens, hidden)) {
+        if (!fused_supported(hidden)) return MHC_ERR_UNSUPPORTED_SHAPE;
+        if (launch_fused_pre(tokens, hidden, residual, w_prepared, scale, base, norm_w, s,
+                             layer_input, pre, post, comb, mixes, rstd, hs) != hipSuccess)
+            return MHC_ERR_DEVICE;
+        return MHC_OK;
+    }
+    const SplitPlan plan =
+        split_plan(tokens, hidden, params->schedule == MHC_SCHEDULE_INVARIANT);
     float* part = static_cast<float*>(workspace);
     if (launch_partial(false, plan, tokens, hidden, nullptr, residual, nullptr, nullptr, nullptr,
                        w_prepared, nullptr, nullptr, part, hs) != hipSuccess)
@@ -252,21 +279,16 @@ mhc_status mhc_boundary(int tokens, int hidden, const uint16_t* x, const uint16_
 
     const Scalars s = scalars(params);
     hipStream_t hs = (hipStream_t)stream;
-    bool fused = false;
-    if (params->schedule == MHC_SCHEDULE_FUSED) {
+    if (use_fused(params->schedule, tokens, hidden)) {
         if (!fused_supported(hidden)) return MHC_ERR_UNSUPPORTED_SHAPE;
-        fused = true;
-    } else if (params->schedule == MHC_SCHEDULE_AUTO) {
-        fused = fused_supported(hidden) && tokens >= kFusedMinTokens;
-    }
-    if (fused) {
         if (launch_fused(tokens, hidden, x, residual, post_prev, comb_prev, pre_lag, w_prepared,
                          scale, base, norm_w, s, residual_out, layer_input, pre_out, post_out,
                          comb_out, mixes, rstd, hs) != hipSuccess)
             return MHC_ERR_DEVICE;
         return MHC_OK;
     }
-    const SplitPlan plan = split_plan(tokens, hidden);
+    const SplitPlan plan =
+        split_plan(tokens, hidden, params->schedule == MHC_SCHEDULE_INVARIANT);
     float* part = static_cast<float*>(workspace);
     // layer_input first receives li; the finishing kernel rescales it in place.
     if (launch_partial(true, plan, tokens, hidden, x, residual, post_prev, comb_prev, pre_lag,

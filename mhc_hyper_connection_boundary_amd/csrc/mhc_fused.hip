@@ -214,6 +214,217 @@ __global__ __launch_bounds__(512) void k_fused(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Non-shifted pre, fused: one 8-wave workgroup per 16-token tile.  Pass 1
+// streams the tile's X through the sums of squares and the projection (same
+// step order and lane map as k_fused, X' = X).  After the fixed-order
+// reduction wave 0 publishes pre, then runs the Sinkhorn; pass 2 reads the
+// tile's X again, which was read a few tens of microseconds earlier and is
+// normally still in the last-level cache, collapses it with the fresh pre,
+// and parks li as k_fused does (LDS for the first steps, then the
+// layer-input buffer) until rstd_li is known.
+// ---------------------------------------------------------------------------
+struct ActX {
+    uint4 X[2][4];  // [block][stream]
+};
+
+__device__ __forceinline__ void load_x4(ActX& a, const uint16_t* __restrict__ Xrow, int hidden,
+                                        int h) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        a.X[0][j] = load_stream(Xrow + (size_t)j * hidden + h);
+        a.X[1][j] = load_stream(Xrow + (size_t)j * hidden + h + kStep);
+    }
+}
+
+// li = bf16(FMA chain over j of pre[j] * X[j], from 0) for 8 elements; adds li^2.
+__device__ __forceinline__ uint4 collapse8(const uint4 (&Xv)[4], const float (&pr)[4],
+                                           float& ssq_li) {
+    uint4 li;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        float acc[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            acc[e] = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t w = word(Xv[j], q);
+                acc[e] = __builtin_fmaf(pr[j], e ? bf_hi(w) : bf_lo(w), acc[e]);
+            }
+        }
+        const uint32_t lw = pack_bf16(acc[0], acc[1]);
+        set_word(li, q, lw);
+        ssq_li = __builtin_fmaf(bf_lo(lw), bf_lo(lw), ssq_li);
+        ssq_li = __builtin_fmaf(bf_hi(lw), bf_hi(lw), ssq_li);
+    }
+    return li;
+}
+
+template <int S>
+__global__ __launch_bounds__(512) void k_fused_pre(
+    int T, const uint16_t* __restrict__ X, const uint4* __restrict__ wprep,
+    const float* __restrict__ scale, const float* __restrict__ base,
+    const uint16_t* __restrict__ norm_w, Scalars p, uint16_t* __restrict__ layer_input,
+    float* __restrict__ pre_out, float* __restrict__ post_out, float* __restrict__ comb_out,
+    float* __restrict__ mixes_out, float* __restrict__ rstd_out) {
+    using Shape = FusedShape<S>;
+    constexpr int hidden = S * kWide * kWaves;
+    __shared__ uint4 li_lds[Shape::kLiLds > 0 ? Shape::kLiLds : 1][kWaves][2][64];
+    __shared__ float red[kWaves][kTile][24];
+    __shared__ float sq[kWaves][4][kTile];
+    __shared__ float tot[kTile][26];
+    __shared__ float pre_s[kTile][4];
+    __shared__ float rli[kTile];
+
+    const int tile = blockIdx.x;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 15;
+    const int g = lane >> 4;
+    const int t = tile * kTile + n;
+    const size_t tc = t < T ? (size_t)t : (size_t)(T - 1);
+    const uint16_t* Xrow = X + tc * 4 * hidden;
+    uint16_t* li_row = layer_input + tc * hidden;
+
+    // Pass 1: sums of squares and the projection.
+    f32x4_t acc[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    float ssq = 0.0f;
+    ActX cur;
+    load_x4(cur, Xrow, hidden, wave * kWide + g * 8);
+#pragma unroll 1
+    for (int i = 0; i < S; ++i) {
+        const int step = i * kWaves + wave;
+        const int h = step * kWide + g * 8;
+        ActX nxt;
+        if (i + 1 < S) load_x4(nxt, Xrow, hidden, h + kWaves * kWide);
+        square_sum(cur.X[0], ssq);
+        square_sum(cur.X[1], ssq);
+        __builtin_amdgcn_sched_barrier(0);
+        uint4 A0[kFragsPerStep], A1[kFragsPerStep];
+        load_frags(A0, wprep, 2 * step, lane);
+        load_frags(A1, wprep, 2 * step + 1, lane);
+        mfma_step(A0, cur.X[0], acc);
+        mfma_step(A1, cur.X[1], acc);
+        cur = nxt;
+    }
+    // Pass 2's first activations are requested before the reductions.
+    load_x4(cur, Xrow, hidden, wave * kWide + g * 8);
+#pragma unroll
+    for (int m = 0; m < 3; ++m)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) red[wave][n][8 * m + 2 * g + j] = mix_of(acc, m, j);
+    sq[wave][g][n] = ssq;
+    __syncthreads();
+    if (threadIdx.x < kTile * 25) {
+        const int tn = threadIdx.x / 25, v = threadIdx.x % 25;
+        float sum = 0.0f;
+        if (v < 24) {
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) sum += red[w][tn][v];
+        } else {
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) sum += sq[w][q][tn];
+        }
+        tot[tn][v] = sum;
+    }
+    __syncthreads();
+    TokenCoef o;
+    const int ctn = lane >> 2, ci = lane & 3;
+    if (wave == 0) {
+        pre_post(o, tot[ctn], ci, hidden, scale, base, p);
+        pre_s[ctn][ci] = o.pre;
+    }
+    __syncthreads();
+    if (wave == 0) {
+        comb_row(o, tot[ctn], ci, scale, base, p);
+        const int tt = tile * kTile + ctn;
+        if (tt < T) {
+            pre_out[(size_t)tt * 4 + ci] = o.pre;
+            post_out[(size_t)tt * 4 + ci] = o.post;
+            *reinterpret_cast<float4*>(comb_out + (size_t)tt * 16 + 4 * ci) =
+                make_float4(o.row[0], o.row[1], o.row[2], o.row[3]);
+            if (mixes_out)
+                for (int k = 0; k < 6; ++k) mixes_out[(size_t)tt * 24 + 6 * ci + k] = tot[ctn][6 * ci + k];
+            if (rstd_out && ci == 0) rstd_out[tt] = o.rstd;
+        }
+    }
+
+    // Pass 2: the collapse with the fresh pre.
+    const float pr[4] = {pre_s[n][0], pre_s[n][1], pre_s[n][2], pre_s[n][3]};
+    float ssq_li = 0.0f;
+#pragma unroll 1
+    for (int i = 0; i < S; ++i) {
+        const int step = i * kWaves + wave;
+        const int h = step * kWide + g * 8;
+        ActX nxt;
+        if (i + 1 < S) load_x4(nxt, Xrow, hidden, h + kWaves * kWide);
+        const uint4 l0 = collapse8(cur.X[0], pr, ssq_li);
+        const uint4 l1 = collapse8(cur.X[1], pr, ssq_li);
+        if (i < Shape::kLiLds) {
+            li_lds[i][wave][0][lane] = l0;
+            li_lds[i][wave][1][lane] = l1;
+        } else {
+            store_stream(li_row + h, l0);
+            store_stream(li_row + h + kStep, l1);
+        }
+        cur = nxt;
+    }
+    sq[wave][g][n] = ssq_li;
+    __syncthreads();
+    if (threadIdx.x < kTile) {
+        float sum = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) sum += sq[w][q][threadIdx.x];
+        rli[threadIdx.x] = 1.0f / sqrtf(sum / (float)hidden + p.norm_eps);
+    }
+    __syncthreads();
+    const float r = rli[n];
+    auto emit = [&](int h, const uint4& li) {
+        uint4 out = li;
+        if (norm_w) {
+            const uint4 nw = *reinterpret_cast<const uint4*>(norm_w + h);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t a = word(li, q), b = word(nw, q);
+                set_word(out, q, pack_bf16((bf_lo(a) * r) * bf_lo(b), (bf_hi(a) * r) * bf_hi(b)));
+            }
+        }
+        store_stream(li_row + h, out);
+    };
+#pragma unroll 2
+    for (int i = 0; i < Shape::kLiLds; ++i) {
+        const int h = (i * kWaves + wave) * kWide + g * 8;
+        emit(h, li_lds[i][wave][0][lane]);
+        emit(h + kStep, li_lds[i][wave][1][lane]);
+    }
+    if (norm_w) {  // (without norm_w the parked li already is the layer input)
+#pragma unroll 2
+        for (int i = Shape::kLiLds; i < S; ++i) {
+            const int h = (i * kWaves + wave) * kWide + g * 8;
+            const uint4 l0 = *reinterpret_cast<const uint4*>(li_row + h);
+            const uint4 l1 = *reinterpret_cast<const uint4*>(li_row + h + kStep);
+            emit(h, l0);
+            emit(h + kStep, l1);
+        }
+    }
+}
+
+template <int S>
+hipError_t launch_pre_s(int T, const uint16_t* X, const void* wprep, const float* scale,
+                        const float* base, const uint16_t* norm_w, const Scalars& p,
+                        uint16_t* layer_input, float* pre_out, float* post_out, float* comb_out,
+                        float* mixes, float* rstd, hipStream_t stream) {
+    hipLaunchKernelGGL(k_fused_pre<S>, dim3((T + kTile - 1) / kTile), dim3(kWaves * 64), 0,
+                       stream, T, X, reinterpret_cast<const uint4*>(wprep), scale, base, norm_w,
+                       p, layer_input, pre_out, post_out, comb_out, mixes, rstd);
+    return hipGetLastError();
+}
+
 template <int S>
 hipError_t launch_s(int T, const uint16_t* x, const uint16_t* X, const float* post_prev,
                     const float* comb_prev, const float* pre_lag, const void* wprep,
@@ -262,6 +473,29 @@ hipError_t launch_fused(int T, int hidden, const uint16_t* x, const uint16_t* X,
             return hipErrorInvalidValue;
     }
 #undef MHC_FUSED_CASE
+}
+
+hipError_t launch_fused_pre(int T, int hidden, const uint16_t* X, const void* wprep,
+                            const float* scale, const float* base, const uint16_t* norm_w,
+                            const Scalars& p, uint16_t* layer_input, float* pre_out,
+                            float* post_out, float* comb_out, float* mixes, float* rstd,
+                            hipStream_t stream) {
+#define MHC_FUSED_PRE_CASE(D)                                                                  \
+    case D:                                                                                    \
+        return launch_pre_s<D / 512>(T, X, wprep, scale, base, norm_w, p, layer_input, pre_out, \
+                                     post_out, comb_out, mixes, rstd, stream);
+    switch (hidden) {
+        MHC_FUSED_PRE_CASE(1024)
+        MHC_FUSED_PRE_CASE(2048)
+        MHC_FUSED_PRE_CASE(4096)
+        MHC_FUSED_PRE_CASE(5120)
+        MHC_FUSED_PRE_CASE(6144)
+        MHC_FUSED_PRE_CASE(7168)
+        MHC_FUSED_PRE_CASE(8192)
+        default:
+            return hipErrorInvalidValue;
+    }
+#undef MHC_FUSED_PRE_CASE
 }
 
 }  // namespace mhc

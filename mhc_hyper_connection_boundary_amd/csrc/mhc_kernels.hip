@@ -473,6 +473,24 @@ __global__ __launch_bounds__(256) void k_post(int hidden, const uint16_t* __rest
     for (int s = 0; s < 4; ++s) *reinterpret_cast<uint4*>(xn_out + (t * 4 + s) * hidden + h) = Xn[s];
 }
 
+// ---------------------------------------------------------------------------
+// Weight prefetch: every thread reads four 16-byte words of the prepared weight
+// so that its lines are resident in the last-level cache (and the reading
+// XCD's L2) when the boundary runs.  The empty asm consumes each value, so the
+// loads are kept; nothing is written.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_prefetch(const uint4* __restrict__ w, int n_words) {
+    const int base = blockIdx.x * 1024 + threadIdx.x;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int i = base + k * 256;
+        if (i < n_words) {
+            const uint4 v = w[i];
+            asm volatile("" ::"v"(v.x), "v"(v.y), "v"(v.z), "v"(v.w));
+        }
+    }
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -482,6 +500,13 @@ hipError_t launch_prepare_weight(const float* w, int hidden, void* out, hipStrea
     const int n_words = (hidden / kStep) * kFragsPerStep * 64;
     hipLaunchKernelGGL(k_prepare_weight, dim3((n_words + 255) / 256), dim3(256), 0, stream, w,
                        hidden, reinterpret_cast<uint4*>(out), n_words);
+    return hipGetLastError();
+}
+
+hipError_t launch_prefetch_weight(const void* wprep, int hidden, hipStream_t stream) {
+    const int n_words = (hidden / kStep) * kFragsPerStep * 64;
+    hipLaunchKernelGGL(k_prefetch, dim3((n_words + 1023) / 1024), dim3(256), 0, stream,
+                       reinterpret_cast<const uint4*>(wprep), n_words);
     return hipGetLastError();
 }
 

@@ -22,10 +22,12 @@ struct SplitPlan {
     int finish_width;
 };
 
-SplitPlan split_plan(int T, int hidden);
+SplitPlan split_plan(int T, int hidden, bool invariant);
 size_t split_workspace_bytes(int T, int hidden);
 
 hipError_t launch_prepare_weight(const float* w, int hidden, void* out, hipStream_t stream);
+
+hipError_t launch_prefetch_weight(const void* wprep, int hidden, hipStream_t stream);
 
 hipError_t launch_post(int T, int hidden, const uint16_t* x, const uint16_t* X,
                        const float* post_prev, const float* comb_prev, uint16_t* xn_out,
@@ -64,5 +66,13 @@ hipError_t launch_fused(int T, int hidden, const uint16_t* x, const uint16_t* X,
                         const uint16_t* norm_w, const Scalars& p, uint16_t* xn_out,
                         uint16_t* layer_input, float* pre_out, float* post_out, float* comb_out,
                         float* mixes, float* rstd, hipStream_t stream);
+
+// Non-shifted pre, fused: one 8-wave workgroup per 16-token tile, two passes
+// over the tile's X (fused_supported widths).
+hipError_t launch_fused_pre(int T, int hidden, const uint16_t* X, const void* wprep,
+                            const float* scale, const float* base, const uint16_t* norm_w,
+                            const Scalars& p, uint16_t* layer_input, float* pre_out,
+                            float* post_out, float* comb_out, float* mixes, float* rstd,
+                            hipStream_t stream);
 
 }  // namespace mhc

@@ -40,7 +40,10 @@ def test_exports_every_declared_symbol(L):
 def test_size_queries(L):
     assert L.mhc_prepared_weight_bytes(7168) == 384 * 7168 == 2752512
     assert L.mhc_prepared_weight_bytes(7000) == 0
-    assert L.mhc_workspace_bytes(32, 7168) > 0
+    # every schedule fits: the finest split's records, 128 B per token per 128 of hidden
+    assert L.mhc_workspace_bytes(32, 7168) == 32 * 7168
+    assert L.mhc_workspace_bytes(8192, 7168) == 8192 * 7168
+    assert L.mhc_workspace_bytes(3, 1280) == 3 * 1280
     assert L.mhc_workspace_bytes(0, 7168) == 0
     assert L.mhc_workspace_bytes(32, 100) == 0
 
@@ -86,6 +89,9 @@ def test_boundary_refusals(L):
     assert call(L, b, prm=ctypes.byref(api.params(sinkhorn_iters=0))) == INVALID
     assert call(L, b, prm=ctypes.byref(api.params(rms_eps=-1.0))) == INVALID
     assert call(L, b, prm=ctypes.byref(api.params(norm_eps=float("nan")))) == INVALID
+    bad_schedule = api.params()
+    bad_schedule.schedule = 4
+    assert call(L, b, prm=ctypes.byref(bad_schedule)) == INVALID
     assert call(L, b, d=1000) == SHAPE
     assert call(L, b, d=128) == SHAPE
     assert call(L, b, T=(1 << 20) + 1) == SHAPE
@@ -163,3 +169,10 @@ def test_pre_mixes_refusals(L):
     assert pm(dm=dm + 4) == MISALIGNED
     assert pm(li=dm + 16) == ALIASING                     # output over the partials
     assert pm(li=sq + (S - 1) * T * 4) == ALIASING       # ... over the last split of sqrsum
+
+
+def test_prefetch_weight_refusals(L):
+    P = ctypes.c_void_p
+    assert L.mhc_prefetch_weight(None, 1024, None) == INVALID
+    assert L.mhc_prefetch_weight(P(GB), 1000, None) == SHAPE
+    assert L.mhc_prefetch_weight(P(GB + 8), 1024, None) == MISALIGNED

@@ -278,6 +278,38 @@ def test_pre_tiny(oracle):
                 fresh=(inp.X, inp.norm_w if norm else None))
 
 
+@pytest.mark.parametrize("T,d", [(37, 1024), (16, 2048), (50, 7168)])
+@pytest.mark.parametrize("schedule", ["split", "fused"])
+def test_pre_schedules(oracle, T, d, schedule):
+    """Both schedules of the non-shifted pre, ragged tails included."""
+    say(f"pre T={T} d={d} {schedule}")
+    inp = WL.make_inputs(WL.Config("ps", d=d, T=T, seed=T + d))
+    dv = Dev(inp)
+    for norm in (True, False):
+        g = dv.pre(norm=norm, schedule=schedule)
+        compare(g, oracle.pre(inp, use_norm=norm), xn=False, label=f"pre {schedule} norm={norm}",
+                fresh=(inp.X, inp.norm_w if norm else None))
+
+
+@pytest.mark.parametrize("name", ["prefill", "stress"])
+def test_pre_large_sampled(oracle, name):
+    """The full-size launch (automatic schedule, fused at these sizes) on sampled tokens."""
+    say(f"pre {name} sampled")
+    inp = WL.make_inputs(name)
+    g = Dev(inp).pre(norm=True)
+    tok = sample_tokens(inp.T, seed=11)
+    o = oracle.pre(inp, tokens=tok, use_norm=True)
+    compare(g, o, tokens=tok, xn=False, label=f"pre {name}", fresh=(inp.X, inp.norm_w))
+
+
+def test_pre_fused_refuses_unsupported_width():
+    inp = WL.make_inputs(WL.Config("pu", d=1280, T=4, seed=1))
+    dv = Dev(inp)
+    with pytest.raises(api.MhcError) as e:
+        dv.pre(schedule="fused")
+    assert e.value.status == 2
+
+
 def test_pre_ragged(oracle):
     say("pre ragged")
     inp = WL.make_inputs(WL.Config("p", d=2048, T=21, seed=5))
@@ -326,3 +358,62 @@ def test_pre_mixes_against_oracle(oracle, T, d, S):
         assert err <= COEF_TOL, f"{k} abs {err:.3g}"
     check_fresh_layer_input(host_bits(li), pre.cpu().numpy(), o, inp.X, inp.norm_w,
                             label="pre_mixes")
+
+
+def prefix(inp, T):
+    """The first T tokens of an input set (same weights)."""
+    import dataclasses
+    return dataclasses.replace(inp, X=inp.X[:T], x=inp.x[:T], post_prev=inp.post_prev[:T],
+                               comb_prev=inp.comb_prev[:T], pre_lag=inp.pre_lag[:T])
+
+
+@pytest.mark.parametrize("d,Ts", [(1024, (1, 5, 16, 37, 300, 2100)), (7168, (1, 3, 32, 40))])
+def test_invariant_bits_do_not_depend_on_batch(oracle, d, Ts):
+    """Batch-invariant schedule: every output of a token is bit-identical
+    whatever the token count (boundary and pre), and within the bars of the
+    oracle."""
+    say(f"invariant d={d} T={Ts}")
+    full = WL.make_inputs(WL.Config("inv", d=d, T=max(Ts), seed=d + 1))
+    ref_b = ref_p = None
+    for T in sorted(Ts, reverse=True):
+        dv = Dev(prefix(full, T))
+        b = dv.boundary(schedule="invariant")
+        p = dv.pre(norm=True, schedule="invariant")
+        if ref_b is None:
+            ref_b, ref_p = b, p
+            tok = sample_tokens(T, n=24, seed=d) if T > 64 else None
+            compare(b, oracle.boundary(prefix(full, T), tokens=tok), tokens=tok,
+                    label="invariant boundary")
+            compare(p, oracle.pre(prefix(full, T), tokens=tok, use_norm=True), tokens=tok,
+                    xn=False, label="invariant pre", fresh=(full.X[:T], full.norm_w))
+            continue
+        for k in b:
+            assert np.array_equal(b[k], ref_b[k][:T]), f"boundary {k} differs at T={T}"
+        for k in p:
+            assert np.array_equal(p[k], ref_p[k][:T]), f"pre {k} differs at T={T}"
+
+
+def test_invariant_equals_auto_for_small_batches():
+    """At hidden 7168 the automatic split for T <= 288 is the invariant one."""
+    say("invariant vs auto")
+    dv = Dev(WL.make_inputs("decode"))
+    a, b = dv.boundary(schedule="auto"), dv.boundary(schedule="invariant")
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_prefetch_weight_changes_nothing():
+    """The prefetch reads only: a boundary after it gives the same bits, also
+    when the prefetch runs on a forked stream."""
+    say("prefetch weight")
+    dv = Dev(WL.make_inputs("decode"))
+    a = dv.boundary()
+    api.prefetch_weight(dv.wp, dv.inp.d)
+    b = dv.boundary()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    api.prefetch_weight(dv.wp, dv.inp.d, side)
+    torch.cuda.current_stream().wait_stream(side)
+    c = dv.boundary()
+    for k in a:
+        assert np.array_equal(a[k], b[k]) and np.array_equal(a[k], c[k]), k
