@@ -189,14 +189,16 @@ def _sets_for(bytes_per_set, cap=64, llc_bytes=256 << 20):
     return max(2, min(cap, -(-2 * llc_bytes // max(1, bytes_per_set))))
 
 
-def entry_point_numbers():
-    """The other entry points, each on its own workloads, timed cold from HIP
-    graph replays against its algorithmic bytes:
+def entry_point_numbers(only=None):
+    """The other entry points and schedules, each on its own workload, timed
+    cold from HIP graph replays against its algorithmic bytes:
       mhc_pre_mixes (partials made elsewhere, no norm): T*(10d + 96 + 100*splits) + 108
       mhc_pre (no norm):                                  T*(10d + 96) + 384d + 108
       mhc_post:                                           T*(18d + 80)
+      mhc_boundary, batch-invariant schedule:             T*(20d + 192) + 386d + 108
     (X read 8d, x read 2d, X' write 8d, layer input write 2d per token; 96 B of
-    coefficients written; 96+4 B of partials read per split.)"""
+    coefficients written; 96+4 B of partials read per split.)  `only` keeps the
+    legs whose name contains it (for profiling one kernel at a time)."""
     import torch
 
     from mhc_hyper_connection_boundary_amd import api
@@ -214,7 +216,13 @@ def entry_point_numbers():
                          timing="HIP graph replay, cold (rotating buffer sets)", **extra)
         print(f"[bench] {name}: {us:.2f} us, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
 
-    for T, d, S in ((4096, 7168, 1), (4096, 4096, 1), (128, 7168, 1), (4096, 7168, 16)):
+    def wanted(name):
+        if only is None:
+            return True
+        exact = any(n == only for n, *_ in legs)
+        return name == only if exact else only in name
+
+    def pre_mixes_leg(T, d, S):
         inp = WL.make_inputs(WL.Config("pm", d=d, T=T, seed=11))
         dm, sq = WL.make_partials(T, d, S, seed=11)
         base = dict(X=bf(inp.X), dm=f(dm), sq=f(sq), scale=f(inp.scale), base=f(inp.base))
@@ -224,36 +232,65 @@ def entry_point_numbers():
         prm = api.params(**inp.params())
         mk = lambda st: (lambda: api.pre_mixes(st["X"], st["dm"], st["sq"], st["scale"],
                                                st["base"], None, prm=prm))
-        us = cold_graph_time(torch, mk, sets) * 1e3
-        record(f"mhc_pre_mixes T={T} d={d} splits={S}", T, d, nbytes, us, splits=S)
-        del sets, base
+        return nbytes, cold_graph_time(torch, mk, sets) * 1e3
 
-    for T, d in ((8192, 7168), (32, 7168)):
-        inp = WL.make_inputs("prefill" if T == 8192 else "decode")
+    def residual_sets(T, d, nbytes):
+        inp = WL.make_inputs("prefill" if T == 8192 else "decode", T=T)
         base = dict(X=bf(inp.X), x=bf(inp.x), post=f(inp.post_prev), comb=f(inp.comb_prev),
-                    scale=f(inp.scale), base=f(inp.base))
+                    pre_lag=f(inp.pre_lag), scale=f(inp.scale), base=f(inp.base),
+                    norm_w=bf(inp.norm_w))
         W = f(inp.W)
-        prm = api.params(**inp.params())
-        nb_pre = T * (10 * d + 96) + 384 * d + 108
-        nb_post = T * (18 * d + 80)
-        n = _sets_for(min(nb_pre, nb_post))
-        sets = [dict(base, wp=api.prepare_weight(W), ws=api.workspace(T, d, dev))]
-        for _ in range(n - 1):
-            st = {k: v.clone() for k, v in base.items()}
-            st.update(wp=api.prepare_weight(W), ws=api.workspace(T, d, dev))
+        sets = []
+        for k in range(_sets_for(nbytes)):
+            st = base if k == 0 else {kk: v.clone() for kk, v in base.items()}
+            st = dict(st, wp=api.prepare_weight(W), ws=api.workspace(T, d, dev))
             sets.append(st)
-        mk_pre = lambda st: (lambda: api.pre(st["X"], st["wp"], st["scale"], st["base"], None,
-                                             prm=prm, ws=st["ws"]))
-        us = cold_graph_time(torch, mk_pre, sets) * 1e3
-        record(f"mhc_pre T={T} d={d}", T, d, nb_pre, us)
+        return inp, sets
+
+    def pre_leg(T, d):
+        nbytes = T * (10 * d + 96) + 384 * d + 108
+        inp, sets = residual_sets(T, d, nbytes)
+        prm = api.params(**inp.params())
+        mk = lambda st: (lambda: api.pre(st["X"], st["wp"], st["scale"], st["base"], None,
+                                         prm=prm, ws=st["ws"]))
+        return nbytes, cold_graph_time(torch, mk, sets) * 1e3
+
+    def post_leg(T, d):
+        nbytes = T * (18 * d + 80)
+        _, sets = residual_sets(T, d, nbytes)
         for st in sets:
             st["out"] = torch.empty_like(st["X"])
-        mk_post = lambda st: (lambda: api.post(st["x"], st["X"], st["post"], st["comb"],
-                                               out=st["out"]))
-        us = cold_graph_time(torch, mk_post, sets) * 1e3
-        record(f"mhc_post T={T} d={d}", T, d, nb_post, us)
-        del sets, base
-    torch.cuda.empty_cache()
+        mk = lambda st: (lambda: api.post(st["x"], st["X"], st["post"], st["comb"], out=st["out"]))
+        return nbytes, cold_graph_time(torch, mk, sets) * 1e3
+
+    def invariant_leg(T, d):
+        nbytes = algorithmic_bytes(T, d)
+        inp, sets = residual_sets(T, d, nbytes)
+        prm = api.params(**inp.params(), schedule="invariant")
+        for st in sets:
+            st["o"] = dict(residual_out=torch.empty_like(st["X"]),
+                           layer_input=torch.empty(T, d, dtype=torch.bfloat16, device=dev),
+                           pre=torch.empty(T, 4, device=dev), post=torch.empty(T, 4, 1, device=dev),
+                           comb=torch.empty(T, 4, 4, device=dev))
+        mk = lambda st: (lambda: api.boundary(st["x"], st["X"], st["post"], st["comb"],
+                                              st["pre_lag"], st["wp"], st["scale"], st["base"],
+                                              st["norm_w"], prm=prm, ws=st["ws"], out=st["o"]))
+        return nbytes, cold_graph_time(torch, mk, sets) * 1e3
+
+    legs = []
+    for T, d, S in ((4096, 7168, 1), (4096, 4096, 1), (128, 7168, 1), (4096, 7168, 16)):
+        legs.append((f"mhc_pre_mixes T={T} d={d} splits={S}", T, d,
+                     lambda T=T, d=d, S=S: pre_mixes_leg(T, d, S), dict(splits=S)))
+    for T in (8192, 32):
+        legs.append((f"mhc_pre T={T} d=7168", T, 7168, lambda T=T: pre_leg(T, 7168), {}))
+        legs.append((f"mhc_post T={T} d=7168", T, 7168, lambda T=T: post_leg(T, 7168), {}))
+        legs.append((f"mhc_boundary invariant T={T} d=7168", T, 7168,
+                     lambda T=T: invariant_leg(T, 7168), {}))
+    for name, T, d, fn, extra in legs:
+        if wanted(name):
+            nbytes, us = fn()
+            record(name, T, d, nbytes, us, **extra)
+            torch.cuda.empty_cache()
     return out
 
 
@@ -331,8 +368,8 @@ def write_traffic_profile(prof_dir):
         f"algorithmic_bytes_per_call: {algorithmic_bytes(T, d)}",
         f"traffic_over_algorithmic: {traffic / algorithmic_bytes(T, d):.3f}",
         "commands (from the repository root, TMPDIR=/tmp):",
-        "  rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/fetch_boundary -o run -- python bench.py --steps 5 --warmup 2 --no-decode --no-cpu-baseline",
-        "  rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/write_boundary -o run -- python bench.py --steps 5 --warmup 2 --no-decode --no-cpu-baseline",
+        "  rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/fetch_boundary -o run -- python bench.py --steps 5 --warmup 2 --no-decode --no-cpu-baseline --no-entry-points",
+        "  rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/write_boundary -o run -- python bench.py --steps 5 --warmup 2 --no-decode --no-cpu-baseline --no-entry-points",
         "  rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/fetch_copy -o run -- python bench.py --copy-calibration",
         "  rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/write_copy -o run -- python bench.py --copy-calibration",
         "  python bench.py --write-traffic-profile <dir>",
@@ -352,7 +389,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-entry-points", action="store_true",
-                    help="skip the mhc_pre / mhc_pre_mixes / mhc_post legs")
+                    help="skip the mhc_pre / mhc_pre_mixes / mhc_post / invariant legs")
+    ap.add_argument("--leg", metavar="NAME",
+                    help="run only the entry-point legs whose name contains NAME and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain 1 GiB device copy and exit")
     ap.add_argument("--write-traffic-profile", metavar="DIR",
@@ -368,6 +407,9 @@ def main():
 
     if a.copy_calibration:
         print(json.dumps(copy_calibration()), flush=True)
+        return
+    if a.leg:
+        print(json.dumps(entry_point_numbers(a.leg)), flush=True)
         return
 
     import torch

@@ -193,26 +193,52 @@ struct TokenCoef {
     float row[4];
 };
 
+// 1/sqrt(x): the hardware estimate (v_rsq_f32, about 1 ulp) refined by one
+// Newton-Raphson step y(1.5 - 0.5 x y^2); x below the smallest normal takes the
+// IEEE path.  Used for rstd and rstd_li, whose arguments are sums of squares
+// plus eps.
+__device__ __forceinline__ float rsqrt_nr(float x) {
+    if (!(x >= 1.17549435e-38f)) return 1.0f / sqrtf(x);
+    const float y = __builtin_amdgcn_rsqf(x);
+    return y * __builtin_fmaf(-0.5f * x * y, y, 1.5f);
+}
+
+// scale[0..2] and the bases of coefficient row i (pre[i], post[i], comb row
+// i), loaded by the lane that will compute that row, ahead of the reductions.
+struct CoefParams {
+    float s0, s1, s2, bpre, bpost;
+    float bcomb[4];
+};
+
+__device__ __forceinline__ CoefParams load_coef_params(const float* __restrict__ scale,
+                                                       const float* __restrict__ base, int i) {
+    CoefParams c;
+    c.s0 = scale[0];
+    c.s1 = scale[1];
+    c.s2 = scale[2];
+    c.bpre = base[i];
+    c.bpost = base[4 + i];
+    const float4 b = *reinterpret_cast<const float4*>(base + 8 + 4 * i);
+    c.bcomb[0] = b.x; c.bcomb[1] = b.y; c.bcomb[2] = b.z; c.bcomb[3] = b.w;
+    return c;
+}
+
 // rstd, pre[i] and post[i] of a token: the cheap part of the coefficients,
 // which the collapse of the non-shifted pre waits for.
 __device__ __forceinline__ void pre_post(TokenCoef& o, const float* tot, int i, int hidden,
-                                         const float* __restrict__ scale,
-                                         const float* __restrict__ base, const Scalars& p) {
-    o.rstd = 1.0f / sqrtf(tot[24] / (4.0f * (float)hidden) + p.rms_eps);
-    o.pre = sigmoid(__builtin_fmaf(tot[i] * o.rstd, scale[0], base[i])) + p.pre_eps;
-    o.post = sigmoid(__builtin_fmaf(tot[4 + i] * o.rstd, scale[1], base[4 + i])) * p.post_mult;
+                                         const CoefParams& cp, const Scalars& p) {
+    o.rstd = rsqrt_nr(tot[24] * (0.25f / (float)hidden) + p.rms_eps);
+    o.pre = sigmoid(__builtin_fmaf(tot[i] * o.rstd, cp.s0, cp.bpre)) + p.pre_eps;
+    o.post = sigmoid(__builtin_fmaf(tot[4 + i] * o.rstd, cp.s1, cp.bpost)) * p.post_mult;
 }
 
 // Row i of the Sinkhorn comb (needs o.rstd from pre_post; all 4 lanes of the
 // quad must call it together).
 __device__ __forceinline__ void comb_row(TokenCoef& o, const float* tot, int i,
-                                         const float* __restrict__ scale,
-                                         const float* __restrict__ base, const Scalars& p) {
-    const float s2 = scale[2];
+                                         const CoefParams& cp, const Scalars& p) {
     float v[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-        v[k] = __builtin_fmaf(tot[8 + 4 * i + k] * o.rstd, s2, base[8 + 4 * i + k]);
+    for (int k = 0; k < 4; ++k) v[k] = __builtin_fmaf(tot[8 + 4 * i + k] * o.rstd, cp.s2, cp.bcomb[k]);
     const float mx = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
     float e[4];
 #pragma unroll
@@ -239,12 +265,10 @@ __device__ __forceinline__ void comb_row(TokenCoef& o, const float* tot, int i,
 }
 
 __device__ __forceinline__ TokenCoef coefficients(const float* tot, int i, int hidden,
-                                                  const float* __restrict__ scale,
-                                                  const float* __restrict__ base,
-                                                  const Scalars& p) {
+                                                  const CoefParams& cp, const Scalars& p) {
     TokenCoef o;
-    pre_post(o, tot, i, hidden, scale, base, p);
-    comb_row(o, tot, i, scale, base, p);
+    pre_post(o, tot, i, hidden, cp, p);
+    comb_row(o, tot, i, cp, p);
     return o;
 }
 

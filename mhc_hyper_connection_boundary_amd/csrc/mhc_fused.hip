@@ -143,6 +143,8 @@ __global__ __launch_bounds__(512) void k_fused(
     }
 
     // Partials of the 8 waves, combined in a fixed order.
+    CoefParams cp;
+    if (wave == 0) cp = load_coef_params(scale, base, lane & 3);
 #pragma unroll
     for (int m = 0; m < 3; ++m)
 #pragma unroll
@@ -163,14 +165,14 @@ __global__ __launch_bounds__(512) void k_fused(
                 for (int q = 0; q < 4; ++q) sum += sq[w][q][tn][v - 24];
         }
         tot[tn][v] = sum;
-        if (v == 25) rli[tn] = 1.0f / sqrtf(sum / (float)hidden + p.norm_eps);
+        if (v == 25) rli[tn] = rsqrt_nr(sum * (1.0f / (float)hidden) + p.norm_eps);
     }
     __syncthreads();
 
     if (wave == 0) {
         const int tn = lane >> 2, i = lane & 3;
         const int tt = tile * kTile + tn;
-        const TokenCoef o = coefficients(tot[tn], i, hidden, scale, base, p);
+        const TokenCoef o = coefficients(tot[tn], i, hidden, cp, p);
         if (tt < T) {
             pre_out[(size_t)tt * 4 + i] = o.pre;
             post_out[(size_t)tt * 4 + i] = o.post;
@@ -310,6 +312,8 @@ __global__ __launch_bounds__(512) void k_fused_pre(
     }
     // Pass 2's first activations are requested before the reductions.
     load_x4(cur, Xrow, hidden, wave * kWide + g * 8);
+    CoefParams cp;
+    if (wave == 0) cp = load_coef_params(scale, base, lane & 3);
 #pragma unroll
     for (int m = 0; m < 3; ++m)
 #pragma unroll
@@ -334,12 +338,12 @@ __global__ __launch_bounds__(512) void k_fused_pre(
     TokenCoef o;
     const int ctn = lane >> 2, ci = lane & 3;
     if (wave == 0) {
-        pre_post(o, tot[ctn], ci, hidden, scale, base, p);
+        pre_post(o, tot[ctn], ci, hidden, cp, p);
         pre_s[ctn][ci] = o.pre;
     }
     __syncthreads();
     if (wave == 0) {
-        comb_row(o, tot[ctn], ci, scale, base, p);
+        comb_row(o, tot[ctn], ci, cp, p);
         const int tt = tile * kTile + ctn;
         if (tt < T) {
             pre_out[(size_t)tt * 4 + ci] = o.pre;
@@ -380,7 +384,7 @@ __global__ __launch_bounds__(512) void k_fused_pre(
         for (int w = 0; w < kWaves; ++w)
 #pragma unroll
             for (int q = 0; q < 4; ++q) sum += sq[w][q][threadIdx.x];
-        rli[threadIdx.x] = 1.0f / sqrtf(sum / (float)hidden + p.norm_eps);
+        rli[threadIdx.x] = rsqrt_nr(sum * (1.0f / (float)hidden) + p.norm_eps);
     }
     __syncthreads();
     const float r = rli[n];

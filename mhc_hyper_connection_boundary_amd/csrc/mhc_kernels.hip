@@ -171,36 +171,45 @@ __device__ __forceinline__ float slice_sum(const float* __restrict__ src, int fi
 }
 
 // Remaining coefficient tokens of a workgroup (tokens hs + k*finish_slices,
-// k >= 1), when there are fewer than 16 rescale workgroups per tile.
+// k >= 1), when there are fewer than 16 rescale workgroups per tile: all at
+// once, one quad of wave 0 per token, with the same two-level slice order as
+// the first token.
 __device__ __forceinline__ void finish_more_coefficients(
     int T, int hidden, int slices, int finish_slices, int tile, int hs, int tid,
     const float* __restrict__ part, const float* __restrict__ scale,
-    const float* __restrict__ base, const Scalars& p, float (*cred)[26], float* ctot,
-    float* __restrict__ pre_out, float* __restrict__ post_out, float* __restrict__ comb_out,
-    float* __restrict__ mixes_out, float* __restrict__ rstd_out) {
-    for (int tn = hs + finish_slices; tn < kTile; tn += finish_slices) {
-        const int t = tile * kTile + tn;
-        if (t >= T) break;
-        __syncthreads();
-        if ((tid & 31) < 25)
-            cred[tid >> 5][tid & 31] =
-                slice_sum(part + (size_t)t * slices * kPart + (tid & 31), tid >> 5, 8, slices);
-        __syncthreads();
-        if (tid < 25) {
-            float sum = 0.0f;
-            for (int q = 0; q < 8; ++q) sum += cred[q][tid];
-            ctot[tid] = sum;
-        }
-        __syncthreads();
-        if (tid < 4) {
-            const TokenCoef o = coefficients(ctot, tid, hidden, scale, base, p);
-            pre_out[(size_t)t * 4 + tid] = o.pre;
-            post_out[(size_t)t * 4 + tid] = o.post;
-            *reinterpret_cast<float4*>(comb_out + (size_t)t * 16 + 4 * tid) =
+    const float* __restrict__ base, const Scalars& p, float (*mred)[8][26],
+    float (*mtot)[26], float* __restrict__ pre_out, float* __restrict__ post_out,
+    float* __restrict__ comb_out, float* __restrict__ mixes_out, float* __restrict__ rstd_out) {
+    const int nk = (kTile - 1 - hs) / finish_slices;  // tokens hs + (k + 1) * finish_slices
+    if (nk <= 0) return;
+    const int first = tile * kTile + hs + finish_slices;
+    for (int item = tid; item < nk * 200; item += blockDim.x) {
+        const int k = item / 200, r = item % 200, grp = r / 25, v = r % 25;
+        const int t = first + k * finish_slices;
+        mred[k][grp][v] =
+            t < T ? slice_sum(part + (size_t)t * slices * kPart + v, grp, 8, slices) : 0.0f;
+    }
+    __syncthreads();
+    for (int item = tid; item < nk * 25; item += blockDim.x) {
+        const int k = item / 25, v = item % 25;
+        float sum = 0.0f;
+        for (int q = 0; q < 8; ++q) sum += mred[k][q][v];
+        mtot[k][v] = sum;
+    }
+    __syncthreads();
+    if (tid < 4 * nk) {
+        const int k = tid >> 2, i = tid & 3;
+        const int t = first + k * finish_slices;
+        const CoefParams cp = load_coef_params(scale, base, i);
+        const TokenCoef o = coefficients(mtot[k], i, hidden, cp, p);
+        if (t < T) {
+            pre_out[(size_t)t * 4 + i] = o.pre;
+            post_out[(size_t)t * 4 + i] = o.post;
+            *reinterpret_cast<float4*>(comb_out + (size_t)t * 16 + 4 * i) =
                 make_float4(o.row[0], o.row[1], o.row[2], o.row[3]);
             if (mixes_out)
-                for (int k = 0; k < 6; ++k) mixes_out[(size_t)t * 24 + 6 * tid + k] = ctot[6 * tid + k];
-            if (rstd_out && tid == 0) rstd_out[t] = o.rstd;
+                for (int kk = 0; kk < 6; ++kk) mixes_out[(size_t)t * 24 + 6 * i + kk] = mtot[k][6 * i + kk];
+            if (rstd_out && i == 0) rstd_out[t] = o.rstd;
         }
     }
 }
@@ -223,6 +232,8 @@ __global__ __launch_bounds__(256) void k_finish(
     __shared__ float rli[kTile];
     __shared__ float cred[8][26];
     __shared__ float ctot[26];
+    __shared__ float mred[kTile - 1][8][26];
+    __shared__ float mtot[kTile - 1][26];
 
     const int tile = blockIdx.x;
     const int hs = blockIdx.y;
@@ -231,7 +242,10 @@ __global__ __launch_bounds__(256) void k_finish(
     const int width = max(0, min(slice_width, hidden - h0));
     const int chunks = width / 8;
 
-    // Rescale chunks u = tid and tid + 256 (the common case); their loads go first.
+    // The coefficient quad's parameters, then the rescale chunks u = tid and
+    // tid + 256 (the common case): all loads go first.
+    CoefParams cp;
+    if (tid < 4) cp = load_coef_params(scale, base, tid);
     uint4 li_v[2], nw_v[2];
     bool have[2];
 #pragma unroll
@@ -265,7 +279,7 @@ __global__ __launch_bounds__(256) void k_finish(
     if (tid < kTile) {
         float sum = 0.0f;
         for (int grp = 0; grp < 16; ++grp) sum += lsum[tid][grp];
-        rli[tid] = 1.0f / sqrtf(sum / (float)hidden + p.norm_eps);
+        rli[tid] = rsqrt_nr(sum * (1.0f / (float)hidden) + p.norm_eps);
     } else if (tid >= 32 && tid < 32 + 25 && coef_first) {
         float sum = 0.0f;
         for (int q = 0; q < 8; ++q) sum += cred[q][tid - 32];
@@ -275,7 +289,7 @@ __global__ __launch_bounds__(256) void k_finish(
     // Phase 3: one quad of wave 0 runs the coefficients (Sinkhorn) of the
     // first token while the other waves rescale li.
     auto emit_coef = [&](int t) {
-        const TokenCoef o = coefficients(ctot, tid, hidden, scale, base, p);
+        const TokenCoef o = coefficients(ctot, tid, hidden, cp, p);
         pre_out[(size_t)t * 4 + tid] = o.pre;
         post_out[(size_t)t * 4 + tid] = o.post;
         *reinterpret_cast<float4*>(comb_out + (size_t)t * 16 + 4 * tid) =
@@ -309,8 +323,9 @@ __global__ __launch_bounds__(256) void k_finish(
         }
     }
     if (finish_slices < kTile)
-        finish_more_coefficients(T, hidden, slices, finish_slices, tile, hs, tid, part, scale, base,
-                                 p, cred, ctot, pre_out, post_out, comb_out, mixes_out, rstd_out);
+        finish_more_coefficients(T, hidden, slices, finish_slices, tile, hs, tid, part, scale,
+                                 base, p, mred, mtot, pre_out, post_out, comb_out, mixes_out,
+                                 rstd_out);
 }
 
 
@@ -327,7 +342,7 @@ struct PartialLayout {
     int splits;
 };
 
-__global__ __launch_bounds__(256) void k_pre_finish(
+__global__ __launch_bounds__(512) void k_pre_finish(
     int T, int hidden, PartialLayout pl, const uint16_t* __restrict__ X,
     const float* __restrict__ scale, const float* __restrict__ base,
     const uint16_t* __restrict__ norm_w, Scalars p, uint16_t* __restrict__ layer_input,
@@ -336,17 +351,21 @@ __global__ __launch_bounds__(256) void k_pre_finish(
     extern __shared__ uint4 li_s[];  // [hidden / 8] when norm_w is given
     __shared__ float tot[26];
     __shared__ float pre_s[4];
-    __shared__ float red[192];
+    __shared__ float red[448];
+    __shared__ float cred[8][26];
     __shared__ float rli;
 
     const int t = blockIdx.x;
     const int tid = threadIdx.x;
     const int nch = hidden / 8;             // 16-byte chunks of a row
-    const int u0 = tid - 64;                // collapse thread index (waves 1-3)
+    const int nc = (int)blockDim.x - 64;    // collapse threads: waves 1.. (192 or 448)
+    const int u0 = tid - 64;                // collapse thread index
     const uint16_t* Xrow = X + (size_t)t * 4 * hidden;
 
     // Waves 1-3 request their first two chunks of X before anything waits;
     // wave 0 gathers the token's projection record.
+    CoefParams cp;
+    if (tid < 4) cp = load_coef_params(scale, base, tid);
     uint4 bufA[4], bufB[4];
     auto load_chunk = [&](uint4 (&b)[4], int cidx) {
         if (cidx < nch) {
@@ -355,20 +374,44 @@ __global__ __launch_bounds__(256) void k_pre_finish(
                 b[j] = *reinterpret_cast<const uint4*>(Xrow + (size_t)j * hidden + cidx * 8);
         }
     };
+    // Thread (group, v) of the first 200 sums splits group, group + 8, ... of
+    // value v (24 mixes, then the sum of squares); the 8 group sums are then
+    // added in group order.  At most 8 loads per thread, issued together.  With
+    // 8 splits or fewer every group holds at most one split, so the plain sum in
+    // split order is the same number and the LDS stage is skipped.
+    const bool two_level = pl.splits > 8;
+    if (!two_level) {
+        if (tid < 25)
+            tot[tid] = tid < 24 ? slice_sum(pl.mix + (size_t)t * pl.mix_tok + tid, 0, 1, pl.splits,
+                                            pl.mix_split)
+                                : slice_sum(pl.ssq + (size_t)t * pl.ssq_tok, 0, 1, pl.splits,
+                                            pl.ssq_split);
+    } else if (tid < 200) {
+        const int grp = tid / 25, v = tid % 25;
+        cred[grp][v] = v < 24 ? slice_sum(pl.mix + (size_t)t * pl.mix_tok + v, grp, 8, pl.splits,
+                                          pl.mix_split)
+                              : slice_sum(pl.ssq + (size_t)t * pl.ssq_tok, grp, 8, pl.splits,
+                                          pl.ssq_split);
+    }
     if (tid >= 64) {
         load_chunk(bufA, u0);
-        load_chunk(bufB, u0 + 192);
-    } else if (tid < 24) {
-        tot[tid] = slice_sum(pl.mix + (size_t)t * pl.mix_tok + tid, 0, 1, pl.splits, pl.mix_split);
-    } else if (tid == 24) {
-        tot[24] = slice_sum(pl.ssq + (size_t)t * pl.ssq_tok, 0, 1, pl.splits, pl.ssq_split);
+        load_chunk(bufB, u0 + nc);
     }
     __syncthreads();
+    if (two_level) {
+        if (tid < 25) {
+            float sum = 0.0f;
+#pragma unroll
+            for (int grp = 0; grp < 8; ++grp) sum += cred[grp][tid];
+            tot[tid] = sum;
+        }
+        __syncthreads();
+    }
     // pre is published as soon as it exists: the collapse does not wait for
     // the Sinkhorn iterations, which wave 0 runs at the end.
     TokenCoef o;
     if (tid < 4) {
-        pre_post(o, tot, tid, hidden, scale, base, p);
+        pre_post(o, tot, tid, hidden, cp, p);
         pre_s[tid] = o.pre;
     }
     __syncthreads();
@@ -380,7 +423,7 @@ __global__ __launch_bounds__(256) void k_pre_finish(
             uint4 Xv[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) Xv[j] = b[j];
-            load_chunk(b, cidx + 384);          // two chunks ahead
+            load_chunk(b, cidx + 2 * nc);       // two chunks ahead
             uint4 li;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -402,24 +445,25 @@ __global__ __launch_bounds__(256) void k_pre_finish(
             if (norm_w) li_s[cidx] = li;
             else *reinterpret_cast<uint4*>(layer_input + (size_t)t * hidden + cidx * 8) = li;
         };
-        for (int cidx = u0; cidx < nch; cidx += 384) {
+        for (int cidx = u0; cidx < nch; cidx += 2 * nc) {
             collapse(bufA, cidx);
-            if (cidx + 192 < nch) collapse(bufB, cidx + 192);
+            if (cidx + nc < nch) collapse(bufB, cidx + nc);
         }
         red[u0] = ssq_li;
     }
     if (norm_w) {
         __syncthreads();
-        if (tid >= 64 && tid < 128) {  // fixed-order reduction of the 192 partial sums
-            float v = (red[u0] + red[u0 + 64]) + red[u0 + 128];
+        if (tid >= 64 && tid < 128) {  // fixed-order reduction of the nc partial sums
+            float v = red[u0];
+            for (int k = 64; k < nc; k += 64) v += red[u0 + k];
 #pragma unroll
             for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-            if (u0 == 0) rli = 1.0f / sqrtf(v / (float)hidden + p.norm_eps);
+            if (u0 == 0) rli = rsqrt_nr(v * (1.0f / (float)hidden) + p.norm_eps);
         }
         __syncthreads();
         if (tid >= 64) {
             const float r = rli;
-            for (int cidx = u0; cidx < nch; cidx += 192) {
+            for (int cidx = u0; cidx < nch; cidx += nc) {
                 const int h = cidx * 8;
                 const uint4 li = li_s[cidx];
                 const uint4 nw = *reinterpret_cast<const uint4*>(norm_w + h);
@@ -435,7 +479,7 @@ __global__ __launch_bounds__(256) void k_pre_finish(
     }
     // Wave 0: the Sinkhorn comb, overlapping the layer-input work above.
     if (tid < 4) {
-        comb_row(o, tot, tid, scale, base, p);
+        comb_row(o, tot, tid, cp, p);
         pre_out[(size_t)t * 4 + tid] = o.pre;
         post_out[(size_t)t * 4 + tid] = o.post;
         *reinterpret_cast<float4*>(comb_out + (size_t)t * 16 + 4 * tid) =
@@ -554,8 +598,11 @@ static hipError_t launch_pre_finish_layout(int T, int hidden, const PartialLayou
                                            const Scalars& p, uint16_t* layer_input,
                                            float* pre_out, float* post_out, float* comb_out,
                                            float* mixes, float* rstd, hipStream_t stream) {
+    // Small batches: 448 collapse threads, so a row of 7168 is requested in
+    // one round trip; large batches: 192, more workgroups per CU.
     const size_t lds = norm_w ? (size_t)hidden * 2 : 0;
-    hipLaunchKernelGGL(k_pre_finish, dim3(T), dim3(256), lds, stream, T, hidden, pl, X, scale,
+    const int threads = T <= 512 ? 512 : 256;
+    hipLaunchKernelGGL(k_pre_finish, dim3(T), dim3(threads), lds, stream, T, hidden, pl, X, scale,
                        base, norm_w, p, layer_input, pre_out, post_out, comb_out, mixes, rstd);
     return hipGetLastError();
 }
