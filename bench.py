@@ -28,7 +28,7 @@ sys.path.insert(0, ROOT)
 METRIC = "mHC boundary tokens/s at d=7168 (decode T=32, prefill T=8192); % HBM roofline"
 HBM_PEAK_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
-TRAFFIC_PROFILE = os.path.join(PROFILES, "k_fused_prefill_traffic.txt")
+TRAFFIC_PROFILE = os.path.join(PROFILES, "k_fused_w4_prefill_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "mhc_hyper_connection_boundary_amd", "csrc", f)
                   for f in ("mhc_fused.hip", "mhc_device.h")]
 COPY_BYTES = 1 << 30
@@ -343,9 +343,9 @@ def _counter_median(directory, counter, kernel_substr):
 
 def write_traffic_profile(prof_dir):
     """Summarises four rocprofv3 --pmc runs (see the command list written into
-    the summary) into profiles/k_fused_prefill_traffic.txt."""
-    f_k, nf = _counter_median(os.path.join(prof_dir, "fetch_boundary"), "FETCH_SIZE", "k_fused")
-    w_k, nw = _counter_median(os.path.join(prof_dir, "write_boundary"), "WRITE_SIZE", "k_fused")
+    the summary) into profiles/k_fused_w4_prefill_traffic.txt."""
+    f_k, nf = _counter_median(os.path.join(prof_dir, "fetch_boundary"), "FETCH_SIZE", "k_fused_w4")
+    w_k, nw = _counter_median(os.path.join(prof_dir, "write_boundary"), "WRITE_SIZE", "k_fused_w4")
     f_c, _ = _counter_median(os.path.join(prof_dir, "fetch_copy"), "FETCH_SIZE", "copyBuffer")
     w_c, _ = _counter_median(os.path.join(prof_dir, "write_copy"), "WRITE_SIZE", "copyBuffer")
     f_scale = COPY_BYTES / (f_c * 1024)
@@ -353,7 +353,7 @@ def write_traffic_profile(prof_dir):
     traffic = f_k * 1024 * f_scale + w_k * 1024 * w_scale
     T, d = 8192, 7168
     lines = [
-        "k_fused prefill (d=7168, T=8192): HBM traffic per launch from rocprofv3 counters",
+        "k_fused_w4<28> prefill (d=7168, T=8192): HBM traffic per launch from rocprofv3 counters",
         f"sources_sha256: {kernel_sources_sha256()}",
         f"fetch_size_kib_per_dispatch: {f_k:.1f}",
         f"write_size_kib_per_dispatch: {w_k:.1f}",
@@ -421,8 +421,12 @@ def main():
     ms, wall = time_calls(torch, lambda k: w.call(), a.steps, a.warmup)
     b = algorithmic_bytes(T, d)
     gbs = b / (ms * 1e-3) / 1e9
-    fused = a.schedule == "fused" or (a.schedule == "auto" and T >= 2048)
-    kernel = f"k_fused<{d // 512}> (one launch per call)" if fused else "k_partial + k_finish"
+    fused = a.schedule == "fused" or (a.schedule == "auto" and T >= 3072)
+    if fused:
+        kernel = (f"k_fused_w4<{d // 256}>" if T >= 8192 else f"k_fused<{d // 512}>") + \
+            " (one launch per call)"
+    else:
+        kernel = "k_partial + k_finish"
     traffic = recorded_traffic() if fused else None
     line = dict(
         metric=METRIC, value=T / (ms * 1e-3), unit="tokens/s", n_gpus=1, steps=a.steps,

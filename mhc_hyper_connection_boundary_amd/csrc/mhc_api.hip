@@ -16,7 +16,8 @@ namespace {
 
 constexpr long kTargetWaves = 2048;  // waves of k_partial work to aim for
 constexpr int kFinishTarget = 512;   // k_finish workgroups to aim for
-constexpr int kFusedMinTokens = 2048; // automatic schedule: fused from this many tokens
+constexpr int kFusedMinTokens = 3072; // automatic schedule: fused from this many tokens
+constexpr int kW4MinTokens = 8192;    // fused schedule: 32-token tiles on 4 waves from here
 
 int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 
@@ -281,9 +282,12 @@ mhc_status mhc_boundary(int tokens, int hidden, const uint16_t* x, const uint16_
     hipStream_t hs = (hipStream_t)stream;
     if (use_fused(params->schedule, tokens, hidden)) {
         if (!fused_supported(hidden)) return MHC_ERR_UNSUPPORTED_SHAPE;
-        if (launch_fused(tokens, hidden, x, residual, post_prev, comb_prev, pre_lag, w_prepared,
-                         scale, base, norm_w, s, residual_out, layer_input, pre_out, post_out,
-                         comb_out, mixes, rstd, hs) != hipSuccess)
+        // 32-token tiles halve the weight-fragment loads per token but need at
+        // least one tile per CU; below that the 16-token kernel fills the chip.
+        const auto launch = tokens >= kW4MinTokens ? launch_fused_w4 : launch_fused;
+        if (launch(tokens, hidden, x, residual, post_prev, comb_prev, pre_lag, w_prepared, scale,
+                   base, norm_w, s, residual_out, layer_input, pre_out, post_out, comb_out, mixes,
+                   rstd, hs) != hipSuccess)
             return MHC_ERR_DEVICE;
         return MHC_OK;
     }

@@ -28,8 +28,9 @@ constexpr int kWide = 2 * kStep;  // hidden elements per wave step: two MFMA k-b
 
 template <int S>                  // S = hidden / (kWaves * kWide): steps per wave
 struct FusedShape {
-    static constexpr int kLiLds = S < 8 ? S : 8;  // steps whose li waits in LDS (16 KB each)
-};                                                // (later steps: layer_input)
+    static constexpr int kLiLds = S < 8 ? S : 8;  // first steps: li waits in LDS (16 KB each)
+    static constexpr int kLiReg = S - kLiLds < 3 ? S - kLiLds : 3;  // last steps: in registers
+};                                                // (steps between: layer_input)
 
 // Activations of one wave step.  Lane (n, g) holds, for token n, the 8 hidden
 // elements 64*step + 32*b + 8*g + [0, 8) of block b = 0, 1: the two 64-byte
@@ -107,13 +108,14 @@ __global__ __launch_bounds__(512) void k_fused(
     // contiguous hidden elements of every row of the tile.
     Act cur;
     load_act(cur, Xrow, xrow, hidden, wave * kWide + g * 8);
-#pragma unroll 1
-    for (int i = 0; i < S; ++i) {
+    // One wave step.  keep: li stays in the caller's registers (last steps);
+    // otherwise it waits in LDS (first steps) or in the layer-input buffer.
+    auto body = [&](int i, bool keep, uint4 (&li)[2]) {
         const int step = i * kWaves + wave;
         const int h = step * kWide + g * 8;
         Act nxt;
         if (i + 1 < S) load_act(nxt, Xrow, xrow, hidden, h + kWaves * kWide);
-        uint4 Xn[2][4], li[2];
+        uint4 Xn[2][4];
 #pragma unroll
         for (int b = 0; b < 2; ++b) update_collapse(cur.X[b], cur.x[b], c, Xn[b], li[b], ssq, ssq_li);
         // A lane past the last token works on token T-1 (tc), so it stores
@@ -123,12 +125,14 @@ __global__ __launch_bounds__(512) void k_fused(
             store_stream(xn_out + (tc * 4 + s) * hidden + h, Xn[0][s]);
             store_stream(xn_out + (tc * 4 + s) * hidden + h + kStep, Xn[1][s]);
         }
-        if (i < Shape::kLiLds) {
-            li_lds[i][wave][0][lane] = li[0];
-            li_lds[i][wave][1][lane] = li[1];
-        } else {
-            store_stream(li_row + h, li[0]);
-            store_stream(li_row + h + kStep, li[1]);
+        if (!keep) {
+            if (i < Shape::kLiLds) {
+                li_lds[i][wave][0][lane] = li[0];
+                li_lds[i][wave][1][lane] = li[1];
+            } else {
+                store_stream(li_row + h, li[0]);
+                store_stream(li_row + h + kStep, li[1]);
+            }
         }
         // The weight fragments (L2-resident) are fetched only now, so they hold
         // no registers during the VALU work above; the other wave of the SIMD
@@ -140,7 +144,15 @@ __global__ __launch_bounds__(512) void k_fused(
         mfma_step(A0, Xn[0], acc);
         mfma_step(A1, Xn[1], acc);
         cur = nxt;
+    };
+#pragma unroll 1
+    for (int i = 0; i < S - Shape::kLiReg; ++i) {
+        uint4 li[2];
+        body(i, false, li);
     }
+    uint4 li_keep[Shape::kLiReg > 0 ? Shape::kLiReg : 1][2];
+#pragma unroll
+    for (int r = 0; r < Shape::kLiReg; ++r) body(S - Shape::kLiReg + r, true, li_keep[r]);
 
     // Partials of the 8 waves, combined in a fixed order.
     CoefParams cp;
@@ -189,6 +201,7 @@ __global__ __launch_bounds__(512) void k_fused(
     // Lanes past the last token rewrite token T-1's identical values.
     const float r = rli[n];
     auto emit = [&](int h, const uint4& li) {
+        if (t >= T) return;  // lanes past the last token leave token T-1 to its own lane
         uint4 out = li;
         if (norm_w) {
             const uint4 nw = *reinterpret_cast<const uint4*>(norm_w + h);
@@ -206,14 +219,257 @@ __global__ __launch_bounds__(512) void k_fused(
         emit(h, li_lds[i][wave][0][lane]);
         emit(h + kStep, li_lds[i][wave][1][lane]);
     }
+#pragma unroll
+    for (int r = 0; r < Shape::kLiReg; ++r) {
+        const int h = ((S - Shape::kLiReg + r) * kWaves + wave) * kWide + g * 8;
+        emit(h, li_keep[r][0]);
+        emit(h + kStep, li_keep[r][1]);
+    }
 #pragma unroll 2
-    for (int i = Shape::kLiLds; i < S; ++i) {
+    for (int i = Shape::kLiLds; i < S - Shape::kLiReg; ++i) {
         const int h = (i * kWaves + wave) * kWide + g * 8;
         const uint4 l0 = *reinterpret_cast<const uint4*>(li_row + h);
         const uint4 l1 = *reinterpret_cast<const uint4*>(li_row + h + kStep);
         emit(h, l0);
         emit(h + kStep, l1);
     }
+}
+
+// ---------------------------------------------------------------------------
+// Fused schedule on 4 waves per workgroup (one per SIMD) with 32-token tiles.
+// The weight fragments are the costly loads of the 8-wave kernel: one 1 KB
+// load per fragment per 16 tokens.  Here each wave carries two 16-token groups
+// (tokens n and n + 16 of the tile in lane n) through every 64-element step and
+// feeds both from one set of fragments, which halves the fragment loads per
+// token while keeping 128-byte row runs.  With one wave per SIMD a wave may
+// hold 512 registers (architectural plus accumulation registers), enough for
+// both groups' activations, their prefetch and the fragments.  Each step issues
+// its fragments first and the next step's activations after them, so the
+// projection never waits on HBM (loads complete in issue order).
+// ---------------------------------------------------------------------------
+constexpr int kWaves4 = 4;
+constexpr int kTileW4 = 32;
+
+template <int S>                  // S = hidden / (kWaves4 * kWide): steps per wave
+struct FusedW4Shape {
+    static constexpr int kLiLds = S < 8 ? S : 8;  // first steps: li waits in LDS (16 KB each)
+    static constexpr int kLiReg = S - kLiLds < 2 ? S - kLiLds : 2;  // last steps: in registers
+};                                                // (steps between: layer_input)
+
+template <int S>
+__global__ __launch_bounds__(256) void k_fused_w4(
+    int T, const uint16_t* __restrict__ x, const uint16_t* __restrict__ X,
+    const float* __restrict__ post_prev, const float* __restrict__ comb_prev,
+    const float* __restrict__ pre_lag, const uint4* __restrict__ wprep,
+    const float* __restrict__ scale, const float* __restrict__ base,
+    const uint16_t* __restrict__ norm_w, Scalars p, uint16_t* __restrict__ xn_out,
+    uint16_t* __restrict__ layer_input, float* __restrict__ pre_out,
+    float* __restrict__ post_out, float* __restrict__ comb_out, float* __restrict__ mixes_out,
+    float* __restrict__ rstd_out) {
+    using Shape = FusedW4Shape<S>;
+    constexpr int hidden = S * kWide * kWaves4;
+    __shared__ uint4 li_lds[Shape::kLiLds > 0 ? Shape::kLiLds : 1][kWaves4][2][2][64];
+    __shared__ float red[kWaves4][kTileW4][24];
+    __shared__ float sq[kWaves4][4][kTileW4][2];
+    __shared__ float tot[kTileW4][26];
+    __shared__ float rli[kTileW4];
+
+    const int tile = blockIdx.x;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 15;
+    const int g = lane >> 4;
+    size_t tc[2];
+    PrevCoef c[2];
+    const uint16_t* Xrow[2];
+    const uint16_t* xrow[2];
+    uint16_t* li_row[2];
+    uint16_t* xn_row[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        // A lane past the last token works on token T-1, so it stores the
+        // same bytes as that token's own lane: no branch needed.
+        const int t = tile * kTileW4 + 16 * q + n;
+        tc[q] = t < T ? (size_t)t : (size_t)(T - 1);
+        load_prev(c[q], post_prev, comb_prev, pre_lag, tc[q]);
+        Xrow[q] = X + tc[q] * 4 * hidden;
+        xrow[q] = x + tc[q] * hidden;
+        li_row[q] = layer_input + tc[q] * hidden;
+        xn_row[q] = xn_out + tc[q] * 4 * hidden;
+    }
+
+    f32x4_t acc[2][3];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int m = 0; m < 3; ++m) acc[q][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float ssq[2] = {0.0f, 0.0f}, ssq_li[2] = {0.0f, 0.0f};
+
+    // Wave w takes steps w, w + 4, ...: the 4 waves cover 256 contiguous
+    // hidden elements of every row of the tile at a time.
+    Act cur[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) load_act(cur[q], Xrow[q], xrow[q], hidden, wave * kWide + g * 8);
+    // One wave step.  keep: li stays in the caller's registers (last steps);
+    // otherwise it waits in LDS (first steps) or in the layer-input buffer.
+    auto body = [&](int i, bool keep, uint4 (&li)[2][2]) {
+        const int step = i * kWaves4 + wave;
+        const int h = step * kWide + g * 8;
+        uint4 A0[kFragsPerStep], A1[kFragsPerStep];
+        load_frags(A0, wprep, 2 * step, lane);
+        load_frags(A1, wprep, 2 * step + 1, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        Act nxt[2];
+        if (i + 1 < S) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q) load_act(nxt[q], Xrow[q], xrow[q], hidden, h + kWaves4 * kWide);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            uint4 Xn[2][4];
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+                update_collapse(cur[q].X[b], cur[q].x[b], c[q], Xn[b], li[q][b], ssq[q], ssq_li[q]);
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2) {
+                store_stream(xn_row[q] + (size_t)s2 * hidden + h, Xn[0][s2]);
+                store_stream(xn_row[q] + (size_t)s2 * hidden + h + kStep, Xn[1][s2]);
+            }
+            if (!keep) {
+                if (i < Shape::kLiLds) {
+                    li_lds[i][wave][q][0][lane] = li[q][0];
+                    li_lds[i][wave][q][1][lane] = li[q][1];
+                } else {
+                    store_stream(li_row[q] + h, li[q][0]);
+                    store_stream(li_row[q] + h + kStep, li[q][1]);
+                }
+            }
+            mfma_step(A0, Xn[0], acc[q]);
+            mfma_step(A1, Xn[1], acc[q]);
+        }
+#pragma unroll
+        for (int q = 0; q < 2; ++q) cur[q] = nxt[q];
+    };
+#pragma unroll 1
+    for (int i = 0; i < S - Shape::kLiReg; ++i) {
+        uint4 li[2][2];
+        body(i, false, li);
+    }
+    uint4 li_keep[Shape::kLiReg > 0 ? Shape::kLiReg : 1][2][2];
+#pragma unroll
+    for (int r = 0; r < Shape::kLiReg; ++r) body(S - Shape::kLiReg + r, true, li_keep[r]);
+
+    // Partials of the 4 waves, combined in a fixed order.
+    CoefParams cp;
+    if (wave < 2) cp = load_coef_params(scale, base, lane & 3);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+#pragma unroll
+        for (int m = 0; m < 3; ++m)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) red[wave][16 * q + n][8 * m + 2 * g + j] = mix_of(acc[q], m, j);
+        sq[wave][g][16 * q + n][0] = ssq[q];
+        sq[wave][g][16 * q + n][1] = ssq_li[q];
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < kTileW4 * 26; idx += kWaves4 * 64) {
+        const int tn = idx / 26, v = idx % 26;
+        float sum = 0.0f;
+        if (v < 24) {
+#pragma unroll
+            for (int w = 0; w < kWaves4; ++w) sum += red[w][tn][v];
+        } else {
+#pragma unroll
+            for (int w = 0; w < kWaves4; ++w)
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) sum += sq[w][qq][tn][v - 24];
+        }
+        tot[tn][v] = sum;
+        if (v == 25) rli[tn] = rsqrt_nr(sum * (1.0f / (float)hidden) + p.norm_eps);
+    }
+    __syncthreads();
+
+    if (wave < 2) {  // 32 tokens x 4 lanes: waves 0 and 1
+        const int tn = 16 * wave + (lane >> 2), ci = lane & 3;
+        const int tt = tile * kTileW4 + tn;
+        const TokenCoef o = coefficients(tot[tn], ci, hidden, cp, p);
+        if (tt < T) {
+            pre_out[(size_t)tt * 4 + ci] = o.pre;
+            post_out[(size_t)tt * 4 + ci] = o.post;
+            *reinterpret_cast<float4*>(comb_out + (size_t)tt * 16 + 4 * ci) =
+                make_float4(o.row[0], o.row[1], o.row[2], o.row[3]);
+            if (mixes_out)
+                for (int k = 0; k < 6; ++k) mixes_out[(size_t)tt * 24 + 6 * ci + k] = tot[tn][6 * ci + k];
+            if (rstd_out && ci == 0) rstd_out[tt] = o.rstd;
+        }
+    }
+
+    // Layer input for this wave's steps: li from LDS, then li parked in the
+    // layer-input buffer (written by this same lane before the barriers above).
+    // Lanes past the last token write nothing here: a lane of the other group
+    // working on the same token T-1 would otherwise read back a value that
+    // has already been normalised.
+    const float r[2] = {rli[n], rli[16 + n]};
+    const bool valid[2] = {tile * kTileW4 + n < T, tile * kTileW4 + 16 + n < T};
+    auto emit = [&](int q, int h, const uint4& li) {
+        if (!valid[q]) return;
+        uint4 out = li;
+        if (norm_w) {
+            const uint4 nw = *reinterpret_cast<const uint4*>(norm_w + h);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t a = word(li, k), b = word(nw, k);
+                set_word(out, k, pack_bf16((bf_lo(a) * r[q]) * bf_lo(b), (bf_hi(a) * r[q]) * bf_hi(b)));
+            }
+        }
+        store_stream(li_row[q] + h, out);
+    };
+#pragma unroll 2
+    for (int i = 0; i < Shape::kLiLds; ++i) {
+        const int h = (i * kWaves4 + wave) * kWide + g * 8;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            emit(q, h, li_lds[i][wave][q][0][lane]);
+            emit(q, h + kStep, li_lds[i][wave][q][1][lane]);
+        }
+    }
+#pragma unroll
+    for (int rr = 0; rr < Shape::kLiReg; ++rr) {
+        const int h = ((S - Shape::kLiReg + rr) * kWaves4 + wave) * kWide + g * 8;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            emit(q, h, li_keep[rr][q][0]);
+            emit(q, h + kStep, li_keep[rr][q][1]);
+        }
+    }
+    if (norm_w) {  // (without norm_w the parked li already is the layer input)
+#pragma unroll 2
+        for (int i = Shape::kLiLds; i < S - Shape::kLiReg; ++i) {
+            const int h = (i * kWaves4 + wave) * kWide + g * 8;
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const uint4 l0 = *reinterpret_cast<const uint4*>(li_row[q] + h);
+                const uint4 l1 = *reinterpret_cast<const uint4*>(li_row[q] + h + kStep);
+                emit(q, h, l0);
+                emit(q, h + kStep, l1);
+            }
+        }
+    }
+}
+
+template <int S>
+hipError_t launch_w4_s(int T, const uint16_t* x, const uint16_t* X, const float* post_prev,
+                       const float* comb_prev, const float* pre_lag, const void* wprep,
+                       const float* scale, const float* base, const uint16_t* norm_w,
+                       const Scalars& p, uint16_t* xn_out, uint16_t* layer_input,
+                       float* pre_out, float* post_out, float* comb_out, float* mixes,
+                       float* rstd, hipStream_t stream) {
+    hipLaunchKernelGGL(k_fused_w4<S>, dim3((T + kTileW4 - 1) / kTileW4), dim3(kWaves4 * 64), 0,
+                       stream, T, x, X, post_prev, comb_prev, pre_lag,
+                       reinterpret_cast<const uint4*>(wprep), scale, base, norm_w, p, xn_out,
+                       layer_input, pre_out, post_out, comb_out, mixes, rstd);
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -389,6 +645,7 @@ __global__ __launch_bounds__(512) void k_fused_pre(
     __syncthreads();
     const float r = rli[n];
     auto emit = [&](int h, const uint4& li) {
+        if (t >= T) return;  // lanes past the last token leave token T-1 to its own lane
         uint4 out = li;
         if (norm_w) {
             const uint4 nw = *reinterpret_cast<const uint4*>(norm_w + h);
@@ -477,6 +734,31 @@ hipError_t launch_fused(int T, int hidden, const uint16_t* x, const uint16_t* X,
             return hipErrorInvalidValue;
     }
 #undef MHC_FUSED_CASE
+}
+
+hipError_t launch_fused_w4(int T, int hidden, const uint16_t* x, const uint16_t* X,
+                           const float* post_prev, const float* comb_prev, const float* pre_lag,
+                           const void* wprep, const float* scale, const float* base,
+                           const uint16_t* norm_w, const Scalars& p, uint16_t* xn_out,
+                           uint16_t* layer_input, float* pre_out, float* post_out,
+                           float* comb_out, float* mixes, float* rstd, hipStream_t stream) {
+#define MHC_W4_CASE(D)                                                                        \
+    case D:                                                                                   \
+        return launch_w4_s<D / 256>(T, x, X, post_prev, comb_prev, pre_lag, wprep, scale,     \
+                                    base, norm_w, p, xn_out, layer_input, pre_out, post_out,  \
+                                    comb_out, mixes, rstd, stream);
+    switch (hidden) {
+        MHC_W4_CASE(1024)
+        MHC_W4_CASE(2048)
+        MHC_W4_CASE(4096)
+        MHC_W4_CASE(5120)
+        MHC_W4_CASE(6144)
+        MHC_W4_CASE(7168)
+        MHC_W4_CASE(8192)
+        default:
+            return hipErrorInvalidValue;
+    }
+#undef MHC_W4_CASE
 }
 
 hipError_t launch_fused_pre(int T, int hidden, const uint16_t* X, const void* wprep,

@@ -182,6 +182,23 @@ def test_boundary_small_full(oracle, T, d, schedule):
     compare(g, o, label=f"T={T} d={d} {schedule}")
 
 
+@pytest.mark.parametrize("T,d,full", [(8192 + 13, 1024, True), (8192 + 29, 2048, False),
+                                      (8192 + 3, 5120, False)])
+def test_boundary_fused_32_token_tiles(oracle, T, d, full):
+    """From 8192 tokens the fused schedule runs 32-token tiles (two token
+    groups per wave).  Ragged tails leave the second group, or both, partly
+    past the last token."""
+    say(f"boundary 32-token tiles T={T} d={d}")
+    inp = WL.make_inputs(WL.Config("w4", d=d, T=T, seed=T + d))
+    g = Dev(inp).boundary(schedule="fused")
+    if full:
+        compare(g, oracle.boundary(inp), label=f"w4 T={T} d={d}")
+    else:
+        tok = np.unique(np.concatenate([sample_tokens(T, n=40, seed=d),
+                                        np.arange(T - 40, T, dtype=np.int32)]))
+        compare(g, oracle.boundary(inp, tokens=tok), tokens=tok, label=f"w4 T={T} d={d}")
+
+
 def test_fused_refuses_unsupported_width():
     inp = WL.make_inputs(WL.Config("u", d=256, T=4, seed=1))
     with pytest.raises(api.MhcError) as e:
