@@ -61,10 +61,12 @@ mhc_status check_params(const mhc_params* p) {
 }
 
 // FUSED is honoured (the caller gets UNSUPPORTED_SHAPE where the width has no
-// fused kernel); AUTO takes the fused kernel from kFusedMinTokens tokens.
-bool use_fused(int schedule, int tokens, int hidden) {
+// fused kernel); AUTO takes the fused kernel from min_tokens tokens: the
+// boundary's from kFusedMinTokens, the non-shifted pre's (two passes over X)
+// only where its 32-token tiles fill the chip, from kW4MinTokens.
+bool use_fused(int schedule, int tokens, int hidden, int min_tokens) {
     if (schedule == MHC_SCHEDULE_FUSED) return true;
-    return schedule == MHC_SCHEDULE_AUTO && fused_supported(hidden) && tokens >= kFusedMinTokens;
+    return schedule == MHC_SCHEDULE_AUTO && fused_supported(hidden) && tokens >= min_tokens;
 }
 
 Scalars scalars(const mhc_params* p) {
@@ -228,10 +230,11 @@ mhc_status mhc_pre(int tokens, int hidden, const uint16_t* residual, const void*
 
     const Scalars s = scalars(params);
     hipStream_t hs = (hipStream_t)stream;
-    if (use_fused(params->schedule, tokens, hidden)) {
+    if (use_fused(params->schedule, tokens, hidden, kW4MinTokens)) {
         if (!fused_supported(hidden)) return MHC_ERR_UNSUPPORTED_SHAPE;
         if (launch_fused_pre(tokens, hidden, residual, w_prepared, scale, base, norm_w, s,
-                             layer_input, pre, post, comb, mixes, rstd, hs) != hipSuccess)
+                             layer_input, pre, post, comb, mixes, rstd, tokens >= kW4MinTokens,
+                             hs) != hipSuccess)
             return MHC_ERR_DEVICE;
         return MHC_OK;
     }
@@ -280,7 +283,7 @@ mhc_status mhc_boundary(int tokens, int hidden, const uint16_t* x, const uint16_
 
     const Scalars s = scalars(params);
     hipStream_t hs = (hipStream_t)stream;
-    if (use_fused(params->schedule, tokens, hidden)) {
+    if (use_fused(params->schedule, tokens, hidden, kFusedMinTokens)) {
         if (!fused_supported(hidden)) return MHC_ERR_UNSUPPORTED_SHAPE;
         // 32-token tiles halve the weight-fragment loads per token but need at
         // least one tile per CU; below that the 16-token kernel fills the chip.

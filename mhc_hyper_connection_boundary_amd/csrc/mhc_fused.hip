@@ -675,6 +675,240 @@ __global__ __launch_bounds__(512) void k_fused_pre(
     }
 }
 
+// Non-shifted pre on 4 waves with 32-token tiles: the two passes of k_fused_pre,
+// with every wave carrying two 16-token groups (lane n: tokens n and n + 16 of
+// the tile) so that pass 1 feeds both groups from one set of weight fragments.
+template <int S>
+__global__ __launch_bounds__(256) void k_fused_pre_w4(
+    int T, const uint16_t* __restrict__ X, const uint4* __restrict__ wprep,
+    const float* __restrict__ scale, const float* __restrict__ base,
+    const uint16_t* __restrict__ norm_w, Scalars p, uint16_t* __restrict__ layer_input,
+    float* __restrict__ pre_out, float* __restrict__ post_out, float* __restrict__ comb_out,
+    float* __restrict__ mixes_out, float* __restrict__ rstd_out) {
+    using Shape = FusedW4Shape<S>;
+    constexpr int hidden = S * kWide * kWaves4;
+    __shared__ uint4 li_lds[Shape::kLiLds > 0 ? Shape::kLiLds : 1][kWaves4][2][2][64];
+    __shared__ float red[kWaves4][kTileW4][24];
+    __shared__ float sq[kWaves4][4][kTileW4];
+    __shared__ float tot[kTileW4][26];
+    __shared__ float pre_s[kTileW4][4];
+    __shared__ float rli[kTileW4];
+
+    const int tile = blockIdx.x;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 15;
+    const int g = lane >> 4;
+    const uint16_t* Xrow[2];
+    uint16_t* li_row[2];
+    bool valid[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int t = tile * kTileW4 + 16 * q + n;
+        valid[q] = t < T;
+        const size_t tc = valid[q] ? (size_t)t : (size_t)(T - 1);
+        Xrow[q] = X + tc * 4 * hidden;
+        li_row[q] = layer_input + tc * hidden;
+    }
+
+    // Pass 1: sums of squares and the projection.
+    f32x4_t acc[2][3];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int m = 0; m < 3; ++m) acc[q][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float ssq[2] = {0.0f, 0.0f};
+    ActX cur[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) load_x4(cur[q], Xrow[q], hidden, wave * kWide + g * 8);
+#pragma unroll 1
+    for (int i = 0; i < S; ++i) {
+        const int step = i * kWaves4 + wave;
+        const int h = step * kWide + g * 8;
+        uint4 A0[kFragsPerStep], A1[kFragsPerStep];
+        load_frags(A0, wprep, 2 * step, lane);
+        load_frags(A1, wprep, 2 * step + 1, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        ActX nxt[2];
+        if (i + 1 < S) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q) load_x4(nxt[q], Xrow[q], hidden, h + kWaves4 * kWide);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            square_sum(cur[q].X[0], ssq[q]);
+            square_sum(cur[q].X[1], ssq[q]);
+            mfma_step(A0, cur[q].X[0], acc[q]);
+            mfma_step(A1, cur[q].X[1], acc[q]);
+        }
+#pragma unroll
+        for (int q = 0; q < 2; ++q) cur[q] = nxt[q];
+    }
+    // Pass 2's first activations are requested before the reductions.
+#pragma unroll
+    for (int q = 0; q < 2; ++q) load_x4(cur[q], Xrow[q], hidden, wave * kWide + g * 8);
+    CoefParams cp;
+    if (wave < 2) cp = load_coef_params(scale, base, lane & 3);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+#pragma unroll
+        for (int m = 0; m < 3; ++m)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) red[wave][16 * q + n][8 * m + 2 * g + j] = mix_of(acc[q], m, j);
+        sq[wave][g][16 * q + n] = ssq[q];
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < kTileW4 * 25; idx += kWaves4 * 64) {
+        const int tn = idx / 25, v = idx % 25;
+        float sum = 0.0f;
+        if (v < 24) {
+#pragma unroll
+            for (int w = 0; w < kWaves4; ++w) sum += red[w][tn][v];
+        } else {
+#pragma unroll
+            for (int w = 0; w < kWaves4; ++w)
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) sum += sq[w][qq][tn];
+        }
+        tot[tn][v] = sum;
+    }
+    __syncthreads();
+    TokenCoef o;
+    const int ctn = 16 * (wave & 1) + (lane >> 2), ci = lane & 3;
+    if (wave < 2) {
+        pre_post(o, tot[ctn], ci, hidden, cp, p);
+        pre_s[ctn][ci] = o.pre;
+    }
+    __syncthreads();
+    if (wave < 2) {  // the Sinkhorn of the 32 tokens, ahead of these waves' collapse
+        comb_row(o, tot[ctn], ci, cp, p);
+        const int tt = tile * kTileW4 + ctn;
+        if (tt < T) {
+            pre_out[(size_t)tt * 4 + ci] = o.pre;
+            post_out[(size_t)tt * 4 + ci] = o.post;
+            *reinterpret_cast<float4*>(comb_out + (size_t)tt * 16 + 4 * ci) =
+                make_float4(o.row[0], o.row[1], o.row[2], o.row[3]);
+            if (mixes_out)
+                for (int k = 0; k < 6; ++k) mixes_out[(size_t)tt * 24 + 6 * ci + k] = tot[ctn][6 * ci + k];
+            if (rstd_out && ci == 0) rstd_out[tt] = o.rstd;
+        }
+    }
+
+    // Pass 2: the collapse with the fresh pre.
+    float pr[2][4];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pr[q][j] = pre_s[16 * q + n][j];
+    float ssq_li[2] = {0.0f, 0.0f};
+    auto body = [&](int i, bool keep, uint4 (&li)[2][2]) {
+        const int step = i * kWaves4 + wave;
+        const int h = step * kWide + g * 8;
+        ActX nxt[2];
+        if (i + 1 < S) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q) load_x4(nxt[q], Xrow[q], hidden, h + kWaves4 * kWide);
+        }
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            li[q][0] = collapse8(cur[q].X[0], pr[q], ssq_li[q]);
+            li[q][1] = collapse8(cur[q].X[1], pr[q], ssq_li[q]);
+            if (!keep) {
+                if (i < Shape::kLiLds) {
+                    li_lds[i][wave][q][0][lane] = li[q][0];
+                    li_lds[i][wave][q][1][lane] = li[q][1];
+                } else {
+                    store_stream(li_row[q] + h, li[q][0]);
+                    store_stream(li_row[q] + h + kStep, li[q][1]);
+                }
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 2; ++q) cur[q] = nxt[q];
+    };
+#pragma unroll 1
+    for (int i = 0; i < S - Shape::kLiReg; ++i) {
+        uint4 li[2][2];
+        body(i, false, li);
+    }
+    uint4 li_keep[Shape::kLiReg > 0 ? Shape::kLiReg : 1][2][2];
+#pragma unroll
+    for (int r = 0; r < Shape::kLiReg; ++r) body(S - Shape::kLiReg + r, true, li_keep[r]);
+
+#pragma unroll
+    for (int q = 0; q < 2; ++q) sq[wave][g][16 * q + n] = ssq_li[q];
+    __syncthreads();
+    if (threadIdx.x < kTileW4) {
+        float sum = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves4; ++w)
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) sum += sq[w][qq][threadIdx.x];
+        rli[threadIdx.x] = rsqrt_nr(sum * (1.0f / (float)hidden) + p.norm_eps);
+    }
+    __syncthreads();
+    // Lanes past the last token write nothing: a lane of the other group
+    // working on the same token T-1 could otherwise read back a value that
+    // has already been normalised.
+    const float r[2] = {rli[n], rli[16 + n]};
+    auto emit = [&](int q, int h, const uint4& li) {
+        if (!valid[q]) return;
+        uint4 out = li;
+        if (norm_w) {
+            const uint4 nw = *reinterpret_cast<const uint4*>(norm_w + h);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t a = word(li, k), b = word(nw, k);
+                set_word(out, k, pack_bf16((bf_lo(a) * r[q]) * bf_lo(b), (bf_hi(a) * r[q]) * bf_hi(b)));
+            }
+        }
+        store_stream(li_row[q] + h, out);
+    };
+#pragma unroll 2
+    for (int i = 0; i < Shape::kLiLds; ++i) {
+        const int h = (i * kWaves4 + wave) * kWide + g * 8;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            emit(q, h, li_lds[i][wave][q][0][lane]);
+            emit(q, h + kStep, li_lds[i][wave][q][1][lane]);
+        }
+    }
+#pragma unroll
+    for (int rr = 0; rr < Shape::kLiReg; ++rr) {
+        const int h = ((S - Shape::kLiReg + rr) * kWaves4 + wave) * kWide + g * 8;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            emit(q, h, li_keep[rr][q][0]);
+            emit(q, h + kStep, li_keep[rr][q][1]);
+        }
+    }
+    if (norm_w) {  // (without norm_w the parked li already is the layer input)
+#pragma unroll 2
+        for (int i = Shape::kLiLds; i < S - Shape::kLiReg; ++i) {
+            const int h = (i * kWaves4 + wave) * kWide + g * 8;
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const uint4 l0 = *reinterpret_cast<const uint4*>(li_row[q] + h);
+                const uint4 l1 = *reinterpret_cast<const uint4*>(li_row[q] + h + kStep);
+                emit(q, h, l0);
+                emit(q, h + kStep, l1);
+            }
+        }
+    }
+}
+
+template <int S>
+hipError_t launch_pre_w4_s(int T, const uint16_t* X, const void* wprep, const float* scale,
+                           const float* base, const uint16_t* norm_w, const Scalars& p,
+                           uint16_t* layer_input, float* pre_out, float* post_out,
+                           float* comb_out, float* mixes, float* rstd, hipStream_t stream) {
+    hipLaunchKernelGGL(k_fused_pre_w4<S>, dim3((T + kTileW4 - 1) / kTileW4), dim3(kWaves4 * 64),
+                       0, stream, T, X, reinterpret_cast<const uint4*>(wprep), scale, base,
+                       norm_w, p, layer_input, pre_out, post_out, comb_out, mixes, rstd);
+    return hipGetLastError();
+}
+
 template <int S>
 hipError_t launch_pre_s(int T, const uint16_t* X, const void* wprep, const float* scale,
                         const float* base, const uint16_t* norm_w, const Scalars& p,
@@ -765,11 +999,15 @@ hipError_t launch_fused_pre(int T, int hidden, const uint16_t* X, const void* wp
                             const float* scale, const float* base, const uint16_t* norm_w,
                             const Scalars& p, uint16_t* layer_input, float* pre_out,
                             float* post_out, float* comb_out, float* mixes, float* rstd,
-                            hipStream_t stream) {
+                            bool tiles32, hipStream_t stream) {
 #define MHC_FUSED_PRE_CASE(D)                                                                  \
     case D:                                                                                    \
-        return launch_pre_s<D / 512>(T, X, wprep, scale, base, norm_w, p, layer_input, pre_out, \
-                                     post_out, comb_out, mixes, rstd, stream);
+        return tiles32 ? launch_pre_w4_s<D / 256>(T, X, wprep, scale, base, norm_w, p,         \
+                                                  layer_input, pre_out, post_out, comb_out,    \
+                                                  mixes, rstd, stream)                         \
+                       : launch_pre_s<D / 512>(T, X, wprep, scale, base, norm_w, p,            \
+                                               layer_input, pre_out, post_out, comb_out, mixes, \
+                                               rstd, stream);
     switch (hidden) {
         MHC_FUSED_PRE_CASE(1024)
         MHC_FUSED_PRE_CASE(2048)

@@ -76,12 +76,13 @@ hipError_t launch_fused_w4(int T, int hidden, const uint16_t* x, const uint16_t*
                            uint16_t* layer_input, float* pre_out, float* post_out,
                            float* comb_out, float* mixes, float* rstd, hipStream_t stream);
 
-// Non-shifted pre, fused: one 8-wave workgroup per 16-token tile, two passes
-// over the tile's X (fused_supported widths).
+// Non-shifted pre, fused: one workgroup per token tile, two passes over the
+// tile's X (fused_supported widths); tiles32 selects 32-token tiles on 4 waves
+// instead of 16-token tiles on 8 waves.
 hipError_t launch_fused_pre(int T, int hidden, const uint16_t* X, const void* wprep,
                             const float* scale, const float* base, const uint16_t* norm_w,
                             const Scalars& p, uint16_t* layer_input, float* pre_out,
                             float* post_out, float* comb_out, float* mixes, float* rstd,
-                            hipStream_t stream);
+                            bool tiles32, hipStream_t stream);
 
 }  // namespace mhc

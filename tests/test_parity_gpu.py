@@ -319,6 +319,18 @@ def test_pre_large_sampled(oracle, name):
     compare(g, o, tokens=tok, xn=False, label=f"pre {name}", fresh=(inp.X, inp.norm_w))
 
 
+@pytest.mark.parametrize("T,d,full", [(8192 + 13, 1024, True), (8192 + 29, 2048, False)])
+def test_pre_fused_32_token_tiles(oracle, T, d, full):
+    """From 8192 tokens the fused pre runs 32-token tiles; ragged tails."""
+    say(f"pre 32-token tiles T={T} d={d}")
+    inp = WL.make_inputs(WL.Config("pw4", d=d, T=T, seed=T + d + 1))
+    g = Dev(inp).pre(norm=True, schedule="fused")
+    tok = None if full else np.unique(np.concatenate(
+        [sample_tokens(T, n=40, seed=d), np.arange(T - 40, T, dtype=np.int32)]))
+    o = oracle.pre(inp, tokens=tok, use_norm=True)
+    compare(g, o, tokens=tok, xn=False, label=f"pre w4 T={T} d={d}", fresh=(inp.X, inp.norm_w))
+
+
 def test_pre_fused_refuses_unsupported_width():
     inp = WL.make_inputs(WL.Config("pu", d=1280, T=4, seed=1))
     dv = Dev(inp)
