@@ -93,18 +93,29 @@ __global__ __launch_bounds__(256) void k_partial(
     const uint16_t* Xrow = X + tc * 4 * hidden;
     const uint16_t* xrow = SHIFTED ? x + tc * hidden : nullptr;
 
-    for (int step = first + wave; step < last; step += 4) {
+    // Step k's weight fragments are requested first, then step k+1's
+    // activations (prefetch), so the projection never waits on HBM: loads
+    // complete in issue order.
+    auto load_x = [&](uint4 (&Xv)[4], uint4& xv, int step) {
         const int h = step * kStep + g * 8;
-        uint4 Xv[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             Xv[j] = *reinterpret_cast<const uint4*>(Xrow + (size_t)j * hidden + h);
-        uint4 xv = make_uint4(0, 0, 0, 0);
+        xv = make_uint4(0, 0, 0, 0);
         if (SHIFTED) xv = *reinterpret_cast<const uint4*>(xrow + h);
+    };
+    uint4 Xv[4], xv;
+    if (first + wave < last) load_x(Xv, xv, first + wave);
+    for (int step = first + wave; step < last; step += 4) {
+        const int h = step * kStep + g * 8;
         uint4 A[kFragsPerStep];
         const uint4* wp = wprep + (size_t)step * kFragsPerStep * 64 + lane;
 #pragma unroll
         for (int i = 0; i < kFragsPerStep; ++i) A[i] = wp[i * 64];
+        __builtin_amdgcn_sched_barrier(0);
+        uint4 Xnx[4], xnx;
+        if (step + 4 < last) load_x(Xnx, xnx, step + 4);
+        __builtin_amdgcn_sched_barrier(0);
 
         uint4 Xn[4];
         if (SHIFTED) {
@@ -122,6 +133,9 @@ __global__ __launch_bounds__(256) void k_partial(
             square_sum(Xv, ssq);
         }
         mfma_step(A, Xn, acc);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) Xv[j] = Xnx[j];
+        xv = xnx;
     }
 
     // Combine the 4 waves in a fixed order: waves ascending, lane groups ascending.
