@@ -44,6 +44,11 @@ def test_size_queries(L):
     assert L.mhc_workspace_bytes(32, 7168) == 32 * 7168
     assert L.mhc_workspace_bytes(8192, 7168) == 8192 * 7168
     assert L.mhc_workspace_bytes(3, 1280) == 3 * 1280
+    # the limits: no 32-bit overflow in the size queries
+    assert L.mhc_workspace_bytes(1 << 20, 16384) == (1 << 20) * 16384
+    assert L.mhc_workspace_bytes((1 << 20) + 1, 16384) == 0
+    assert L.mhc_prepared_weight_bytes(16384) == 384 * 16384
+    assert L.mhc_prepared_weight_bytes(16640) == 0
     assert L.mhc_workspace_bytes(0, 7168) == 0
     assert L.mhc_workspace_bytes(32, 100) == 0
 

@@ -136,7 +136,8 @@ def compare(g, o, tokens=None, xn=True, label="", fresh=None):
         d = np.where(g["layer_input"][sel] == o["layer_input"], 0, 1)
     om = o["mixes"]
     rms = np.sqrt((om ** 2).mean(axis=1, keepdims=True))
-    rel = np.abs(g["mixes"][sel] - om) / np.maximum(np.abs(om), rms)
+    # (an all-zero token has zero mixes: the floor makes it demand exact zeros)
+    rel = np.abs(g["mixes"][sel] - om) / np.maximum(np.maximum(np.abs(om), rms), 1e-30)
     assert rel.max() <= MIX_TOL, f"{label} mixes rel {rel.max():.3g}"
     rr = np.abs(g["rstd"][sel] - o["rstd"]) / o["rstd"]
     assert rr.max() <= MIX_TOL, f"{label} rstd rel {rr.max():.3g}"
@@ -446,3 +447,56 @@ def test_prefetch_weight_changes_nothing():
     c = dv.boundary()
     for k in a:
         assert np.array_equal(a[k], b[k]) and np.array_equal(a[k], c[k]), k
+
+
+def test_maximum_hidden(oracle):
+    """hidden = 16384 (the largest the library takes; split kernels only), ragged
+    token count: boundary, pre, pre from partials and post against the oracle."""
+    T, d = 37, 16384
+    say(f"maximum hidden T={T} d={d}")
+    inp = WL.make_inputs(WL.Config("maxd", d=d, T=T, seed=99))
+    dv = Dev(inp)
+    compare(dv.boundary(), oracle.boundary(inp), label="max hidden boundary")
+    compare(dv.boundary(schedule="invariant"), oracle.boundary(inp), label="max hidden invariant")
+    compare(dv.pre(norm=True), oracle.pre(inp, use_norm=True), xn=False, label="max hidden pre",
+            fresh=(inp.X, inp.norm_w))
+    with pytest.raises(api.MhcError):
+        dv.boundary(schedule="fused")
+    dm, sq = WL.make_partials(T, d, 64, seed=5)
+    li, pre, post, comb = api.pre_mixes(dv.X, dev_f32(dm), dev_f32(sq), dv.scale, dv.base,
+                                        dv.norm_w, prm=dv.prm())
+    torch.cuda.synchronize()
+    o = oracle.pre_from_mixes(inp.X, dm, sq, inp.scale, inp.base, inp.norm_w, inp.params())
+    check_fresh_layer_input(host_bits(li), pre.cpu().numpy(), o, inp.X, inp.norm_w,
+                            label="max hidden pre_mixes")
+    got = host_bits(api.post(dv.x, dv.X, dv.post, dv.comb))
+    assert np.array_equal(got, oracle.boundary(inp)["xn"])
+
+
+@pytest.mark.parametrize("schedule", ["split", "fused"])
+def test_boundary_degenerate_parameters(oracle, schedule):
+    """Degenerate settings of the method, against the oracle: one Sinkhorn
+    iteration (row softmax and a single column pass), many iterations, every eps
+    at zero, and an all-zero token (X = x = 0: X' = 0, the mixes vanish, rstd is
+    1/sqrt(eps) and the layer input is 0)."""
+    say(f"boundary degenerate {schedule}")
+    inp = WL.make_inputs(WL.Config("dg", d=1024, T=21, seed=77))
+    inp.X[5] = 0
+    inp.x[5] = 0
+    dv = Dev(inp)
+    for kw in (dict(sinkhorn_iters=1), dict(sinkhorn_iters=2), dict(sinkhorn_iters=100)):
+        g = dv.boundary(schedule=schedule, **kw)
+        prm = dict(inp.params(), **kw)
+        o = oracle.run(True, inp.X, inp.x, inp.post_prev, inp.comb_prev, inp.pre_lag, inp.W,
+                       inp.scale, inp.base, inp.norm_w, prm)
+        compare(g, o, label=f"{schedule} {kw}")
+        assert np.all(g["layer_input"][5] & 0x7FFF == 0)
+    zero = dict(rms_eps=0.0, pre_eps=0.0, sinkhorn_eps=0.0, norm_eps=0.0)
+    nz = np.arange(21) != 5          # the zero token has no defined rstd without eps
+    g = dv.boundary(schedule=schedule, **zero)
+    o = oracle.run(True, inp.X, inp.x, inp.post_prev, inp.comb_prev, inp.pre_lag, inp.W,
+                   inp.scale, inp.base, inp.norm_w, dict(inp.params(), **zero),
+                   tokens=np.nonzero(nz)[0].astype(np.int32))
+    compare(g, o, tokens=np.nonzero(nz)[0], label=f"{schedule} eps 0")
+    # without eps the last column pass leaves exact unit column sums (up to FP32)
+    np.testing.assert_allclose(g["comb"][nz].sum(axis=1), 1.0, atol=2e-6)
