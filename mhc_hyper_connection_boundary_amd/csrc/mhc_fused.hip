@@ -1,22 +1,28 @@
-// Fused schedule of the mHC boundary: one workgroup of 8 waves owns a tile of
-// 16 tokens and all of hidden, so the partial sums never leave the chip.
+// Fused schedules of the mHC boundary and of the non-shifted pre: one
+// workgroup owns a tile of tokens and all of hidden, so the partial sums never
+// leave the chip.  Two shapes:
+//   k_fused / k_fused_pre        8 waves, 16-token tiles (one token group per
+//                                wave; two waves per SIMD);
+//   k_fused_w4 / k_fused_pre_w4  4 waves, 32-token tiles (two token groups per
+//                                wave sharing each weight fragment; one wave per
+//                                SIMD, so a wave may hold 512 registers).
+// The host picks the 32-token shape once there is a tile per CU (8192 tokens).
 //
 // A wave step covers 64 hidden elements of the tile (two 32-element MFMA
-// k-blocks); wave w takes steps w, w+8, w+16, ...  Every lane reads both
-// 64-byte halves of each 128-byte line it touches back to back, and the 8
-// waves together sweep 1 KB of every row at a time, so HBM sees long runs.
+// k-blocks); wave w takes steps w, w + waves, ...  Every lane reads both
+// 64-byte halves of each 128-byte line it touches back to back, and the waves
+// together sweep contiguous kilobytes of every row, so HBM sees long runs.
 // While a wave computes step i (residual update, X' store, lagged collapse,
 // sums of squares) the activations of step i+1 are in flight; the weight
-// fragments of step i are fetched after that VALU work, then projected on
-// the matrix cores.
+// fragments of step i come from L2 and feed the matrix cores.
 //
-// The BF16 li of the tile (16 x hidden) must wait for rstd_li, which depends
-// on the whole row: the first 8 steps of every wave park it in LDS (128 KB),
-// later steps in the layer-input buffer itself, which the epilogue reads back
-// and overwrites with the normalised values.  After the loop the 8 waves'
-// partials are combined in LDS in a fixed order; wave 0 computes pre / post /
-// Sinkhorn comb (one quad per token) while the other waves already write the
-// layer input.
+// The BF16 li of the tile must wait for rstd_li, which depends on the whole
+// row: the first 8 steps of every wave park it in LDS, the last few in
+// registers, the steps between in the layer-input buffer itself, which the
+// epilogue reads back and overwrites with the normalised values.  After the
+// loop the waves' partials are combined in LDS in a fixed order; one quad per
+// token computes pre / post / Sinkhorn comb while the other waves already
+// write the layer input.
 #include "mhc_device.h"
 #include "mhc_launch.h"
 
