@@ -176,8 +176,8 @@ __device__ __forceinline__ float quad_xor2(float v) {
 __device__ __forceinline__ float sigmoid(float v) { return 1.0f / (1.0f + expf(-v)); }
 
 // 1/x for a positive normal x: the hardware estimate (v_rcp_f32, within 1 ulp)
-// refined by one Newton-Raphson step r + r(1 - x r).  Used for the Sinkhorn
-// normalisations, whose sums lie in [eps, 4 + 5 eps].
+// refined by one Newton-Raphson step r + r(1 - x r).  Used for the softmax sum
+// of the comb logits, which lies in [1, 4].
 __device__ __forceinline__ float recip(float x) {
     const float r = __builtin_amdgcn_rcpf(x);
     return __builtin_fmaf(r, __builtin_fmaf(-x, r, 1.0f), r);
@@ -248,8 +248,13 @@ __device__ __forceinline__ void comb_row(TokenCoef& o, const float* tot, int i,
 #pragma unroll
     for (int k = 0; k < 4; ++k) c[k] = __builtin_fmaf(e[k], inv, p.sinkhorn_eps);
     for (int it = 0; it < p.sinkhorn_iters; ++it) {
+        // The iterations use the bare hardware reciprocal (within 1 ulp): the
+        // normalisations are a contraction, so each step's rounding is damped
+        // by the ones after it, and the dependent chain is 2 FMAs shorter per
+        // normalisation than with a Newton step (measured: the same largest
+        // comb error against the oracle, 2e-7 on the peaked stress logits).
         if (it > 0) {
-            const float rinv = recip((((c[0] + c[1]) + c[2]) + c[3]) + p.sinkhorn_eps);
+            const float rinv = __builtin_amdgcn_rcpf((((c[0] + c[1]) + c[2]) + c[3]) + p.sinkhorn_eps);
 #pragma unroll
             for (int k = 0; k < 4; ++k) c[k] *= rinv;
         }
@@ -257,7 +262,7 @@ __device__ __forceinline__ void comb_row(TokenCoef& o, const float* tot, int i,
         for (int k = 0; k < 4; ++k) {
             float s = c[k] + quad_xor1(c[k]);      // rows (0+1) and (2+3)
             s = s + quad_xor2(s);                   // (0+1) + (2+3)
-            c[k] *= recip(s + p.sinkhorn_eps);
+            c[k] *= __builtin_amdgcn_rcpf(s + p.sinkhorn_eps);
         }
     }
 #pragma unroll
