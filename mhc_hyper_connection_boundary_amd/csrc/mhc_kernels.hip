@@ -357,7 +357,7 @@ struct PartialLayout {
 };
 
 __global__ __launch_bounds__(512) void k_pre_finish(
-    int T, int hidden, PartialLayout pl, const uint16_t* __restrict__ X,
+    int hidden, PartialLayout pl, const uint16_t* __restrict__ X,
     const float* __restrict__ scale, const float* __restrict__ base,
     const uint16_t* __restrict__ norm_w, Scalars p, uint16_t* __restrict__ layer_input,
     float* __restrict__ pre_out, float* __restrict__ post_out, float* __restrict__ comb_out,
@@ -616,7 +616,7 @@ static hipError_t launch_pre_finish_layout(int T, int hidden, const PartialLayou
     // one round trip; large batches: 192, more workgroups per CU.
     const size_t lds = norm_w ? (size_t)hidden * 2 : 0;
     const int threads = T <= 512 ? 512 : 256;
-    hipLaunchKernelGGL(k_pre_finish, dim3(T), dim3(threads), lds, stream, T, hidden, pl, X, scale,
+    hipLaunchKernelGGL(k_pre_finish, dim3(T), dim3(threads), lds, stream, hidden, pl, X, scale,
                        base, norm_w, p, layer_input, pre_out, post_out, comb_out, mixes, rstd);
     return hipGetLastError();
 }
