@@ -513,3 +513,30 @@ def test_determinism_stress():
             b = dv.boundary(schedule=schedule)
             for k in a:
                 assert np.array_equal(a[k], b[k]), f"{schedule}: {k} differs between runs"
+
+
+def _random_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        T = int(rng.integers(1, 400))
+        d = int(rng.choice([256, 512, 768, 1024, 1280, 2048, 3072, 4096, 5120, 6144]))
+        iters = int(rng.integers(1, 30))
+        eps = float(10.0 ** rng.uniform(-8, -4))
+        cases.append((T, d, iters, eps))
+    return cases
+
+
+@pytest.mark.parametrize("T,d,iters,eps", _random_cases(8, seed=2024))
+def test_random_shapes_and_parameters(oracle, T, d, iters, eps):
+    """A seeded sweep of token counts, widths, Sinkhorn iterations and eps values
+    through every schedule the width has (boundary) and the pre."""
+    say(f"random T={T} d={d} iters={iters} eps={eps:.2e}")
+    inp = WL.make_inputs(WL.Config("rnd", d=d, T=T, seed=T * 31 + d, sinkhorn_iters=iters,
+                                   eps=eps, rms_eps=eps))
+    dv = Dev(inp)
+    o = oracle.boundary(inp)
+    for schedule in ("auto", "split", "invariant") + (("fused",) if d in FUSED_D else ()):
+        compare(dv.boundary(schedule=schedule), o, label=f"random {schedule}")
+    compare(dv.pre(norm=True), oracle.pre(inp, use_norm=True), xn=False, label="random pre",
+            fresh=(inp.X, inp.norm_w))
