@@ -315,7 +315,7 @@ def cpu_baseline(inp, budget_s=10.0):
 
 
 def copy_calibration():
-    """A plain 1 GiB device copy: the box's practical streaming ceiling and the
+    """A plain 1 GiB device copy: the device's practical streaming ceiling and the
     reference reading for the FETCH_SIZE / WRITE_SIZE counters."""
     import torch
 
