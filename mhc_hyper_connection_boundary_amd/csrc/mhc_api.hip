@@ -15,7 +15,7 @@ namespace mhc {
 namespace {
 
 constexpr long kTargetWaves = 2048;  // waves of k_partial work to aim for
-constexpr int kFinishTarget = 512;   // k_finish workgroups to aim for
+constexpr int kFinishTarget = 2048;  // k_finish workgroups to aim for
 constexpr int kFusedMinTokens = 3072; // automatic schedule: fused from this many tokens
 constexpr int kW4MinTokens = 8192;    // fused schedule: 32-token tiles on 4 waves from here
 
