@@ -344,7 +344,7 @@ __global__ __launch_bounds__(256) void k_finish(
 
 
 // ---------------------------------------------------------------------------
-// Non-shifted pre, kernel 2: one workgroup (256 threads) per token.
+// Non-shifted pre, kernel 2: one workgroup (256 or 512 threads) per token.
 // ---------------------------------------------------------------------------
 // Where the partial sums of the projection live: value v (24 mixes, then the
 // sum of squares) of token t in split q is
@@ -362,10 +362,11 @@ __global__ __launch_bounds__(512) void k_pre_finish(
     const uint16_t* __restrict__ norm_w, Scalars p, uint16_t* __restrict__ layer_input,
     float* __restrict__ pre_out, float* __restrict__ post_out, float* __restrict__ comb_out,
     float* __restrict__ mixes_out, float* __restrict__ rstd_out) {
-    extern __shared__ uint4 li_s[];  // [hidden / 8] when norm_w is given
+    // With norm_w: li of the row, [hidden / 8] chunks, then the sum of squares
+    // of each chunk, [hidden / 8] floats.
+    extern __shared__ uint4 li_s[];
     __shared__ float tot[26];
     __shared__ float pre_s[4];
-    __shared__ float red[448];
     __shared__ float cred[8][26];
     __shared__ float rli;
 
@@ -374,6 +375,7 @@ __global__ __launch_bounds__(512) void k_pre_finish(
     const int nch = hidden / 8;             // 16-byte chunks of a row
     const int nc = (int)blockDim.x - 64;    // collapse threads: waves 1.. (192 or 448)
     const int u0 = tid - 64;                // collapse thread index
+    float* const chunk_ssq = reinterpret_cast<float*>(li_s + nch);
     const uint16_t* Xrow = X + (size_t)t * 4 * hidden;
 
     // Waves 1-3 request their first two chunks of X before anything waits;
@@ -432,13 +434,13 @@ __global__ __launch_bounds__(512) void k_pre_finish(
 
     if (tid >= 64) {
         const float pr[4] = {pre_s[0], pre_s[1], pre_s[2], pre_s[3]};
-        float ssq_li = 0.0f;
         auto collapse = [&](uint4 (&b)[4], int cidx) {
             uint4 Xv[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) Xv[j] = b[j];
             load_chunk(b, cidx + 2 * nc);       // two chunks ahead
             uint4 li;
+            float ssq_li = 0.0f;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 float acc[2];
@@ -456,20 +458,25 @@ __global__ __launch_bounds__(512) void k_pre_finish(
                 ssq_li = __builtin_fmaf(bf_lo(lw), bf_lo(lw), ssq_li);
                 ssq_li = __builtin_fmaf(bf_hi(lw), bf_hi(lw), ssq_li);
             }
-            if (norm_w) li_s[cidx] = li;
-            else *reinterpret_cast<uint4*>(layer_input + (size_t)t * hidden + cidx * 8) = li;
+            if (norm_w) {
+                li_s[cidx] = li;
+                chunk_ssq[cidx] = ssq_li;
+            } else *reinterpret_cast<uint4*>(layer_input + (size_t)t * hidden + cidx * 8) = li;
         };
         for (int cidx = u0; cidx < nch; cidx += 2 * nc) {
             collapse(bufA, cidx);
             if (cidx + nc < nch) collapse(bufB, cidx + nc);
         }
-        red[u0] = ssq_li;
     }
     if (norm_w) {
         __syncthreads();
-        if (tid >= 64 && tid < 128) {  // fixed-order reduction of the nc partial sums
-            float v = red[u0];
-            for (int k = 64; k < nc; k += 64) v += red[u0 + k];
+        // Chunk sums in an order fixed by hidden alone (the number of collapse
+        // threads varies with the batch): lane l adds chunks l, l + 64, ... in
+        // order, then the 64 lanes are combined by the butterfly.
+        if (tid >= 64 && tid < 128) {
+            float v = 0.0f;
+#pragma unroll 4
+            for (int k = u0; k < nch; k += 64) v += chunk_ssq[k];
 #pragma unroll
             for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
             if (u0 == 0) rli = rsqrt_nr(v * (1.0f / (float)hidden) + p.norm_eps);
@@ -614,7 +621,7 @@ static hipError_t launch_pre_finish_layout(int T, int hidden, const PartialLayou
                                            float* mixes, float* rstd, hipStream_t stream) {
     // Small batches: 448 collapse threads, so a row of 7168 is requested in
     // one round trip; large batches: 192, more workgroups per CU.
-    const size_t lds = norm_w ? (size_t)hidden * 2 : 0;
+    const size_t lds = norm_w ? (size_t)hidden * 2 + (size_t)hidden / 8 * sizeof(float) : 0;
     const int threads = T <= 512 ? 512 : 256;
     hipLaunchKernelGGL(k_pre_finish, dim3(T), dim3(threads), lds, stream, hidden, pl, X, scale,
                        base, norm_w, p, layer_input, pre_out, post_out, comb_out, mixes, rstd);
