@@ -22,7 +22,10 @@
 // epilogue reads back and overwrites with the normalised values.  After the
 // loop the waves' partials are combined in LDS in a fixed order; one quad per
 // token computes pre / post / Sinkhorn comb while the other waves already
-// write the layer input.
+// write the layer input.  Every CU finishes its tile at about the same time,
+// so nothing overlaps the epilogue: its loads (norm_w, the first parked steps)
+// are requested before the reductions, and several parked steps stay in
+// flight while it writes.
 #include "mhc_device.h"
 #include "mhc_launch.h"
 
@@ -34,9 +37,17 @@ constexpr int kWide = 2 * kStep;  // hidden elements per wave step: two MFMA k-b
 
 template <int S>                  // S = hidden / (kWaves * kWide): steps per wave
 struct FusedShape {
+    static constexpr int kSteps = S;
     static constexpr int kLiLds = S < 8 ? S : 8;  // first steps: li waits in LDS (16 KB each)
     static constexpr int kLiReg = S - kLiLds < 3 ? S - kLiLds : 3;  // last steps: in registers
 };                                                // (steps between: layer_input)
+
+template <int S>                  // the 8-wave pre keeps no li in registers
+struct FusedPreShape {
+    static constexpr int kSteps = S;
+    static constexpr int kLiLds = FusedShape<S>::kLiLds;
+    static constexpr int kLiReg = 0;
+};
 
 // Activations of one wave step.  Lane (n, g) holds, for token n, the 8 hidden
 // elements 64*step + 32*b + 8*g + [0, 8) of block b = 0, 1: the two 64-byte
@@ -73,6 +84,126 @@ __device__ __forceinline__ void load_frags(uint4 (&A)[kFragsPerStep], const uint
 #pragma unroll
     for (int i = 0; i < kFragsPerStep; ++i) A[i] = wp[i * 64];
 }
+
+// Writing the layer input of a token tile once rstd_li is known.  The li of
+// a wave's steps sits in LDS (first kLiLds steps), in registers (last kLiReg)
+// or, for the steps between, in the layer-input buffer itself.  prefetch()
+// runs right after the main loop: it requests norm_w of the on-chip steps, then
+// the first kDepth parked steps (li, written earlier by this same lane, and
+// norm_w); since loads complete in issue order, the on-chip steps never wait
+// for parked ones, and all of it is in flight during the reductions and the
+// Sinkhorn.  emit() then writes the on-chip steps and the parked ones, each
+// parked step's slot refilled kDepth steps ahead.  A lane owns kGroups tokens
+// (16 apart); lanes past the last token write nothing, since another lane
+// working on the same token T-1 would otherwise read back a value that has
+// already been normalised.  Kernels short of registers request the on-chip
+// steps' norm_w as they write (kNwEarly false) and keep fewer parked steps in
+// flight (kMaxDepth).
+template <class Shape, int kWavesN, int kGroups, bool kNwEarly, int kMaxDepth>
+struct LayerInputEpilogue {
+    static constexpr int kParkEnd = Shape::kSteps - Shape::kLiReg;  // parked: [kLiLds, kParkEnd)
+    static constexpr int kParked = kParkEnd - Shape::kLiLds;
+    static constexpr int kDepth =  // parked steps in flight
+        kParked < kMaxDepth ? (kParked > 0 ? kParked : 1) : kMaxDepth;
+    static constexpr int kLds = Shape::kLiLds > 0 ? Shape::kLiLds : 1;
+    static constexpr int kReg = Shape::kLiReg > 0 ? Shape::kLiReg : 1;
+
+    const uint16_t* norm_w;
+    uint16_t* li_row[kGroups];
+    bool valid[kGroups];
+    int wave, g;
+    uint4 ring_li[kDepth][kGroups][2], ring_nw[kDepth][2];
+    uint4 lds_nw[kNwEarly ? kLds : 1][2], keep_nw[kNwEarly ? kReg : 1][2];
+
+    __device__ __forceinline__ int step_h(int i) const { return (i * kWavesN + wave) * kWide + g * 8; }
+
+    __device__ __forceinline__ void load_parked(int i) {
+        const int slot = (i - Shape::kLiLds) % kDepth, h = step_h(i);
+        ring_nw[slot][0] = load_stream(norm_w + h);
+        ring_nw[slot][1] = load_stream(norm_w + h + kStep);
+#pragma unroll
+        for (int q = 0; q < kGroups; ++q)
+            if (valid[q]) {
+                ring_li[slot][q][0] = load_stream(li_row[q] + h);
+                ring_li[slot][q][1] = load_stream(li_row[q] + h + kStep);
+            }
+    }
+
+    __device__ __forceinline__ void prefetch() {
+        if (!norm_w) return;
+        if (kNwEarly) {
+#pragma unroll
+            for (int i = 0; i < Shape::kLiLds; ++i) {
+                lds_nw[i][0] = load_stream(norm_w + step_h(i));
+                lds_nw[i][1] = load_stream(norm_w + step_h(i) + kStep);
+            }
+#pragma unroll
+            for (int rr = 0; rr < Shape::kLiReg; ++rr) {
+                keep_nw[rr][0] = load_stream(norm_w + step_h(kParkEnd + rr));
+                keep_nw[rr][1] = load_stream(norm_w + step_h(kParkEnd + rr) + kStep);
+            }
+        }
+#pragma unroll
+        for (int i = Shape::kLiLds; i < kParkEnd && i < Shape::kLiLds + kDepth; ++i) load_parked(i);
+    }
+
+    __device__ __forceinline__ uint4 nw_at(const uint4 (&early)[2], int b, int h) const {
+        return kNwEarly ? early[b] : load_stream(norm_w + h);
+    }
+
+    __device__ __forceinline__ void put(int q, int h, const uint4& li, const uint4& nw, float r) {
+        if (!valid[q]) return;
+        uint4 out = li;
+        if (norm_w) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t a = word(li, k), b = word(nw, k);
+                set_word(out, k, pack_bf16((bf_lo(a) * r) * bf_lo(b), (bf_hi(a) * r) * bf_hi(b)));
+            }
+        }
+        store_stream(li_row[q] + h, out);
+    }
+
+    // lds_li(i, q, b) and keep_li(rr, q, b): li of block b of token group q in
+    // LDS step i and in register step rr.
+    template <class LdsLi, class KeepLi>
+    __device__ __forceinline__ void emit(const LdsLi& lds_li, const KeepLi& keep_li,
+                                         const float (&r)[kGroups]) {
+#pragma unroll
+        for (int i = 0; i < Shape::kLiLds; ++i) {
+            const int h = step_h(i);
+            const uint4 nw0 = norm_w ? nw_at(lds_nw[kNwEarly ? i : 0], 0, h) : uint4{};
+            const uint4 nw1 = norm_w ? nw_at(lds_nw[kNwEarly ? i : 0], 1, h + kStep) : uint4{};
+#pragma unroll
+            for (int q = 0; q < kGroups; ++q) {
+                put(q, h, lds_li(i, q, 0), nw0, r[q]);
+                put(q, h + kStep, lds_li(i, q, 1), nw1, r[q]);
+            }
+        }
+#pragma unroll
+        for (int rr = 0; rr < Shape::kLiReg; ++rr) {
+            const int h = step_h(kParkEnd + rr);
+            const uint4 nw0 = norm_w ? nw_at(keep_nw[kNwEarly ? rr : 0], 0, h) : uint4{};
+            const uint4 nw1 = norm_w ? nw_at(keep_nw[kNwEarly ? rr : 0], 1, h + kStep) : uint4{};
+#pragma unroll
+            for (int q = 0; q < kGroups; ++q) {
+                put(q, h, keep_li(rr, q, 0), nw0, r[q]);
+                put(q, h + kStep, keep_li(rr, q, 1), nw1, r[q]);
+            }
+        }
+        if (!norm_w) return;  // without norm_w the parked li already is the layer input
+#pragma unroll
+        for (int i = Shape::kLiLds; i < kParkEnd; ++i) {
+            const int slot = (i - Shape::kLiLds) % kDepth, h = step_h(i);
+#pragma unroll
+            for (int q = 0; q < kGroups; ++q) {
+                put(q, h, ring_li[slot][q][0], ring_nw[slot][0], r[q]);
+                put(q, h + kStep, ring_li[slot][q][1], ring_nw[slot][1], r[q]);
+            }
+            if (i + kDepth < kParkEnd) load_parked(i + kDepth);
+        }
+    }
+};
 
 template <int S>
 __global__ __launch_bounds__(512) void k_fused(
@@ -159,6 +290,8 @@ __global__ __launch_bounds__(512) void k_fused(
     uint4 li_keep[Shape::kLiReg > 0 ? Shape::kLiReg : 1][2];
 #pragma unroll
     for (int r = 0; r < Shape::kLiReg; ++r) body(S - Shape::kLiReg + r, true, li_keep[r]);
+    LayerInputEpilogue<Shape, kWaves, 1, false, 2> out{norm_w, {li_row}, {t < T}, wave, g};
+    out.prefetch();
 
     // Partials of the 8 waves, combined in a fixed order.
     CoefParams cp;
@@ -202,43 +335,10 @@ __global__ __launch_bounds__(512) void k_fused(
         }
     }
 
-    // Layer input for this wave's steps: li from LDS, then li parked in the
-    // layer-input buffer (written by this same lane before the barrier above).
-    // Lanes past the last token rewrite token T-1's identical values.
-    const float r = rli[n];
-    auto emit = [&](int h, const uint4& li) {
-        if (t >= T) return;  // lanes past the last token leave token T-1 to its own lane
-        uint4 out = li;
-        if (norm_w) {
-            const uint4 nw = *reinterpret_cast<const uint4*>(norm_w + h);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint32_t a = word(li, q), b = word(nw, q);
-                set_word(out, q, pack_bf16((bf_lo(a) * r) * bf_lo(b), (bf_hi(a) * r) * bf_hi(b)));
-            }
-        }
-        store_stream(li_row + h, out);
-    };
-#pragma unroll 2
-    for (int i = 0; i < Shape::kLiLds; ++i) {
-        const int h = (i * kWaves + wave) * kWide + g * 8;
-        emit(h, li_lds[i][wave][0][lane]);
-        emit(h + kStep, li_lds[i][wave][1][lane]);
-    }
-#pragma unroll
-    for (int r = 0; r < Shape::kLiReg; ++r) {
-        const int h = ((S - Shape::kLiReg + r) * kWaves + wave) * kWide + g * 8;
-        emit(h, li_keep[r][0]);
-        emit(h + kStep, li_keep[r][1]);
-    }
-#pragma unroll 2
-    for (int i = Shape::kLiLds; i < S - Shape::kLiReg; ++i) {
-        const int h = (i * kWaves + wave) * kWide + g * 8;
-        const uint4 l0 = *reinterpret_cast<const uint4*>(li_row + h);
-        const uint4 l1 = *reinterpret_cast<const uint4*>(li_row + h + kStep);
-        emit(h, l0);
-        emit(h + kStep, l1);
-    }
+    // Layer input for this wave's steps.
+    const float r[1] = {rli[n]};
+    out.emit([&](int i, int, int b) { return li_lds[i][wave][b][lane]; },
+             [&](int rr, int, int b) { return li_keep[rr][b]; }, r);
 }
 
 // ---------------------------------------------------------------------------
@@ -256,8 +356,11 @@ __global__ __launch_bounds__(512) void k_fused(
 constexpr int kWaves4 = 4;
 constexpr int kTileW4 = 32;
 
-template <int S>                  // S = hidden / (kWaves4 * kWide): steps per wave
+// S = hidden / (kWaves4 * kWide): steps per wave; li of the last (at most 2)
+// steps stays in registers.  More registers spill.
+template <int S>
 struct FusedW4Shape {
+    static constexpr int kSteps = S;
     static constexpr int kLiLds = S < 8 ? S : 8;  // first steps: li waits in LDS (16 KB each)
     static constexpr int kLiReg = S - kLiLds < 2 ? S - kLiLds : 2;  // last steps: in registers
 };                                                // (steps between: layer_input)
@@ -365,6 +468,9 @@ __global__ __launch_bounds__(256) void k_fused_w4(
     uint4 li_keep[Shape::kLiReg > 0 ? Shape::kLiReg : 1][2][2];
 #pragma unroll
     for (int r = 0; r < Shape::kLiReg; ++r) body(S - Shape::kLiReg + r, true, li_keep[r]);
+    LayerInputEpilogue<Shape, kWaves4, 2, true, 5> out{
+        norm_w, {li_row[0], li_row[1]}, {tile * kTileW4 + n < T, tile * kTileW4 + 16 + n < T}, wave, g};
+    out.prefetch();
 
     // Partials of the 4 waves, combined in a fixed order.
     CoefParams cp;
@@ -411,57 +517,10 @@ __global__ __launch_bounds__(256) void k_fused_w4(
         }
     }
 
-    // Layer input for this wave's steps: li from LDS, then li parked in the
-    // layer-input buffer (written by this same lane before the barriers above).
-    // Lanes past the last token write nothing here: a lane of the other group
-    // working on the same token T-1 would otherwise read back a value that
-    // has already been normalised.
+    // Layer input for this wave's steps.
     const float r[2] = {rli[n], rli[16 + n]};
-    const bool valid[2] = {tile * kTileW4 + n < T, tile * kTileW4 + 16 + n < T};
-    auto emit = [&](int q, int h, const uint4& li) {
-        if (!valid[q]) return;
-        uint4 out = li;
-        if (norm_w) {
-            const uint4 nw = *reinterpret_cast<const uint4*>(norm_w + h);
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const uint32_t a = word(li, k), b = word(nw, k);
-                set_word(out, k, pack_bf16((bf_lo(a) * r[q]) * bf_lo(b), (bf_hi(a) * r[q]) * bf_hi(b)));
-            }
-        }
-        store_stream(li_row[q] + h, out);
-    };
-#pragma unroll 2
-    for (int i = 0; i < Shape::kLiLds; ++i) {
-        const int h = (i * kWaves4 + wave) * kWide + g * 8;
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            emit(q, h, li_lds[i][wave][q][0][lane]);
-            emit(q, h + kStep, li_lds[i][wave][q][1][lane]);
-        }
-    }
-#pragma unroll
-    for (int rr = 0; rr < Shape::kLiReg; ++rr) {
-        const int h = ((S - Shape::kLiReg + rr) * kWaves4 + wave) * kWide + g * 8;
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            emit(q, h, li_keep[rr][q][0]);
-            emit(q, h + kStep, li_keep[rr][q][1]);
-        }
-    }
-    if (norm_w) {  // (without norm_w the parked li already is the layer input)
-#pragma unroll 2
-        for (int i = Shape::kLiLds; i < S - Shape::kLiReg; ++i) {
-            const int h = (i * kWaves4 + wave) * kWide + g * 8;
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const uint4 l0 = *reinterpret_cast<const uint4*>(li_row[q] + h);
-                const uint4 l1 = *reinterpret_cast<const uint4*>(li_row[q] + h + kStep);
-                emit(q, h, l0);
-                emit(q, h + kStep, l1);
-            }
-        }
-    }
+    out.emit([&](int i, int q, int b) { return li_lds[i][wave][q][b][lane]; },
+             [&](int rr, int q, int b) { return li_keep[rr][q][b]; }, r);
 }
 
 template <int S>
@@ -533,6 +592,7 @@ __global__ __launch_bounds__(512) void k_fused_pre(
     float* __restrict__ pre_out, float* __restrict__ post_out, float* __restrict__ comb_out,
     float* __restrict__ mixes_out, float* __restrict__ rstd_out) {
     using Shape = FusedShape<S>;
+    using PreShape = FusedPreShape<S>;
     constexpr int hidden = S * kWide * kWaves;
     __shared__ uint4 li_lds[Shape::kLiLds > 0 ? Shape::kLiLds : 1][kWaves][2][64];
     __shared__ float red[kWaves][kTile][24];
@@ -638,6 +698,8 @@ __global__ __launch_bounds__(512) void k_fused_pre(
         }
         cur = nxt;
     }
+    LayerInputEpilogue<PreShape, kWaves, 1, true, 5> out{norm_w, {li_row}, {t < T}, wave, g};
+    out.prefetch();
     sq[wave][g][n] = ssq_li;
     __syncthreads();
     if (threadIdx.x < kTile) {
@@ -649,41 +711,11 @@ __global__ __launch_bounds__(512) void k_fused_pre(
         rli[threadIdx.x] = rsqrt_nr(sum * (1.0f / (float)hidden) + p.norm_eps);
     }
     __syncthreads();
-    const float r = rli[n];
-    auto emit = [&](int h, const uint4& li) {
-        if (t >= T) return;  // lanes past the last token leave token T-1 to its own lane
-        uint4 out = li;
-        if (norm_w) {
-            const uint4 nw = *reinterpret_cast<const uint4*>(norm_w + h);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint32_t a = word(li, q), b = word(nw, q);
-                set_word(out, q, pack_bf16((bf_lo(a) * r) * bf_lo(b), (bf_hi(a) * r) * bf_hi(b)));
-            }
-        }
-        store_stream(li_row + h, out);
-    };
-#pragma unroll 2
-    for (int i = 0; i < Shape::kLiLds; ++i) {
-        const int h = (i * kWaves + wave) * kWide + g * 8;
-        emit(h, li_lds[i][wave][0][lane]);
-        emit(h + kStep, li_lds[i][wave][1][lane]);
-    }
-    if (norm_w) {  // (without norm_w the parked li already is the layer input)
-#pragma unroll 2
-        for (int i = Shape::kLiLds; i < S; ++i) {
-            const int h = (i * kWaves + wave) * kWide + g * 8;
-            const uint4 l0 = *reinterpret_cast<const uint4*>(li_row + h);
-            const uint4 l1 = *reinterpret_cast<const uint4*>(li_row + h + kStep);
-            emit(h, l0);
-            emit(h + kStep, l1);
-        }
-    }
+    const float r[1] = {rli[n]};
+    out.emit([&](int i, int, int b) { return li_lds[i][wave][b][lane]; },
+             [&](int, int, int) { return uint4{}; }, r);
 }
 
-// Non-shifted pre on 4 waves with 32-token tiles: the two passes of k_fused_pre,
-// with every wave carrying two 16-token groups (lane n: tokens n and n + 16 of
-// the tile) so that pass 1 feeds both groups from one set of weight fragments.
 template <int S>
 __global__ __launch_bounds__(256) void k_fused_pre_w4(
     int T, const uint16_t* __restrict__ X, const uint4* __restrict__ wprep,
@@ -841,6 +873,8 @@ __global__ __launch_bounds__(256) void k_fused_pre_w4(
     uint4 li_keep[Shape::kLiReg > 0 ? Shape::kLiReg : 1][2][2];
 #pragma unroll
     for (int r = 0; r < Shape::kLiReg; ++r) body(S - Shape::kLiReg + r, true, li_keep[r]);
+    LayerInputEpilogue<Shape, kWaves4, 2, true, 5> out{norm_w, {li_row[0], li_row[1]}, {valid[0], valid[1]}, wave, g};
+    out.prefetch();
 
 #pragma unroll
     for (int q = 0; q < 2; ++q) sq[wave][g][16 * q + n] = ssq_li[q];
@@ -854,54 +888,9 @@ __global__ __launch_bounds__(256) void k_fused_pre_w4(
         rli[threadIdx.x] = rsqrt_nr(sum * (1.0f / (float)hidden) + p.norm_eps);
     }
     __syncthreads();
-    // Lanes past the last token write nothing: a lane of the other group
-    // working on the same token T-1 could otherwise read back a value that
-    // has already been normalised.
     const float r[2] = {rli[n], rli[16 + n]};
-    auto emit = [&](int q, int h, const uint4& li) {
-        if (!valid[q]) return;
-        uint4 out = li;
-        if (norm_w) {
-            const uint4 nw = *reinterpret_cast<const uint4*>(norm_w + h);
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const uint32_t a = word(li, k), b = word(nw, k);
-                set_word(out, k, pack_bf16((bf_lo(a) * r[q]) * bf_lo(b), (bf_hi(a) * r[q]) * bf_hi(b)));
-            }
-        }
-        store_stream(li_row[q] + h, out);
-    };
-#pragma unroll 2
-    for (int i = 0; i < Shape::kLiLds; ++i) {
-        const int h = (i * kWaves4 + wave) * kWide + g * 8;
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            emit(q, h, li_lds[i][wave][q][0][lane]);
-            emit(q, h + kStep, li_lds[i][wave][q][1][lane]);
-        }
-    }
-#pragma unroll
-    for (int rr = 0; rr < Shape::kLiReg; ++rr) {
-        const int h = ((S - Shape::kLiReg + rr) * kWaves4 + wave) * kWide + g * 8;
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            emit(q, h, li_keep[rr][q][0]);
-            emit(q, h + kStep, li_keep[rr][q][1]);
-        }
-    }
-    if (norm_w) {  // (without norm_w the parked li already is the layer input)
-#pragma unroll 2
-        for (int i = Shape::kLiLds; i < S - Shape::kLiReg; ++i) {
-            const int h = (i * kWaves4 + wave) * kWide + g * 8;
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const uint4 l0 = *reinterpret_cast<const uint4*>(li_row[q] + h);
-                const uint4 l1 = *reinterpret_cast<const uint4*>(li_row[q] + h + kStep);
-                emit(q, h, l0);
-                emit(q, h + kStep, l1);
-            }
-        }
-    }
+    out.emit([&](int i, int q, int b) { return li_lds[i][wave][q][b][lane]; },
+             [&](int rr, int q, int b) { return li_keep[rr][q][b]; }, r);
 }
 
 template <int S>
