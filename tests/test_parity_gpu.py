@@ -184,11 +184,12 @@ def test_boundary_small_full(oracle, T, d, schedule):
 
 
 @pytest.mark.parametrize("T,d,full", [(8192 + 13, 1024, True), (8192 + 29, 2048, False),
-                                      (8192 + 3, 5120, False)])
+                                      (8192 + 3, 5120, False), (8192 + 7, 8192, False)])
 def test_boundary_fused_32_token_tiles(oracle, T, d, full):
     """From 8192 tokens the fused schedule runs 32-token tiles (two token
     groups per wave).  Ragged tails leave the second group, or both, partly
-    past the last token."""
+    past the last token.  From d=4096 some li steps wait in the output buffer
+    (10 at d=5120, 22 at d=8192, more than the 5 the epilogue keeps in flight)."""
     say(f"boundary 32-token tiles T={T} d={d}")
     inp = WL.make_inputs(WL.Config("w4", d=d, T=T, seed=T + d))
     g = Dev(inp).boundary(schedule="fused")
@@ -320,7 +321,8 @@ def test_pre_large_sampled(oracle, name):
     compare(g, o, tokens=tok, xn=False, label=f"pre {name}", fresh=(inp.X, inp.norm_w))
 
 
-@pytest.mark.parametrize("T,d,full", [(8192 + 13, 1024, True), (8192 + 29, 2048, False)])
+@pytest.mark.parametrize("T,d,full", [(8192 + 13, 1024, True), (8192 + 29, 2048, False),
+                                      (8192 + 5, 4096, False)])
 def test_pre_fused_32_token_tiles(oracle, T, d, full):
     """From 8192 tokens the fused pre runs 32-token tiles; ragged tails."""
     say(f"pre 32-token tiles T={T} d={d}")
