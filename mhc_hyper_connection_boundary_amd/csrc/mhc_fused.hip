@@ -356,12 +356,13 @@ __global__ __launch_bounds__(512) void k_fused(
 constexpr int kWaves4 = 4;
 constexpr int kTileW4 = 32;
 
-// S = hidden / (kWaves4 * kWide): steps per wave; li of the last (at most 2)
-// steps stays in registers.  More registers spill.
-template <int S>
+// S = hidden / (kWaves4 * kWide): steps per wave; li of the first (at most
+// LdsMax) steps waits in LDS, 16 KB each, and of the last (at most 2) in
+// registers.  More registers spill.
+template <int S, int LdsMax = 8>
 struct FusedW4Shape {
     static constexpr int kSteps = S;
-    static constexpr int kLiLds = S < 8 ? S : 8;  // first steps: li waits in LDS (16 KB each)
+    static constexpr int kLiLds = S < LdsMax ? S : LdsMax;  // first steps: li waits in LDS
     static constexpr int kLiReg = S - kLiLds < 2 ? S - kLiLds : 2;  // last steps: in registers
 };                                                // (steps between: layer_input)
 
@@ -375,11 +376,10 @@ __global__ __launch_bounds__(256) void k_fused_w4(
     uint16_t* __restrict__ layer_input, float* __restrict__ pre_out,
     float* __restrict__ post_out, float* __restrict__ comb_out, float* __restrict__ mixes_out,
     float* __restrict__ rstd_out) {
-    using Shape = FusedW4Shape<S>;
+    // 9 li steps in LDS: the cross-wave sums need no buffer per wave.
+    using Shape = FusedW4Shape<S, 9>;
     constexpr int hidden = S * kWide * kWaves4;
     __shared__ uint4 li_lds[Shape::kLiLds > 0 ? Shape::kLiLds : 1][kWaves4][2][2][64];
-    __shared__ float red[kWaves4][kTileW4][24];
-    __shared__ float sq[kWaves4][4][kTileW4][2];
     __shared__ float tot[kTileW4][26];
     __shared__ float rli[kTileW4];
 
@@ -472,34 +472,46 @@ __global__ __launch_bounds__(256) void k_fused_w4(
         norm_w, {li_row[0], li_row[1]}, {tile * kTileW4 + n < T, tile * kTileW4 + 16 + n < T}, wave, g};
     out.prefetch();
 
-    // Partials of the 4 waves, combined in a fixed order.
+    // Partials of the 4 waves, added into tot one wave at a time from 0.0f,
+    // wave 0 first: each mix is ((w0 + w1) + w2) + w3, each sum of squares
+    // adds the k-groups 0..3 of wave 0, then of wave 1, ...  Lane group 0 of
+    // a wave gathers the four k-group values of its token.
     CoefParams cp;
     if (wave < 2) cp = load_coef_params(scale, base, lane & 3);
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int w = 0; w < kWaves4; ++w) {
+        if (wave == w) {
 #pragma unroll
-        for (int m = 0; m < 3; ++m)
+            for (int q = 0; q < 2; ++q) {
+                const int tn = 16 * q + n;
 #pragma unroll
-            for (int j = 0; j < 2; ++j) red[wave][16 * q + n][8 * m + 2 * g + j] = mix_of(acc[q], m, j);
-        sq[wave][g][16 * q + n][0] = ssq[q];
-        sq[wave][g][16 * q + n][1] = ssq_li[q];
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < kTileW4 * 26; idx += kWaves4 * 64) {
-        const int tn = idx / 26, v = idx % 26;
-        float sum = 0.0f;
-        if (v < 24) {
+                for (int m = 0; m < 3; ++m)
 #pragma unroll
-            for (int w = 0; w < kWaves4; ++w) sum += red[w][tn][v];
-        } else {
+                    for (int j = 0; j < 2; ++j) {
+                        const int v = 8 * m + 2 * g + j;
+                        tot[tn][v] = (w == 0 ? 0.0f : tot[tn][v]) + mix_of(acc[q], m, j);
+                    }
+                float part[2][4];
 #pragma unroll
-            for (int w = 0; w < kWaves4; ++w)
+                for (int gg = 0; gg < 4; ++gg) {
+                    part[0][gg] = __shfl(ssq[q], n + 16 * gg);
+                    part[1][gg] = __shfl(ssq_li[q], n + 16 * gg);
+                }
+                if (g == 0) {
 #pragma unroll
-                for (int qq = 0; qq < 4; ++qq) sum += sq[w][qq][tn][v - 24];
+                    for (int e = 0; e < 2; ++e) {
+                        float t = w == 0 ? 0.0f : tot[tn][24 + e];
+#pragma unroll
+                        for (int gg = 0; gg < 4; ++gg) t += part[e][gg];
+                        tot[tn][24 + e] = t;
+                    }
+                }
+            }
         }
-        tot[tn][v] = sum;
-        if (v == 25) rli[tn] = rsqrt_nr(sum * (1.0f / (float)hidden) + p.norm_eps);
+        __syncthreads();
     }
+    if (threadIdx.x < kTileW4)
+        rli[threadIdx.x] = rsqrt_nr(tot[threadIdx.x][25] * (1.0f / (float)hidden) + p.norm_eps);
     __syncthreads();
 
     if (wave < 2) {  // 32 tokens x 4 lanes: waves 0 and 1
@@ -723,14 +735,17 @@ __global__ __launch_bounds__(256) void k_fused_pre_w4(
     const uint16_t* __restrict__ norm_w, Scalars p, uint16_t* __restrict__ layer_input,
     float* __restrict__ pre_out, float* __restrict__ post_out, float* __restrict__ comb_out,
     float* __restrict__ mixes_out, float* __restrict__ rstd_out) {
-    using Shape = FusedW4Shape<S>;
+    using Shape = FusedW4Shape<S, 9>;
     constexpr int hidden = S * kWide * kWaves4;
     __shared__ uint4 li_lds[Shape::kLiLds > 0 ? Shape::kLiLds : 1][kWaves4][2][2][64];
-    __shared__ float red[kWaves4][kTileW4][24];
     __shared__ float sq[kWaves4][4][kTileW4];
     __shared__ float tot[kTileW4][26];
     __shared__ float pre_s[kTileW4][4];
     __shared__ float rli[kTileW4];
+    // Pass 1's per-wave mixes live in the li area: pass 2 writes li only after
+    // they have been summed (barriers in between).
+    static_assert(sizeof(float) * kWaves4 * kTileW4 * 24 <= sizeof(li_lds), "mix partials fit");
+    float (*red)[kTileW4][24] = reinterpret_cast<float (*)[kTileW4][24]>(&li_lds[0][0][0][0][0]);
 
     const int tile = blockIdx.x;
     const int wave = threadIdx.x >> 6;
