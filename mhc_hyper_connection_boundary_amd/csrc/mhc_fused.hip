@@ -17,7 +17,7 @@
 // fragments of step i come from L2 and feed the matrix cores.
 //
 // The BF16 li of the tile must wait for rstd_li, which depends on the whole
-// row: the first 8 steps of every wave park it in LDS, the last few in
+// row: the first 8 or 9 steps of every wave park it in LDS, the last few in
 // registers, the steps between in the layer-input buffer itself, which the
 // epilogue reads back and overwrites with the normalised values.  After the
 // loop the waves' partials are combined in LDS in a fixed order; one quad per
