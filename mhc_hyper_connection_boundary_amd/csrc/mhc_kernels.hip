@@ -56,17 +56,21 @@ __global__ __launch_bounds__(256) void k_prepare_weight(const float* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// Split schedule, kernel 1: partial sums over a run of hidden steps.
+// Split schedule, kernel 1: partial sums over a run of hidden steps.  A wave
+// carries G groups of 16 tokens (tokens n, n + 16, ... of the workgroup's
+// tile in lane n) through every step and feeds all of them from one set of
+// weight fragments.  Each token's sums have the same order for any G.
 // ---------------------------------------------------------------------------
-template <bool SHIFTED>
+template <bool SHIFTED, int G>
 __global__ __launch_bounds__(256) void k_partial(
     int T, int hidden, int steps_per_wave, int slices, const uint16_t* __restrict__ x,
     const uint16_t* __restrict__ X, const float* __restrict__ post_prev,
     const float* __restrict__ comb_prev, const float* __restrict__ pre_lag,
     const uint4* __restrict__ wprep, uint16_t* __restrict__ xn_out,
     uint16_t* __restrict__ li_out, float* __restrict__ part) {
-    __shared__ float red[4][kTile][24];
-    __shared__ float sq[4][4][kTile][2];
+    constexpr int kTok = kTile * G;  // tokens of the workgroup
+    __shared__ float red[4][kTok][24];
+    __shared__ float sq[4][4][kTok][2];
 
     const int tile = blockIdx.x;
     const int slice = blockIdx.y;
@@ -74,12 +78,20 @@ __global__ __launch_bounds__(256) void k_partial(
     const int lane = threadIdx.x & 63;
     const int n = lane & 15;
     const int g = lane >> 4;
-    const int t = tile * kTile + n;
-    const bool valid = t < T;
-    const size_t tc = valid ? (size_t)t : (size_t)(T - 1);
-
-    PrevCoef c;
-    if (SHIFTED) load_prev(c, post_prev, comb_prev, pre_lag, tc);
+    bool valid[G];
+    size_t tc[G];
+    PrevCoef c[G];
+    const uint16_t* Xrow[G];
+    const uint16_t* xrow[G];
+#pragma unroll
+    for (int q = 0; q < G; ++q) {
+        const int t = tile * kTok + 16 * q + n;
+        valid[q] = t < T;
+        tc[q] = valid[q] ? (size_t)t : (size_t)(T - 1);
+        if (SHIFTED) load_prev(c[q], post_prev, comb_prev, pre_lag, tc[q]);
+        Xrow[q] = X + tc[q] * 4 * hidden;
+        xrow[q] = SHIFTED ? x + tc[q] * hidden : nullptr;
+    }
 
     // The slice covers steps [slice*4*spw, (slice+1)*4*spw); its 4 waves take
     // them interleaved (wave w: first + w, first + 4 + w, ...) so the waves read
@@ -88,24 +100,32 @@ __global__ __launch_bounds__(256) void k_partial(
     const int first = slice * 4 * steps_per_wave;
     const int last = min(first + 4 * steps_per_wave, nsteps);
 
-    f32x4_t acc[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    float ssq = 0.0f, ssq_li = 0.0f;
-    const uint16_t* Xrow = X + tc * 4 * hidden;
-    const uint16_t* xrow = SHIFTED ? x + tc * hidden : nullptr;
+    f32x4_t acc[G][3];
+    float ssq[G], ssq_li[G];
+#pragma unroll
+    for (int q = 0; q < G; ++q) {
+#pragma unroll
+        for (int m = 0; m < 3; ++m) acc[q][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        ssq[q] = 0.0f;
+        ssq_li[q] = 0.0f;
+    }
 
     // Step k's weight fragments are requested first, then step k+1's
     // activations (prefetch), so the projection never waits on HBM: loads
     // complete in issue order.
-    auto load_x = [&](uint4 (&Xv)[4], uint4& xv, int step) {
+    auto load_x = [&](uint4 (&Xv)[4], uint4& xv, int q, int step) {
         const int h = step * kStep + g * 8;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            Xv[j] = *reinterpret_cast<const uint4*>(Xrow + (size_t)j * hidden + h);
+            Xv[j] = *reinterpret_cast<const uint4*>(Xrow[q] + (size_t)j * hidden + h);
         xv = make_uint4(0, 0, 0, 0);
-        if (SHIFTED) xv = *reinterpret_cast<const uint4*>(xrow + h);
+        if (SHIFTED) xv = *reinterpret_cast<const uint4*>(xrow[q] + h);
     };
-    uint4 Xv[4], xv;
-    if (first + wave < last) load_x(Xv, xv, first + wave);
+    uint4 Xv[G][4], xv[G];
+    if (first + wave < last) {
+#pragma unroll
+        for (int q = 0; q < G; ++q) load_x(Xv[q], xv[q], q, first + wave);
+    }
     for (int step = first + wave; step < last; step += 4) {
         const int h = step * kStep + g * 8;
         uint4 A[kFragsPerStep];
@@ -113,40 +133,52 @@ __global__ __launch_bounds__(256) void k_partial(
 #pragma unroll
         for (int i = 0; i < kFragsPerStep; ++i) A[i] = wp[i * 64];
         __builtin_amdgcn_sched_barrier(0);
-        uint4 Xnx[4], xnx;
-        if (step + 4 < last) load_x(Xnx, xnx, step + 4);
+        uint4 Xnx[G][4], xnx[G];
+        if (step + 4 < last) {
+#pragma unroll
+            for (int q = 0; q < G; ++q) load_x(Xnx[q], xnx[q], q, step + 4);
+        }
         __builtin_amdgcn_sched_barrier(0);
 
-        uint4 Xn[4];
-        if (SHIFTED) {
-            uint4 li;
-            update_collapse(Xv, xv, c, Xn, li, ssq, ssq_li);
-            if (valid) {
 #pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    *reinterpret_cast<uint4*>(xn_out + (tc * 4 + s) * hidden + h) = Xn[s];
-                *reinterpret_cast<uint4*>(li_out + tc * hidden + h) = li;
+        for (int q = 0; q < G; ++q) {
+            uint4 Xn[4];
+            if (SHIFTED) {
+                uint4 li;
+                update_collapse(Xv[q], xv[q], c[q], Xn, li, ssq[q], ssq_li[q]);
+                if (valid[q]) {
+#pragma unroll
+                    for (int s = 0; s < 4; ++s)
+                        *reinterpret_cast<uint4*>(xn_out + (tc[q] * 4 + s) * hidden + h) = Xn[s];
+                    *reinterpret_cast<uint4*>(li_out + tc[q] * hidden + h) = li;
+                }
+            } else {
+#pragma unroll
+                for (int s = 0; s < 4; ++s) Xn[s] = Xv[q][s];
+                square_sum(Xv[q], ssq[q]);
             }
-        } else {
-#pragma unroll
-            for (int s = 0; s < 4; ++s) Xn[s] = Xv[s];
-            square_sum(Xv, ssq);
+            mfma_step(A, Xn, acc[q]);
         }
-        mfma_step(A, Xn, acc);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) Xv[j] = Xnx[j];
-        xv = xnx;
+        for (int q = 0; q < G; ++q) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) Xv[q][j] = Xnx[q][j];
+            xv[q] = xnx[q];
+        }
     }
 
     // Combine the 4 waves in a fixed order: waves ascending, lane groups ascending.
 #pragma unroll
-    for (int m = 0; m < 3; ++m)
+    for (int q = 0; q < G; ++q) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) red[wave][n][8 * m + 2 * g + j] = mix_of(acc, m, j);
-    sq[wave][g][n][0] = ssq;
-    sq[wave][g][n][1] = ssq_li;
+        for (int m = 0; m < 3; ++m)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) red[wave][16 * q + n][8 * m + 2 * g + j] = mix_of(acc[q], m, j);
+        sq[wave][g][16 * q + n][0] = ssq[q];
+        sq[wave][g][16 * q + n][1] = ssq_li[q];
+    }
     __syncthreads();
-    for (int i = threadIdx.x; i < kTile * 26; i += blockDim.x) {
+    for (int i = threadIdx.x; i < kTok * 26; i += blockDim.x) {
         const int tn = i / 26, v = i % 26;
         float sum;
         if (v < 24) {
@@ -156,7 +188,7 @@ __global__ __launch_bounds__(256) void k_partial(
             for (int w = 0; w < 4; ++w)
                 for (int q = 0; q < 4; ++q) sum += sq[w][q][tn][v - 24];
         }
-        const int tt = tile * kTile + tn;
+        const int tt = tile * kTok + tn;
         if (tt < T) part[((size_t)tt * slices + slice) * kPart + v] = sum;
     }
 }
@@ -584,20 +616,42 @@ hipError_t launch_post(int T, int hidden, const uint16_t* x, const uint16_t* X,
     return hipGetLastError();
 }
 
+// Token groups per wave in k_partial: two groups share each fragment load,
+// which pays once a wave streams several steps; with one or a few steps per
+// wave the single-group kernel's higher occupancy wins (measured at d=7168:
+// boundary T=2048 100 -> 92 us with two groups, T=256 21.6 -> 24.0 us).  The
+// records are the same bits either way.
+constexpr int kTwoGroupStepsShifted = 8;
+constexpr int kTwoGroupStepsPre = 4;
+
+template <int G>
+static void launch_partial_g(bool shifted, const SplitPlan& plan, int T, int hidden,
+                             const uint16_t* x, const uint16_t* X, const float* post_prev,
+                             const float* comb_prev, const float* pre_lag, const uint4* w,
+                             uint16_t* xn_out, uint16_t* li_out, float* part, hipStream_t stream) {
+    const dim3 grid((T + kTile * G - 1) / (kTile * G), plan.slices);
+    if (shifted)
+        hipLaunchKernelGGL((k_partial<true, G>), grid, dim3(256), 0, stream, T, hidden,
+                           plan.steps_per_wave, plan.slices, x, X, post_prev, comb_prev, pre_lag,
+                           w, xn_out, li_out, part);
+    else
+        hipLaunchKernelGGL((k_partial<false, G>), grid, dim3(256), 0, stream, T, hidden,
+                           plan.steps_per_wave, plan.slices, nullptr, X, nullptr, nullptr,
+                           nullptr, w, nullptr, nullptr, part);
+}
+
 hipError_t launch_partial(bool shifted, const SplitPlan& plan, int T, int hidden,
                           const uint16_t* x, const uint16_t* X, const float* post_prev,
                           const float* comb_prev, const float* pre_lag, const void* wprep,
                           uint16_t* xn_out, uint16_t* li_out, float* part, hipStream_t stream) {
-    const dim3 grid((T + kTile - 1) / kTile, plan.slices);
     const uint4* w = reinterpret_cast<const uint4*>(wprep);
-    if (shifted)
-        hipLaunchKernelGGL(k_partial<true>, grid, dim3(256), 0, stream, T, hidden,
-                           plan.steps_per_wave, plan.slices, x, X, post_prev, comb_prev, pre_lag,
-                           w, xn_out, li_out, part);
+    const int two = shifted ? kTwoGroupStepsShifted : kTwoGroupStepsPre;
+    if (plan.steps_per_wave >= two)
+        launch_partial_g<2>(shifted, plan, T, hidden, x, X, post_prev, comb_prev, pre_lag, w,
+                            xn_out, li_out, part, stream);
     else
-        hipLaunchKernelGGL(k_partial<false>, grid, dim3(256), 0, stream, T, hidden,
-                           plan.steps_per_wave, plan.slices, nullptr, X, nullptr, nullptr,
-                           nullptr, w, nullptr, nullptr, part);
+        launch_partial_g<1>(shifted, plan, T, hidden, x, X, post_prev, comb_prev, pre_lag, w,
+                            xn_out, li_out, part, stream);
     return hipGetLastError();
 }
 

@@ -201,6 +201,25 @@ def test_boundary_fused_32_token_tiles(oracle, T, d, full):
         compare(g, oracle.boundary(inp, tokens=tok), tokens=tok, label=f"w4 T={T} d={d}")
 
 
+@pytest.mark.parametrize("kind,T,d", [("boundary", 2048 + 19, 7168), ("pre", 1024 + 21, 4096)])
+def test_split_two_token_groups_ragged(oracle, kind, T, d):
+    """At these sizes the split schedule's first kernel carries two 16-token
+    groups per wave (8+ steps per wave for the boundary, 4+ for the pre); the
+    last workgroup's second group is partly past the last token."""
+    say(f"split two groups {kind} T={T} d={d}")
+    inp = WL.make_inputs(WL.Config("g2", d=d, T=T, seed=T + 3 * d))
+    dv = Dev(inp)
+    tok = np.unique(np.concatenate([sample_tokens(T, n=32, seed=d),
+                                    np.arange(T - 40, T, dtype=np.int32)]))
+    if kind == "boundary":
+        g = dv.boundary(schedule="split")
+        compare(g, oracle.boundary(inp, tokens=tok), tokens=tok, label=f"split2 T={T} d={d}")
+    else:
+        g = dv.pre(norm=True, schedule="split")
+        compare(g, oracle.pre(inp, tokens=tok, use_norm=True), tokens=tok, xn=False,
+                label=f"pre split2 T={T} d={d}", fresh=(inp.X, inp.norm_w))
+
+
 def test_fused_refuses_unsupported_width():
     inp = WL.make_inputs(WL.Config("u", d=256, T=4, seed=1))
     with pytest.raises(api.MhcError) as e:
@@ -312,7 +331,8 @@ def test_pre_schedules(oracle, T, d, schedule):
 
 @pytest.mark.parametrize("name", ["prefill", "stress"])
 def test_pre_large_sampled(oracle, name):
-    """The full-size launch (automatic schedule, fused at these sizes) on sampled tokens."""
+    """The full-size launch (automatic schedule: split, two token groups per wave at
+    these sizes) on sampled tokens."""
     say(f"pre {name} sampled")
     inp = WL.make_inputs(name)
     g = Dev(inp).pre(norm=True)
