@@ -193,6 +193,53 @@ def decode_numbers(steps, schedule):
                 roofline_frac_cold=b / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
 
 
+def percentiles_us(torch, fn, n=30):
+    """Per-call HIP-event times of n back-to-back calls (µs): p10, median, p90."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+    q = lambda p: ts[min(n - 1, int(round(p * (n - 1))))]
+    return dict(p10=q(0.1), p50=q(0.5), p90=q(0.9))
+
+
+def config_numbers():
+    """The two other timed configurations of the workload table: the decode wave
+    limit (d=7168, T=256; graph replays, hot and cold) and the numerical stress
+    batch (d=4096, T=16384, mixed-scale residual; eager calls like the headline)."""
+    import torch
+
+    out = {}
+    w = Workload("decode_wave")
+    T, d = w.inp.T, w.inp.d
+    b = algorithmic_bytes(T, d)
+    hot_ms = graph_time(torch, [w.call] * 20, 10)
+    sets = [({k: v.clone() for k, v in w.t.items()}, w.wp.clone()) for _ in range(_sets_for(b))]
+    cold_ms = graph_time(torch, [lambda t=t, wp=wp: w.call(t, wp) for t, wp in sets] * 2, 4)
+    out["decode wave limit d=7168 T=256"] = dict(
+        timing="HIP graph replay", us_per_call_hot=hot_ms * 1e3, us_per_call_cold=cold_ms * 1e3,
+        tokens_per_s_cold=T / (cold_ms * 1e-3), bytes_per_call=b,
+        gbs_cold=b / (cold_ms * 1e-3) / 1e9, roofline_frac_cold=b / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
+    del w, sets
+    torch.cuda.empty_cache()
+    w = Workload("stress")
+    T, d = w.inp.T, w.inp.d
+    b = algorithmic_bytes(T, d)
+    settle(torch, w.call, 0.1)
+    ms, _ = time_calls(torch, lambda k: w.call(), 30, 5)
+    out["stress d=4096 T=16384"] = dict(
+        timing="HIP events over 30 eager calls", us_per_call=ms * 1e3,
+        us_per_call_percentiles=percentiles_us(torch, w.call), tokens_per_s=T / (ms * 1e-3),
+        bytes_per_call=b, gbs=b / (ms * 1e-3) / 1e9, roofline_frac=b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
+    del w
+    torch.cuda.empty_cache()
+    return out
+
+
 def cold_graph_time(torch, make_call, sets, reps=3, min_calls=24):
     """Per-call device time of make_call(set) rotated over `sets` (distinct
     buffers whose total exceeds the last-level cache), replayed from a HIP graph."""
@@ -384,8 +431,8 @@ def write_traffic_profile(prof_dir):
         f"algorithmic_bytes_per_call: {algorithmic_bytes(T, d)}",
         f"traffic_over_algorithmic: {traffic / algorithmic_bytes(T, d):.3f}",
         "commands (from the repository root, TMPDIR=/tmp):",
-        "  rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/fetch_boundary -o run -- python bench.py --steps 5 --warmup 2 --no-decode --no-cpu-baseline --no-entry-points",
-        "  rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/write_boundary -o run -- python bench.py --steps 5 --warmup 2 --no-decode --no-cpu-baseline --no-entry-points",
+        "  rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/fetch_boundary -o run -- python bench.py --steps 5 --warmup 2 --no-decode --no-cpu-baseline --no-entry-points --no-configs",
+        "  rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/write_boundary -o run -- python bench.py --steps 5 --warmup 2 --no-decode --no-cpu-baseline --no-entry-points --no-configs",
         "  rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/fetch_copy -o run -- python bench.py --copy-calibration",
         "  rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/write_copy -o run -- python bench.py --copy-calibration",
         "  python bench.py --write-traffic-profile <dir>",
@@ -406,6 +453,8 @@ def main():
     ap.add_argument("--schedule", default="auto", choices=["auto", "split", "fused"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the decode wave limit (T=256) and stress (d=4096, T=16384) lines")
     ap.add_argument("--no-entry-points", action="store_true",
                     help="skip the mhc_pre / mhc_pre_mixes / mhc_post / invariant legs")
     ap.add_argument("--leg", metavar="NAME",
@@ -438,6 +487,7 @@ def main():
           file=sys.stderr, flush=True)
     settle(torch, w.call, a.settle)
     ms, wall = time_calls(torch, lambda k: w.call(), a.steps, a.warmup)
+    pct = percentiles_us(torch, w.call)
     b = algorithmic_bytes(T, d)
     gbs = b / (ms * 1e-3) / 1e9
     fused = a.schedule == "fused" or (a.schedule == "auto" and T >= 3072)
@@ -456,10 +506,14 @@ def main():
         roofline=dict(bound="hbm", achieved=gbs, peak=HBM_PEAK_GBS, unit="GB/s",
                       frac=gbs / HBM_PEAK_GBS, traffic=traffic, bytes_per_call=b,
                       kernel=kernel),
+        us_per_call_percentiles=pct,
     )
     if not a.no_decode:
         print("[bench] decode T=32", file=sys.stderr, flush=True)
         line["decode_t32"] = decode_numbers(200, a.schedule)
+    if not a.no_configs:
+        print("[bench] decode wave limit T=256, stress d=4096 T=16384", file=sys.stderr, flush=True)
+        line["configs"] = config_numbers()
     if not a.no_entry_points:
         del w
         torch.cuda.empty_cache()
