@@ -1,8 +1,10 @@
 // gfx950 kernels of the mHC boundary and their host-side launchers.
 //
 // Split schedule (any token count):
-//   k_partial   one workgroup = 4 waves on one 16-token tile and a contiguous
-//               run of hidden steps.  Each wave streams its steps: 16-byte
+//   k_partial   one workgroup = 4 waves on a tile of one or two 16-token
+//               groups and a contiguous run of hidden steps (two groups share
+//               each weight-fragment load once a wave streams 8 or more steps,
+//               4 for the pre).  Each wave streams its steps: 16-byte
 //               loads of X and x, residual update, lagged collapse, stores of
 //               X' and li, sums of squares, and the projection on the matrix
 //               cores.  The 4 waves' partials are combined in LDS in a fixed
