@@ -17,6 +17,9 @@ namespace {
 constexpr long kTargetWaves = 2048;  // waves of k_partial work to aim for
 constexpr int kFinishTarget = 2048;  // k_finish workgroups to aim for
 constexpr int kFusedMinTokens = 3072; // automatic schedule: fused from this many tokens
+constexpr int kTwoGroupStepsShifted = 8;  // split boundary: two token groups per wave from here
+constexpr int kTwoGroupStepsPre = 4;      // split pre: two groups from here (fewer registers)
+constexpr int kRoundCost = 4;             // split grid: fixed cost of a round of workgroups, in steps
 constexpr int kW4MinTokens = 8192;    // fused schedule: 32-token tiles on 4 waves from here
 
 int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
@@ -83,15 +86,41 @@ Scalars scalars(const mhc_params* p) {
 
 }  // namespace
 
-SplitPlan split_plan(int T, int hidden, bool invariant) {
+SplitPlan split_plan(int T, int hidden, bool invariant, bool shifted) {
     SplitPlan plan;
     const int nsteps = hidden / kStep;
     const int tiles = ceil_div(T, kTile);
-    const long wave_steps = (long)tiles * nsteps;
+    const int max_spw = ceil_div(nsteps, 4);
     // Batch-invariant: one step per wave whatever T is, so every sum of a token
-    // has the same order for every batch.
-    int spw = invariant ? 1 : (int)std::max<long>(1, wave_steps / kTargetWaves);
-    spw = std::min(spw, ceil_div(nsteps, 4));
+    // has the same order for every batch.  Otherwise about kTargetWaves waves.
+    int spw = invariant ? 1 : (int)std::max<long>(1, (long)tiles * nsteps / kTargetWaves);
+    spw = std::min(spw, max_spw);
+    plan.groups = 1;
+    if (spw > 1) {
+        // Several steps per wave: two token groups share each fragment load
+        // once there are enough steps.  For the boundary the steps per wave
+        // (at least 2) are then chosen so the grid fills whole rounds of the
+        // workgroups the device holds at once: the least rounds x (steps per
+        // wave + a fixed cost of kRoundCost steps per round).  (The pre keeps
+        // the plain rule: measured, the same choice gains at some sizes and
+        // loses at others there.)
+        plan.groups = spw >= (shifted ? kTwoGroupStepsShifted : kTwoGroupStepsPre) ? 2 : 1;
+        const long resident = shifted ? partial_resident_workgroups(shifted, plan.groups) : 0;
+        if (resident > 0) {
+            const long group_tiles = ceil_div(T, kTile * plan.groups);
+            long best = -1;
+            for (int s = 1; s <= max_spw; ++s) {
+                const int w = ceil_div(nsteps, 4 * s);
+                if (w < 2) break;
+                const long rounds = (group_tiles * ceil_div(nsteps, 4 * w) + resident - 1) / resident;
+                const long cost = rounds * (w + kRoundCost);
+                if (best < 0 || cost < best) {
+                    best = cost;
+                    spw = w;
+                }
+            }
+        }
+    }
     plan.steps_per_wave = spw;
     plan.slices = ceil_div(nsteps, 4L * spw);
     int fs = std::max(1, std::min(ceil_div(kFinishTarget, tiles), hidden / 256));
@@ -102,7 +131,7 @@ SplitPlan split_plan(int T, int hidden, bool invariant) {
 
 // The finest split (one step per wave) has the most slices: enough for every plan.
 size_t split_workspace_bytes(int T, int hidden) {
-    return (size_t)T * split_plan(T, hidden, true).slices * kPart * sizeof(float);
+    return (size_t)T * split_plan(T, hidden, true, true).slices * kPart * sizeof(float);
 }
 
 }  // namespace mhc
@@ -240,7 +269,7 @@ mhc_status mhc_pre(int tokens, int hidden, const uint16_t* residual, const void*
         return MHC_OK;
     }
     const SplitPlan plan =
-        split_plan(tokens, hidden, params->schedule == MHC_SCHEDULE_INVARIANT);
+        split_plan(tokens, hidden, params->schedule == MHC_SCHEDULE_INVARIANT, false);
     float* part = static_cast<float*>(workspace);
     if (launch_partial(false, plan, tokens, hidden, nullptr, residual, nullptr, nullptr, nullptr,
                        w_prepared, nullptr, nullptr, part, hs) != hipSuccess)
@@ -296,7 +325,7 @@ mhc_status mhc_boundary(int tokens, int hidden, const uint16_t* x, const uint16_
         return MHC_OK;
     }
     const SplitPlan plan =
-        split_plan(tokens, hidden, params->schedule == MHC_SCHEDULE_INVARIANT);
+        split_plan(tokens, hidden, params->schedule == MHC_SCHEDULE_INVARIANT, true);
     float* part = static_cast<float*>(workspace);
     // layer_input first receives li; the finishing kernel rescales it in place.
     if (launch_partial(true, plan, tokens, hidden, x, residual, post_prev, comb_prev, pre_lag,

@@ -16,6 +16,8 @@
 //   k_pre_finish (non-shifted pre) one workgroup per token: coefficients
 //               first, then the collapse with the fresh pre and the RMSNorm.
 // Weight preparation: k_prepare_weight.
+#include <atomic>
+
 #include "mhc_device.h"
 #include "mhc_launch.h"
 
@@ -618,14 +620,6 @@ hipError_t launch_post(int T, int hidden, const uint16_t* x, const uint16_t* X,
     return hipGetLastError();
 }
 
-// Token groups per wave in k_partial: two groups share each fragment load,
-// which pays once a wave streams several steps; with one or a few steps per
-// wave the single-group kernel's higher occupancy wins (measured at d=7168:
-// boundary T=2048 100 -> 92 us with two groups, T=256 21.6 -> 24.0 us).  The
-// records are the same bits either way.
-constexpr int kTwoGroupStepsShifted = 8;
-constexpr int kTwoGroupStepsPre = 4;
-
 template <int G>
 static void launch_partial_g(bool shifted, const SplitPlan& plan, int T, int hidden,
                              const uint16_t* x, const uint16_t* X, const float* post_prev,
@@ -647,14 +641,37 @@ hipError_t launch_partial(bool shifted, const SplitPlan& plan, int T, int hidden
                           const float* comb_prev, const float* pre_lag, const void* wprep,
                           uint16_t* xn_out, uint16_t* li_out, float* part, hipStream_t stream) {
     const uint4* w = reinterpret_cast<const uint4*>(wprep);
-    const int two = shifted ? kTwoGroupStepsShifted : kTwoGroupStepsPre;
-    if (plan.steps_per_wave >= two)
+    if (plan.groups == 2)
         launch_partial_g<2>(shifted, plan, T, hidden, x, X, post_prev, comb_prev, pre_lag, w,
                             xn_out, li_out, part, stream);
     else
         launch_partial_g<1>(shifted, plan, T, hidden, x, X, post_prev, comb_prev, pre_lag, w,
                             xn_out, li_out, part, stream);
     return hipGetLastError();
+}
+
+int partial_resident_workgroups(bool shifted, int groups) {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cache[kMaxDevices][2][2];  // 0: not asked yet; -1: unknown
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    std::atomic<int>& slot = cache[dev][shifted ? 1 : 0][groups == 2 ? 1 : 0];
+    int v = slot.load(std::memory_order_relaxed);
+    if (v == 0) {
+        int units = 0, per_unit = 0;
+        hipError_t e = hipDeviceGetAttribute(&units, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e == hipSuccess) {
+            if (shifted)
+                e = groups == 2 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_unit, k_partial<true, 2>, 256, 0)
+                                : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_unit, k_partial<true, 1>, 256, 0);
+            else
+                e = groups == 2 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_unit, k_partial<false, 2>, 256, 0)
+                                : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_unit, k_partial<false, 1>, 256, 0);
+        }
+        v = (e == hipSuccess && units > 0 && per_unit > 0) ? units * per_unit : -1;
+        slot.store(v, std::memory_order_relaxed);
+    }
+    return v > 0 ? v : 0;
 }
 
 hipError_t launch_finish(const SplitPlan& plan, int T, int hidden, const float* part,

@@ -16,13 +16,19 @@ struct Scalars;
 //   k_finish:  grid (tiles, finish_slices); workgroup q rescales hidden
 //              [q * finish_width, (q + 1) * finish_width).
 struct SplitPlan {
+    int groups;          // 16-token groups per wave in the partial kernel (1 or 2)
     int steps_per_wave;
     int slices;
     int finish_slices;
     int finish_width;
 };
 
-SplitPlan split_plan(int T, int hidden, bool invariant);
+SplitPlan split_plan(int T, int hidden, bool invariant, bool shifted);
+
+// Workgroups of the partial kernel (shifted or not, 1 or 2 token groups) the
+// current device holds at once: compute units times resident workgroups per
+// unit.  0 if the runtime cannot say.
+int partial_resident_workgroups(bool shifted, int groups);
 size_t split_workspace_bytes(int T, int hidden);
 
 hipError_t launch_prepare_weight(const float* w, int hidden, void* out, hipStream_t stream);

@@ -201,7 +201,8 @@ def test_boundary_fused_32_token_tiles(oracle, T, d, full):
         compare(g, oracle.boundary(inp, tokens=tok), tokens=tok, label=f"w4 T={T} d={d}")
 
 
-@pytest.mark.parametrize("kind,T,d", [("boundary", 2048 + 19, 7168), ("pre", 1024 + 21, 4096)])
+@pytest.mark.parametrize("kind,T,d", [("boundary", 2048 + 19, 7168), ("boundary", 1536 + 5, 7168),
+                                        ("pre", 1024 + 21, 4096)])
 def test_split_two_token_groups_ragged(oracle, kind, T, d):
     """At these sizes the split schedule's first kernel carries two 16-token
     groups per wave (8+ steps per wave for the boundary, 4+ for the pre); the
