@@ -98,14 +98,15 @@ SplitPlan split_plan(int T, int hidden, bool invariant, bool shifted) {
     plan.groups = 1;
     if (spw > 1) {
         // Several steps per wave: two token groups share each fragment load
-        // once there are enough steps.  For the boundary the steps per wave
-        // (at least 2) are then chosen so the grid fills whole rounds of the
-        // workgroups the device holds at once: the least rounds x (steps per
-        // wave + a fixed cost of kRoundCost steps per round).  (The pre keeps
-        // the plain rule: measured, the same choice gains at some sizes and
-        // loses at others there.)
+        // once there are enough steps.  The steps per wave (at least 2) are
+        // then chosen so the grid fills whole rounds of slots: the least
+        // rounds x (steps per wave + a fixed cost of kRoundCost steps per
+        // round).  The boundary's slots are the workgroups the device holds
+        // at once; the pre's are the compute units (one workgroup each), which
+        // measured faster there than filling every resident slot.
         plan.groups = spw >= (shifted ? kTwoGroupStepsShifted : kTwoGroupStepsPre) ? 2 : 1;
-        const long resident = shifted ? partial_resident_workgroups(shifted, plan.groups) : 0;
+        const long resident = shifted ? partial_resident_workgroups(shifted, plan.groups)
+                                      : device_compute_units();
         if (resident > 0) {
             const long group_tiles = ceil_div(T, kTile * plan.groups);
             long best = -1;

@@ -650,24 +650,51 @@ hipError_t launch_partial(bool shifted, const SplitPlan& plan, int T, int hidden
     return hipGetLastError();
 }
 
-int partial_resident_workgroups(bool shifted, int groups) {
-    constexpr int kMaxDevices = 64;
-    static std::atomic<int> cache[kMaxDevices][2][2];  // 0: not asked yet; -1: unknown
+namespace {
+constexpr int kMaxDevices = 64;
+
+int current_device() {
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    return hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices ? dev : -1;
+}
+
+int query_compute_units(int dev) {
+    int units = 0;
+    return hipDeviceGetAttribute(&units, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess
+               ? units
+               : 0;
+}
+}  // namespace
+
+int device_compute_units() {
+    static std::atomic<int> cache[kMaxDevices];  // 0: not asked yet; -1: unknown
+    const int dev = current_device();
+    if (dev < 0) return 0;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        const int units = query_compute_units(dev);
+        v = units > 0 ? units : -1;
+        cache[dev].store(v, std::memory_order_relaxed);
+    }
+    return v > 0 ? v : 0;
+}
+
+int partial_resident_workgroups(bool shifted, int groups) {
+    static std::atomic<int> cache[kMaxDevices][2][2];  // 0: not asked yet; -1: unknown
+    const int dev = current_device();
+    if (dev < 0) return 0;
     std::atomic<int>& slot = cache[dev][shifted ? 1 : 0][groups == 2 ? 1 : 0];
     int v = slot.load(std::memory_order_relaxed);
     if (v == 0) {
-        int units = 0, per_unit = 0;
-        hipError_t e = hipDeviceGetAttribute(&units, hipDeviceAttributeMultiprocessorCount, dev);
-        if (e == hipSuccess) {
-            if (shifted)
-                e = groups == 2 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_unit, k_partial<true, 2>, 256, 0)
-                                : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_unit, k_partial<true, 1>, 256, 0);
-            else
-                e = groups == 2 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_unit, k_partial<false, 2>, 256, 0)
-                                : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_unit, k_partial<false, 1>, 256, 0);
-        }
+        const int units = query_compute_units(dev);
+        int per_unit = 0;
+        hipError_t e;
+        if (shifted)
+            e = groups == 2 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_unit, k_partial<true, 2>, 256, 0)
+                            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_unit, k_partial<true, 1>, 256, 0);
+        else
+            e = groups == 2 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_unit, k_partial<false, 2>, 256, 0)
+                            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_unit, k_partial<false, 1>, 256, 0);
         v = (e == hipSuccess && units > 0 && per_unit > 0) ? units * per_unit : -1;
         slot.store(v, std::memory_order_relaxed);
     }

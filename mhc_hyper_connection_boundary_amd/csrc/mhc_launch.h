@@ -29,6 +29,9 @@ SplitPlan split_plan(int T, int hidden, bool invariant, bool shifted);
 // current device holds at once: compute units times resident workgroups per
 // unit.  0 if the runtime cannot say.
 int partial_resident_workgroups(bool shifted, int groups);
+
+// Compute units of the current device; 0 if the runtime cannot say.
+int device_compute_units();
 size_t split_workspace_bytes(int T, int hidden);
 
 hipError_t launch_prepare_weight(const float* w, int hidden, void* out, hipStream_t stream);
