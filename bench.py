@@ -490,6 +490,7 @@ def main():
     pct = percentiles_us(torch, w.call)
     b = algorithmic_bytes(T, d)
     gbs = b / (ms * 1e-3) / 1e9
+    # (on 256 compute units AUTO runs the 32-token fused kernel at this size)
     fused = a.schedule == "fused" or (a.schedule == "auto" and T >= 3072)
     if fused:
         kernel = (f"k_fused_w4<{d // 256}>" if T >= 8192 else f"k_fused<{d // 512}>") + \

@@ -63,15 +63,39 @@ mhc_status check_params(const mhc_params* p) {
     return MHC_OK;
 }
 
-// FUSED is honoured (the caller gets UNSUPPORTED_SHAPE where the width has no
-// fused kernel); AUTO takes the boundary's fused kernel from kFusedMinTokens.
+// Which kernels run mhc_boundary.  FUSED is honoured (the caller gets
+// UNSUPPORTED_SHAPE where the width has no fused kernel): 16-token tiles below
+// kW4MinTokens, 32-token tiles from there.  AUTO takes a fused kernel only
+// where its tiles fill the device's rounds of compute units (one workgroup
+// each), since a partly filled last round costs a whole round:
+//   16-token tiles from kFusedMinTokens while one round holds them all;
+//   32-token tiles where they fill at least 7/8 of whole rounds;
+//   the split schedule otherwise.
+// Measured at d=7168 (split / 16-token / 32-token, us): T=4096 181 / 177 / 251,
+// T=5120 232 / 285 / 272, T=6144 274 / 308 / 285, T=7168 330 / 326 / 297,
+// T=8192 343 / - / 313, T=12288 537 / - / 559, T=14336 656 / - / 585.  Where the
+// compute-unit count is unknown, AUTO falls back to 16-token tiles from
+// kFusedMinTokens and 32-token tiles from kW4MinTokens.
+enum class BoundaryPath { Split, Fused16, Fused32 };
+
+BoundaryPath boundary_path(int schedule, int tokens, int hidden) {
+    if (schedule == MHC_SCHEDULE_FUSED)
+        return tokens >= kW4MinTokens ? BoundaryPath::Fused32 : BoundaryPath::Fused16;
+    if (schedule != MHC_SCHEDULE_AUTO || !fused_supported(hidden) || tokens < kFusedMinTokens)
+        return BoundaryPath::Split;
+    const long units = device_compute_units();
+    if (units <= 0)
+        return tokens >= kW4MinTokens ? BoundaryPath::Fused32 : BoundaryPath::Fused16;
+    if (ceil_div(tokens, 16) <= units) return BoundaryPath::Fused16;
+    const long tiles32 = ceil_div(tokens, 32);
+    const long rounds = (tiles32 + units - 1) / units;
+    if (8 * tiles32 >= 7 * rounds * units) return BoundaryPath::Fused32;
+    return BoundaryPath::Split;
+}
+
 // The non-shifted pre reads X twice on either schedule, and its split runs
 // faster at every size measured (d=7168, T=8192: 227 against 259 us with
 // RMSNorm), so AUTO keeps it split.
-bool use_fused(int schedule, int tokens, int hidden, int min_tokens) {
-    if (schedule == MHC_SCHEDULE_FUSED) return true;
-    return schedule == MHC_SCHEDULE_AUTO && fused_supported(hidden) && tokens >= min_tokens;
-}
 
 Scalars scalars(const mhc_params* p) {
     Scalars s;
@@ -314,11 +338,12 @@ mhc_status mhc_boundary(int tokens, int hidden, const uint16_t* x, const uint16_
 
     const Scalars s = scalars(params);
     hipStream_t hs = (hipStream_t)stream;
-    if (use_fused(params->schedule, tokens, hidden, kFusedMinTokens)) {
+    const BoundaryPath path = boundary_path(params->schedule, tokens, hidden);
+    if (path != BoundaryPath::Split) {
         if (!fused_supported(hidden)) return MHC_ERR_UNSUPPORTED_SHAPE;
         // 32-token tiles halve the weight-fragment loads per token but need at
         // least one tile per CU; below that the 16-token kernel fills the chip.
-        const auto launch = tokens >= kW4MinTokens ? launch_fused_w4 : launch_fused;
+        const auto launch = path == BoundaryPath::Fused32 ? launch_fused_w4 : launch_fused;
         if (launch(tokens, hidden, x, residual, post_prev, comb_prev, pre_lag, w_prepared, scale,
                    base, norm_w, s, residual_out, layer_input, pre_out, post_out, comb_out, mixes,
                    rstd, hs) != hipSuccess)

@@ -221,6 +221,19 @@ def test_split_two_token_groups_ragged(oracle, kind, T, d):
                 label=f"pre split2 T={T} d={d}", fresh=(inp.X, inp.norm_w))
 
 
+@pytest.mark.parametrize("T", [7168 + 7, 5120 + 3])
+def test_auto_between_tile_rounds(oracle, T):
+    """AUTO takes the 32-token fused kernel where its tiles fill at least 7/8 of
+    whole rounds of compute units (7175 tokens on 256 units) and the split
+    schedule where a round would be left partly idle (5123 tokens); ragged."""
+    say(f"auto T={T} d=7168")
+    inp = WL.make_inputs(WL.Config("at", d=7168, T=T, seed=T))
+    g = Dev(inp).boundary(schedule="auto")
+    tok = np.unique(np.concatenate([sample_tokens(T, n=32, seed=T),
+                                    np.arange(T - 40, T, dtype=np.int32)]))
+    compare(g, oracle.boundary(inp, tokens=tok), tokens=tok, label=f"auto T={T}")
+
+
 def test_fused_refuses_unsupported_width():
     inp = WL.make_inputs(WL.Config("u", d=256, T=4, seed=1))
     with pytest.raises(api.MhcError) as e:
