@@ -80,8 +80,10 @@ typedef enum {
  * an order fixed by hidden alone, so a token's outputs are bit-identical for
  * any token count T and any position in the batch.  It runs the split kernels
  * with one 32-element step per wave (the finest split).  AUTO and SPLIT pick
- * that same split while ceil(T / 16) * hidden < 131072 (T <= 288 at hidden
- * 7168), so small decode batches give the same bits under all three. */
+ * that same split while its workgroups, ceil(T / 16) * hidden / 128, fit in
+ * one round (mhc_boundary: the device's resident workgroups, T <= 144 at
+ * hidden 7168 on 256 compute units; mhc_pre: one workgroup per compute unit,
+ * T <= 64), so small decode batches give the same bits under all three. */
 typedef enum {
     MHC_SCHEDULE_AUTO = 0,        /* mhc_boundary: FUSED where it exists and its token tiles
                                      fill the device's compute units: 16-token tiles from 3072

@@ -120,12 +120,12 @@ SplitPlan split_plan(int T, int hidden, bool invariant, bool shifted) {
     int spw = invariant ? 1 : (int)std::max<long>(1, (long)tiles * nsteps / kTargetWaves);
     spw = std::min(spw, max_spw);
     plan.groups = 1;
-    if (spw > 1) {
-        // Several steps per wave: two token groups share each fragment load
-        // once there are enough steps.  The steps per wave (at least 2) are
-        // then chosen so the grid fills whole rounds of slots: the least
-        // rounds x (steps per wave + a fixed cost of kRoundCost steps per
-        // round).  The boundary's slots are the workgroups the device holds
+    if (!invariant) {
+        // Two token groups share each fragment load once there are enough
+        // steps per wave.  The steps per wave are then chosen so the grid
+        // fills whole rounds of slots: the least rounds x (steps per wave + a
+        // fixed cost of kRoundCost steps per round).  While the finest split
+        // fits one round this keeps one step per wave, as INVARIANT does.  The boundary's slots are the workgroups the device holds
         // at once; the pre's are the compute units (one workgroup each), which
         // measured faster there than filling every resident slot.
         plan.groups = spw >= (shifted ? kTwoGroupStepsShifted : kTwoGroupStepsPre) ? 2 : 1;
@@ -136,7 +136,6 @@ SplitPlan split_plan(int T, int hidden, bool invariant, bool shifted) {
             long best = -1;
             for (int s = 1; s <= max_spw; ++s) {
                 const int w = ceil_div(nsteps, 4 * s);
-                if (w < 2) break;
                 const long rounds = (group_tiles * ceil_div(nsteps, 4 * w) + resident - 1) / resident;
                 const long cost = rounds * (w + kRoundCost);
                 if (best < 0 || cost < best) {

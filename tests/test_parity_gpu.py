@@ -461,13 +461,18 @@ def test_invariant_bits_do_not_depend_on_batch(oracle, d, Ts):
             assert np.array_equal(p[k], ref_p[k][:T]), f"pre {k} differs at T={T}"
 
 
-def test_invariant_equals_auto_for_small_batches():
-    """At hidden 7168 the automatic split for T <= 288 is the invariant one."""
-    say("invariant vs auto")
-    dv = Dev(WL.make_inputs("decode"))
+@pytest.mark.parametrize("T", [32, 64])
+def test_invariant_equals_auto_for_small_batches(T):
+    """At hidden 7168 the automatic split for small batches (the finest split
+    fits one round of resident workgroups) is the invariant one."""
+    say(f"invariant vs auto T={T}")
+    dv = Dev(WL.make_inputs("decode", T=T))
     a, b = dv.boundary(schedule="auto"), dv.boundary(schedule="invariant")
     for k in a:
         assert np.array_equal(a[k], b[k]), k
+    pa, pb = dv.pre(norm=True, schedule="auto"), dv.pre(norm=True, schedule="invariant")
+    for k in pa:
+        assert np.array_equal(pa[k], pb[k]), k
 
 
 def test_prefetch_weight_changes_nothing():
