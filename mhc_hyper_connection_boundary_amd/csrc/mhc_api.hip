@@ -19,7 +19,7 @@ constexpr int kFinishTarget = 2048;  // k_finish workgroups to aim for
 constexpr int kFusedMinTokens = 3072; // automatic schedule: fused from this many tokens
 constexpr int kTwoGroupStepsShifted = 8;  // split boundary: two token groups per wave from here
 constexpr int kTwoGroupStepsPre = 4;      // split pre: two groups from here (fewer registers)
-constexpr int kRoundCost = 4;             // split grid: fixed cost of a round of workgroups, in steps
+constexpr int kRoundCost = 2;             // split grid: fixed cost of a round of workgroups, in steps
 constexpr int kW4MinTokens = 8192;    // fused schedule: 32-token tiles on 4 waves from here
 
 int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
@@ -68,12 +68,14 @@ mhc_status check_params(const mhc_params* p) {
 // kW4MinTokens, 32-token tiles from there.  AUTO takes a fused kernel only
 // where its tiles fill the device's rounds of compute units (one workgroup
 // each), since a partly filled last round costs a whole round:
-//   16-token tiles from kFusedMinTokens while one round holds them all;
 //   32-token tiles where they fill at least 7/8 of whole rounds;
+//   else 16-token tiles from kFusedMinTokens where they fill at least 7/8 of
+//   one round;
 //   the split schedule otherwise.
-// Measured at d=7168 (split / 16-token / 32-token, us): T=4096 181 / 177 / 251,
-// T=5120 232 / 285 / 272, T=6144 274 / 308 / 285, T=7168 330 / 326 / 297,
-// T=8192 343 / - / 313, T=12288 537 / - / 559, T=14336 656 / - / 585.  Where the
+// Measured at d=7168 (split / 16-token / 32-token, us): T=3072 141 / 157 / 233,
+// T=4096 181 / 177 / 251, T=5120 232 / 285 / 272, T=6144 274 / 308 / 285,
+// T=7168 330 / 326 / 297, T=8192 343 / - / 313, T=12288 537 / - / 559,
+// T=14336 656 / - / 585.  Where the
 // compute-unit count is unknown, AUTO falls back to 16-token tiles from
 // kFusedMinTokens and 32-token tiles from kW4MinTokens.
 enum class BoundaryPath { Split, Fused16, Fused32 };
@@ -86,10 +88,10 @@ BoundaryPath boundary_path(int schedule, int tokens, int hidden) {
     const long units = device_compute_units();
     if (units <= 0)
         return tokens >= kW4MinTokens ? BoundaryPath::Fused32 : BoundaryPath::Fused16;
-    if (ceil_div(tokens, 16) <= units) return BoundaryPath::Fused16;
     const long tiles32 = ceil_div(tokens, 32);
-    const long rounds = (tiles32 + units - 1) / units;
-    if (8 * tiles32 >= 7 * rounds * units) return BoundaryPath::Fused32;
+    if (8 * tiles32 >= 7 * ((tiles32 + units - 1) / units) * units) return BoundaryPath::Fused32;
+    const long tiles16 = ceil_div(tokens, 16);
+    if (tiles16 <= units && 8 * tiles16 >= 7 * units) return BoundaryPath::Fused16;
     return BoundaryPath::Split;
 }
 
