@@ -19,6 +19,7 @@ constexpr int kFinishTarget = 2048;  // k_finish workgroups to aim for
 constexpr int kFusedMinTokens = 3072; // automatic schedule: fused from this many tokens
 constexpr int kTwoGroupStepsShifted = 8;  // split boundary: two token groups per wave from here
 constexpr int kTwoGroupStepsPre = 4;      // split pre: two groups from here (fewer registers)
+constexpr int kFourGroupStepsPre = 16;    // split pre: four groups from here
 constexpr int kRoundCost = 2;             // split grid: fixed cost of a round of workgroups, in steps
 constexpr int kW4MinTokens = 8192;    // fused schedule: 32-token tiles on 4 waves from here
 
@@ -123,14 +124,15 @@ SplitPlan split_plan(int T, int hidden, bool invariant, bool shifted) {
     spw = std::min(spw, max_spw);
     plan.groups = 1;
     if (!invariant) {
-        // Two token groups share each fragment load once there are enough
-        // steps per wave.  The steps per wave are then chosen so the grid
+        // Two token groups (four for the pre, whose kernel has the registers)
+        // share each fragment load once there are enough steps per wave.  The steps per wave are then chosen so the grid
         // fills whole rounds of slots: the least rounds x (steps per wave + a
         // fixed cost of kRoundCost steps per round).  While the finest split
         // fits one round this keeps one step per wave, as INVARIANT does.  The boundary's slots are the workgroups the device holds
         // at once; the pre's are the compute units (one workgroup each), which
         // measured faster there than filling every resident slot.
         plan.groups = spw >= (shifted ? kTwoGroupStepsShifted : kTwoGroupStepsPre) ? 2 : 1;
+        if (!shifted && spw >= kFourGroupStepsPre) plan.groups = 4;
         const long resident = shifted ? partial_resident_workgroups(shifted, plan.groups)
                                       : device_compute_units();
         if (resident > 0) {

@@ -1,10 +1,10 @@
 // gfx950 kernels of the mHC boundary and their host-side launchers.
 //
 // Split schedule (any token count):
-//   k_partial   one workgroup = 4 waves on a tile of one or two 16-token
-//               groups and a contiguous run of hidden steps (two groups share
-//               each weight-fragment load once a wave streams 8 or more steps,
-//               4 for the pre).  Each wave streams its steps: 16-byte
+//   k_partial   one workgroup = 4 waves on a tile of one, two or four 16-token
+//               groups and a contiguous run of hidden steps (the groups share
+//               each weight-fragment load; how many is the split plan's
+//               choice).  Each wave streams its steps: 16-byte
 //               loads of X and x, residual update, lagged collapse, stores of
 //               X' and li, sums of squares, and the projection on the matrix
 //               cores.  The 4 waves' partials are combined in LDS in a fixed
@@ -626,11 +626,12 @@ static void launch_partial_g(bool shifted, const SplitPlan& plan, int T, int hid
                              const float* comb_prev, const float* pre_lag, const uint4* w,
                              uint16_t* xn_out, uint16_t* li_out, float* part, hipStream_t stream) {
     const dim3 grid((T + kTile * G - 1) / (kTile * G), plan.slices);
-    if (shifted)
-        hipLaunchKernelGGL((k_partial<true, G>), grid, dim3(256), 0, stream, T, hidden,
-                           plan.steps_per_wave, plan.slices, x, X, post_prev, comb_prev, pre_lag,
-                           w, xn_out, li_out, part);
-    else
+    if (shifted) {
+        if constexpr (G <= 2)  // (four groups would spill in the shifted kernel)
+            hipLaunchKernelGGL((k_partial<true, G>), grid, dim3(256), 0, stream, T, hidden,
+                               plan.steps_per_wave, plan.slices, x, X, post_prev, comb_prev,
+                               pre_lag, w, xn_out, li_out, part);
+    } else
         hipLaunchKernelGGL((k_partial<false, G>), grid, dim3(256), 0, stream, T, hidden,
                            plan.steps_per_wave, plan.slices, nullptr, X, nullptr, nullptr,
                            nullptr, w, nullptr, nullptr, part);
@@ -641,7 +642,10 @@ hipError_t launch_partial(bool shifted, const SplitPlan& plan, int T, int hidden
                           const float* comb_prev, const float* pre_lag, const void* wprep,
                           uint16_t* xn_out, uint16_t* li_out, float* part, hipStream_t stream) {
     const uint4* w = reinterpret_cast<const uint4*>(wprep);
-    if (plan.groups == 2)
+    if (plan.groups == 4 && !shifted)
+        launch_partial_g<4>(shifted, plan, T, hidden, x, X, post_prev, comb_prev, pre_lag, w,
+                            xn_out, li_out, part, stream);
+    else if (plan.groups == 2)
         launch_partial_g<2>(shifted, plan, T, hidden, x, X, post_prev, comb_prev, pre_lag, w,
                             xn_out, li_out, part, stream);
     else

@@ -16,7 +16,7 @@ struct Scalars;
 //   k_finish:  grid (tiles, finish_slices); workgroup q rescales hidden
 //              [q * finish_width, (q + 1) * finish_width).
 struct SplitPlan {
-    int groups;          // 16-token groups per wave in the partial kernel (1 or 2)
+    int groups;          // 16-token groups per wave in the partial kernel (1, 2 or 4)
     int steps_per_wave;
     int slices;
     int finish_slices;

@@ -202,11 +202,11 @@ def test_boundary_fused_32_token_tiles(oracle, T, d, full):
 
 
 @pytest.mark.parametrize("kind,T,d", [("boundary", 2048 + 19, 7168), ("boundary", 1536 + 5, 7168),
-                                        ("pre", 1024 + 21, 4096)])
-def test_split_two_token_groups_ragged(oracle, kind, T, d):
+                                        ("pre", 1024 + 21, 4096), ("pre", 4096 + 11, 7168)])
+def test_split_token_groups_ragged(oracle, kind, T, d):
     """At these sizes the split schedule's first kernel carries two 16-token
-    groups per wave (8+ steps per wave for the boundary, 4+ for the pre); the
-    last workgroup's second group is partly past the last token."""
+    groups per wave (four for the pre at 4107 tokens); the last workgroup's
+    later groups are partly or wholly past the last token."""
     say(f"split two groups {kind} T={T} d={d}")
     inp = WL.make_inputs(WL.Config("g2", d=d, T=T, seed=T + 3 * d))
     dv = Dev(inp)
