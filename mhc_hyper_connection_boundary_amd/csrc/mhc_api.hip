@@ -125,12 +125,14 @@ SplitPlan split_plan(int T, int hidden, bool invariant, bool shifted) {
     plan.groups = 1;
     if (!invariant) {
         // Two token groups (four for the pre, whose kernel has the registers)
-        // share each fragment load once there are enough steps per wave.  The steps per wave are then chosen so the grid
-        // fills whole rounds of slots: the least rounds x (steps per wave + a
-        // fixed cost of kRoundCost steps per round).  While the finest split
-        // fits one round this keeps one step per wave, as INVARIANT does.  The boundary's slots are the workgroups the device holds
-        // at once; the pre's are the compute units (one workgroup each), which
-        // measured faster there than filling every resident slot.
+        // share each fragment load once there are enough steps per wave.  The
+        // steps per wave are then chosen so the grid fills whole rounds of
+        // slots: the least rounds x (steps per wave + a fixed cost of
+        // kRoundCost steps per round).  While the finest split fits one round
+        // this keeps one step per wave, as INVARIANT does.  The boundary's
+        // slots are the workgroups the device holds at once; the pre's are the
+        // compute units (one workgroup each), which measured faster there than
+        // filling every resident slot.
         plan.groups = spw >= (shifted ? kTwoGroupStepsShifted : kTwoGroupStepsPre) ? 2 : 1;
         if (!shifted && spw >= kFourGroupStepsPre) plan.groups = 4;
         const long resident = shifted ? partial_resident_workgroups(shifted, plan.groups)
