@@ -71,7 +71,10 @@ typedef enum {
 
 /* Scheduling choice for mhc_boundary and mhc_pre (results are identical up
  * to the accumulation order of the FP32 sums; each choice is deterministic:
- * the same call on the same inputs gives the same bits).  FUSED exists for
+ * the same call on the same inputs gives the same bits on the same device).
+ * AUTO and SPLIT size the split to the current device's compute units and
+ * occupancy, so on a device with another compute-unit count they may sum in
+ * another order; INVARIANT does not depend on the device.  FUSED exists for
  * hidden in {1024, 2048, 4096, 5120, 6144, 7168, 8192}; asked for any other
  * width it returns MHC_ERR_UNSUPPORTED_SHAPE.
  *
