@@ -6,7 +6,7 @@
 //   k_fused_w4 / k_fused_pre_w4  4 waves, 32-token tiles (two token groups per
 //                                wave sharing each weight fragment; one wave per
 //                                SIMD, so a wave may hold 512 registers).
-// The host picks the 32-token shape once there is a tile per CU (8192 tokens).
+// The host picks the shape whose tiles fill whole rounds of compute units.
 //
 // A wave step covers 64 hidden elements of the tile (two 32-element MFMA
 // k-blocks); wave w takes steps w, w + waves, ...  Every lane reads both
