@@ -88,11 +88,12 @@ typedef enum {
  * hidden 7168 on 256 compute units; mhc_pre: one workgroup per compute unit,
  * T <= 64), so small decode batches give the same bits under all three. */
 typedef enum {
-    MHC_SCHEDULE_AUTO = 0,        /* mhc_boundary: FUSED where it exists and its token tiles
-                                     fill the device's compute units: 32-token tiles where they
-                                     fill at least 7/8 of whole rounds, else 16-token tiles
-                                     (from 3072 tokens) where they fill at least 7/8 of one
-                                     round; else SPLIT.  mhc_pre: SPLIT */
+    MHC_SCHEDULE_AUTO = 0,        /* mhc_boundary: the fused kernels where they exist and
+                                     their tiles fill the device's compute units: 4-wave tiles
+                                     of ceil(T / (rounds x units)) <= 32 tokens (tokens spread
+                                     evenly over whole rounds) where that is at least 18, else
+                                     16-token tiles (from 3072 tokens) where they fill at least
+                                     7/8 of one round; else SPLIT.  mhc_pre: SPLIT */
     MHC_SCHEDULE_SPLIT = 1,       /* hidden split over many workgroups + finishing kernel */
     MHC_SCHEDULE_FUSED = 2,       /* one workgroup per token tile owns all of hidden: 16-token
                                      tiles on 8 waves, or from 8192 tokens 32-token tiles on

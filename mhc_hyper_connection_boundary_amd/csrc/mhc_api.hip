@@ -21,6 +21,7 @@ constexpr int kTwoGroupStepsShifted = 8;  // split boundary: two token groups pe
 constexpr int kTwoGroupStepsPre = 4;      // split pre: two groups from here (fewer registers)
 constexpr int kFourGroupStepsPre = 16;    // split pre: four groups from here
 constexpr int kRoundCost = 2;             // split grid: fixed cost of a round of workgroups, in steps
+constexpr int kW4MinTileTokens = 18;  // automatic schedule: balanced 4-wave tiles of at least this
 constexpr int kW4MinTokens = 8192;    // fused schedule: 32-token tiles on 4 waves from here
 
 int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
@@ -66,34 +67,44 @@ mhc_status check_params(const mhc_params* p) {
 
 // Which kernels run mhc_boundary.  FUSED is honoured (the caller gets
 // UNSUPPORTED_SHAPE where the width has no fused kernel): 16-token tiles below
-// kW4MinTokens, 32-token tiles from there.  AUTO takes a fused kernel only
-// where its tiles fill the device's rounds of compute units (one workgroup
-// each), since a partly filled last round costs a whole round:
-//   32-token tiles where they fill at least 7/8 of whole rounds;
+// kW4MinTokens, 32-token tiles from there.  AUTO spreads the tokens evenly over
+// whole rounds of compute units (one workgroup each), since a partly filled
+// last round costs a whole round:
+//   4-wave tiles of the balanced size ceil(T / (rounds x units)) (at most 32)
+//   where that is at least kW4MinTileTokens;
 //   else 16-token tiles from kFusedMinTokens where they fill at least 7/8 of
 //   one round;
 //   the split schedule otherwise.
-// Measured at d=7168 (split / 16-token / 32-token, us): T=3072 141 / 157 / 233,
-// T=4096 181 / 177 / 251, T=5120 232 / 285 / 272, T=6144 274 / 308 / 285,
-// T=7168 330 / 326 / 297, T=8192 343 / - / 313, T=12288 537 / - / 559,
-// T=14336 656 / - / 585.  Where the
-// compute-unit count is unknown, AUTO falls back to 16-token tiles from
-// kFusedMinTokens and 32-token tiles from kW4MinTokens.
+// Measured cold at d=7168 (us): 32-token tiles or split before -> balanced
+// tiles: T=6144 274 -> 256, T=7168 298 -> 285, T=9216 419 -> 404, T=12288
+// 530 -> 486, T=14336 580 -> 548; T=8192 and 16384 unchanged.  18-token tiles
+// are level with the split in one round (T=4608: 215 against 212) and ahead of
+// it in two (T=9216), so they are the smallest taken.  Where the compute-unit
+// count is unknown, AUTO
+// falls back to 16-token tiles from kFusedMinTokens and 32-token tiles from
+// kW4MinTokens.
 enum class BoundaryPath { Split, Fused16, Fused32 };
+struct BoundaryChoice {
+    BoundaryPath path;
+    int tile_tokens;  // Fused32: tokens per tile (at most 32)
+};
 
-BoundaryPath boundary_path(int schedule, int tokens, int hidden) {
+BoundaryChoice boundary_path(int schedule, int tokens, int hidden) {
     if (schedule == MHC_SCHEDULE_FUSED)
-        return tokens >= kW4MinTokens ? BoundaryPath::Fused32 : BoundaryPath::Fused16;
+        return tokens >= kW4MinTokens ? BoundaryChoice{BoundaryPath::Fused32, 32}
+                                      : BoundaryChoice{BoundaryPath::Fused16, 16};
     if (schedule != MHC_SCHEDULE_AUTO || !fused_supported(hidden) || tokens < kFusedMinTokens)
-        return BoundaryPath::Split;
+        return {BoundaryPath::Split, 0};
     const long units = device_compute_units();
     if (units <= 0)
-        return tokens >= kW4MinTokens ? BoundaryPath::Fused32 : BoundaryPath::Fused16;
-    const long tiles32 = ceil_div(tokens, 32);
-    if (8 * tiles32 >= 7 * ((tiles32 + units - 1) / units) * units) return BoundaryPath::Fused32;
+        return tokens >= kW4MinTokens ? BoundaryChoice{BoundaryPath::Fused32, 32}
+                                      : BoundaryChoice{BoundaryPath::Fused16, 16};
+    const long rounds = (ceil_div(tokens, 32) + units - 1) / units;
+    const int balanced = (int)ceil_div(tokens, (int)(rounds * units));
+    if (balanced >= kW4MinTileTokens) return {BoundaryPath::Fused32, balanced};
     const long tiles16 = ceil_div(tokens, 16);
-    if (tiles16 <= units && 8 * tiles16 >= 7 * units) return BoundaryPath::Fused16;
-    return BoundaryPath::Split;
+    if (tiles16 <= units && 8 * tiles16 >= 7 * units) return {BoundaryPath::Fused16, 16};
+    return {BoundaryPath::Split, 0};
 }
 
 // The non-shifted pre reads X twice on either schedule, and its split runs
@@ -343,16 +354,19 @@ mhc_status mhc_boundary(int tokens, int hidden, const uint16_t* x, const uint16_
 
     const Scalars s = scalars(params);
     hipStream_t hs = (hipStream_t)stream;
-    const BoundaryPath path = boundary_path(params->schedule, tokens, hidden);
-    if (path != BoundaryPath::Split) {
+    const BoundaryChoice choice = boundary_path(params->schedule, tokens, hidden);
+    if (choice.path != BoundaryPath::Split) {
         if (!fused_supported(hidden)) return MHC_ERR_UNSUPPORTED_SHAPE;
-        // 32-token tiles halve the weight-fragment loads per token but need at
-        // least one tile per CU; below that the 16-token kernel fills the chip.
-        const auto launch = path == BoundaryPath::Fused32 ? launch_fused_w4 : launch_fused;
-        if (launch(tokens, hidden, x, residual, post_prev, comb_prev, pre_lag, w_prepared, scale,
-                   base, norm_w, s, residual_out, layer_input, pre_out, post_out, comb_out, mixes,
-                   rstd, hs) != hipSuccess)
-            return MHC_ERR_DEVICE;
+        const hipError_t e =
+            choice.path == BoundaryPath::Fused32
+                ? launch_fused_w4(tokens, choice.tile_tokens, hidden, x, residual, post_prev,
+                                  comb_prev, pre_lag, w_prepared, scale, base, norm_w, s,
+                                  residual_out, layer_input, pre_out, post_out, comb_out, mixes,
+                                  rstd, hs)
+                : launch_fused(tokens, hidden, x, residual, post_prev, comb_prev, pre_lag,
+                               w_prepared, scale, base, norm_w, s, residual_out, layer_input,
+                               pre_out, post_out, comb_out, mixes, rstd, hs);
+        if (e != hipSuccess) return MHC_ERR_DEVICE;
         return MHC_OK;
     }
     const SplitPlan plan =

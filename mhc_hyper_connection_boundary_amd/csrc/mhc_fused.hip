@@ -368,7 +368,7 @@ struct FusedW4Shape {
 
 template <int S>
 __global__ __launch_bounds__(256) void k_fused_w4(
-    int T, const uint16_t* __restrict__ x, const uint16_t* __restrict__ X,
+    int T, int tile_tokens, const uint16_t* __restrict__ x, const uint16_t* __restrict__ X,
     const float* __restrict__ post_prev, const float* __restrict__ comb_prev,
     const float* __restrict__ pre_lag, const uint4* __restrict__ wprep,
     const float* __restrict__ scale, const float* __restrict__ base,
@@ -388,7 +388,12 @@ __global__ __launch_bounds__(256) void k_fused_w4(
     const int lane = threadIdx.x & 63;
     const int n = lane & 15;
     const int g = lane >> 4;
+    // The tile holds tokens [t0, t_end): tile_tokens of them (at most 32),
+    // fewer in the last tile.
+    const int t0 = tile * tile_tokens;
+    const int t_end = min(t0 + tile_tokens, T);
     size_t tc[2];
+    bool valid[2];
     PrevCoef c[2];
     const uint16_t* Xrow[2];
     const uint16_t* xrow[2];
@@ -396,10 +401,11 @@ __global__ __launch_bounds__(256) void k_fused_w4(
     uint16_t* xn_row[2];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-        // A lane past the last token works on token T-1, so it stores the
-        // same bytes as that token's own lane: no branch needed.
-        const int t = tile * kTileW4 + 16 * q + n;
-        tc[q] = t < T ? (size_t)t : (size_t)(T - 1);
+        // A lane past the tile's last token works on that token, so it stores
+        // the same bytes as the token's own lane: no branch needed.
+        const int t = t0 + 16 * q + n;
+        valid[q] = t < t_end;
+        tc[q] = valid[q] ? (size_t)t : (size_t)(t_end - 1);
         load_prev(c[q], post_prev, comb_prev, pre_lag, tc[q]);
         Xrow[q] = X + tc[q] * 4 * hidden;
         xrow[q] = x + tc[q] * hidden;
@@ -469,7 +475,7 @@ __global__ __launch_bounds__(256) void k_fused_w4(
 #pragma unroll
     for (int r = 0; r < Shape::kLiReg; ++r) body(S - Shape::kLiReg + r, true, li_keep[r]);
     LayerInputEpilogue<Shape, kWaves4, 2, true, 5> out{
-        norm_w, {li_row[0], li_row[1]}, {tile * kTileW4 + n < T, tile * kTileW4 + 16 + n < T}, wave, g};
+        norm_w, {li_row[0], li_row[1]}, {valid[0], valid[1]}, wave, g};
     out.prefetch();
 
     // Partials of the 4 waves, added into tot one wave at a time from 0.0f,
@@ -516,9 +522,9 @@ __global__ __launch_bounds__(256) void k_fused_w4(
 
     if (wave < 2) {  // 32 tokens x 4 lanes: waves 0 and 1
         const int tn = 16 * wave + (lane >> 2), ci = lane & 3;
-        const int tt = tile * kTileW4 + tn;
+        const int tt = t0 + tn;
         const TokenCoef o = coefficients(tot[tn], ci, hidden, cp, p);
-        if (tt < T) {
+        if (tt < t_end) {
             pre_out[(size_t)tt * 4 + ci] = o.pre;
             post_out[(size_t)tt * 4 + ci] = o.post;
             *reinterpret_cast<float4*>(comb_out + (size_t)tt * 16 + 4 * ci) =
@@ -536,14 +542,15 @@ __global__ __launch_bounds__(256) void k_fused_w4(
 }
 
 template <int S>
-hipError_t launch_w4_s(int T, const uint16_t* x, const uint16_t* X, const float* post_prev,
+hipError_t launch_w4_s(int T, int tile_tokens, const uint16_t* x, const uint16_t* X, const float* post_prev,
                        const float* comb_prev, const float* pre_lag, const void* wprep,
                        const float* scale, const float* base, const uint16_t* norm_w,
                        const Scalars& p, uint16_t* xn_out, uint16_t* layer_input,
                        float* pre_out, float* post_out, float* comb_out, float* mixes,
                        float* rstd, hipStream_t stream) {
-    hipLaunchKernelGGL(k_fused_w4<S>, dim3((T + kTileW4 - 1) / kTileW4), dim3(kWaves4 * 64), 0,
-                       stream, T, x, X, post_prev, comb_prev, pre_lag,
+    hipLaunchKernelGGL(k_fused_w4<S>, dim3((T + tile_tokens - 1) / tile_tokens),
+                       dim3(kWaves4 * 64), 0, stream, T, tile_tokens, x, X, post_prev, comb_prev,
+                       pre_lag,
                        reinterpret_cast<const uint4*>(wprep), scale, base, norm_w, p, xn_out,
                        layer_input, pre_out, post_out, comb_out, mixes, rstd);
     return hipGetLastError();
@@ -980,15 +987,17 @@ hipError_t launch_fused(int T, int hidden, const uint16_t* x, const uint16_t* X,
 #undef MHC_FUSED_CASE
 }
 
-hipError_t launch_fused_w4(int T, int hidden, const uint16_t* x, const uint16_t* X,
-                           const float* post_prev, const float* comb_prev, const float* pre_lag,
-                           const void* wprep, const float* scale, const float* base,
-                           const uint16_t* norm_w, const Scalars& p, uint16_t* xn_out,
-                           uint16_t* layer_input, float* pre_out, float* post_out,
-                           float* comb_out, float* mixes, float* rstd, hipStream_t stream) {
+hipError_t launch_fused_w4(int T, int tile_tokens, int hidden, const uint16_t* x,
+                           const uint16_t* X, const float* post_prev, const float* comb_prev,
+                           const float* pre_lag, const void* wprep, const float* scale,
+                           const float* base, const uint16_t* norm_w, const Scalars& p,
+                           uint16_t* xn_out, uint16_t* layer_input, float* pre_out,
+                           float* post_out, float* comb_out, float* mixes, float* rstd,
+                           hipStream_t stream) {
+    if (tile_tokens < 1 || tile_tokens > kTileW4) return hipErrorInvalidValue;
 #define MHC_W4_CASE(D)                                                                        \
     case D:                                                                                   \
-        return launch_w4_s<D / 256>(T, x, X, post_prev, comb_prev, pre_lag, wprep, scale,     \
+        return launch_w4_s<D / 256>(T, tile_tokens, x, X, post_prev, comb_prev, pre_lag, wprep, scale, \
                                     base, norm_w, p, xn_out, layer_input, pre_out, post_out,  \
                                     comb_out, mixes, rstd, stream);
     switch (hidden) {

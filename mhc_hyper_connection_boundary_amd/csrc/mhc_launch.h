@@ -76,14 +76,15 @@ hipError_t launch_fused(int T, int hidden, const uint16_t* x, const uint16_t* X,
                         uint16_t* layer_input, float* pre_out, float* post_out, float* comb_out,
                         float* mixes, float* rstd, hipStream_t stream);
 
-// Fused schedule on 4 waves with 32-token tiles (two token groups per wave share
-// the weight fragments); same widths as launch_fused.
-hipError_t launch_fused_w4(int T, int hidden, const uint16_t* x, const uint16_t* X,
-                           const float* post_prev, const float* comb_prev, const float* pre_lag,
-                           const void* wprep, const float* scale, const float* base,
-                           const uint16_t* norm_w, const Scalars& p, uint16_t* xn_out,
-                           uint16_t* layer_input, float* pre_out, float* post_out,
-                           float* comb_out, float* mixes, float* rstd, hipStream_t stream);
+// Fused schedule on 4 waves with tiles of tile_tokens <= 32 tokens (two token
+// groups per wave share the weight fragments); same widths as launch_fused.
+hipError_t launch_fused_w4(int T, int tile_tokens, int hidden, const uint16_t* x,
+                           const uint16_t* X, const float* post_prev, const float* comb_prev,
+                           const float* pre_lag, const void* wprep, const float* scale,
+                           const float* base, const uint16_t* norm_w, const Scalars& p,
+                           uint16_t* xn_out, uint16_t* layer_input, float* pre_out,
+                           float* post_out, float* comb_out, float* mixes, float* rstd,
+                           hipStream_t stream);
 
 // Non-shifted pre, fused: one workgroup per token tile, two passes over the
 // tile's X (fused_supported widths); tiles32 selects 32-token tiles on 4 waves

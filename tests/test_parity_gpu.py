@@ -221,17 +221,26 @@ def test_split_token_groups_ragged(oracle, kind, T, d):
                 label=f"pre split2 T={T} d={d}", fresh=(inp.X, inp.norm_w))
 
 
-@pytest.mark.parametrize("T", [7168 + 7, 5120 + 3])
-def test_auto_between_tile_rounds(oracle, T):
-    """AUTO takes the 32-token fused kernel where its tiles fill at least 7/8 of
-    whole rounds of compute units (7175 tokens on 256 units) and the split
-    schedule where a round would be left partly idle (5123 tokens); ragged."""
-    say(f"auto T={T} d=7168")
-    inp = WL.make_inputs(WL.Config("at", d=7168, T=T, seed=T))
+@pytest.mark.parametrize("T,d", [(7168 + 7, 7168), (5120 + 3, 7168), (9216 + 3, 4096),
+                                 (4096 + 600, 2048)])
+def test_auto_balanced_tiles(oracle, T, d):
+    """AUTO spreads the tokens over whole rounds of compute units with 4-wave
+    tiles of ceil(T / (rounds x units)) tokens (29, 21, 19 and 19 tokens on
+    256 units; two rounds at 9219), or takes the split where such tiles would
+    be small.  Tokens on both sides of every sampled tile edge are checked,
+    and the ragged tail."""
+    import torch
+    units = torch.cuda.get_device_properties(0).multi_processor_count
+    rounds = -(-(-(-T // 32)) // units)
+    tile = -(-T // (rounds * units))
+    say(f"auto T={T} d={d} (balanced tile {tile} tokens on {units} units)")
+    inp = WL.make_inputs(WL.Config("at", d=d, T=T, seed=T + d))
     g = Dev(inp).boundary(schedule="auto")
-    tok = np.unique(np.concatenate([sample_tokens(T, n=32, seed=T),
-                                    np.arange(T - 40, T, dtype=np.int32)]))
-    compare(g, oracle.boundary(inp, tokens=tok), tokens=tok, label=f"auto T={T}")
+    edges = np.arange(tile, T, tile * 37, dtype=np.int64)
+    tok = np.unique(np.concatenate([sample_tokens(T, n=24, seed=T), edges - 1, edges,
+                                    np.arange(T - 40, T)]).astype(np.int32))
+    tok = tok[(tok >= 0) & (tok < T)]
+    compare(g, oracle.boundary(inp, tokens=tok), tokens=tok, label=f"auto T={T} d={d}")
 
 
 def test_fused_refuses_unsupported_width():
