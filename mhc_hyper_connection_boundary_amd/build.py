@@ -1,8 +1,15 @@
-"""Builds libmhc.so (the HIP kernels and the C ABI) for gfx950 with hipcc."""
+"""Builds libmhc.so (the HIP kernels and the C ABI) for gfx950 with hipcc.
+
+Each source compiles to its own object in parallel (each object carries its
+own gfx950 code object; no relocatable device code is needed, since no kernel
+calls device code in another file), then one hipcc call links the library.
+"""
 from __future__ import annotations
 
 import os
 import subprocess
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -11,8 +18,9 @@ LIB = os.path.join(PKG, "libmhc.so")
 SOURCES = ["mhc_api.hip", "mhc_kernels.hip", "mhc_fused.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
+ARCH = ["--offload-arch=gfx950"]
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-O3", "-std=c++17", "-fPIC",
     "-ffp-contract=off",
     # packed FP32 instructions stay off (v_pk_fma_f32 and friends are not used)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -20,11 +28,7 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False, resource_usage: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), *srcs, "-o", LIB + ".tmp"]
-    if resource_usage:
-        cmd.insert(1, "-Rpass-analysis=kernel-resource-usage")
+def _run(cmd: list[str], verbose: bool) -> str:
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -32,9 +36,28 @@ def build(verbose: bool = False, resource_usage: bool = False) -> str:
                      if "packed-fp32-ops" not in l)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed:\n{msgs}")
-    if verbose and msgs.strip():
-        print(msgs)
-    os.replace(LIB + ".tmp", LIB)
+    return msgs
+
+
+def build(verbose: bool = False, resource_usage: bool = False) -> str:
+    with tempfile.TemporaryDirectory(prefix="mhc_build_") as tmp:
+        jobs = []
+        for s in SOURCES:
+            obj = os.path.join(tmp, os.path.splitext(s)[0] + ".o")
+            cmd = [HIPCC, *ARCH, *FLAGS, "-I", os.path.join(ROOT, "include"),
+                   "-c", os.path.join(CSRC, s), "-o", obj]
+            if resource_usage:
+                cmd.insert(1, "-Rpass-analysis=kernel-resource-usage")
+            jobs.append((cmd, obj))
+        with ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+            outs = list(ex.map(lambda j: _run(j[0], verbose), jobs))
+        outs.append(_run([HIPCC, *ARCH, "-shared", "-fPIC", *(o for _, o in jobs),
+                          "-o", LIB + ".tmp"], verbose))
+        if verbose:
+            for m in outs:
+                if m.strip():
+                    print(m)
+        os.replace(LIB + ".tmp", LIB)
     return LIB
 
 
