@@ -99,7 +99,12 @@ __device__ __forceinline__ void load_frags(uint4 (&A)[kFragsPerStep], const uint
 // already been normalised.  Kernels short of registers request the on-chip
 // steps' norm_w as they write (kNwEarly false) and keep fewer parked steps in
 // flight (kMaxDepth).
-template <class Shape, int kWavesN, int kGroups, bool kNwEarly, int kMaxDepth>
+//
+// kNorm: norm_w is given.  Every kernel is built both ways and the host picks
+// one, so no load sits under a branch on it: after a conditional block that
+// loads, the compiler waits for every outstanding load where the paths join,
+// which would expose the whole prefetch at once.
+template <class Shape, int kWavesN, int kGroups, bool kNwEarly, int kMaxDepth, bool kNorm>
 struct LayerInputEpilogue {
     static constexpr int kParkEnd = Shape::kSteps - Shape::kLiReg;  // parked: [kLiLds, kParkEnd)
     static constexpr int kParked = kParkEnd - Shape::kLiLds;
@@ -117,44 +122,47 @@ struct LayerInputEpilogue {
 
     __device__ __forceinline__ int step_h(int i) const { return (i * kWavesN + wave) * kWide + g * 8; }
 
+    // Lanes past the last token read the row of token T-1, whatever another
+    // lane has written there; put() drops their values.
     __device__ __forceinline__ void load_parked(int i) {
         const int slot = (i - Shape::kLiLds) % kDepth, h = step_h(i);
         ring_nw[slot][0] = load_stream(norm_w + h);
         ring_nw[slot][1] = load_stream(norm_w + h + kStep);
 #pragma unroll
-        for (int q = 0; q < kGroups; ++q)
-            if (valid[q]) {
-                ring_li[slot][q][0] = load_stream(li_row[q] + h);
-                ring_li[slot][q][1] = load_stream(li_row[q] + h + kStep);
-            }
+        for (int q = 0; q < kGroups; ++q) {
+            ring_li[slot][q][0] = load_stream(li_row[q] + h);
+            ring_li[slot][q][1] = load_stream(li_row[q] + h + kStep);
+        }
     }
 
     __device__ __forceinline__ void prefetch() {
-        if (!norm_w) return;
-        if (kNwEarly) {
+        if constexpr (kNorm) {
+            if constexpr (kNwEarly) {
 #pragma unroll
-            for (int i = 0; i < Shape::kLiLds; ++i) {
-                lds_nw[i][0] = load_stream(norm_w + step_h(i));
-                lds_nw[i][1] = load_stream(norm_w + step_h(i) + kStep);
+                for (int i = 0; i < Shape::kLiLds; ++i) {
+                    lds_nw[i][0] = load_stream(norm_w + step_h(i));
+                    lds_nw[i][1] = load_stream(norm_w + step_h(i) + kStep);
+                }
+#pragma unroll
+                for (int rr = 0; rr < Shape::kLiReg; ++rr) {
+                    keep_nw[rr][0] = load_stream(norm_w + step_h(kParkEnd + rr));
+                    keep_nw[rr][1] = load_stream(norm_w + step_h(kParkEnd + rr) + kStep);
+                }
             }
 #pragma unroll
-            for (int rr = 0; rr < Shape::kLiReg; ++rr) {
-                keep_nw[rr][0] = load_stream(norm_w + step_h(kParkEnd + rr));
-                keep_nw[rr][1] = load_stream(norm_w + step_h(kParkEnd + rr) + kStep);
-            }
+            for (int i = Shape::kLiLds; i < kParkEnd && i < Shape::kLiLds + kDepth; ++i) load_parked(i);
         }
-#pragma unroll
-        for (int i = Shape::kLiLds; i < kParkEnd && i < Shape::kLiLds + kDepth; ++i) load_parked(i);
     }
 
     __device__ __forceinline__ uint4 nw_at(const uint4 (&early)[2], int b, int h) const {
+        if constexpr (!kNorm) return uint4{};
         return kNwEarly ? early[b] : load_stream(norm_w + h);
     }
 
     __device__ __forceinline__ void put(int q, int h, const uint4& li, const uint4& nw, float r) {
         if (!valid[q]) return;
         uint4 out = li;
-        if (norm_w) {
+        if constexpr (kNorm) {
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const uint32_t a = word(li, k), b = word(nw, k);
@@ -172,8 +180,8 @@ struct LayerInputEpilogue {
 #pragma unroll
         for (int i = 0; i < Shape::kLiLds; ++i) {
             const int h = step_h(i);
-            const uint4 nw0 = norm_w ? nw_at(lds_nw[kNwEarly ? i : 0], 0, h) : uint4{};
-            const uint4 nw1 = norm_w ? nw_at(lds_nw[kNwEarly ? i : 0], 1, h + kStep) : uint4{};
+            const uint4 nw0 = nw_at(lds_nw[kNwEarly ? i : 0], 0, h);
+            const uint4 nw1 = nw_at(lds_nw[kNwEarly ? i : 0], 1, h + kStep);
 #pragma unroll
             for (int q = 0; q < kGroups; ++q) {
                 put(q, h, lds_li(i, q, 0), nw0, r[q]);
@@ -183,15 +191,15 @@ struct LayerInputEpilogue {
 #pragma unroll
         for (int rr = 0; rr < Shape::kLiReg; ++rr) {
             const int h = step_h(kParkEnd + rr);
-            const uint4 nw0 = norm_w ? nw_at(keep_nw[kNwEarly ? rr : 0], 0, h) : uint4{};
-            const uint4 nw1 = norm_w ? nw_at(keep_nw[kNwEarly ? rr : 0], 1, h + kStep) : uint4{};
+            const uint4 nw0 = nw_at(keep_nw[kNwEarly ? rr : 0], 0, h);
+            const uint4 nw1 = nw_at(keep_nw[kNwEarly ? rr : 0], 1, h + kStep);
 #pragma unroll
             for (int q = 0; q < kGroups; ++q) {
                 put(q, h, keep_li(rr, q, 0), nw0, r[q]);
                 put(q, h + kStep, keep_li(rr, q, 1), nw1, r[q]);
             }
         }
-        if (!norm_w) return;  // without norm_w the parked li already is the layer input
+        if constexpr (!kNorm) return;  // without norm_w the parked li already is the layer input
 #pragma unroll
         for (int i = Shape::kLiLds; i < kParkEnd; ++i) {
             const int slot = (i - Shape::kLiLds) % kDepth, h = step_h(i);
@@ -205,7 +213,7 @@ struct LayerInputEpilogue {
     }
 };
 
-template <int S>
+template <int S, bool kNorm>  // kNorm: norm_w is given
 __global__ __launch_bounds__(512) void k_fused(
     int T, const uint16_t* __restrict__ x, const uint16_t* __restrict__ X,
     const float* __restrict__ post_prev, const float* __restrict__ comb_prev,
@@ -290,12 +298,14 @@ __global__ __launch_bounds__(512) void k_fused(
     uint4 li_keep[Shape::kLiReg > 0 ? Shape::kLiReg : 1][2];
 #pragma unroll
     for (int r = 0; r < Shape::kLiReg; ++r) body(S - Shape::kLiReg + r, true, li_keep[r]);
-    LayerInputEpilogue<Shape, kWaves, 1, false, 2> out{norm_w, {li_row}, {t < T}, wave, g};
+    // The coefficient parameters are requested before the epilogue's loads, so
+    // that waiting for them does not wait for those.
+    CoefParams cp;
+    if (wave == 0) cp = load_coef_params(scale, base, lane & 3);
+    LayerInputEpilogue<Shape, kWaves, 1, false, 2, kNorm> out{norm_w, {li_row}, {t < T}, wave, g};
     out.prefetch();
 
     // Partials of the 8 waves, combined in a fixed order.
-    CoefParams cp;
-    if (wave == 0) cp = load_coef_params(scale, base, lane & 3);
 #pragma unroll
     for (int m = 0; m < 3; ++m)
 #pragma unroll
@@ -366,7 +376,7 @@ struct FusedW4Shape {
     static constexpr int kLiReg = S - kLiLds < 2 ? S - kLiLds : 2;  // last steps: in registers
 };                                                // (steps between: layer_input)
 
-template <int S>
+template <int S, bool kNorm>  // kNorm: norm_w is given
 __global__ __launch_bounds__(256) void k_fused_w4(
     int T, int tile_tokens, const uint16_t* __restrict__ x, const uint16_t* __restrict__ X,
     const float* __restrict__ post_prev, const float* __restrict__ comb_prev,
@@ -474,7 +484,11 @@ __global__ __launch_bounds__(256) void k_fused_w4(
     uint4 li_keep[Shape::kLiReg > 0 ? Shape::kLiReg : 1][2][2];
 #pragma unroll
     for (int r = 0; r < Shape::kLiReg; ++r) body(S - Shape::kLiReg + r, true, li_keep[r]);
-    LayerInputEpilogue<Shape, kWaves4, 2, true, 5> out{
+    // The coefficient parameters are requested before the epilogue's loads, so
+    // that waiting for them does not wait for those.
+    CoefParams cp;
+    if (wave < 2) cp = load_coef_params(scale, base, lane & 3);
+    LayerInputEpilogue<Shape, kWaves4, 2, true, 5, kNorm> out{
         norm_w, {li_row[0], li_row[1]}, {valid[0], valid[1]}, wave, g};
     out.prefetch();
 
@@ -482,8 +496,6 @@ __global__ __launch_bounds__(256) void k_fused_w4(
     // wave 0 first: each mix is ((w0 + w1) + w2) + w3, each sum of squares
     // adds the k-groups 0..3 of wave 0, then of wave 1, ...  Lane group 0 of
     // a wave gathers the four k-group values of its token.
-    CoefParams cp;
-    if (wave < 2) cp = load_coef_params(scale, base, lane & 3);
 #pragma unroll
     for (int w = 0; w < kWaves4; ++w) {
         if (wave == w) {
@@ -548,9 +560,9 @@ hipError_t launch_w4_s(int T, int tile_tokens, const uint16_t* x, const uint16_t
                        const Scalars& p, uint16_t* xn_out, uint16_t* layer_input,
                        float* pre_out, float* post_out, float* comb_out, float* mixes,
                        float* rstd, hipStream_t stream) {
-    hipLaunchKernelGGL(k_fused_w4<S>, dim3((T + tile_tokens - 1) / tile_tokens),
-                       dim3(kWaves4 * 64), 0, stream, T, tile_tokens, x, X, post_prev, comb_prev,
-                       pre_lag,
+    hipLaunchKernelGGL((norm_w ? k_fused_w4<S, true> : k_fused_w4<S, false>),
+                       dim3((T + tile_tokens - 1) / tile_tokens), dim3(kWaves4 * 64), 0, stream,
+                       T, tile_tokens, x, X, post_prev, comb_prev, pre_lag,
                        reinterpret_cast<const uint4*>(wprep), scale, base, norm_w, p, xn_out,
                        layer_input, pre_out, post_out, comb_out, mixes, rstd);
     return hipGetLastError();
@@ -603,7 +615,7 @@ __device__ __forceinline__ uint4 collapse8(const uint4 (&Xv)[4], const float (&p
     return li;
 }
 
-template <int S>
+template <int S, bool kNorm>  // kNorm: norm_w is given
 __global__ __launch_bounds__(512) void k_fused_pre(
     int T, const uint16_t* __restrict__ X, const uint4* __restrict__ wprep,
     const float* __restrict__ scale, const float* __restrict__ base,
@@ -717,7 +729,7 @@ __global__ __launch_bounds__(512) void k_fused_pre(
         }
         cur = nxt;
     }
-    LayerInputEpilogue<PreShape, kWaves, 1, true, 5> out{norm_w, {li_row}, {t < T}, wave, g};
+    LayerInputEpilogue<PreShape, kWaves, 1, true, 5, kNorm> out{norm_w, {li_row}, {t < T}, wave, g};
     out.prefetch();
     sq[wave][g][n] = ssq_li;
     __syncthreads();
@@ -735,7 +747,7 @@ __global__ __launch_bounds__(512) void k_fused_pre(
              [&](int, int, int) { return uint4{}; }, r);
 }
 
-template <int S>
+template <int S, bool kNorm>  // kNorm: norm_w is given
 __global__ __launch_bounds__(256) void k_fused_pre_w4(
     int T, const uint16_t* __restrict__ X, const uint4* __restrict__ wprep,
     const float* __restrict__ scale, const float* __restrict__ base,
@@ -895,7 +907,8 @@ __global__ __launch_bounds__(256) void k_fused_pre_w4(
     uint4 li_keep[Shape::kLiReg > 0 ? Shape::kLiReg : 1][2][2];
 #pragma unroll
     for (int r = 0; r < Shape::kLiReg; ++r) body(S - Shape::kLiReg + r, true, li_keep[r]);
-    LayerInputEpilogue<Shape, kWaves4, 2, true, 5> out{norm_w, {li_row[0], li_row[1]}, {valid[0], valid[1]}, wave, g};
+    LayerInputEpilogue<Shape, kWaves4, 2, true, 5, kNorm> out{
+        norm_w, {li_row[0], li_row[1]}, {valid[0], valid[1]}, wave, g};
     out.prefetch();
 
 #pragma unroll
@@ -920,9 +933,10 @@ hipError_t launch_pre_w4_s(int T, const uint16_t* X, const void* wprep, const fl
                            const float* base, const uint16_t* norm_w, const Scalars& p,
                            uint16_t* layer_input, float* pre_out, float* post_out,
                            float* comb_out, float* mixes, float* rstd, hipStream_t stream) {
-    hipLaunchKernelGGL(k_fused_pre_w4<S>, dim3((T + kTileW4 - 1) / kTileW4), dim3(kWaves4 * 64),
-                       0, stream, T, X, reinterpret_cast<const uint4*>(wprep), scale, base,
-                       norm_w, p, layer_input, pre_out, post_out, comb_out, mixes, rstd);
+    hipLaunchKernelGGL((norm_w ? k_fused_pre_w4<S, true> : k_fused_pre_w4<S, false>),
+                       dim3((T + kTileW4 - 1) / kTileW4), dim3(kWaves4 * 64), 0, stream, T, X,
+                       reinterpret_cast<const uint4*>(wprep), scale, base, norm_w, p,
+                       layer_input, pre_out, post_out, comb_out, mixes, rstd);
     return hipGetLastError();
 }
 
@@ -931,9 +945,10 @@ hipError_t launch_pre_s(int T, const uint16_t* X, const void* wprep, const float
                         const float* base, const uint16_t* norm_w, const Scalars& p,
                         uint16_t* layer_input, float* pre_out, float* post_out, float* comb_out,
                         float* mixes, float* rstd, hipStream_t stream) {
-    hipLaunchKernelGGL(k_fused_pre<S>, dim3((T + kTile - 1) / kTile), dim3(kWaves * 64), 0,
-                       stream, T, X, reinterpret_cast<const uint4*>(wprep), scale, base, norm_w,
-                       p, layer_input, pre_out, post_out, comb_out, mixes, rstd);
+    hipLaunchKernelGGL((norm_w ? k_fused_pre<S, true> : k_fused_pre<S, false>),
+                       dim3((T + kTile - 1) / kTile), dim3(kWaves * 64), 0, stream, T, X,
+                       reinterpret_cast<const uint4*>(wprep), scale, base, norm_w, p,
+                       layer_input, pre_out, post_out, comb_out, mixes, rstd);
     return hipGetLastError();
 }
 
@@ -944,7 +959,8 @@ hipError_t launch_s(int T, const uint16_t* x, const uint16_t* X, const float* po
                     const Scalars& p, uint16_t* xn_out, uint16_t* layer_input, float* pre_out,
                     float* post_out, float* comb_out, float* mixes, float* rstd,
                     hipStream_t stream) {
-    hipLaunchKernelGGL(k_fused<S>, dim3((T + kTile - 1) / kTile), dim3(kWaves * 64), 0, stream,
+    hipLaunchKernelGGL((norm_w ? k_fused<S, true> : k_fused<S, false>),
+                       dim3((T + kTile - 1) / kTile), dim3(kWaves * 64), 0, stream,
                        T, x, X, post_prev, comb_prev, pre_lag,
                        reinterpret_cast<const uint4*>(wprep), scale, base, norm_w, p, xn_out,
                        layer_input, pre_out, post_out, comb_out, mixes, rstd);
