@@ -276,6 +276,30 @@ def test_boundary_no_norm_is_li(oracle):
     compare(g, o, label="no-norm")
 
 
+@pytest.mark.parametrize("kind,T,d,schedule", [
+    ("boundary", 37, 2048, "fused"),          # 16-token tiles on 8 waves
+    ("boundary", 8192 + 13, 1024, "fused"),   # 32-token tiles, ragged last tile
+    ("boundary", 4696, 2048, "auto"),         # balanced 4-wave tiles
+    ("pre", 50, 7168, "fused"),               # 16-token tiles on 8 waves
+    ("pre", 8192 + 13, 1024, "fused"),        # 32-token tiles
+])
+def test_fused_without_norm(oracle, kind, T, d, schedule):
+    """Each fused kernel is built with and without norm_w; the copies without
+    it write li itself as the layer input, parked steps included."""
+    say(f"{kind} without norm_w T={T} d={d} {schedule}")
+    inp = WL.make_inputs(WL.Config("nn", d=d, T=T, seed=T + 3 * d))
+    dv = Dev(inp)
+    if kind == "boundary":
+        g = dv.boundary(norm=False, schedule=schedule)
+        o = oracle.boundary(inp, use_norm=False)
+        assert np.array_equal(g["layer_input"], o["li"])
+        compare(g, o, label=f"no-norm {T} {d}")
+    else:
+        g = dv.pre(norm=False, schedule=schedule)
+        compare(g, oracle.pre(inp, use_norm=False), xn=False, label=f"pre no-norm {T} {d}",
+                fresh=(inp.X, None))
+
+
 def test_boundary_special_cases(oracle):
     say("boundary special cases")
     inp = WL.make_inputs(WL.Config("sc", d=512, T=18, seed=9))
