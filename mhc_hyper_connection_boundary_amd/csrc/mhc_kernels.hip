@@ -200,24 +200,43 @@ __global__ __launch_bounds__(256) void k_partial(
 // ---------------------------------------------------------------------------
 // Split schedule, kernel 2: totals, coefficients, layer input.
 //
-// Sum over slices q of part[t][q][v], q ascending.  The loads are issued in
-// batches of 8 so they overlap; the additions keep the slice order.
+// Sum over slices q = first, first + stride, ... < count of part[t][q][v], q
+// ascending.  The loads are issued in batches of 8 so they overlap; the
+// additions keep the slice order.  slice_first requests the first batch (the
+// only one unless count > 8 * stride) at addresses clamped to the last slice,
+// so that a caller can request several sums before waiting and no load sits
+// under a branch (after a conditional block that loads, the compiler waits
+// for every outstanding load); slice_rest adds it and any further batches.
+// count >= 1.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float slice_sum(const float* __restrict__ src, int first, int stride,
-                                           int count, size_t elem_stride = kPart) {
+__device__ __forceinline__ void slice_first(float (&v)[8], const float* __restrict__ src,
+                                            int first, int stride, int count,
+                                            size_t elem_stride = kPart) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = src[(size_t)min(first + k * stride, count - 1) * elem_stride];
+}
+
+__device__ __forceinline__ float slice_rest(const float (&v)[8], const float* __restrict__ src,
+                                            int first, int stride, int count,
+                                            size_t elem_stride = kPart) {
     float sum = 0.0f;
-    for (int q0 = first; q0 < count; q0 += 8 * stride) {
-        float v[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int q = q0 + k * stride;
-            v[k] = q < count ? src[(size_t)q * elem_stride] : 0.0f;
-        }
+    for (int k = 0; k < 8; ++k) sum = first + k * stride < count ? sum + v[k] : sum;
+    for (int q0 = first + 8 * stride; q0 < count; q0 += 8 * stride) {
+        float w[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k)
-            if (q0 + k * stride < count) sum += v[k];
+        for (int k = 0; k < 8; ++k) w[k] = src[(size_t)min(q0 + k * stride, count - 1) * elem_stride];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) sum = q0 + k * stride < count ? sum + w[k] : sum;
     }
     return sum;
+}
+
+__device__ __forceinline__ float slice_sum(const float* __restrict__ src, int first, int stride,
+                                           int count, size_t elem_stride = kPart) {
+    float v[8];
+    slice_first(v, src, first, stride, count, elem_stride);
+    return slice_rest(v, src, first, stride, count, elem_stride);
 }
 
 // Remaining coefficient tokens of a workgroup (tokens hs + k*finish_slices,
@@ -292,10 +311,12 @@ __global__ __launch_bounds__(256) void k_finish(
     const int width = max(0, min(slice_width, hidden - h0));
     const int chunks = width / 8;
 
-    // The coefficient quad's parameters, then the rescale chunks u = tid and
-    // tid + 256 (the common case): all loads go first.
-    CoefParams cp;
-    if (tid < 4) cp = load_coef_params(scale, base, tid);
+    // All loads go first, none under a branch: the coefficient parameters, the
+    // rescale chunks u = tid and tid + 256 (the common case), then the first
+    // batches of the slice sums.  Lanes without work read one shared address
+    // (so their requests coalesce) and their results are dropped.
+    const CoefParams cp = load_coef_params(scale, base, tid & 3);
+    const uint16_t* nw_src = norm_w ? norm_w : layer_input;
     uint4 li_v[2], nw_v[2];
     bool have[2];
 #pragma unroll
@@ -303,27 +324,31 @@ __global__ __launch_bounds__(256) void k_finish(
         const int u = tid + k * (int)blockDim.x;
         const int tn = chunks ? u / chunks : kTile, cidx = chunks ? u % chunks : 0;
         have[k] = norm_w && u < kTile * chunks && tile * kTile + tn < T;
-        if (have[k]) {
-            const int h = h0 + cidx * 8;
-            li_v[k] = *reinterpret_cast<const uint4*>(layer_input + (size_t)(tile * kTile + tn) * hidden + h);
-            nw_v[k] = *reinterpret_cast<const uint4*>(norm_w + h);
-        }
+        const size_t t = have[k] ? (size_t)(tile * kTile + tn) : 0;
+        const int h = have[k] ? h0 + cidx * 8 : 0;
+        li_v[k] = *reinterpret_cast<const uint4*>(layer_input + t * hidden + h);
+        nw_v[k] = *reinterpret_cast<const uint4*>(nw_src + h);
     }
 
     // Phase 1: partial sums of li squares (thread (tn, group) adds slices
     // group, group + 16, ...) and of the first coefficient token's 25 values
     // (thread (v, group) adds slices group, group + 8, ...).
-    {
-        const int tn = tid >> 4, grp = tid & 15;
-        const int t = tile * kTile + tn;
-        lsum[tn][grp] = t < T ? slice_sum(part + (size_t)t * slices * kPart + 25, grp, 16, slices)
-                              : 0.0f;
-    }
+    const int ltn = tid >> 4, lgrp = tid & 15;
+    const int lt = tile * kTile + ltn;
+    const float* lsrc = part + (size_t)min(lt, T - 1) * slices * kPart + 25;
+    float lv[8];
+    slice_first(lv, lsrc, lgrp, 16, slices);
     const int t_first = tile * kTile + hs;
     const bool coef_first = hs < kTile && t_first < T;
-    if (coef_first && (tid & 31) < 25)
-        cred[tid >> 5][tid & 31] =
-            slice_sum(part + (size_t)t_first * slices * kPart + (tid & 31), tid >> 5, 8, slices);
+    // (first = slices: every request clamps to the last slice of token 0)
+    const float* csrc = coef_first ? part + (size_t)t_first * slices * kPart + min(tid & 31, 24) : part;
+    const int cfirst = coef_first ? tid >> 5 : slices;
+    float cv[8];
+    slice_first(cv, csrc, cfirst, 8, slices);
+    const float ls = slice_rest(lv, lsrc, lgrp, 16, slices);
+    const float cs = slice_rest(cv, csrc, cfirst, 8, slices);
+    lsum[ltn][lgrp] = lt < T ? ls : 0.0f;
+    if (coef_first && (tid & 31) < 25) cred[tid >> 5][tid & 31] = cs;
     __syncthreads();
     // Phase 2: totals.
     if (tid < kTile) {
