@@ -96,15 +96,13 @@ __device__ __forceinline__ void load_frags(uint4 (&A)[kFragsPerStep], const uint
 // parked step's slot refilled kDepth steps ahead.  A lane owns kGroups tokens
 // (16 apart); lanes past the last token write nothing, since another lane
 // working on the same token T-1 would otherwise read back a value that has
-// already been normalised.  Kernels short of registers request the on-chip
-// steps' norm_w as they write (kNwEarly false) and keep fewer parked steps in
-// flight (kMaxDepth).
+// already been normalised.  kMaxDepth bounds the parked steps in flight.
 //
 // kNorm: norm_w is given.  Every kernel is built both ways and the host picks
 // one, so no load sits under a branch on it: after a conditional block that
 // loads, the compiler waits for every outstanding load where the paths join,
 // which would expose the whole prefetch at once.
-template <class Shape, int kWavesN, int kGroups, bool kNwEarly, int kMaxDepth, bool kNorm>
+template <class Shape, int kWavesN, int kGroups, int kMaxDepth, bool kNorm>
 struct LayerInputEpilogue {
     static constexpr int kParkEnd = Shape::kSteps - Shape::kLiReg;  // parked: [kLiLds, kParkEnd)
     static constexpr int kParked = kParkEnd - Shape::kLiLds;
@@ -118,7 +116,7 @@ struct LayerInputEpilogue {
     bool valid[kGroups];
     int wave, g;
     uint4 ring_li[kDepth][kGroups][2], ring_nw[kDepth][2];
-    uint4 lds_nw[kNwEarly ? kLds : 1][2], keep_nw[kNwEarly ? kReg : 1][2];
+    uint4 lds_nw[kLds][2], keep_nw[kReg][2];
 
     __device__ __forceinline__ int step_h(int i) const { return (i * kWavesN + wave) * kWide + g * 8; }
 
@@ -137,27 +135,21 @@ struct LayerInputEpilogue {
 
     __device__ __forceinline__ void prefetch() {
         if constexpr (kNorm) {
-            if constexpr (kNwEarly) {
 #pragma unroll
-                for (int i = 0; i < Shape::kLiLds; ++i) {
-                    lds_nw[i][0] = load_stream(norm_w + step_h(i));
-                    lds_nw[i][1] = load_stream(norm_w + step_h(i) + kStep);
-                }
+            for (int i = 0; i < Shape::kLiLds; ++i) {
+                lds_nw[i][0] = load_stream(norm_w + step_h(i));
+                lds_nw[i][1] = load_stream(norm_w + step_h(i) + kStep);
+            }
 #pragma unroll
-                for (int rr = 0; rr < Shape::kLiReg; ++rr) {
-                    keep_nw[rr][0] = load_stream(norm_w + step_h(kParkEnd + rr));
-                    keep_nw[rr][1] = load_stream(norm_w + step_h(kParkEnd + rr) + kStep);
-                }
+            for (int rr = 0; rr < Shape::kLiReg; ++rr) {
+                keep_nw[rr][0] = load_stream(norm_w + step_h(kParkEnd + rr));
+                keep_nw[rr][1] = load_stream(norm_w + step_h(kParkEnd + rr) + kStep);
             }
 #pragma unroll
             for (int i = Shape::kLiLds; i < kParkEnd && i < Shape::kLiLds + kDepth; ++i) load_parked(i);
         }
     }
 
-    __device__ __forceinline__ uint4 nw_at(const uint4 (&early)[2], int b, int h) const {
-        if constexpr (!kNorm) return uint4{};
-        return kNwEarly ? early[b] : load_stream(norm_w + h);
-    }
 
     __device__ __forceinline__ void put(int q, int h, const uint4& li, const uint4& nw, float r) {
         if (!valid[q]) return;
@@ -180,23 +172,19 @@ struct LayerInputEpilogue {
 #pragma unroll
         for (int i = 0; i < Shape::kLiLds; ++i) {
             const int h = step_h(i);
-            const uint4 nw0 = nw_at(lds_nw[kNwEarly ? i : 0], 0, h);
-            const uint4 nw1 = nw_at(lds_nw[kNwEarly ? i : 0], 1, h + kStep);
 #pragma unroll
             for (int q = 0; q < kGroups; ++q) {
-                put(q, h, lds_li(i, q, 0), nw0, r[q]);
-                put(q, h + kStep, lds_li(i, q, 1), nw1, r[q]);
+                put(q, h, lds_li(i, q, 0), lds_nw[i][0], r[q]);
+                put(q, h + kStep, lds_li(i, q, 1), lds_nw[i][1], r[q]);
             }
         }
 #pragma unroll
         for (int rr = 0; rr < Shape::kLiReg; ++rr) {
             const int h = step_h(kParkEnd + rr);
-            const uint4 nw0 = nw_at(keep_nw[kNwEarly ? rr : 0], 0, h);
-            const uint4 nw1 = nw_at(keep_nw[kNwEarly ? rr : 0], 1, h + kStep);
 #pragma unroll
             for (int q = 0; q < kGroups; ++q) {
-                put(q, h, keep_li(rr, q, 0), nw0, r[q]);
-                put(q, h + kStep, keep_li(rr, q, 1), nw1, r[q]);
+                put(q, h, keep_li(rr, q, 0), keep_nw[rr][0], r[q]);
+                put(q, h + kStep, keep_li(rr, q, 1), keep_nw[rr][1], r[q]);
             }
         }
         if constexpr (!kNorm) return;  // without norm_w the parked li already is the layer input
@@ -302,7 +290,7 @@ __global__ __launch_bounds__(512) void k_fused(
     // that waiting for them does not wait for those.
     CoefParams cp;
     if (wave == 0) cp = load_coef_params(scale, base, lane & 3);
-    LayerInputEpilogue<Shape, kWaves, 1, false, 2, kNorm> out{norm_w, {li_row}, {t < T}, wave, g};
+    LayerInputEpilogue<Shape, kWaves, 1, 3, kNorm> out{norm_w, {li_row}, {t < T}, wave, g};
     out.prefetch();
 
     // Partials of the 8 waves, combined in a fixed order.
@@ -488,7 +476,7 @@ __global__ __launch_bounds__(256) void k_fused_w4(
     // that waiting for them does not wait for those.
     CoefParams cp;
     if (wave < 2) cp = load_coef_params(scale, base, lane & 3);
-    LayerInputEpilogue<Shape, kWaves4, 2, true, 5, kNorm> out{
+    LayerInputEpilogue<Shape, kWaves4, 2, 5, kNorm> out{
         norm_w, {li_row[0], li_row[1]}, {valid[0], valid[1]}, wave, g};
     out.prefetch();
 
@@ -729,7 +717,7 @@ __global__ __launch_bounds__(512) void k_fused_pre(
         }
         cur = nxt;
     }
-    LayerInputEpilogue<PreShape, kWaves, 1, true, 5, kNorm> out{norm_w, {li_row}, {t < T}, wave, g};
+    LayerInputEpilogue<PreShape, kWaves, 1, 5, kNorm> out{norm_w, {li_row}, {t < T}, wave, g};
     out.prefetch();
     sq[wave][g][n] = ssq_li;
     __syncthreads();
@@ -907,7 +895,7 @@ __global__ __launch_bounds__(256) void k_fused_pre_w4(
     uint4 li_keep[Shape::kLiReg > 0 ? Shape::kLiReg : 1][2][2];
 #pragma unroll
     for (int r = 0; r < Shape::kLiReg; ++r) body(S - Shape::kLiReg + r, true, li_keep[r]);
-    LayerInputEpilogue<Shape, kWaves4, 2, true, 5, kNorm> out{
+    LayerInputEpilogue<Shape, kWaves4, 2, 5, kNorm> out{
         norm_w, {li_row[0], li_row[1]}, {valid[0], valid[1]}, wave, g};
     out.prefetch();
 
