@@ -151,8 +151,12 @@ SplitPlan split_plan(int T, int hidden, bool invariant, bool shifted) {
         if (resident > 0) {
             const long group_tiles = ceil_div(T, kTile * plan.groups);
             long best = -1;
+            // (the pre's four-group kernel takes whole 64-element steps: an even
+            // number of 32-element steps per wave)
+            const bool even = !shifted && plan.groups == 4;
             for (int s = 1; s <= max_spw; ++s) {
-                const int w = ceil_div(nsteps, 4 * s);
+                int w = ceil_div(nsteps, 4 * s);
+                if (even) w += w & 1;
                 const long rounds = (group_tiles * ceil_div(nsteps, 4 * w) + resident - 1) / resident;
                 const long cost = rounds * (w + kRoundCost);
                 if (best < 0 || cost < best) {

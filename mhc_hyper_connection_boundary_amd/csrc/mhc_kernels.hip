@@ -9,6 +9,9 @@
 //               X' and li, sums of squares, and the projection on the matrix
 //               cores.  The 4 waves' partials are combined in LDS in a fixed
 //               order and written as one record per (token, slice).
+//   k_partial_pre_wide  the non-shifted pre's four-group form with 64-element
+//               wave steps (both 64-byte halves of each 128-byte line per
+//               lane), for plans with an even number of 32-element steps.
 //   k_finish    one workgroup per (tile, hidden slice): sums the records of
 //               its tokens over the slices in slice order, forms rstd_li and
 //               rescales li into the layer input; it also computes pre /
@@ -191,6 +194,121 @@ __global__ __launch_bounds__(256) void k_partial(
             sum = 0.0f;
             for (int w = 0; w < 4; ++w)
                 for (int q = 0; q < 4; ++q) sum += sq[w][q][tn][v - 24];
+        }
+        const int tt = tile * kTok + tn;
+        if (tt < T) part[((size_t)tt * slices + slice) * kPart + v] = sum;
+    }
+}
+
+// Non-shifted partial kernel with 64-element wave steps: two 32-element
+// k-blocks per step, every lane reading both 64-byte halves of each 128-byte
+// line it touches, as in the fused kernels.  Launched for four token groups
+// and an even number of 32-element steps per wave (the slice then holds
+// whole 64-element steps); the records are the same as k_partial's, the order
+// of each lane's sums within the slice differs.  (With two groups it would
+// need 306 registers, one workgroup per CU instead of two, and measured
+// slower.)
+template <int G>
+__global__ __launch_bounds__(256) void k_partial_pre_wide(
+    int T, int hidden, int steps_per_wave, int slices, const uint16_t* __restrict__ X,
+    const uint4* __restrict__ wprep, float* __restrict__ part) {
+    constexpr int kTok = kTile * G;
+    __shared__ float red[4][kTok][24];
+    __shared__ float sq[4][4][kTok];
+
+    const int tile = blockIdx.x;
+    const int slice = blockIdx.y;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 15;
+    const int g = lane >> 4;
+    const uint16_t* Xrow[G];
+#pragma unroll
+    for (int q = 0; q < G; ++q) {
+        const int t = tile * kTok + 16 * q + n;
+        Xrow[q] = X + (size_t)(t < T ? t : T - 1) * 4 * hidden;
+    }
+
+    // The slice covers 32-element steps [first, last), both even: 64-element
+    // steps [first / 2, last / 2), wave w taking first / 2 + w, + 4, ...
+    const int nsteps = hidden / kStep;
+    const int first = slice * 4 * steps_per_wave;
+    const int last = min(first + 4 * steps_per_wave, nsteps);
+    const int wlast = last / 2;
+
+    f32x4_t acc[G][3];
+    float ssq[G];
+#pragma unroll
+    for (int q = 0; q < G; ++q) {
+#pragma unroll
+        for (int m = 0; m < 3; ++m) acc[q][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        ssq[q] = 0.0f;
+    }
+
+    auto load_w = [&](uint4 (&a)[2][4], int q, int ws) {
+        const int h = ws * 2 * kStep + g * 8;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            a[0][j] = *reinterpret_cast<const uint4*>(Xrow[q] + (size_t)j * hidden + h);
+            a[1][j] = *reinterpret_cast<const uint4*>(Xrow[q] + (size_t)j * hidden + h + kStep);
+        }
+    };
+    uint4 cur[G][2][4];
+    if (first / 2 + wave < wlast) {
+#pragma unroll
+        for (int q = 0; q < G; ++q) load_w(cur[q], q, first / 2 + wave);
+    }
+    for (int ws = first / 2 + wave; ws < wlast; ws += 4) {
+        uint4 A0[kFragsPerStep], A1[kFragsPerStep];
+        const uint4* wp = wprep + (size_t)(2 * ws) * kFragsPerStep * 64 + lane;
+#pragma unroll
+        for (int i = 0; i < kFragsPerStep; ++i) {
+            A0[i] = wp[i * 64];
+            A1[i] = wp[(kFragsPerStep + i) * 64];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        uint4 nxt[G][2][4];
+        if (ws + 4 < wlast) {
+#pragma unroll
+            for (int q = 0; q < G; ++q) load_w(nxt[q], q, ws + 4);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q = 0; q < G; ++q) {
+            square_sum(cur[q][0], ssq[q]);
+            square_sum(cur[q][1], ssq[q]);
+            mfma_step(A0, cur[q][0], acc[q]);
+            mfma_step(A1, cur[q][1], acc[q]);
+        }
+#pragma unroll
+        for (int q = 0; q < G; ++q)
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) cur[q][b][j] = nxt[q][b][j];
+    }
+
+    // Combine the 4 waves in a fixed order: waves ascending, lane groups ascending.
+#pragma unroll
+    for (int q = 0; q < G; ++q) {
+#pragma unroll
+        for (int m = 0; m < 3; ++m)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) red[wave][16 * q + n][8 * m + 2 * g + j] = mix_of(acc[q], m, j);
+        sq[wave][g][16 * q + n] = ssq[q];
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < kTok * 26; i += blockDim.x) {
+        const int tn = i / 26, v = i % 26;
+        float sum;
+        if (v < 24) {
+            sum = ((red[0][tn][v] + red[1][tn][v]) + red[2][tn][v]) + red[3][tn][v];
+        } else if (v == 24) {
+            sum = 0.0f;
+            for (int w = 0; w < 4; ++w)
+                for (int q = 0; q < 4; ++q) sum += sq[w][q][tn];
+        } else {
+            sum = 0.0f;
         }
         const int tt = tile * kTok + tn;
         if (tt < T) part[((size_t)tt * slices + slice) * kPart + v] = sum;
@@ -656,10 +774,18 @@ static void launch_partial_g(bool shifted, const SplitPlan& plan, int T, int hid
             hipLaunchKernelGGL((k_partial<true, G>), grid, dim3(256), 0, stream, T, hidden,
                                plan.steps_per_wave, plan.slices, x, X, post_prev, comb_prev,
                                pre_lag, w, xn_out, li_out, part);
-    } else
+    } else {
+        if constexpr (G == 4) {
+            if (plan.steps_per_wave % 2 == 0) {
+                hipLaunchKernelGGL((k_partial_pre_wide<G>), grid, dim3(256), 0, stream, T, hidden,
+                                   plan.steps_per_wave, plan.slices, X, w, part);
+                return;
+            }
+        }
         hipLaunchKernelGGL((k_partial<false, G>), grid, dim3(256), 0, stream, T, hidden,
                            plan.steps_per_wave, plan.slices, nullptr, X, nullptr, nullptr,
                            nullptr, w, nullptr, nullptr, part);
+    }
 }
 
 hipError_t launch_partial(bool shifted, const SplitPlan& plan, int T, int hidden,

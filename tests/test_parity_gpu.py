@@ -202,11 +202,13 @@ def test_boundary_fused_32_token_tiles(oracle, T, d, full):
 
 
 @pytest.mark.parametrize("kind,T,d", [("boundary", 2048 + 19, 7168), ("boundary", 1536 + 5, 7168),
-                                        ("pre", 1024 + 21, 4096), ("pre", 4096 + 11, 7168)])
+                                        ("pre", 1024 + 21, 4096), ("pre", 4096 + 11, 7168),
+                                        ("pre", 16384 + 5, 2048), ("pre", 6144 + 27, 5120)])
 def test_split_token_groups_ragged(oracle, kind, T, d):
     """At these sizes the split schedule's first kernel carries two 16-token
-    groups per wave (four for the pre at 4107 tokens); the last workgroup's
-    later groups are partly or wholly past the last token."""
+    groups per wave (four for the pre from 4107 tokens at d=7168, with
+    64-element wave steps); the last workgroup's later groups are partly or
+    wholly past the last token."""
     say(f"split two groups {kind} T={T} d={d}")
     inp = WL.make_inputs(WL.Config("g2", d=d, T=T, seed=T + 3 * d))
     dv = Dev(inp)
