@@ -269,6 +269,46 @@ __device__ __forceinline__ void comb_row(TokenCoef& o, const float* tot, int i,
     for (int k = 0; k < 4; ++k) o.row[k] = c[k];
 }
 
+// Rotations within a DPP row of 16 lanes.
+__device__ __forceinline__ float row_ror8(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                 0x128, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_ror4(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                 0x124, 0xF, 0xF, false));
+}
+
+// The Sinkhorn comb of one token on the 16 lanes of one DPP row (all 16 must
+// call it together): lane 4i + k owns element (i, k) and returns it.  Row
+// sums run (c0 + c1) + (c2 + c3) over the quad, column sums (r0 + r2) +
+// (r1 + r3) through rotations by 8 and 4 lanes; additions commute, so every
+// lane of a row or column gets the same bits.  The softmax's row maximum and
+// sum follow the same pattern.  Each iteration is a chain of about 10
+// instructions against about 30 when one lane owns a row.
+__device__ __forceinline__ float comb16(const float* tot, int lane16, float rstd, float s2,
+                                        float bcomb, const Scalars& p) {
+    const float v = __builtin_fmaf(tot[8 + lane16] * rstd, s2, bcomb);
+    float mx = fmaxf(v, quad_xor1(v));
+    mx = fmaxf(mx, quad_xor2(mx));
+    const float e = expf(v - mx);
+    float se = e + quad_xor1(e);
+    se = se + quad_xor2(se);
+    float c = __builtin_fmaf(e, recip(se), p.sinkhorn_eps);
+    for (int it = 0; it < p.sinkhorn_iters; ++it) {
+        // (the bare hardware reciprocal, as in comb_row)
+        if (it > 0) {
+            float r = c + quad_xor1(c);
+            r = r + quad_xor2(r);
+            c *= __builtin_amdgcn_rcpf(r + p.sinkhorn_eps);
+        }
+        float q = c + row_ror8(c);
+        q = q + row_ror4(q);
+        c *= __builtin_amdgcn_rcpf(q + p.sinkhorn_eps);
+    }
+    return c;
+}
+
 __device__ __forceinline__ TokenCoef coefficients(const float* tot, int i, int hidden,
                                                   const CoefParams& cp, const Scalars& p) {
     TokenCoef o;

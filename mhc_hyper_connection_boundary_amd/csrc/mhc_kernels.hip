@@ -359,8 +359,8 @@ __device__ __forceinline__ float slice_sum(const float* __restrict__ src, int fi
 
 // Remaining coefficient tokens of a workgroup (tokens hs + k*finish_slices,
 // k >= 1), when there are fewer than 16 rescale workgroups per tile: all at
-// once, one quad of wave 0 per token, with the same two-level slice order as
-// the first token.
+// once, 16 lanes per token, with the same two-level slice order and the same
+// comb arithmetic as the first token.
 __device__ __forceinline__ void finish_more_coefficients(
     int T, int hidden, int slices, int finish_slices, int tile, int hs, int tid,
     const float* __restrict__ part, const float* __restrict__ scale,
@@ -384,19 +384,22 @@ __device__ __forceinline__ void finish_more_coefficients(
         mtot[k][v] = sum;
     }
     __syncthreads();
-    if (tid < 4 * nk) {
-        const int k = tid >> 2, i = tid & 3;
+    if (tid < 16 * nk) {  // 16 lanes per token, as for the first token
+        const int k = tid >> 4, l16 = tid & 15, i = tid & 3;
         const int t = first + k * finish_slices;
         const CoefParams cp = load_coef_params(scale, base, i);
-        const TokenCoef o = coefficients(mtot[k], i, hidden, cp, p);
+        TokenCoef o;
+        pre_post(o, mtot[k], i, hidden, cp, p);
+        const float c = comb16(mtot[k], l16, o.rstd, cp.s2, base[8 + l16], p);
         if (t < T) {
-            pre_out[(size_t)t * 4 + i] = o.pre;
-            post_out[(size_t)t * 4 + i] = o.post;
-            *reinterpret_cast<float4*>(comb_out + (size_t)t * 16 + 4 * i) =
-                make_float4(o.row[0], o.row[1], o.row[2], o.row[3]);
-            if (mixes_out)
-                for (int kk = 0; kk < 6; ++kk) mixes_out[(size_t)t * 24 + 6 * i + kk] = mtot[k][6 * i + kk];
-            if (rstd_out && i == 0) rstd_out[t] = o.rstd;
+            comb_out[(size_t)t * 16 + l16] = c;
+            if (l16 < 4) {
+                pre_out[(size_t)t * 4 + i] = o.pre;
+                post_out[(size_t)t * 4 + i] = o.post;
+                if (mixes_out)
+                    for (int kk = 0; kk < 6; ++kk) mixes_out[(size_t)t * 24 + 6 * i + kk] = mtot[k][6 * i + kk];
+                if (rstd_out && i == 0) rstd_out[t] = o.rstd;
+            }
         }
     }
 }
@@ -434,6 +437,7 @@ __global__ __launch_bounds__(256) void k_finish(
     // batches of the slice sums.  Lanes without work read one shared address
     // (so their requests coalesce) and their results are dropped.
     const CoefParams cp = load_coef_params(scale, base, tid & 3);
+    const float bcomb = base[8 + (tid & 15)];
     const uint16_t* nw_src = norm_w ? norm_w : layer_input;
     uint4 li_v[2], nw_v[2];
     bool have[2];
@@ -479,19 +483,22 @@ __global__ __launch_bounds__(256) void k_finish(
         ctot[tid - 32] = sum;
     }
     __syncthreads();
-    // Phase 3: one quad of wave 0 runs the coefficients (Sinkhorn) of the
-    // first token while the other waves rescale li.
+    // Phase 3: 16 lanes of wave 0 run the coefficients of the first token (the
+    // Sinkhorn comb on all of them, pre / post on the first 4) while the other
+    // waves rescale li.
     auto emit_coef = [&](int t) {
-        const TokenCoef o = coefficients(ctot, tid, hidden, cp, p);
-        pre_out[(size_t)t * 4 + tid] = o.pre;
-        post_out[(size_t)t * 4 + tid] = o.post;
-        *reinterpret_cast<float4*>(comb_out + (size_t)t * 16 + 4 * tid) =
-            make_float4(o.row[0], o.row[1], o.row[2], o.row[3]);
-        if (mixes_out)
-            for (int k = 0; k < 6; ++k) mixes_out[(size_t)t * 24 + 6 * tid + k] = ctot[6 * tid + k];
-        if (rstd_out && tid == 0) rstd_out[t] = o.rstd;
+        TokenCoef o;
+        pre_post(o, ctot, tid & 3, hidden, cp, p);
+        comb_out[(size_t)t * 16 + tid] = comb16(ctot, tid, o.rstd, cp.s2, bcomb, p);
+        if (tid < 4) {
+            pre_out[(size_t)t * 4 + tid] = o.pre;
+            post_out[(size_t)t * 4 + tid] = o.post;
+            if (mixes_out)
+                for (int k = 0; k < 6; ++k) mixes_out[(size_t)t * 24 + 6 * tid + k] = ctot[6 * tid + k];
+            if (rstd_out && tid == 0) rstd_out[t] = o.rstd;
+        }
     };
-    if (coef_first && tid < 4) emit_coef(t_first);
+    if (coef_first && tid < 16) emit_coef(t_first);
 
     auto rescale = [&](int u, const uint4& li, const uint4& nw) {
         const int tn = u / chunks, cidx = u % chunks;
@@ -561,6 +568,7 @@ __global__ __launch_bounds__(512) void k_pre_finish(
     // wave 0 gathers the token's projection record.
     CoefParams cp;
     if (tid < 4) cp = load_coef_params(scale, base, tid);
+    const float comb_s2 = scale[2], comb_b = base[8 + (tid & 15)];  // (the comb's 16 lanes)
     uint4 bufA[4], bufB[4];
     auto load_chunk = [&](uint4 (&b)[4], int cidx) {
         if (cidx < nch) {
@@ -677,16 +685,18 @@ __global__ __launch_bounds__(512) void k_pre_finish(
             }
         }
     }
-    // Wave 0: the Sinkhorn comb, overlapping the layer-input work above.
-    if (tid < 4) {
-        comb_row(o, tot, tid, cp, p);
-        pre_out[(size_t)t * 4 + tid] = o.pre;
-        post_out[(size_t)t * 4 + tid] = o.post;
-        *reinterpret_cast<float4*>(comb_out + (size_t)t * 16 + 4 * tid) =
-            make_float4(o.row[0], o.row[1], o.row[2], o.row[3]);
-        if (mixes_out)
-            for (int k = 0; k < 6; ++k) mixes_out[(size_t)t * 24 + 6 * tid + k] = tot[6 * tid + k];
-        if (rstd_out && tid == 0) rstd_out[t] = o.rstd;
+    // Wave 0: the Sinkhorn comb on 16 lanes (rstd as pre_post forms it),
+    // overlapping the layer-input work above.
+    if (tid < 16) {
+        const float rstd = rsqrt_nr(tot[24] * (0.25f / (float)hidden) + p.rms_eps);
+        comb_out[(size_t)t * 16 + tid] = comb16(tot, tid, rstd, comb_s2, comb_b, p);
+        if (tid < 4) {
+            pre_out[(size_t)t * 4 + tid] = o.pre;
+            post_out[(size_t)t * 4 + tid] = o.post;
+            if (mixes_out)
+                for (int k = 0; k < 6; ++k) mixes_out[(size_t)t * 24 + 6 * tid + k] = tot[6 * tid + k];
+            if (rstd_out && tid == 0) rstd_out[t] = o.rstd;
+        }
     }
 }
 
