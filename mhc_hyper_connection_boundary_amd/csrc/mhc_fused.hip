@@ -12,6 +12,8 @@
 // k-blocks); wave w takes steps w, w + waves, ...  Every lane reads both
 // 64-byte halves of each 128-byte line it touches back to back, and the waves
 // together sweep contiguous kilobytes of every row, so HBM sees long runs.
+// k_fused_w4 goes further: each of its load instructions reads whole 128-byte
+// runs of 8 rows, and ds_bpermute moves the data into the matrix-core layout.
 // While a wave computes step i (residual update, X' store, lagged collapse,
 // sums of squares) the activations of step i+1 are in flight; the weight
 // fragments of step i come from L2 and feed the matrix cores.
@@ -76,6 +78,41 @@ __device__ __forceinline__ void load_act(Act& a, const uint16_t* __restrict__ Xr
     }
     a.x[0] = load_stream(xrow + h);
     a.x[1] = load_stream(xrow + h + kStep);
+}
+
+// Row-layout activations of one wave step: instruction i, stream j: lane L
+// holds row 8i + L/8 of the token group, bytes 16(L%8) of the step's 128-byte
+// run, so each load instruction reads 8 rows x 128 bytes; HBM serves such
+// runs faster than 16 rows x 64 bytes (a plain mover: 4.91 against
+// 4.60 TB/s).
+struct ActRows {
+    uint4 X[2][4];  // [instruction][stream]
+    uint4 x[2];
+};
+
+template <int kHidden>
+__device__ __forceinline__ void load_rows(ActRows& a, const uint16_t* __restrict__ X,
+                                          const uint16_t* __restrict__ x, const int (&tok)[2], int hl) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const uint16_t* Xr = X + (size_t)tok[i] * (4 * kHidden) + hl;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) a.X[i][j] = load_stream(Xr + j * kHidden);
+        a.x[i] = load_stream(x + (size_t)tok[i] * kHidden + hl);
+    }
+}
+
+// Lane (g, n) of block b takes chunk 4b + g of row n: from instruction n / 8,
+// lane 8(n % 8) + 4b + g.
+__device__ __forceinline__ uint4 rows_to_mfma(const uint4& r0, const uint4& r1, int idx, bool hi) {
+    uint4 o;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int v0 = __builtin_amdgcn_ds_bpermute(idx, (int)word(r0, k));
+        const int v1 = __builtin_amdgcn_ds_bpermute(idx, (int)word(r1, k));
+        set_word(o, k, (uint32_t)(hi ? v1 : v0));
+    }
+    return o;
 }
 
 __device__ __forceinline__ void load_frags(uint4 (&A)[kFragsPerStep], const uint4* __restrict__ wprep,
@@ -393,8 +430,6 @@ __global__ __launch_bounds__(256) void k_fused_w4(
     size_t tc[2];
     bool valid[2];
     PrevCoef c[2];
-    const uint16_t* Xrow[2];
-    const uint16_t* xrow[2];
     uint16_t* li_row[2];
     uint16_t* xn_row[2];
 #pragma unroll
@@ -405,8 +440,6 @@ __global__ __launch_bounds__(256) void k_fused_w4(
         valid[q] = t < t_end;
         tc[q] = valid[q] ? (size_t)t : (size_t)(t_end - 1);
         load_prev(c[q], post_prev, comb_prev, pre_lag, tc[q]);
-        Xrow[q] = X + tc[q] * 4 * hidden;
-        xrow[q] = x + tc[q] * hidden;
         li_row[q] = layer_input + tc[q] * hidden;
         xn_row[q] = xn_out + tc[q] * 4 * hidden;
     }
@@ -419,10 +452,24 @@ __global__ __launch_bounds__(256) void k_fused_w4(
     float ssq[2] = {0.0f, 0.0f}, ssq_li[2] = {0.0f, 0.0f};
 
     // Wave w takes steps w, w + 4, ...: the 4 waves cover 256 contiguous
-    // hidden elements of every row of the tile at a time.
-    Act cur[2];
+    // hidden elements of every row of the tile at a time.  The activations
+    // are loaded in row layout (8 rows x 128 bytes per instruction) and moved
+    // into the matrix-core layout with ds_bpermute just before use: lane L
+    // loads row 8i + L/8 (tokens clamped to the tile's last one, as above).
+    int tok[2][2];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) load_act(cur[q], Xrow[q], xrow[q], hidden, wave * kWide + g * 8);
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int t = t0 + 16 * q + 8 * i + (lane >> 3);
+            tok[q][i] = t < t_end ? t : t_end - 1;
+        }
+    const int hl0 = (lane & 7) * 8;
+    const int pidx[2] = {(8 * (n & 7) + g) * 4, (8 * (n & 7) + 4 + g) * 4};
+    const bool phi = n >= 8;
+    ActRows cur[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) load_rows<hidden>(cur[q], X, x, tok[q], wave * kWide + hl0);
     // One wave step.  keep: li stays in the caller's registers (last steps);
     // otherwise it waits in LDS (first steps) or in the layer-input buffer.
     auto body = [&](int i, bool keep, uint4 (&li)[2][2]) {
@@ -432,18 +479,23 @@ __global__ __launch_bounds__(256) void k_fused_w4(
         load_frags(A0, wprep, 2 * step, lane);
         load_frags(A1, wprep, 2 * step + 1, lane);
         __builtin_amdgcn_sched_barrier(0);
-        Act nxt[2];
+        ActRows nxt[2];
         if (i + 1 < S) {
 #pragma unroll
-            for (int q = 0; q < 2; ++q) load_act(nxt[q], Xrow[q], xrow[q], hidden, h + kWaves4 * kWide);
+            for (int q = 0; q < 2; ++q) load_rows<hidden>(nxt[q], X, x, tok[q], step * kWide + hl0 + kWaves4 * kWide);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             uint4 Xn[2][4];
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
-                update_collapse(cur[q].X[b], cur[q].x[b], c[q], Xn[b], li[q][b], ssq[q], ssq_li[q]);
+            for (int b = 0; b < 2; ++b) {
+                uint4 Xs[4], xs;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) Xs[j] = rows_to_mfma(cur[q].X[0][j], cur[q].X[1][j], pidx[b], phi);
+                xs = rows_to_mfma(cur[q].x[0], cur[q].x[1], pidx[b], phi);
+                update_collapse(Xs, xs, c[q], Xn[b], li[q][b], ssq[q], ssq_li[q]);
+            }
 #pragma unroll
             for (int s2 = 0; s2 < 4; ++s2) {
                 store_stream(xn_row[q] + (size_t)s2 * hidden + h, Xn[0][s2]);
