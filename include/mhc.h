@@ -41,6 +41,9 @@
  *     surface at the caller's next synchronisation.
  *   - Results are deterministic: every reduction runs in a fixed order, so
  *     equal inputs give bitwise-equal outputs from call to call.
+ *   - An empty batch (tokens == 0) is a no-op: once the parameters and
+ *     `hidden` pass their checks the call returns MHC_OK without reading any
+ *     pointer (they may be NULL) and without enqueueing anything.
  */
 #ifndef MHC_H
 #define MHC_H
@@ -61,7 +64,7 @@ extern "C" {
 
 typedef enum {
     MHC_OK = 0,
-    MHC_ERR_INVALID_ARGUMENT = 1, /* tokens <= 0, NULL required pointer, iters < 1, eps < 0 */
+    MHC_ERR_INVALID_ARGUMENT = 1, /* tokens < 0, NULL required pointer, iters < 1, eps < 0 */
     MHC_ERR_UNSUPPORTED_SHAPE = 2,/* hidden % 256 != 0, hidden outside [256, 16384], tokens > MHC_MAX_TOKENS */
     MHC_ERR_MISALIGNED = 3,       /* a pointer not 16-byte aligned */
     MHC_ERR_ALIASING = 4,         /* an output overlaps another output or an input */
@@ -131,7 +134,7 @@ size_t mhc_prepared_weight_bytes(int hidden);
 /* Device workspace bytes that mhc_pre / mhc_boundary need for `tokens`
  * tokens of `hidden` under every schedule (partial sums of the split kernels:
  * 128 bytes per token per 128 elements of hidden, T * hidden bytes in all). */
-size_t mhc_workspace_bytes(int tokens, int hidden);
+size_t mhc_workspace_bytes(int tokens, int hidden);  /* 0 for tokens == 0 or an invalid shape */
 
 /* Round W to TF32, split it into BF16 high/low parts and write them in the
  * layout above.  (prepare_boundary_weight on the vLLM page.)

@@ -239,11 +239,12 @@ mhc_status mhc_pre_mixes(int tokens, int hidden, int splits, const uint16_t* res
                          void* stream) {
     mhc_status st = check_params(params);
     if (st != MHC_OK) return st;
-    if (tokens <= 0 || splits < 1 || splits > 64) return MHC_ERR_INVALID_ARGUMENT;
+    if (tokens < 0 || splits < 1 || splits > 64) return MHC_ERR_INVALID_ARGUMENT;
+    if (tokens > MHC_MAX_TOKENS || !shape_ok(hidden)) return MHC_ERR_UNSUPPORTED_SHAPE;
+    if (tokens == 0) return MHC_OK;
     if (!residual || !dot_mix || !sqrsum || !scale || !base || !layer_input || !pre || !post ||
         !comb)
         return MHC_ERR_INVALID_ARGUMENT;
-    if (tokens > MHC_MAX_TOKENS || !shape_ok(hidden)) return MHC_ERR_UNSUPPORTED_SHAPE;
     const void* ptrs[] = {residual, dot_mix, sqrsum, scale, base, norm_w, layer_input, pre, post,
                           comb};
     for (const void* q : ptrs)
@@ -272,9 +273,11 @@ mhc_status mhc_prefetch_weight(const void* w_prepared, int hidden, void* stream)
 mhc_status mhc_post(int tokens, int hidden, const uint16_t* x, const uint16_t* residual,
                     const float* post_prev, const float* comb_prev, uint16_t* residual_out,
                     void* stream) {
-    if (tokens <= 0 || !x || !residual || !post_prev || !comb_prev || !residual_out)
-        return MHC_ERR_INVALID_ARGUMENT;
+    if (tokens < 0) return MHC_ERR_INVALID_ARGUMENT;
     if (tokens > MHC_MAX_TOKENS || !shape_ok(hidden)) return MHC_ERR_UNSUPPORTED_SHAPE;
+    if (tokens == 0) return MHC_OK;
+    if (!x || !residual || !post_prev || !comb_prev || !residual_out)
+        return MHC_ERR_INVALID_ARGUMENT;
     const void* ptrs[] = {x, residual, post_prev, comb_prev, residual_out};
     for (const void* q : ptrs)
         if (!aligned(q)) return MHC_ERR_MISALIGNED;
@@ -296,10 +299,13 @@ mhc_status mhc_pre(int tokens, int hidden, const uint16_t* residual, const void*
                    size_t workspace_bytes, void* stream) {
     mhc_status st = check_params(params);
     if (st != MHC_OK) return st;
-    if (tokens <= 0) return MHC_ERR_INVALID_ARGUMENT;
+    if (tokens < 0) return MHC_ERR_INVALID_ARGUMENT;
+    if (tokens > MHC_MAX_TOKENS || !shape_ok(hidden)) return MHC_ERR_UNSUPPORTED_SHAPE;
+    if (params->schedule == MHC_SCHEDULE_FUSED && !fused_supported(hidden))
+        return MHC_ERR_UNSUPPORTED_SHAPE;
+    if (tokens == 0) return MHC_OK;
     if (!residual || !w_prepared || !scale || !base || !layer_input || !pre || !post || !comb)
         return MHC_ERR_INVALID_ARGUMENT;
-    if (tokens > MHC_MAX_TOKENS || !shape_ok(hidden)) return MHC_ERR_UNSUPPORTED_SHAPE;
     const void* ptrs[] = {residual, w_prepared, scale, base, norm_w, layer_input, pre, post,
                           comb, mixes, rstd, workspace};
     for (const void* q : ptrs)
@@ -345,11 +351,14 @@ mhc_status mhc_boundary(int tokens, int hidden, const uint16_t* x, const uint16_
                         void* workspace, size_t workspace_bytes, void* stream) {
     mhc_status st = check_params(params);
     if (st != MHC_OK) return st;
-    if (tokens <= 0) return MHC_ERR_INVALID_ARGUMENT;
+    if (tokens < 0) return MHC_ERR_INVALID_ARGUMENT;
+    if (tokens > MHC_MAX_TOKENS || !shape_ok(hidden)) return MHC_ERR_UNSUPPORTED_SHAPE;
+    if (params->schedule == MHC_SCHEDULE_FUSED && !fused_supported(hidden))
+        return MHC_ERR_UNSUPPORTED_SHAPE;
+    if (tokens == 0) return MHC_OK;
     if (!x || !residual || !post_prev || !comb_prev || !pre_lag || !w_prepared || !scale ||
         !base || !residual_out || !layer_input || !pre_out || !post_out || !comb_out)
         return MHC_ERR_INVALID_ARGUMENT;
-    if (tokens > MHC_MAX_TOKENS || !shape_ok(hidden)) return MHC_ERR_UNSUPPORTED_SHAPE;
     const void* ptrs[] = {x, residual, post_prev, comb_prev, pre_lag, w_prepared, scale, base,
                           norm_w, residual_out, layer_input, pre_out, post_out, comb_out,
                           mixes, rstd, workspace};

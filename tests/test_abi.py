@@ -86,7 +86,6 @@ def call(L, b, **over):
 
 def test_boundary_refusals(L):
     b = Buffers(L)
-    assert call(L, b, T=0) == INVALID
     assert call(L, b, T=-3) == INVALID
     assert call(L, b, x=0) == INVALID
     assert call(L, b, li=0) == INVALID
@@ -120,7 +119,6 @@ def test_pre_refusals(L):
                          P(a["base"]), None, prm, P(li) if li else None, P(a["pre_out"]),
                          P(a["post_out"]), P(a["comb_out"]), None, None,
                          P(ws) if ws else None, wsb, None)
-    assert pre(T=0) == INVALID
     assert pre(residual=0) == INVALID
     assert pre(d=300) == SHAPE
     assert pre(li=a["li"] + 4) == MISALIGNED
@@ -145,7 +143,6 @@ def test_post_refusals(L):
     def post(T=T, d=D, x=a["x"], res=a["residual"], out=a["res_out"]):
         return L.mhc_post(T, d, P(x) if x else None, P(res), P(a["post"]), P(a["comb"]),
                           P(out) if out else None, None)
-    assert post(T=0) == INVALID
     assert post(x=0) == INVALID
     assert post(out=0) == INVALID
     assert post(d=1000) == SHAPE
@@ -165,7 +162,6 @@ def test_pre_mixes_refusals(L):
         return L.mhc_pre_mixes(T, d, S, P(res) if res else None, P(dm) if dm else None, P(sq),
                                P(a["scale"]), P(a["base"]), None, prm, P(li), P(a["pre_out"]),
                                P(a["post_out"]), P(a["comb_out"]), None)
-    assert pm(T=0) == INVALID
     assert pm(S=0) == INVALID
     assert pm(S=65) == INVALID
     assert pm(dm=0) == INVALID
@@ -181,3 +177,31 @@ def test_prefetch_weight_refusals(L):
     assert L.mhc_prefetch_weight(None, 1024, None) == INVALID
     assert L.mhc_prefetch_weight(P(GB), 1000, None) == SHAPE
     assert L.mhc_prefetch_weight(P(GB + 8), 1024, None) == MISALIGNED
+
+
+def test_empty_batch_is_a_noop(L):
+    """tokens == 0 returns OK once the parameters and hidden pass their checks,
+    reading no pointer (all NULL here) and enqueueing nothing."""
+    prm = ctypes.byref(api.params())
+    bad = ctypes.byref(api.params(sinkhorn_iters=0))
+    N = None
+
+    def boundary(d=D, p=prm):
+        return L.mhc_boundary(0, d, *([N] * 9), p, *([N] * 8), 0, N)
+
+    def pre(d=D, p=prm):
+        return L.mhc_pre(0, d, *([N] * 5), p, *([N] * 7), 0, N)
+
+    assert boundary() == OK
+    assert pre() == OK
+    assert L.mhc_post(0, D, *([N] * 6)) == OK
+    assert L.mhc_pre_mixes(0, D, 1, *([N] * 6), prm, *([N] * 5)) == OK
+    # the checks that do not depend on the batch still apply
+    assert boundary(d=300) == SHAPE and pre(d=300) == SHAPE
+    assert L.mhc_post(0, 300, *([N] * 6)) == SHAPE
+    assert boundary(p=bad) == INVALID and pre(p=bad) == INVALID
+    assert L.mhc_pre_mixes(0, D, 0, *([N] * 6), prm, *([N] * 5)) == INVALID
+    assert boundary(p=N) == INVALID
+    fused = ctypes.byref(api.params(schedule="fused"))
+    assert boundary(d=1280, p=fused) == SHAPE and pre(d=1280, p=fused) == SHAPE
+    assert boundary(d=1024, p=fused) == OK

@@ -323,6 +323,26 @@ def test_boundary_special_cases(oracle):
     np.testing.assert_allclose(g["comb"], 0.25, atol=1e-6)
 
 
+@pytest.mark.parametrize("schedule", ["auto", "split", "fused", "invariant"])
+def test_empty_batch(oracle, schedule):
+    """T = 0 is a no-op on every entry point: empty outputs, no error, and the
+    next call on the same buffers is unaffected."""
+    say(f"empty batch {schedule}")
+    inp = WL.make_inputs(WL.Config("empty", d=1024, T=8, seed=31))
+    dv = Dev(inp)
+    prm = dv.prm(schedule=schedule)
+    r = api.boundary(dv.x[:0], dv.X[:0], dv.post[:0], dv.comb[:0], dv.pre_lag[:0], dv.wp,
+                     dv.scale, dv.base, dv.norm_w, prm=prm, debug=True)
+    p = api.pre(dv.X[:0], dv.wp, dv.scale, dv.base, dv.norm_w, prm=prm, debug=True)
+    q = api.post(dv.x[:0], dv.X[:0], dv.post[:0], dv.comb[:0])
+    m = api.pre_mixes(dv.X[:0], torch.zeros(2, 0, 24, device="cuda"),
+                      torch.zeros(2, 0, device="cuda"), dv.scale, dv.base, dv.norm_w, prm=prm)
+    torch.cuda.synchronize()
+    for t in (*r, *p, q, *m):
+        assert t.shape[0] == 0
+    compare(dv.boundary(schedule=schedule), oracle.boundary(inp), label=f"after empty {schedule}")
+
+
 @pytest.mark.parametrize("schedule", ["auto", "fused"])
 @pytest.mark.parametrize("name", ["decode", "decode_wave"])
 def test_boundary_decode_configs(oracle, name, schedule):
