@@ -62,6 +62,12 @@ extern "C" {
 #define MHC_MIN_HIDDEN 256
 #define MHC_MAX_HIDDEN 16384
 
+/* Status codes.  The refusals mirror the ones of mhc_shifted_post_pre_boundary
+ * on the vLLM page, which returns None for a token count out of range or for a
+ * tensor that is not contiguous or not 16-byte aligned; here each cause has a
+ * code of its own and nothing is enqueued.  MHC_ERR_WORKSPACE has no
+ * counterpart there (that kernel keeps its partial sums on chip): it sits at
+ * 5, so MHC_ERR_DEVICE is 6. */
 typedef enum {
     MHC_OK = 0,
     MHC_ERR_INVALID_ARGUMENT = 1, /* tokens < 0, NULL required pointer, iters < 1, eps < 0 */
@@ -116,6 +122,8 @@ typedef struct {
 } mhc_params;
 
 /* Bytes of the prepared weight for `hidden`: 384 * hidden (0 if unsupported).
+ * The counterpart of boundary_weight_shape on the vLLM page (the size of
+ * prepare_boundary_weight's output), for the layout below.
  *
  * Layout (uint16 BF16 elements).  Element (step, s, m, l, e) with
  * step in [0, hidden/32), s in [0,4), m in [0,3), l in [0,64), e in [0,8) sits at
@@ -133,7 +141,11 @@ size_t mhc_prepared_weight_bytes(int hidden);
 
 /* Device workspace bytes that mhc_pre / mhc_boundary need for `tokens`
  * tokens of `hidden` under every schedule (partial sums of the split kernels:
- * 128 bytes per token per 128 elements of hidden, T * hidden bytes in all). */
+ * 128 bytes per token per 128 elements of hidden, T * hidden bytes in all).
+ * The vLLM page's kernel reduces a token's partial sums over its 16-CTA
+ * cluster on chip (module description: fixed-order reductions; the kernel's
+ * "totals in rank order"); the split schedules here pass them between
+ * workgroups through this workspace instead. */
 size_t mhc_workspace_bytes(int tokens, int hidden);  /* 0 for tokens == 0 or an invalid shape */
 
 /* Round W to TF32, split it into BF16 high/low parts and write them in the
@@ -220,7 +232,7 @@ mhc_status mhc_post(int tokens, int hidden, const uint16_t* x, const uint16_t* r
  * Errors: INVALID_ARGUMENT (NULL), UNSUPPORTED_SHAPE, MISALIGNED, DEVICE. */
 mhc_status mhc_prefetch_weight(const void* w_prepared, int hidden, void* stream);
 
-/* Static text for a status code. */
+/* Static text for a status code (the refusal causes listed with mhc_status). */
 const char* mhc_status_string(mhc_status status);
 
 /* MHC_ABI_VERSION of the loaded library. */

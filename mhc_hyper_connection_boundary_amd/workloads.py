@@ -18,7 +18,8 @@ BF16 arrays are returned as their uint16 bit patterns.
 
 Draw order (fixed, one ``numpy.random.default_rng(seed)`` stream):
 X, x, post_prev, comb_prev mixture weights, pre_lag, W, base, norm_w noise,
-then the stress permutation.
+then the stress permutation, then (routed comb_prev family only) the dominant
+permutation of every token.
 """
 from __future__ import annotations
 
@@ -47,6 +48,10 @@ class Config:
     eps: float = 1e-6         # pre eps and Sinkhorn eps
     rms_eps: float = 1e-6     # mix RMS eps and layer-input RMSNorm eps
     post_mult: float = 2.0
+    scale: tuple = (0.01, 0.01, 0.01)  # per-group scales: pre, post, comb
+    comb_family: str = "mixture"  # "mixture": Dirichlet(1) weights over the 24
+                                  # permutations; "routed": 0.9 on one permutation
+                                  # per token plus 0.1 of such a mixture
 
 
 CONFIGS = {
@@ -112,6 +117,17 @@ def _doubly_stochastic(rng: np.random.Generator, T: int) -> np.ndarray:
     return m.astype(np.float32)
 
 
+def _routed(rng: np.random.Generator, mixture: np.ndarray) -> np.ndarray:
+    """Strongly routed doubly stochastic matrices: 0.9 of one permutation
+    matrix (drawn per token) plus 0.1 of the given mixture, so most of each
+    destination stream comes from one source stream."""
+    T = mixture.shape[0]
+    pick = rng.integers(0, len(_PERMS), size=T)
+    m = np.zeros((T, N_HC, N_HC), dtype=np.float64)
+    m[np.arange(T)[:, None], np.arange(N_HC)[None, :], _PERMS[pick]] = 1.0
+    return (0.9 * m + 0.1 * mixture.astype(np.float64)).astype(np.float32)
+
+
 def make_inputs(cfg: Config | str, T: int | None = None) -> Inputs:
     """Draw one input set.  ``T`` overrides the token count (same recipe)."""
     if isinstance(cfg, str):
@@ -126,7 +142,8 @@ def make_inputs(cfg: Config | str, T: int | None = None) -> Inputs:
     comb_prev = _doubly_stochastic(rng, T)
     pre_lag = rng.uniform(0.0, 1.0, size=(T, N_HC)).astype(np.float32)
     W = (rng.standard_normal((MIXES, N_HC * d)) / np.sqrt(N_HC * d)).astype(np.float32)
-    scale = np.full(3, 0.01, dtype=np.float32)
+    scale = np.array(cfg.scale, dtype=np.float32)
+    assert scale.shape == (3,)
     base = (rng.standard_normal(MIXES) * 0.1).astype(np.float32)
     if cfg.norm == "ones":
         norm_w = np.ones(d, dtype=np.float32)
@@ -138,6 +155,10 @@ def make_inputs(cfg: Config | str, T: int | None = None) -> Inputs:
         k = -(-T // 100)  # ceil(1% of T)
         X[perm[:k]] *= np.float32(1e3)
         X[perm[k:2 * k]] *= np.float32(1e-3)
+    if cfg.comb_family == "routed":
+        comb_prev = _routed(rng, comb_prev)
+    else:
+        assert cfg.comb_family == "mixture", cfg.comb_family
     inp = Inputs(cfg, to_bf16_bits(X), to_bf16_bits(x), post_prev, comb_prev,
                  pre_lag, W, scale, base, to_bf16_bits(norm_w))
     _check_no_subnormals(inp)

@@ -573,3 +573,108 @@ def test_pre_from_mixes_fresh_pre_selects_stream(oracle):
     base[:4] = [-200.0, -200.0, 40.0, -200.0]
     r = oracle.pre_from_mixes(inp.X, dm, sq, scale, base, None, dict(PARAMS, pre_eps=0.0))
     assert np.array_equal(r["layer_input"], inp.X[:, 2])
+
+
+# ---- coefficient groups: which scale and which mix row feeds which output --------
+
+def _closed_pre_post(base, eps):
+    """pre = sigmoid(base) + eps and post = 2 sigmoid(base) for the bases used below
+    (0 -> 1/2, ln 3 -> 3/4, -ln 3 -> 1/4)."""
+    sig = {0.0: 0.5, float(np.float32(math.log(3.0))): 0.75, float(np.float32(-math.log(3.0))): 0.25}
+    return (np.array([sig[float(b)] for b in base[:4]]) + eps,
+            2.0 * np.array([sig[float(b)] for b in base[4:8]]))
+
+
+@pytest.mark.parametrize("group", [0, 1, 2])
+def test_each_scale_drives_only_its_own_group(oracle, group):
+    """Only scale[group] nonzero: the other two groups do not see the residual.
+    Their outputs are the same for every token and equal the scale-0 closed
+    forms (pre = sigmoid(base) + eps, post = 2 sigmoid(base), comb = Sinkhorn of
+    the bases alone), while group `group` differs from token to token.  Any
+    permutation of the three scales fails one of the three cases."""
+    inp = _tiny(T=6, seed=41)
+    l3 = float(np.float32(math.log(3.0)))
+    inp.base[:8] = [0.0, l3, -l3, 0.0, l3, 0.0, -l3, l3]
+    inp.scale[:] = 0.0
+    inp.scale[group] = 2.0
+    r = oracle.boundary(inp)
+    eps = float(np.float32(1e-6))
+    want_pre, want_post = _closed_pre_post(inp.base, eps)
+    comb0 = oracle.run(True, inp.X[:1], inp.x[:1], inp.post_prev[:1], inp.comb_prev[:1],
+                       inp.pre_lag[:1], inp.W, np.zeros(3, np.float32), inp.base, inp.norm_w,
+                       inp.params())["comb"][0]
+    spread = lambda a: np.abs(a - a[:1]).max()
+    if group != 0:
+        np.testing.assert_allclose(r["pre"], np.broadcast_to(want_pre, r["pre"].shape), atol=1e-15)
+    else:
+        assert spread(r["pre"]) > 1e-3
+    if group != 1:
+        np.testing.assert_allclose(r["post"], np.broadcast_to(want_post, r["post"].shape), atol=1e-15)
+    else:
+        assert spread(r["post"]) > 1e-3
+    if group != 2:
+        assert np.array_equal(r["comb"], np.broadcast_to(comb0, r["comb"].shape))
+    else:
+        assert spread(r["comb"]) > 1e-3
+
+
+def test_comb_logits_are_row_major_bases_through_coefficients(oracle):
+    """scale = 0, Sinkhorn eps 0 and many passes: the new comb is the doubly
+    stochastic scaling of exp(B) with B[i][k] = base[8 + 4i + k] (Sinkhorn's
+    theorem, solved independently by a root finder).  The bases are far from
+    symmetric, so reading them transposed lands on the transpose and fails."""
+    inp = _tiny(T=2, seed=42)
+    inp.scale[:] = 0.0
+    B = np.array([[0.0, 1.5, -0.5, 2.0], [-1.0, 0.3, 1.2, 0.0],
+                  [0.7, -2.0, 0.0, 0.4], [1.1, 0.2, -0.8, -1.5]], np.float32)
+    inp.base[8:] = B.ravel()
+    p = dict(PARAMS, sinkhorn_eps=0.0, sinkhorn_iters=3000)
+    r = oracle.run(True, inp.X, inp.x, inp.post_prev, inp.comb_prev, inp.pre_lag, inp.W,
+                   inp.scale, inp.base, inp.norm_w, p)
+    want = _doubly_stochastic_scaling(np.exp(B.astype(np.float64)))
+    assert np.abs(want - want.T).max() > 0.05
+    for t in range(inp.T):
+        np.testing.assert_allclose(r["comb"][t], want, atol=1e-9)
+
+
+def test_mix_rows_and_scales_reach_their_coefficients(oracle):
+    """X' = c everywhere and every row n of W a constant w_n (exact in TF32), rms
+    eps 0: mix_n * rstd = sign(c) * 4d * w_n exactly.  With distinct scales
+    (0.5, 0.25, 0.125) and zero bases, pre_j = sigmoid(0.5 sign(c) 4d w_j) + eps,
+    post_j = 2 sigmoid(0.25 sign(c) 4d w_{4+j}), and with Sinkhorn eps 0 and
+    many passes the comb is the doubly stochastic scaling of exp(L), L[i][k] =
+    0.125 sign(c) 4d w_{8+4i+k} (root finder).  A swapped scale, a shifted mix
+    row or a transposed comb logit each fail."""
+    c = -0.75
+    inp = _constant_xn(_tiny(T=2, seed=43), c)
+    d = inp.d
+    k = np.array([3, -5, 7, 1, -2, 6, -7, 4, 5, -3, 8, 0, -6, 2, -1, 7,
+                  -8, 3, 1, -4, 6, -2, 0, 5], np.float64)
+    w = k / (4.0 * d)                       # 4d w_n = k_n: exact in FP32 and TF32
+    inp.W[:] = w[:, None].astype(np.float32)
+    inp.scale[:] = [0.5, 0.25, 0.125]
+    inp.base[:] = 0.0
+    p = dict(PARAMS, rms_eps=0.0, sinkhorn_eps=0.0, sinkhorn_iters=3000)
+    r = oracle.run(True, inp.X, inp.x, inp.post_prev, inp.comb_prev, inp.pre_lag, inp.W,
+                   inp.scale, inp.base, None, p)
+    s = -1.0                                # sign(c)
+    sig = lambda v: 1.0 / (1.0 + np.exp(-v))
+    eps = float(np.float32(1e-6))
+    np.testing.assert_allclose(r["mixes"][0], c * 4 * d * w, rtol=1e-15, atol=1e-15)
+    np.testing.assert_allclose(r["pre"][0], sig(0.5 * s * k[:4]) + eps, rtol=1e-14)
+    np.testing.assert_allclose(r["post"][0], 2.0 * sig(0.25 * s * k[4:8]), rtol=1e-14)
+    L = 0.125 * s * k[8:].reshape(4, 4)
+    want = _doubly_stochastic_scaling(np.exp(L))
+    assert np.abs(want - want.T).max() > 0.05
+    np.testing.assert_allclose(r["comb"][0], want, atol=1e-9)
+
+
+def test_routed_previous_comb_is_doubly_stochastic():
+    """The routed comb_prev family: positive, rows and columns sum to 1 (up to
+    FP32 rounding), and one entry per row carries at least 0.9."""
+    inp = WL.make_inputs(WL.Config("routed", d=256, T=64, seed=5, comb_family="routed"))
+    cp = inp.comb_prev.astype(np.float64)
+    assert np.all(cp > 0)
+    np.testing.assert_allclose(cp.sum(1), 1.0, atol=1e-6)
+    np.testing.assert_allclose(cp.sum(2), 1.0, atol=1e-6)
+    assert np.all(cp.max(2) >= 0.9)

@@ -8,8 +8,9 @@ max(|o|, rms of the token's mixes); rstd relative error <= 2e-5; pre / post /
 comb absolute error <= 1e-5.  The non-shifted pre collapses with the pre it has
 just computed, FP32 here and FP64 in the oracle: its layer input is held to the
 bound that this difference carries through the collapse (fresh_pre_bound).
-Full-size configurations compare sampled tokens (the oracle is per token) on the
-full GPU launch.
+Every comparison covers every token of the launch, the full-size configurations
+included; each prints its largest errors and, for the fresh-pre layer input, the
+fraction of bit-identical elements.
 """
 import numpy as np
 import pytest
@@ -22,6 +23,9 @@ pytestmark = pytest.mark.gpu
 
 MIX_TOL = 2e-5
 COEF_TOL = 1e-5
+# Fraction of the fresh-pre layer input that must be bit-identical to the
+# oracle's (the rest lies within the derived bound of fresh_pre_bound).
+FRESH_EXACT_FLOOR = 0.9
 
 
 def say(msg):
@@ -114,7 +118,8 @@ def check_fresh_layer_input(g_li, g_pre, o, X_bits, norm_w_bits, label=""):
     excess = np.abs(a - b) - bound
     assert excess.max() <= 0, f"{label} layer_input off by {excess.max():.3g} beyond the bound"
     exact = float((g_li == o["layer_input"]).mean())
-    assert exact >= 0.9, f"{label} only {exact:.3f} of the layer input is bit-identical"
+    assert exact >= FRESH_EXACT_FLOOR, \
+        f"{label} only {exact:.4f} of the layer input is bit-identical"
     return exact
 
 
@@ -126,25 +131,33 @@ def compare(g, o, tokens=None, xn=True, label="", fresh=None):
         gx = g["xn"][sel]
         bad = gx != o["xn"]
         assert not bad.any(), f"{label} X' differs at {np.argwhere(bad)[:5]}"
+    st = {}
     if fresh is None:
         d = ulp_distance(g["layer_input"][sel], o["layer_input"])
+        st["layer_input_max_ulp"] = int(d.max()) if d.size else 0
         assert d.max() <= 1, f"{label} layer_input ulp distance {d.max()}"
     else:
         Xb, nw = fresh
-        exact = check_fresh_layer_input(g["layer_input"][sel], g["pre"][sel], o, Xb[sel], nw,
-                                        label)
+        st["fresh_layer_input_exact"] = check_fresh_layer_input(
+            g["layer_input"][sel], g["pre"][sel], o, Xb[sel], nw, label)
         d = np.where(g["layer_input"][sel] == o["layer_input"], 0, 1)
+    st["layer_input_exact"] = float((d == 0).mean())
     om = o["mixes"]
     rms = np.sqrt((om ** 2).mean(axis=1, keepdims=True))
     # (an all-zero token has zero mixes: the floor makes it demand exact zeros)
     rel = np.abs(g["mixes"][sel] - om) / np.maximum(np.maximum(np.abs(om), rms), 1e-30)
+    st["mixes_rel"] = float(rel.max())
     assert rel.max() <= MIX_TOL, f"{label} mixes rel {rel.max():.3g}"
     rr = np.abs(g["rstd"][sel] - o["rstd"]) / o["rstd"]
+    st["rstd_rel"] = float(rr.max())
     assert rr.max() <= MIX_TOL, f"{label} rstd rel {rr.max():.3g}"
     for k in ("pre", "post", "comb"):
         err = np.abs(g[k][sel].reshape(o[k].shape) - o[k]).max()
+        st[f"{k}_abs"] = float(err)
         assert err <= COEF_TOL, f"{label} {k} abs {err:.3g}"
-    return dict(layer_input_exact=float((d == 0).mean()), mixes_rel=float(rel.max()))
+    say(f"{label}: " + ", ".join(f"{k}={v:.4g}" if isinstance(v, float) else f"{k}={v}"
+                                  for k, v in st.items()))
+    return st
 
 
 def sample_tokens(T, n=48, seed=0):
@@ -183,9 +196,9 @@ def test_boundary_small_full(oracle, T, d, schedule):
     compare(g, o, label=f"T={T} d={d} {schedule}")
 
 
-@pytest.mark.parametrize("T,d,full", [(8192 + 13, 1024, True), (8192 + 29, 2048, False),
-                                      (8192 + 3, 5120, False), (8192 + 7, 8192, False)])
-def test_boundary_fused_32_token_tiles(oracle, T, d, full):
+@pytest.mark.parametrize("T,d", [(8192 + 13, 1024), (8192 + 29, 2048), (8192 + 3, 5120),
+                                 (8192 + 7, 8192)])
+def test_boundary_fused_32_token_tiles(oracle, T, d):
     """From 8192 tokens the fused schedule runs 32-token tiles (two token
     groups per wave).  Ragged tails leave the second group, or both, partly
     past the last token.  From d=4096 some li steps wait in the output buffer
@@ -193,12 +206,7 @@ def test_boundary_fused_32_token_tiles(oracle, T, d, full):
     say(f"boundary 32-token tiles T={T} d={d}")
     inp = WL.make_inputs(WL.Config("w4", d=d, T=T, seed=T + d))
     g = Dev(inp).boundary(schedule="fused")
-    if full:
-        compare(g, oracle.boundary(inp), label=f"w4 T={T} d={d}")
-    else:
-        tok = np.unique(np.concatenate([sample_tokens(T, n=40, seed=d),
-                                        np.arange(T - 40, T, dtype=np.int32)]))
-        compare(g, oracle.boundary(inp, tokens=tok), tokens=tok, label=f"w4 T={T} d={d}")
+    compare(g, oracle.boundary(inp), label=f"w4 T={T} d={d}")
 
 
 @pytest.mark.parametrize("kind,T,d", [("boundary", 2048 + 19, 7168), ("boundary", 1536 + 5, 7168),
@@ -212,15 +220,13 @@ def test_split_token_groups_ragged(oracle, kind, T, d):
     say(f"split two groups {kind} T={T} d={d}")
     inp = WL.make_inputs(WL.Config("g2", d=d, T=T, seed=T + 3 * d))
     dv = Dev(inp)
-    tok = np.unique(np.concatenate([sample_tokens(T, n=32, seed=d),
-                                    np.arange(T - 40, T, dtype=np.int32)]))
     if kind == "boundary":
         g = dv.boundary(schedule="split")
-        compare(g, oracle.boundary(inp, tokens=tok), tokens=tok, label=f"split2 T={T} d={d}")
+        compare(g, oracle.boundary(inp), label=f"split2 T={T} d={d}")
     else:
         g = dv.pre(norm=True, schedule="split")
-        compare(g, oracle.pre(inp, tokens=tok, use_norm=True), tokens=tok, xn=False,
-                label=f"pre split2 T={T} d={d}", fresh=(inp.X, inp.norm_w))
+        compare(g, oracle.pre(inp, use_norm=True), xn=False, label=f"pre split2 T={T} d={d}",
+                fresh=(inp.X, inp.norm_w))
 
 
 @pytest.mark.parametrize("T,d", [(7168 + 7, 7168), (5120 + 3, 7168), (9216 + 3, 4096),
@@ -229,8 +235,7 @@ def test_auto_balanced_tiles(oracle, T, d):
     """AUTO spreads the tokens over whole rounds of compute units with 4-wave
     tiles of ceil(T / (rounds x units)) tokens (29, 21, 19 and 19 tokens on
     256 units; two rounds at 9219), or takes the split where such tiles would
-    be small.  Tokens on both sides of every sampled tile edge are checked,
-    and the ragged tail."""
+    be small.  Every token is checked."""
     import torch
     units = torch.cuda.get_device_properties(0).multi_processor_count
     rounds = -(-(-(-T // 32)) // units)
@@ -238,11 +243,7 @@ def test_auto_balanced_tiles(oracle, T, d):
     say(f"auto T={T} d={d} (balanced tile {tile} tokens on {units} units)")
     inp = WL.make_inputs(WL.Config("at", d=d, T=T, seed=T + d))
     g = Dev(inp).boundary(schedule="auto")
-    edges = np.arange(tile, T, tile * 37, dtype=np.int64)
-    tok = np.unique(np.concatenate([sample_tokens(T, n=24, seed=T), edges - 1, edges,
-                                    np.arange(T - 40, T)]).astype(np.int32))
-    tok = tok[(tok >= 0) & (tok < T)]
-    compare(g, oracle.boundary(inp, tokens=tok), tokens=tok, label=f"auto T={T} d={d}")
+    compare(g, oracle.boundary(inp), label=f"auto T={T} d={d}")
 
 
 def test_fused_refuses_unsupported_width():
@@ -355,14 +356,14 @@ def test_boundary_decode_configs(oracle, name, schedule):
 
 @pytest.mark.parametrize("schedule", ["auto", "split"])
 @pytest.mark.parametrize("name", ["prefill", "stress"])
-def test_boundary_large_configs_sampled(oracle, name, schedule):
-    say(f"boundary {name} schedule={schedule} (sampled tokens)")
+def test_boundary_large_configs(oracle, name, schedule):
+    """The prefill (d=7168, T=8192) and stress (d=4096, T=16384) batches, every
+    token against the oracle."""
+    say(f"boundary {name} schedule={schedule} (all tokens)")
     inp = WL.make_inputs(name)
     dv = Dev(inp)
     g = dv.boundary(schedule=schedule)
-    tok = sample_tokens(inp.T, seed=len(name))
-    stats = compare(g, oracle.boundary(inp, tokens=tok), tokens=tok, label=f"{name} {schedule}")
-    say(f"{name} {schedule}: {stats}")
+    compare(g, oracle.boundary(inp), label=f"{name} {schedule}")
     if name == "stress":
         # columns sum to 1 - eps/S after the final column pass, rows close to 1
         cs = g["comb"].sum(axis=1)
@@ -399,28 +400,23 @@ def test_pre_schedules(oracle, T, d, schedule):
 
 
 @pytest.mark.parametrize("name", ["prefill", "stress"])
-def test_pre_large_sampled(oracle, name):
-    """The full-size launch (automatic schedule: split, two token groups per wave at
-    these sizes) on sampled tokens."""
-    say(f"pre {name} sampled")
+def test_pre_large(oracle, name):
+    """The full-size launch (automatic schedule) against the oracle on every token."""
+    say(f"pre {name} (all tokens)")
     inp = WL.make_inputs(name)
     g = Dev(inp).pre(norm=True)
-    tok = sample_tokens(inp.T, seed=11)
-    o = oracle.pre(inp, tokens=tok, use_norm=True)
-    compare(g, o, tokens=tok, xn=False, label=f"pre {name}", fresh=(inp.X, inp.norm_w))
+    o = oracle.pre(inp, use_norm=True)
+    compare(g, o, xn=False, label=f"pre {name}", fresh=(inp.X, inp.norm_w))
 
 
-@pytest.mark.parametrize("T,d,full", [(8192 + 13, 1024, True), (8192 + 29, 2048, False),
-                                      (8192 + 5, 4096, False)])
-def test_pre_fused_32_token_tiles(oracle, T, d, full):
+@pytest.mark.parametrize("T,d", [(8192 + 13, 1024), (8192 + 29, 2048), (8192 + 5, 4096)])
+def test_pre_fused_32_token_tiles(oracle, T, d):
     """From 8192 tokens the fused pre runs 32-token tiles; ragged tails."""
     say(f"pre 32-token tiles T={T} d={d}")
     inp = WL.make_inputs(WL.Config("pw4", d=d, T=T, seed=T + d + 1))
     g = Dev(inp).pre(norm=True, schedule="fused")
-    tok = None if full else np.unique(np.concatenate(
-        [sample_tokens(T, n=40, seed=d), np.arange(T - 40, T, dtype=np.int32)]))
-    o = oracle.pre(inp, tokens=tok, use_norm=True)
-    compare(g, o, tokens=tok, xn=False, label=f"pre w4 T={T} d={d}", fresh=(inp.X, inp.norm_w))
+    o = oracle.pre(inp, use_norm=True)
+    compare(g, o, xn=False, label=f"pre w4 T={T} d={d}", fresh=(inp.X, inp.norm_w))
 
 
 def test_pre_fused_refuses_unsupported_width():
@@ -458,9 +454,8 @@ def test_post_matches_boundary_residual(oracle, T, d):
     dv = Dev(inp)
     got = host_bits(api.post(dv.x, dv.X, dv.post, dv.comb))
     torch.cuda.synchronize()
-    tok = sample_tokens(T, seed=3) if T > 64 else None
-    o = oracle.boundary(inp, tokens=tok)
-    assert np.array_equal(got if tok is None else got[tok], o["xn"])
+    o = oracle.boundary(inp)
+    assert np.array_equal(got, o["xn"])
 
 
 @pytest.mark.parametrize("T,d,S", [(1, 256, 1), (37, 1024, 3), (200, 7168, 16), (64, 4096, 64)])
@@ -504,10 +499,8 @@ def test_invariant_bits_do_not_depend_on_batch(oracle, d, Ts):
         p = dv.pre(norm=True, schedule="invariant")
         if ref_b is None:
             ref_b, ref_p = b, p
-            tok = sample_tokens(T, n=24, seed=d) if T > 64 else None
-            compare(b, oracle.boundary(prefix(full, T), tokens=tok), tokens=tok,
-                    label="invariant boundary")
-            compare(p, oracle.pre(prefix(full, T), tokens=tok, use_norm=True), tokens=tok,
+            compare(b, oracle.boundary(prefix(full, T)), label="invariant boundary")
+            compare(p, oracle.pre(prefix(full, T), use_norm=True),
                     xn=False, label="invariant pre", fresh=(full.X[:T], full.norm_w))
             continue
         for k in b:
@@ -616,25 +609,93 @@ def test_determinism_stress():
 def _random_cases(n, seed):
     rng = np.random.default_rng(seed)
     cases = []
-    for _ in range(n):
+    for k in range(n):
         T = int(rng.integers(1, 400))
         d = int(rng.choice([256, 512, 768, 1024, 1280, 2048, 3072, 4096, 5120, 6144]))
         iters = int(rng.integers(1, 30))
         eps = float(10.0 ** rng.uniform(-8, -4))
-        cases.append((T, d, iters, eps))
+        scale = tuple(float(v) for v in rng.uniform(0.005, 0.8, 3))
+        cases.append((T, d, iters, eps, scale, "routed" if k % 2 else "mixture"))
     return cases
 
 
-@pytest.mark.parametrize("T,d,iters,eps", _random_cases(8, seed=2024))
-def test_random_shapes_and_parameters(oracle, T, d, iters, eps):
-    """A seeded sweep of token counts, widths, Sinkhorn iterations and eps values
-    through every schedule the width has (boundary) and the pre."""
-    say(f"random T={T} d={d} iters={iters} eps={eps:.2e}")
+@pytest.mark.parametrize("T,d,iters,eps,scale,family", _random_cases(8, seed=2024))
+def test_random_shapes_and_parameters(oracle, T, d, iters, eps, scale, family):
+    """A seeded sweep of token counts, widths, Sinkhorn iterations, eps values,
+    per-group scales and comb_prev families through every schedule the width has
+    (boundary) and the pre."""
+    say(f"random T={T} d={d} iters={iters} eps={eps:.2e} scale={scale} {family}")
     inp = WL.make_inputs(WL.Config("rnd", d=d, T=T, seed=T * 31 + d, sinkhorn_iters=iters,
-                                   eps=eps, rms_eps=eps))
+                                   eps=eps, rms_eps=eps, scale=scale, comb_family=family))
     dv = Dev(inp)
     o = oracle.boundary(inp)
     for schedule in ("auto", "split", "invariant") + (("fused",) if d in FUSED_D else ()):
         compare(dv.boundary(schedule=schedule), o, label=f"random {schedule}")
     compare(dv.pre(norm=True), oracle.pre(inp, use_norm=True), xn=False, label="random pre",
             fresh=(inp.X, inp.norm_w))
+
+
+# Per-group scales far apart, a strongly routed comb_prev and comb bases far from
+# symmetric: a scale applied to the wrong group of coefficients, a comb logit read
+# transposed or a mix row sent to the wrong coefficient fails these cases.  Every
+# kernel that computes coefficients is covered: the split finisher's first-token
+# path (hidden 7168: one coefficient token per rescale workgroup) and its
+# several-tokens path (hidden 1024: fewer than 16 rescale workgroups per tile),
+# both fused tile shapes, AUTO's balanced tiles, the invariant split, both pre
+# schedules and the pre from partials.
+DISTINCT = (0.31, 0.047, 0.83)
+
+
+def distinct_inputs(T, d, seed):
+    inp = WL.make_inputs(WL.Config("dist", d=d, T=T, seed=seed, scale=DISTINCT,
+                                   comb_family="routed"))
+    rng = np.random.default_rng(seed + 1)
+    inp.base[8:] = (rng.standard_normal(16) * 1.5).astype(np.float32)
+    b = inp.base[8:].reshape(4, 4)
+    assert np.abs(b - b.T).max() > 1.0
+    return inp
+
+
+@pytest.mark.parametrize("kind,T,d,schedule", [
+    ("boundary", 32, 7168, "split"),
+    ("boundary", 40, 1024, "split"),
+    ("boundary", 37, 2048, "fused"),
+    ("boundary", 8192 + 13, 1024, "fused"),
+    ("boundary", 4696, 2048, "auto"),
+    ("boundary", 300, 1024, "invariant"),
+    ("pre", 50, 7168, "split"),
+    ("pre", 37, 2048, "fused"),
+    ("pre", 8192 + 13, 1024, "fused"),
+    ("pre", 300, 1024, "invariant"),
+])
+def test_distinct_scales_every_schedule(oracle, kind, T, d, schedule):
+    say(f"distinct scales {kind} T={T} d={d} {schedule}")
+    inp = distinct_inputs(T, d, seed=T + d)
+    dv = Dev(inp)
+    if kind == "boundary":
+        g = dv.boundary(schedule=schedule)
+        o = oracle.boundary(inp)
+        compare(g, o, label=f"distinct {kind} {schedule}")
+    else:
+        g = dv.pre(norm=True, schedule=schedule)
+        o = oracle.pre(inp, use_norm=True)
+        compare(g, o, xn=False, label=f"distinct {kind} {schedule}", fresh=(inp.X, inp.norm_w))
+    # the coefficients really differ between groups and tokens
+    assert np.abs(o["comb"] - o["comb"].transpose(0, 2, 1)).max() > 0.05
+
+
+def test_distinct_scales_pre_mixes(oracle):
+    T, d, S = 64, 4096, 3
+    say(f"distinct scales pre_mixes T={T} d={d} splits={S}")
+    inp = distinct_inputs(T, d, seed=5)
+    dm, sq = WL.make_partials(T, d, S, seed=6)
+    dv = Dev(inp)
+    li, pre, post, comb = api.pre_mixes(dv.X, dev_f32(dm), dev_f32(sq), dv.scale, dv.base,
+                                        dv.norm_w, prm=dv.prm())
+    torch.cuda.synchronize()
+    o = oracle.pre_from_mixes(inp.X, dm, sq, inp.scale, inp.base, inp.norm_w, inp.params())
+    for k, g in (("pre", pre), ("post", post), ("comb", comb)):
+        err = np.abs(g.cpu().numpy().reshape(o[k].shape) - o[k]).max()
+        assert err <= COEF_TOL, f"{k} abs {err:.3g}"
+    check_fresh_layer_input(host_bits(li), pre.cpu().numpy(), o, inp.X, inp.norm_w,
+                            label="distinct pre_mixes")
