@@ -68,7 +68,7 @@ __global__ __launch_bounds__(256) void k_prepare_weight(const float* __restrict_
 // tile in lane n) through every step and feeds all of them from one set of
 // weight fragments.  Each token's sums have the same order for any G.
 // ---------------------------------------------------------------------------
-template <bool SHIFTED, int G>
+template <bool SHIFTED, int G, bool NT>
 __global__ __launch_bounds__(256) void k_partial(
     int T, int hidden, int steps_per_wave, int slices, const uint16_t* __restrict__ x,
     const uint16_t* __restrict__ X, const float* __restrict__ post_prev,
@@ -79,8 +79,8 @@ __global__ __launch_bounds__(256) void k_partial(
     __shared__ float red[4][kTok][24];
     __shared__ float sq[4][4][kTok][2];
 
-    const int tile = blockIdx.x;
-    const int slice = blockIdx.y;
+    const int tile = blockIdx.x / slices;  // (tile-major grid)
+    const int slice = blockIdx.x - tile * slices;
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int n = lane & 15;
@@ -123,10 +123,9 @@ __global__ __launch_bounds__(256) void k_partial(
     auto load_x = [&](uint4 (&Xv)[4], uint4& xv, int q, int step) {
         const int h = step * kStep + g * 8;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            Xv[j] = *reinterpret_cast<const uint4*>(Xrow[q] + (size_t)j * hidden + h);
+        for (int j = 0; j < 4; ++j) Xv[j] = ld16<NT>(Xrow[q] + (size_t)j * hidden + h);
         xv = make_uint4(0, 0, 0, 0);
-        if (SHIFTED) xv = *reinterpret_cast<const uint4*>(xrow[q] + h);
+        if (SHIFTED) xv = ld16<NT>(xrow[q] + h);
     };
     uint4 Xv[G][4], xv[G];
     if (first + wave < last) {
@@ -155,8 +154,7 @@ __global__ __launch_bounds__(256) void k_partial(
                 update_collapse(Xv[q], xv[q], c[q], Xn, li, ssq[q], ssq_li[q]);
                 if (valid[q]) {
 #pragma unroll
-                    for (int s = 0; s < 4; ++s)
-                        *reinterpret_cast<uint4*>(xn_out + (tc[q] * 4 + s) * hidden + h) = Xn[s];
+                    for (int s = 0; s < 4; ++s) st16<NT>(xn_out + (tc[q] * 4 + s) * hidden + h, Xn[s]);
                     *reinterpret_cast<uint4*>(li_out + tc[q] * hidden + h) = li;
                 }
             } else {
@@ -208,7 +206,7 @@ __global__ __launch_bounds__(256) void k_partial(
 // of each lane's sums within the slice differs.  (With two groups it would
 // need 306 registers, one workgroup per CU instead of two, and measured
 // slower.)
-template <int G>
+template <int G, bool NT>
 __global__ __launch_bounds__(256) void k_partial_pre_wide(
     int T, int hidden, int steps_per_wave, int slices, const uint16_t* __restrict__ X,
     const uint4* __restrict__ wprep, float* __restrict__ part) {
@@ -216,8 +214,8 @@ __global__ __launch_bounds__(256) void k_partial_pre_wide(
     __shared__ float red[4][kTok][24];
     __shared__ float sq[4][4][kTok];
 
-    const int tile = blockIdx.x;
-    const int slice = blockIdx.y;
+    const int tile = blockIdx.x / slices;  // (tile-major grid)
+    const int slice = blockIdx.x - tile * slices;
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int n = lane & 15;
@@ -249,8 +247,8 @@ __global__ __launch_bounds__(256) void k_partial_pre_wide(
         const int h = ws * 2 * kStep + g * 8;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            a[0][j] = *reinterpret_cast<const uint4*>(Xrow[q] + (size_t)j * hidden + h);
-            a[1][j] = *reinterpret_cast<const uint4*>(Xrow[q] + (size_t)j * hidden + h + kStep);
+            a[0][j] = ld16<NT>(Xrow[q] + (size_t)j * hidden + h);
+            a[1][j] = ld16<NT>(Xrow[q] + (size_t)j * hidden + h + kStep);
         }
     };
     uint4 cur[G][2][4];
@@ -425,8 +423,8 @@ __global__ __launch_bounds__(256) void k_finish(
     __shared__ float mred[kTile - 1][8][26];
     __shared__ float mtot[kTile - 1][26];
 
-    const int tile = blockIdx.x;
-    const int hs = blockIdx.y;
+    const int tile = blockIdx.x / finish_slices;  // (tile-major grid)
+    const int hs = blockIdx.x - tile * finish_slices;
     const int tid = threadIdx.x;
     const int h0 = hs * slice_width;
     const int width = max(0, min(slice_width, hidden - h0));
@@ -701,18 +699,19 @@ __global__ __launch_bounds__(512) void k_pre_finish(
 }
 
 // ---------------------------------------------------------------------------
-// Residual update alone.  Workgroup (token, chunk group): 256 threads, thread
-// i covers hidden [8*(blockIdx.y*256 + i), +8) of all four streams, so every
-// wave instruction reads or writes 1 KB of one row.  The token's coefficients
-// are workgroup-uniform (scalar loads).
+// Residual update alone.  Workgroup (token, chunk group), token-major in a
+// 1-D grid: 256 threads, thread i covers hidden [8*(chunk*256 + i), +8) of all
+// four streams, so every wave instruction reads or writes 1 KB of one row and
+// neighbouring workgroups cover the rest of the token's rows.  The token's
+// coefficients are workgroup-uniform (scalar loads).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_post(int hidden, const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(256) void k_post(int hidden, int chunks, const uint16_t* __restrict__ x,
                                               const uint16_t* __restrict__ X,
                                               const float* __restrict__ post_prev,
                                               const float* __restrict__ comb_prev,
                                               uint16_t* __restrict__ xn_out) {
-    const size_t t = blockIdx.x;
-    const int h = (blockIdx.y * blockDim.x + threadIdx.x) * 8;
+    const size_t t = blockIdx.x / chunks;
+    const int h = ((blockIdx.x - (int)t * chunks) * blockDim.x + threadIdx.x) * 8;
     if (h >= hidden) return;
     PrevCoef c;
     load_prev(c, post_prev, comb_prev, post_prev, t);  // (pre unused)
@@ -767,35 +766,48 @@ hipError_t launch_prefetch_weight(const void* wprep, int hidden, hipStream_t str
 hipError_t launch_post(int T, int hidden, const uint16_t* x, const uint16_t* X,
                        const float* post_prev, const float* comb_prev, uint16_t* xn_out,
                        hipStream_t stream) {
-    const dim3 grid(T, (hidden / 8 + 255) / 256);
-    hipLaunchKernelGGL(k_post, grid, dim3(256), 0, stream, hidden, x, X, post_prev, comb_prev,
-                       xn_out);
+    const int chunks = (hidden / 8 + 255) / 256;
+    hipLaunchKernelGGL(k_post, dim3((unsigned)T * (unsigned)chunks), dim3(256), 0, stream, hidden,
+                       chunks, x, X, post_prev, comb_prev, xn_out);
     return hipGetLastError();
 }
 
-template <int G>
+template <int G, bool NT>
 static void launch_partial_g(bool shifted, const SplitPlan& plan, int T, int hidden,
                              const uint16_t* x, const uint16_t* X, const float* post_prev,
                              const float* comb_prev, const float* pre_lag, const uint4* w,
                              uint16_t* xn_out, uint16_t* li_out, float* part, hipStream_t stream) {
-    const dim3 grid((T + kTile * G - 1) / (kTile * G), plan.slices);
+    const dim3 grid((unsigned)((T + kTile * G - 1) / (kTile * G)) * (unsigned)plan.slices);
     if (shifted) {
         if constexpr (G <= 2)  // (four groups would spill in the shifted kernel)
-            hipLaunchKernelGGL((k_partial<true, G>), grid, dim3(256), 0, stream, T, hidden,
+            hipLaunchKernelGGL((k_partial<true, G, NT>), grid, dim3(256), 0, stream, T, hidden,
                                plan.steps_per_wave, plan.slices, x, X, post_prev, comb_prev,
                                pre_lag, w, xn_out, li_out, part);
     } else {
         if constexpr (G == 4) {
             if (plan.steps_per_wave % 2 == 0) {
-                hipLaunchKernelGGL((k_partial_pre_wide<G>), grid, dim3(256), 0, stream, T, hidden,
-                                   plan.steps_per_wave, plan.slices, X, w, part);
+                hipLaunchKernelGGL((k_partial_pre_wide<G, NT>), grid, dim3(256), 0, stream, T,
+                                   hidden, plan.steps_per_wave, plan.slices, X, w, part);
                 return;
             }
         }
-        hipLaunchKernelGGL((k_partial<false, G>), grid, dim3(256), 0, stream, T, hidden,
+        hipLaunchKernelGGL((k_partial<false, G, NT>), grid, dim3(256), 0, stream, T, hidden,
                            plan.steps_per_wave, plan.slices, nullptr, X, nullptr, nullptr,
                            nullptr, w, nullptr, nullptr, part);
     }
+}
+
+template <int G>
+static void launch_partial_nt(bool shifted, const SplitPlan& plan, int T, int hidden,
+                              const uint16_t* x, const uint16_t* X, const float* post_prev,
+                              const float* comb_prev, const float* pre_lag, const uint4* w,
+                              uint16_t* xn_out, uint16_t* li_out, float* part, hipStream_t stream) {
+    if (plan.stream)
+        launch_partial_g<G, true>(shifted, plan, T, hidden, x, X, post_prev, comb_prev, pre_lag,
+                                  w, xn_out, li_out, part, stream);
+    else
+        launch_partial_g<G, false>(shifted, plan, T, hidden, x, X, post_prev, comb_prev, pre_lag,
+                                   w, xn_out, li_out, part, stream);
 }
 
 hipError_t launch_partial(bool shifted, const SplitPlan& plan, int T, int hidden,
@@ -804,14 +816,14 @@ hipError_t launch_partial(bool shifted, const SplitPlan& plan, int T, int hidden
                           uint16_t* xn_out, uint16_t* li_out, float* part, hipStream_t stream) {
     const uint4* w = reinterpret_cast<const uint4*>(wprep);
     if (plan.groups == 4 && !shifted)
-        launch_partial_g<4>(shifted, plan, T, hidden, x, X, post_prev, comb_prev, pre_lag, w,
-                            xn_out, li_out, part, stream);
+        launch_partial_nt<4>(shifted, plan, T, hidden, x, X, post_prev, comb_prev, pre_lag, w,
+                             xn_out, li_out, part, stream);
     else if (plan.groups == 2)
-        launch_partial_g<2>(shifted, plan, T, hidden, x, X, post_prev, comb_prev, pre_lag, w,
-                            xn_out, li_out, part, stream);
+        launch_partial_nt<2>(shifted, plan, T, hidden, x, X, post_prev, comb_prev, pre_lag, w,
+                             xn_out, li_out, part, stream);
     else
-        launch_partial_g<1>(shifted, plan, T, hidden, x, X, post_prev, comb_prev, pre_lag, w,
-                            xn_out, li_out, part, stream);
+        launch_partial_nt<1>(shifted, plan, T, hidden, x, X, post_prev, comb_prev, pre_lag, w,
+                             xn_out, li_out, part, stream);
     return hipGetLastError();
 }
 
@@ -855,11 +867,11 @@ int partial_resident_workgroups(bool shifted, int groups) {
         int per_unit = 0;
         hipError_t e;
         if (shifted)
-            e = groups == 2 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_unit, k_partial<true, 2>, 256, 0)
-                            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_unit, k_partial<true, 1>, 256, 0);
+            e = groups == 2 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_unit, k_partial<true, 2, false>, 256, 0)
+                            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_unit, k_partial<true, 1, false>, 256, 0);
         else
-            e = groups == 2 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_unit, k_partial<false, 2>, 256, 0)
-                            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_unit, k_partial<false, 1>, 256, 0);
+            e = groups == 2 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_unit, k_partial<false, 2, false>, 256, 0)
+                            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_unit, k_partial<false, 1, false>, 256, 0);
         v = (e == hipSuccess && units > 0 && per_unit > 0) ? units * per_unit : -1;
         slot.store(v, std::memory_order_relaxed);
     }
@@ -871,7 +883,7 @@ hipError_t launch_finish(const SplitPlan& plan, int T, int hidden, const float* 
                          const Scalars& p, uint16_t* layer_input, float* pre_out,
                          float* post_out, float* comb_out, float* mixes, float* rstd,
                          hipStream_t stream) {
-    const dim3 grid((T + kTile - 1) / kTile, plan.finish_slices);
+    const dim3 grid((unsigned)((T + kTile - 1) / kTile) * (unsigned)plan.finish_slices);
     hipLaunchKernelGGL(k_finish, grid, dim3(256), 0, stream, T, hidden, plan.slices,
                        plan.finish_slices, plan.finish_width, part, scale, base, norm_w, p,
                        layer_input, pre_out, post_out, comb_out, mixes, rstd);

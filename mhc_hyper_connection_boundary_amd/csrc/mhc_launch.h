@@ -9,11 +9,16 @@ namespace mhc {
 
 struct Scalars;
 
-// Work split of the split schedule for (T, hidden):
-//   k_partial: grid (tiles, slices); slice q covers hidden steps
+// Work split of the split schedule for (T, hidden).  Both kernels take a 1-D
+// grid in tile-major order: workgroup id = tile * slices + slice, so the
+// workgroups in flight at any moment cover whole rows of a few consecutive
+// token tiles (HBM serves that far better than the same bytes spread over
+// every tile of the batch: 5.6 against 4.9 TB/s for a mover of the boundary's
+// bytes).
+//   k_partial: slice q of a tile covers hidden steps
 //              [4q * steps_per_wave, 4(q + 1) * steps_per_wave) of 32 elements,
 //              interleaved over its 4 waves.
-//   k_finish:  grid (tiles, finish_slices); workgroup q rescales hidden
+//   k_finish:  workgroup q of a 16-token tile rescales hidden
 //              [q * finish_width, (q + 1) * finish_width).
 struct SplitPlan {
     int groups;          // 16-token groups per wave in the partial kernel (1, 2 or 4)
@@ -21,6 +26,7 @@ struct SplitPlan {
     int slices;
     int finish_slices;
     int finish_width;
+    bool stream;         // nontemporal hints on the residual streams (large batches)
 };
 
 SplitPlan split_plan(int T, int hidden, bool invariant, bool shifted);
