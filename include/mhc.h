@@ -61,6 +61,9 @@ extern "C" {
 #define MHC_MAX_TOKENS (1 << 20)
 #define MHC_MIN_HIDDEN 256
 #define MHC_MAX_HIDDEN 16384
+/* Size of the device array that mhc_boundary_noalloc uses in place of a
+ * workspace (16 MiB per GPU, held until the process ends). */
+#define MHC_NOALLOC_SCRATCH_BYTES (16u << 20)
 
 /* Status codes.  The refusals mirror the ones of mhc_shifted_post_pre_boundary
  * on the vLLM page, which returns None for a token count out of range or for a
@@ -75,7 +78,9 @@ typedef enum {
     MHC_ERR_MISALIGNED = 3,       /* a pointer not 16-byte aligned */
     MHC_ERR_ALIASING = 4,         /* an output overlaps another output or an input */
     MHC_ERR_WORKSPACE = 5,        /* workspace NULL or smaller than mhc_workspace_bytes() */
-    MHC_ERR_DEVICE = 6            /* a HIP call or kernel launch failed */
+    MHC_ERR_DEVICE = 6,           /* a HIP call or kernel launch failed */
+    MHC_ERR_SCRATCH_LIMIT = 7     /* mhc_boundary_noalloc: the batch's schedule needs more
+                                     partial-record space than MHC_NOALLOC_SCRATCH_BYTES */
 } mhc_status;
 
 /* Scheduling choice for mhc_boundary and mhc_pre (results are identical up
@@ -192,6 +197,33 @@ mhc_status mhc_boundary(int tokens, int hidden, const uint16_t* x, const uint16_
                         uint16_t* residual_out, uint16_t* layer_input, float* pre_out,
                         float* post_out, float* comb_out, float* mixes, float* rstd,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* mhc_boundary for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The same arguments, kernels and results as mhc_boundary (bit for bit), but
+ * no workspace: the split schedules' partial records go to a device array of
+ * MHC_NOALLOC_SCRATCH_BYTES inside the library (one per GPU, looked up on the
+ * first call on each device and kept until the process ends).  The call itself
+ * allocates nothing.
+ *   Limit: batches whose schedule needs more record space than the array
+ *   holds return MHC_ERR_SCRATCH_LIMIT with nothing enqueued.  The records take
+ *   128 bytes per token per hidden slice of the split schedule; the fused
+ *   kernels need none.  (INVARIANT: tokens * hidden bytes; at hidden 7168 AUTO
+ *   fits every batch, since it runs the fused kernels from 3072 tokens.)
+ *   Sharing: every call on one GPU uses the same array, so calls that overlap
+ *   in time on one GPU (concurrent streams) race and give wrong results;
+ *   calls ordered on one stream are safe.  Each call overwrites what it needs,
+ *   so nothing has to be cleared between calls.
+ * Errors: those of mhc_boundary, with MHC_ERR_SCRATCH_LIMIT in place of
+ * MHC_ERR_WORKSPACE. */
+mhc_status mhc_boundary_noalloc(int tokens, int hidden, const uint16_t* x,
+                                const uint16_t* residual, const float* post_prev,
+                                const float* comb_prev, const float* pre_lag,
+                                const void* w_prepared, const float* scale, const float* base,
+                                const uint16_t* norm_w, const mhc_params* params,
+                                uint16_t* residual_out, uint16_t* layer_input, float* pre_out,
+                                float* post_out, float* comb_out, float* mixes, float* rstd,
+                                void* stream);
 
 /* Non-shifted pre from a projection computed elsewhere (the blog's "pure" path:
  * mhc_pre_big_fuse with precomputed dot_mix and sqrsum, optionally split-K):

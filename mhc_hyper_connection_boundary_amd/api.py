@@ -15,7 +15,7 @@ ABI_VERSION = 1
 
 SCHEDULES = {"auto": 0, "split": 1, "fused": 2, "invariant": 3}
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape", 3: "misaligned",
-          4: "aliasing", 5: "workspace", 6: "device"}
+          4: "aliasing", 5: "workspace", 6: "device", 7: "scratch limit"}
 
 
 class MhcError(RuntimeError):
@@ -63,6 +63,8 @@ def lib() -> ctypes.CDLL:
         L.mhc_post.argtypes = [I, I, P, P, P, P, P, P]
         L.mhc_boundary.restype = I
         L.mhc_boundary.argtypes = [I, I, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, Z, P]
+        L.mhc_boundary_noalloc.restype = I
+        L.mhc_boundary_noalloc.argtypes = [I, I, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
         if L.mhc_abi_version() != ABI_VERSION:
             raise RuntimeError("libmhc.so ABI version mismatch")
         _lib = L
@@ -173,6 +175,21 @@ def boundary(x, residual, post_prev, comb_prev, pre_lag, w_prepared, scale, base
              out: dict | None = None):
     """Shifted mHC boundary.  Returns (new_residual, new_post [T,4,1], new_comb [T,4,4],
     layer_input, new_pre), plus (mixes, rstd) when debug=True."""
+    return _boundary(False, x, residual, post_prev, comb_prev, pre_lag, w_prepared, scale, base,
+                     norm_w, prm, debug, ws, out)
+
+
+def boundary_noalloc(x, residual, post_prev, comb_prev, pre_lag, w_prepared, scale, base,
+                     norm_w=None, *, prm: Params | None = None, debug: bool = False,
+                     out: dict | None = None):
+    """mhc_boundary_noalloc: the boundary without a workspace (the library's own
+    device scratch holds the partial records).  Same returns as boundary()."""
+    return _boundary(True, x, residual, post_prev, comb_prev, pre_lag, w_prepared, scale, base,
+                     norm_w, prm, debug, None, out)
+
+
+def _boundary(noalloc, x, residual, post_prev, comb_prev, pre_lag, w_prepared, scale, base,
+              norm_w, prm, debug, ws, out):
     T, hidden, dev = _shape_of_residual(residual)
     f32, bf16 = torch.float32, torch.bfloat16
     _check("x", x, bf16, (T, hidden), dev)
@@ -199,14 +216,16 @@ def boundary(x, residual, post_prev, comb_prev, pre_lag, w_prepared, scale, base
     comb = torch.empty(T, 4, 4, dtype=torch.float32, device=dev) if "comb" not in o else o["comb"]
     mixes = torch.empty(T, 24, dtype=torch.float32, device=dev) if debug else None
     rstd = torch.empty(T, dtype=torch.float32, device=dev) if debug else None
-    if ws is None:
-        ws = workspace(T, hidden, dev)
-    _check_workspace(ws, T, hidden, dev)
-    _status("mhc_boundary", lib().mhc_boundary(
-        T, hidden, _ptr(x), _ptr(residual), _ptr(post_prev), _ptr(comb_prev), _ptr(pre_lag),
-        _ptr(w_prepared), _ptr(scale), _ptr(base), _ptr(norm_w), ctypes.byref(prm),
-        _ptr(nres), _ptr(li), _ptr(pre), _ptr(post), _ptr(comb), _ptr(mixes), _ptr(rstd),
-        _ptr(ws), ws.numel(), _stream()))
+    args = (T, hidden, _ptr(x), _ptr(residual), _ptr(post_prev), _ptr(comb_prev), _ptr(pre_lag),
+            _ptr(w_prepared), _ptr(scale), _ptr(base), _ptr(norm_w), ctypes.byref(prm),
+            _ptr(nres), _ptr(li), _ptr(pre), _ptr(post), _ptr(comb), _ptr(mixes), _ptr(rstd))
+    if noalloc:
+        _status("mhc_boundary_noalloc", lib().mhc_boundary_noalloc(*args, _stream()))
+    else:
+        if ws is None:
+            ws = workspace(T, hidden, dev)
+        _check_workspace(ws, T, hidden, dev)
+        _status("mhc_boundary", lib().mhc_boundary(*args, _ptr(ws), ws.numel(), _stream()))
     res = (nres, post, comb, li, pre)
     return res + (mixes, rstd) if debug else res
 

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "mhc.h"
 #include "mhc_device.h"
@@ -216,6 +217,113 @@ size_t split_workspace_bytes(int T, int hidden) {
 
 using namespace mhc;
 
+// ---- mhc_boundary: validation and launches shared by both entry points --------
+
+namespace {
+
+// Everything but the workspace: parameters, shape, required pointers, alignment
+// and aliasing among the inputs and outputs.
+mhc_status check_boundary(int tokens, int hidden, const uint16_t* x, const uint16_t* residual,
+                          const float* post_prev, const float* comb_prev, const float* pre_lag,
+                          const void* w_prepared, const float* scale, const float* base,
+                          const uint16_t* norm_w, const mhc_params* params,
+                          uint16_t* residual_out, uint16_t* layer_input, float* pre_out,
+                          float* post_out, float* comb_out, float* mixes, float* rstd) {
+    mhc_status st = check_params(params);
+    if (st != MHC_OK) return st;
+    if (tokens < 0) return MHC_ERR_INVALID_ARGUMENT;
+    if (tokens > MHC_MAX_TOKENS || !shape_ok(hidden)) return MHC_ERR_UNSUPPORTED_SHAPE;
+    if (params->schedule == MHC_SCHEDULE_FUSED && !fused_supported(hidden))
+        return MHC_ERR_UNSUPPORTED_SHAPE;
+    if (tokens == 0) return MHC_OK;
+    if (!x || !residual || !post_prev || !comb_prev || !pre_lag || !w_prepared || !scale ||
+        !base || !residual_out || !layer_input || !pre_out || !post_out || !comb_out)
+        return MHC_ERR_INVALID_ARGUMENT;
+    const void* ptrs[] = {x, residual, post_prev, comb_prev, pre_lag, w_prepared, scale, base,
+                          norm_w, residual_out, layer_input, pre_out, post_out, comb_out,
+                          mixes, rstd};
+    for (const void* q : ptrs)
+        if (q && !aligned(q)) return MHC_ERR_MISALIGNED;
+    const size_t T = tokens, d = hidden;
+    const Span outs[] = {{residual_out, T * 4 * d * 2}, {layer_input, T * d * 2},
+                         {pre_out, T * 16}, {post_out, T * 16}, {comb_out, T * 64},
+                         {mixes, mixes ? T * 96 : 0}, {rstd, rstd ? T * 4 : 0}};
+    const Span ins[] = {{x, T * d * 2}, {residual, T * 4 * d * 2}, {post_prev, T * 16},
+                        {comb_prev, T * 64}, {pre_lag, T * 16}, {w_prepared, 384 * d},
+                        {scale, 12}, {base, 96}, {norm_w, norm_w ? d * 2 : 0}};
+    if (any_alias(outs, 7, ins, 9)) return MHC_ERR_ALIASING;
+    return MHC_OK;
+}
+
+// Bytes of partial records the boundary's schedule for this batch writes: the
+// split schedules' [T][slices][32] FP32 records; 0 on the fused kernels.
+size_t boundary_scratch_bytes(int tokens, int hidden, int schedule) {
+    if (boundary_path(schedule, tokens, hidden).path != BoundaryPath::Split) return 0;
+    const SplitPlan plan = split_plan(tokens, hidden, schedule == MHC_SCHEDULE_INVARIANT, true);
+    return (size_t)tokens * plan.slices * kPart * sizeof(float);
+}
+
+// Launches of a validated call; part receives the split schedules' records.
+mhc_status run_boundary(int tokens, int hidden, const uint16_t* x, const uint16_t* residual,
+                        const float* post_prev, const float* comb_prev, const float* pre_lag,
+                        const void* w_prepared, const float* scale, const float* base,
+                        const uint16_t* norm_w, const mhc_params* params,
+                        uint16_t* residual_out, uint16_t* layer_input, float* pre_out,
+                        float* post_out, float* comb_out, float* mixes, float* rstd, float* part,
+                        hipStream_t hs) {
+    const Scalars s = scalars(params);
+    const BoundaryChoice choice = boundary_path(params->schedule, tokens, hidden);
+    if (choice.path != BoundaryPath::Split) {
+        if (!fused_supported(hidden)) return MHC_ERR_UNSUPPORTED_SHAPE;
+        const hipError_t e =
+            choice.path == BoundaryPath::Fused32
+                ? launch_fused_w4(tokens, choice.tile_tokens, hidden, x, residual, post_prev,
+                                  comb_prev, pre_lag, w_prepared, scale, base, norm_w, s,
+                                  residual_out, layer_input, pre_out, post_out, comb_out, mixes,
+                                  rstd, hs)
+                : launch_fused(tokens, hidden, x, residual, post_prev, comb_prev, pre_lag,
+                               w_prepared, scale, base, norm_w, s, residual_out, layer_input,
+                               pre_out, post_out, comb_out, mixes, rstd, hs);
+        return e == hipSuccess ? MHC_OK : MHC_ERR_DEVICE;
+    }
+    const SplitPlan plan =
+        split_plan(tokens, hidden, params->schedule == MHC_SCHEDULE_INVARIANT, true);
+    // layer_input first receives li; the finishing kernel rescales it in place.
+    if (launch_partial(true, plan, tokens, hidden, x, residual, post_prev, comb_prev, pre_lag,
+                       w_prepared, residual_out, layer_input, part, hs) != hipSuccess)
+        return MHC_ERR_DEVICE;
+    if (launch_finish(plan, tokens, hidden, part, scale, base, norm_w, s, layer_input, pre_out,
+                      post_out, comb_out, mixes, rstd, hs) != hipSuccess)
+        return MHC_ERR_DEVICE;
+    return MHC_OK;
+}
+
+// ---- the no-allocation entry point's scratch ---------------------------------------
+//
+// For callers that cannot allocate (graph capture, serving loops, harnesses
+// that forbid hipMalloc): a device array holding the split schedules' partial
+// records, MHC_NOALLOC_SCRATCH_BYTES in size.  Every GPU that the library runs
+// on holds its own copy until the process ends.  Host code never passes the
+// array's name to a kernel: it is only a host-side stand-in.  The device
+// address is looked up once per device, with that device current, and kept.
+static __device__ __align__(256) unsigned char scratch[MHC_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kScratchDevices = 64;
+
+void* scratch_address() {
+    static std::atomic<void*> addr[kScratchDevices];
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) return nullptr;
+    void* p = addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        addr[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
+
+}  // namespace
+
 extern "C" {
 
 int mhc_abi_version(void) { return MHC_ABI_VERSION; }
@@ -229,6 +337,8 @@ const char* mhc_status_string(mhc_status s) {
         case MHC_ERR_ALIASING: return "output overlaps another buffer";
         case MHC_ERR_WORKSPACE: return "workspace missing or too small";
         case MHC_ERR_DEVICE: return "HIP launch failed";
+        case MHC_ERR_SCRATCH_LIMIT:
+            return "batch needs more than the no-allocation entry point's scratch";
     }
     return "unknown status";
 }
@@ -371,61 +481,47 @@ mhc_status mhc_boundary(int tokens, int hidden, const uint16_t* x, const uint16_
                         uint16_t* residual_out, uint16_t* layer_input, float* pre_out,
                         float* post_out, float* comb_out, float* mixes, float* rstd,
                         void* workspace, size_t workspace_bytes, void* stream) {
-    mhc_status st = check_params(params);
-    if (st != MHC_OK) return st;
-    if (tokens < 0) return MHC_ERR_INVALID_ARGUMENT;
-    if (tokens > MHC_MAX_TOKENS || !shape_ok(hidden)) return MHC_ERR_UNSUPPORTED_SHAPE;
-    if (params->schedule == MHC_SCHEDULE_FUSED && !fused_supported(hidden))
-        return MHC_ERR_UNSUPPORTED_SHAPE;
-    if (tokens == 0) return MHC_OK;
-    if (!x || !residual || !post_prev || !comb_prev || !pre_lag || !w_prepared || !scale ||
-        !base || !residual_out || !layer_input || !pre_out || !post_out || !comb_out)
-        return MHC_ERR_INVALID_ARGUMENT;
-    const void* ptrs[] = {x, residual, post_prev, comb_prev, pre_lag, w_prepared, scale, base,
-                          norm_w, residual_out, layer_input, pre_out, post_out, comb_out,
-                          mixes, rstd, workspace};
-    for (const void* q : ptrs)
-        if (q && !aligned(q)) return MHC_ERR_MISALIGNED;
+    mhc_status st = check_boundary(tokens, hidden, x, residual, post_prev, comb_prev, pre_lag,
+                                   w_prepared, scale, base, norm_w, params, residual_out,
+                                   layer_input, pre_out, post_out, comb_out, mixes, rstd);
+    if (st != MHC_OK || tokens == 0) return st;
+    if (workspace && !aligned(workspace)) return MHC_ERR_MISALIGNED;
     const size_t T = tokens, d = hidden;
     const size_t need = mhc_workspace_bytes(tokens, hidden);
-    const Span outs[] = {{residual_out, T * 4 * d * 2}, {layer_input, T * d * 2},
-                         {pre_out, T * 16}, {post_out, T * 16}, {comb_out, T * 64},
-                         {mixes, mixes ? T * 96 : 0}, {rstd, rstd ? T * 4 : 0},
-                         {workspace, need}};
-    const Span ins[] = {{x, T * d * 2}, {residual, T * 4 * d * 2}, {post_prev, T * 16},
-                        {comb_prev, T * 64}, {pre_lag, T * 16}, {w_prepared, 384 * d},
-                        {scale, 12}, {base, 96}, {norm_w, norm_w ? d * 2 : 0}};
-    if (any_alias(outs, 8, ins, 9)) return MHC_ERR_ALIASING;
+    const Span ws{workspace, need};
+    const Span others[] = {{x, T * d * 2}, {residual, T * 4 * d * 2}, {post_prev, T * 16},
+                           {comb_prev, T * 64}, {pre_lag, T * 16}, {w_prepared, 384 * d},
+                           {scale, 12}, {base, 96}, {norm_w, norm_w ? d * 2 : 0},
+                           {residual_out, T * 4 * d * 2}, {layer_input, T * d * 2},
+                           {pre_out, T * 16}, {post_out, T * 16}, {comb_out, T * 64},
+                           {mixes, mixes ? T * 96 : 0}, {rstd, rstd ? T * 4 : 0}};
+    if (any_alias(&ws, 1, others, 16)) return MHC_ERR_ALIASING;
     if (!workspace || workspace_bytes < need) return MHC_ERR_WORKSPACE;
+    return run_boundary(tokens, hidden, x, residual, post_prev, comb_prev, pre_lag, w_prepared,
+                        scale, base, norm_w, params, residual_out, layer_input, pre_out, post_out,
+                        comb_out, mixes, rstd, static_cast<float*>(workspace),
+                        (hipStream_t)stream);
+}
 
-    const Scalars s = scalars(params);
-    hipStream_t hs = (hipStream_t)stream;
-    const BoundaryChoice choice = boundary_path(params->schedule, tokens, hidden);
-    if (choice.path != BoundaryPath::Split) {
-        if (!fused_supported(hidden)) return MHC_ERR_UNSUPPORTED_SHAPE;
-        const hipError_t e =
-            choice.path == BoundaryPath::Fused32
-                ? launch_fused_w4(tokens, choice.tile_tokens, hidden, x, residual, post_prev,
-                                  comb_prev, pre_lag, w_prepared, scale, base, norm_w, s,
-                                  residual_out, layer_input, pre_out, post_out, comb_out, mixes,
-                                  rstd, hs)
-                : launch_fused(tokens, hidden, x, residual, post_prev, comb_prev, pre_lag,
-                               w_prepared, scale, base, norm_w, s, residual_out, layer_input,
-                               pre_out, post_out, comb_out, mixes, rstd, hs);
-        if (e != hipSuccess) return MHC_ERR_DEVICE;
-        return MHC_OK;
-    }
-    const SplitPlan plan =
-        split_plan(tokens, hidden, params->schedule == MHC_SCHEDULE_INVARIANT, true);
-    float* part = static_cast<float*>(workspace);
-    // layer_input first receives li; the finishing kernel rescales it in place.
-    if (launch_partial(true, plan, tokens, hidden, x, residual, post_prev, comb_prev, pre_lag,
-                       w_prepared, residual_out, layer_input, part, hs) != hipSuccess)
-        return MHC_ERR_DEVICE;
-    if (launch_finish(plan, tokens, hidden, part, scale, base, norm_w, s, layer_input, pre_out,
-                      post_out, comb_out, mixes, rstd, hs) != hipSuccess)
-        return MHC_ERR_DEVICE;
-    return MHC_OK;
+mhc_status mhc_boundary_noalloc(int tokens, int hidden, const uint16_t* x,
+                                const uint16_t* residual, const float* post_prev,
+                                const float* comb_prev, const float* pre_lag,
+                                const void* w_prepared, const float* scale, const float* base,
+                                const uint16_t* norm_w, const mhc_params* params,
+                                uint16_t* residual_out, uint16_t* layer_input, float* pre_out,
+                                float* post_out, float* comb_out, float* mixes, float* rstd,
+                                void* stream) {
+    mhc_status st = check_boundary(tokens, hidden, x, residual, post_prev, comb_prev, pre_lag,
+                                   w_prepared, scale, base, norm_w, params, residual_out,
+                                   layer_input, pre_out, post_out, comb_out, mixes, rstd);
+    if (st != MHC_OK || tokens == 0) return st;
+    if (boundary_scratch_bytes(tokens, hidden, params->schedule) > sizeof(scratch))
+        return MHC_ERR_SCRATCH_LIMIT;
+    float* part = static_cast<float*>(scratch_address());
+    if (!part) return MHC_ERR_DEVICE;
+    return run_boundary(tokens, hidden, x, residual, post_prev, comb_prev, pre_lag, w_prepared,
+                        scale, base, norm_w, params, residual_out, layer_input, pre_out, post_out,
+                        comb_out, mixes, rstd, part, (hipStream_t)stream);
 }
 
 }  // extern "C"

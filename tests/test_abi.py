@@ -205,3 +205,23 @@ def test_empty_batch_is_a_noop(L):
     fused = ctypes.byref(api.params(schedule="fused"))
     assert boundary(d=1280, p=fused) == SHAPE and pre(d=1280, p=fused) == SHAPE
     assert boundary(d=1024, p=fused) == OK
+
+
+def test_boundary_noalloc_refusals(L):
+    """The no-allocation entry point validates like mhc_boundary, and refuses a
+    batch whose schedule needs more record space than its device array holds
+    (here INVARIANT: tokens * hidden bytes of records) before any HIP call."""
+    assert L.mhc_status_string(7) == b"batch needs more than the no-allocation entry point's scratch"
+    b = Buffers(L)
+
+    def noalloc(**over):
+        return L.mhc_boundary_noalloc(*b.args(**over)[:-3], None)
+    assert noalloc(T=-1) == INVALID
+    assert noalloc(x=0) == INVALID
+    assert noalloc(d=1000) == SHAPE
+    assert noalloc(residual=b.addr["residual"] + 2) == MISALIGNED
+    assert noalloc(li=b.addr["res_out"] + 64) == ALIASING
+    assert noalloc(T=0) == OK
+    inv = ctypes.byref(api.params(schedule="invariant"))
+    big = Buffers(L, T=4096, d=8192)          # 4096 * 8192 bytes of records > 16 MiB
+    assert L.mhc_boundary_noalloc(*big.args(prm=inv)[:-3], None) == 7
