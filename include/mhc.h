@@ -63,7 +63,7 @@ extern "C" {
 #define MHC_MAX_HIDDEN 16384
 /* Size of the device array that mhc_boundary_noalloc uses in place of a
  * workspace (16 MiB per GPU, held until the process ends). */
-#define MHC_NOALLOC_SCRATCH_BYTES (16u << 20)
+#define MHC_NOALLOC_SCRATCH_BYTES (64u << 20)
 
 /* Status codes.  The refusals mirror the ones of mhc_shifted_post_pre_boundary
  * on the vLLM page, which returns None for a token count out of range or for a
@@ -112,7 +112,10 @@ typedef enum {
     MHC_SCHEDULE_FUSED = 2,       /* one workgroup per token tile owns all of hidden: 16-token
                                      tiles on 8 waves, or from 8192 tokens 32-token tiles on
                                      4 waves */
-    MHC_SCHEDULE_INVARIANT = 3    /* batch-invariant: split with an order fixed by hidden */
+    MHC_SCHEDULE_INVARIANT = 3,   /* batch-invariant: split with an order fixed by hidden */
+    MHC_SCHEDULE_STREAM = 4       /* mhc_boundary: one persistent launch over a queue of
+                                     (64-token tile, 256-element slice) items in tile-major
+                                     order; mhc_pre: SPLIT */
 } mhc_schedule;
 
 /* Runtime scalars (the pages pass them as kernel arguments). */

@@ -13,7 +13,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmhc.so")
 ABI_VERSION = 1
 
-SCHEDULES = {"auto": 0, "split": 1, "fused": 2, "invariant": 3}
+SCHEDULES = {"auto": 0, "split": 1, "fused": 2, "invariant": 3, "stream": 4}
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape", 3: "misaligned",
           4: "aliasing", 5: "workspace", 6: "device", 7: "scratch limit"}
 
@@ -154,8 +154,11 @@ def workspace_bytes(tokens: int, hidden: int) -> int:
 
 
 def workspace(tokens: int, hidden: int, device=None) -> torch.Tensor:
+    """A workspace for batches up to `tokens` tokens of `hidden`: zero-filled, as
+    the library requires before first use (every call leaves it ready for the
+    next)."""
     n = max(workspace_bytes(tokens, hidden), 16)
-    return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
+    return torch.zeros(n, dtype=torch.uint8, device=device or "cuda")
 
 
 def prepare_weight(w: torch.Tensor) -> torch.Tensor:

@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmhc.so")
-SOURCES = ["mhc_api.hip", "mhc_kernels.hip", "mhc_fused.hip"]
+SOURCES = ["mhc_api.hip", "mhc_kernels.hip", "mhc_fused.hip", "mhc_stream.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 ARCH = ["--offload-arch=gfx950"]

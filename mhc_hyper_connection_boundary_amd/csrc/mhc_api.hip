@@ -68,7 +68,7 @@ mhc_status check_params(const mhc_params* p) {
     if (!(p->rms_eps >= 0.f) || !(p->pre_eps >= 0.f) || !(p->sinkhorn_eps >= 0.f) ||
         !(p->norm_eps >= 0.f) || !(p->post_mult == p->post_mult))
         return MHC_ERR_INVALID_ARGUMENT;
-    if (p->schedule < MHC_SCHEDULE_AUTO || p->schedule > MHC_SCHEDULE_INVARIANT)
+    if (p->schedule < MHC_SCHEDULE_AUTO || p->schedule > MHC_SCHEDULE_STREAM)
         return MHC_ERR_INVALID_ARGUMENT;
     return MHC_OK;
 }
@@ -91,13 +91,14 @@ mhc_status check_params(const mhc_params* p) {
 // count is unknown, AUTO
 // falls back to 16-token tiles from kFusedMinTokens and 32-token tiles from
 // kW4MinTokens.
-enum class BoundaryPath { Split, Fused16, Fused32 };
+enum class BoundaryPath { Split, Fused16, Fused32, Stream };
 struct BoundaryChoice {
     BoundaryPath path;
     int tile_tokens;  // Fused32: tokens per tile (at most 32)
 };
 
 BoundaryChoice boundary_path(int schedule, int tokens, int hidden) {
+    if (schedule == MHC_SCHEDULE_STREAM) return {BoundaryPath::Stream, 0};
     if (schedule == MHC_SCHEDULE_FUSED)
         return tokens >= kW4MinTokens ? BoundaryChoice{BoundaryPath::Fused32, 32}
                                       : BoundaryChoice{BoundaryPath::Fused16, 16};
@@ -208,6 +209,9 @@ SplitPlan split_plan(int T, int hidden, bool invariant, bool shifted) {
     return plan;
 }
 
+static_assert(kCounterBytes >= 4 * (3 + 3 * ((size_t)MHC_MAX_TOKENS + 63) / 64),
+              "the counters region covers every batch size");
+
 // The finest split (one step per wave) has the most slices: enough for every plan.
 size_t split_workspace_bytes(int T, int hidden) {
     return (size_t)T * split_plan(T, hidden, true, true).slices * kPart * sizeof(float);
@@ -258,9 +262,11 @@ mhc_status check_boundary(int tokens, int hidden, const uint16_t* x, const uint1
 // Bytes of partial records the boundary's schedule for this batch writes: the
 // split schedules' [T][slices][32] FP32 records; 0 on the fused kernels.
 size_t boundary_scratch_bytes(int tokens, int hidden, int schedule) {
-    if (boundary_path(schedule, tokens, hidden).path != BoundaryPath::Split) return 0;
+    const BoundaryPath path = boundary_path(schedule, tokens, hidden).path;
+    if (path == BoundaryPath::Stream) return kCounterBytes + stream_data_bytes(tokens, hidden);
+    if (path != BoundaryPath::Split) return 0;
     const SplitPlan plan = split_plan(tokens, hidden, schedule == MHC_SCHEDULE_INVARIANT, true);
-    return (size_t)tokens * plan.slices * kPart * sizeof(float);
+    return kCounterBytes + (size_t)tokens * plan.slices * kPart * sizeof(float);
 }
 
 // Launches of a validated call; part receives the split schedules' records.
@@ -269,10 +275,19 @@ mhc_status run_boundary(int tokens, int hidden, const uint16_t* x, const uint16_
                         const void* w_prepared, const float* scale, const float* base,
                         const uint16_t* norm_w, const mhc_params* params,
                         uint16_t* residual_out, uint16_t* layer_input, float* pre_out,
-                        float* post_out, float* comb_out, float* mixes, float* rstd, float* part,
+                        float* post_out, float* comb_out, float* mixes, float* rstd, void* ws,
                         hipStream_t hs) {
     const Scalars s = scalars(params);
+    float* const part = reinterpret_cast<float*>(static_cast<char*>(ws) + kCounterBytes);
     const BoundaryChoice choice = boundary_path(params->schedule, tokens, hidden);
+    if (choice.path == BoundaryPath::Stream) {
+        const StreamPlan plan = stream_plan(tokens, hidden);
+        return launch_stream(plan, tokens, hidden, x, residual, post_prev, comb_prev, pre_lag,
+                             w_prepared, scale, base, norm_w, s, residual_out, layer_input,
+                             pre_out, post_out, comb_out, mixes, rstd, ws, hs) == hipSuccess
+                   ? MHC_OK
+                   : MHC_ERR_DEVICE;
+    }
     if (choice.path != BoundaryPath::Split) {
         if (!fused_supported(hidden)) return MHC_ERR_UNSUPPORTED_SHAPE;
         const hipError_t e =
@@ -349,7 +364,8 @@ size_t mhc_prepared_weight_bytes(int hidden) {
 
 size_t mhc_workspace_bytes(int tokens, int hidden) {
     if (tokens <= 0 || tokens > MHC_MAX_TOKENS || !shape_ok(hidden)) return 0;
-    return split_workspace_bytes(tokens, hidden);
+    return kCounterBytes +
+           std::max(split_workspace_bytes(tokens, hidden), stream_data_bytes(tokens, hidden));
 }
 
 mhc_status mhc_prepare_weight(const float* w, int hidden, void* w_prepared, void* stream) {
@@ -464,7 +480,8 @@ mhc_status mhc_pre(int tokens, int hidden, const uint16_t* residual, const void*
     }
     const SplitPlan plan =
         split_plan(tokens, hidden, params->schedule == MHC_SCHEDULE_INVARIANT, false);
-    float* part = static_cast<float*>(workspace);
+    // (past the streaming schedule's counters, which it must not touch)
+    float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterBytes);
     if (launch_partial(false, plan, tokens, hidden, nullptr, residual, nullptr, nullptr, nullptr,
                        w_prepared, nullptr, nullptr, part, hs) != hipSuccess)
         return MHC_ERR_DEVICE;
@@ -499,8 +516,7 @@ mhc_status mhc_boundary(int tokens, int hidden, const uint16_t* x, const uint16_
     if (!workspace || workspace_bytes < need) return MHC_ERR_WORKSPACE;
     return run_boundary(tokens, hidden, x, residual, post_prev, comb_prev, pre_lag, w_prepared,
                         scale, base, norm_w, params, residual_out, layer_input, pre_out, post_out,
-                        comb_out, mixes, rstd, static_cast<float*>(workspace),
-                        (hipStream_t)stream);
+                        comb_out, mixes, rstd, workspace, (hipStream_t)stream);
 }
 
 mhc_status mhc_boundary_noalloc(int tokens, int hidden, const uint16_t* x,
@@ -517,11 +533,11 @@ mhc_status mhc_boundary_noalloc(int tokens, int hidden, const uint16_t* x,
     if (st != MHC_OK || tokens == 0) return st;
     if (boundary_scratch_bytes(tokens, hidden, params->schedule) > sizeof(scratch))
         return MHC_ERR_SCRATCH_LIMIT;
-    float* part = static_cast<float*>(scratch_address());
-    if (!part) return MHC_ERR_DEVICE;
+    void* ws = scratch_address();
+    if (!ws) return MHC_ERR_DEVICE;
     return run_boundary(tokens, hidden, x, residual, post_prev, comb_prev, pre_lag, w_prepared,
                         scale, base, norm_w, params, residual_out, layer_input, pre_out, post_out,
-                        comb_out, mixes, rstd, part, (hipStream_t)stream);
+                        comb_out, mixes, rstd, ws, (hipStream_t)stream);
 }
 
 }  // extern "C"

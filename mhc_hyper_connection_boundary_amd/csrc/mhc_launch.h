@@ -101,4 +101,35 @@ hipError_t launch_fused_pre(int T, int hidden, const uint16_t* X, const void* wp
                             float* post_out, float* comb_out, float* mixes, float* rstd,
                             bool tiles32, hipStream_t stream);
 
+// Every workspace starts with the streaming schedule's queue and tile
+// counters: a fixed region sized for the largest batch (2^20 tokens in 64-token
+// tiles), which no other kernel writes and which the streaming kernel leaves
+// zero after every call, so that one workspace can serve every schedule and
+// batch size.  The split schedules' records and the streaming schedule's data
+// follow it.
+constexpr size_t kCounterBytes = ((size_t)4 * (3 + 3 * (((size_t)1 << 20) / 64)) + 255) / 256 * 256;
+
+// Streaming schedule of the boundary (one persistent launch, work queue of
+// (64-token tile, 32*kb-element slice) items).  After the counters the
+// workspace holds rstd_li per token and the partial records.
+struct StreamPlan {
+    int kb;          // 32-element k-blocks per item
+    int slices;      // items per tile
+    int tiles;       // 64-token tiles
+    int lag;         // tile r is finished by the items of tile r + lag
+    int items;       // queue length: (tiles + lag) * slices
+    int grid;        // persistent workgroups
+    int sync_words;  // counters at the start of the workspace
+};
+
+StreamPlan stream_plan(int T, int hidden);
+size_t stream_data_bytes(int T, int hidden);  // after the counters
+hipError_t launch_stream(const StreamPlan& plan, int T, int hidden, const uint16_t* x,
+                         const uint16_t* X, const float* post_prev, const float* comb_prev,
+                         const float* pre_lag, const void* wprep, const float* scale,
+                         const float* base, const uint16_t* norm_w, const Scalars& p,
+                         uint16_t* xn_out, uint16_t* layer_input, float* pre_out,
+                         float* post_out, float* comb_out, float* mixes, float* rstd,
+                         void* workspace, hipStream_t stream);  // workspace: counters first
+
 }  // namespace mhc

@@ -37,15 +37,22 @@ def test_exports_every_declared_symbol(L):
     assert L.mhc_status_string(3) == b"pointer not 16-byte aligned"
 
 
+COUNTERS = 196864   # the streaming schedule's counters: 4 * (3 + 3 * 2^20 / 64), rounded to 256
+
+
+def stream_data(T, d):
+    return -(-4 * T // 256) * 256 + T * (d // 256) * 128
+
+
 def test_size_queries(L):
     assert L.mhc_prepared_weight_bytes(7168) == 384 * 7168 == 2752512
     assert L.mhc_prepared_weight_bytes(7000) == 0
-    # every schedule fits: the finest split's records, 128 B per token per 128 of hidden
-    assert L.mhc_workspace_bytes(32, 7168) == 32 * 7168
-    assert L.mhc_workspace_bytes(8192, 7168) == 8192 * 7168
-    assert L.mhc_workspace_bytes(3, 1280) == 3 * 1280
+    # every schedule fits: the counters, then the larger of the finest split's
+    # records (128 B per token per 128 of hidden) and the streaming data
+    for T, d in ((32, 7168), (8192, 7168), (3, 1280), (1, 256), (5, 256)):
+        assert L.mhc_workspace_bytes(T, d) == COUNTERS + max(T * d, stream_data(T, d)), (T, d)
     # the limits: no 32-bit overflow in the size queries
-    assert L.mhc_workspace_bytes(1 << 20, 16384) == (1 << 20) * 16384
+    assert L.mhc_workspace_bytes(1 << 20, 16384) == COUNTERS + (1 << 20) * 16384
     assert L.mhc_workspace_bytes((1 << 20) + 1, 16384) == 0
     assert L.mhc_prepared_weight_bytes(16384) == 384 * 16384
     assert L.mhc_prepared_weight_bytes(16640) == 0
@@ -94,7 +101,7 @@ def test_boundary_refusals(L):
     assert call(L, b, prm=ctypes.byref(api.params(rms_eps=-1.0))) == INVALID
     assert call(L, b, prm=ctypes.byref(api.params(norm_eps=float("nan")))) == INVALID
     bad_schedule = api.params()
-    bad_schedule.schedule = 4
+    bad_schedule.schedule = 5
     assert call(L, b, prm=ctypes.byref(bad_schedule)) == INVALID
     assert call(L, b, d=1000) == SHAPE
     assert call(L, b, d=128) == SHAPE
@@ -223,5 +230,5 @@ def test_boundary_noalloc_refusals(L):
     assert noalloc(li=b.addr["res_out"] + 64) == ALIASING
     assert noalloc(T=0) == OK
     inv = ctypes.byref(api.params(schedule="invariant"))
-    big = Buffers(L, T=4096, d=8192)          # 4096 * 8192 bytes of records > 16 MiB
+    big = Buffers(L, T=8192, d=16384)         # 8192 * 16384 bytes of records > 64 MiB
     assert L.mhc_boundary_noalloc(*big.args(prm=inv)[:-3], None) == 7

@@ -11,7 +11,8 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("schedule,d,T", [("split", 7168, 32), ("fused", 2048, 40), ("fused", 1024, 8192 + 5),
-                                          ("invariant", 1024, 300)])
+                                          ("invariant", 1024, 300), ("stream", 7168, 32),
+                                          ("stream", 2048, 3000 + 7)])
 def test_graph_replay_matches_eager(schedule, d, T):
     print(f"[graph] schedule={schedule} d={d} T={T}", flush=True)
     inp = WL.make_inputs(WL.Config("g", d=d, T=T, seed=d + T))

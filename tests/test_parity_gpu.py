@@ -183,7 +183,7 @@ def test_prepare_weight_bit_exact(oracle, d):
 FUSED_D = {1024, 2048, 4096, 5120, 6144, 7168, 8192}
 
 
-@pytest.mark.parametrize("schedule", ["split", "fused"])
+@pytest.mark.parametrize("schedule", ["split", "fused", "stream"])
 @pytest.mark.parametrize("T,d", [(8, 256), (37, 1024), (1, 512), (50, 2048), (3, 5120), (17, 6144),
                                  (20, 8192), (9, 768), (5, 1280)])
 def test_boundary_small_full(oracle, T, d, schedule):
@@ -324,7 +324,7 @@ def test_boundary_special_cases(oracle):
     np.testing.assert_allclose(g["comb"], 0.25, atol=1e-6)
 
 
-@pytest.mark.parametrize("schedule", ["auto", "split", "fused", "invariant"])
+@pytest.mark.parametrize("schedule", ["auto", "split", "fused", "invariant", "stream"])
 def test_empty_batch(oracle, schedule):
     """T = 0 is a no-op on every entry point: empty outputs, no error, and the
     next call on the same buffers is unaffected."""
@@ -344,7 +344,7 @@ def test_empty_batch(oracle, schedule):
     compare(dv.boundary(schedule=schedule), oracle.boundary(inp), label=f"after empty {schedule}")
 
 
-@pytest.mark.parametrize("schedule", ["auto", "fused"])
+@pytest.mark.parametrize("schedule", ["auto", "fused", "stream"])
 @pytest.mark.parametrize("name", ["decode", "decode_wave"])
 def test_boundary_decode_configs(oracle, name, schedule):
     say(f"boundary {name} schedule={schedule}")
@@ -354,7 +354,7 @@ def test_boundary_decode_configs(oracle, name, schedule):
     say(f"{name} {schedule}: {stats}")
 
 
-@pytest.mark.parametrize("schedule", ["auto", "split"])
+@pytest.mark.parametrize("schedule", ["auto", "split", "stream"])
 @pytest.mark.parametrize("name", ["prefill", "stress"])
 def test_boundary_large_configs(oracle, name, schedule):
     """The prefill (d=7168, T=8192) and stress (d=4096, T=16384) batches, every
@@ -435,7 +435,7 @@ def test_pre_ragged(oracle):
             fresh=(inp.X, inp.norm_w))
 
 
-@pytest.mark.parametrize("schedule", ["split", "fused"])
+@pytest.mark.parametrize("schedule", ["split", "fused", "stream"])
 def test_determinism_decode(schedule):
     say(f"determinism decode {schedule}")
     dv = Dev(WL.make_inputs("decode"))
@@ -564,7 +564,7 @@ def test_maximum_hidden(oracle):
     assert np.array_equal(got, oracle.boundary(inp)["xn"])
 
 
-@pytest.mark.parametrize("schedule", ["split", "fused"])
+@pytest.mark.parametrize("schedule", ["split", "fused", "stream"])
 def test_boundary_degenerate_parameters(oracle, schedule):
     """Degenerate settings of the method, against the oracle: one Sinkhorn
     iteration (row softmax and a single column pass), many iterations, every eps
@@ -598,7 +598,7 @@ def test_determinism_stress():
     bitwise-identical outputs over three runs, and so does its split schedule."""
     say("determinism stress")
     dv = Dev(WL.make_inputs("stress"))
-    for schedule in ("auto", "split"):
+    for schedule in ("auto", "split", "stream"):
         a = dv.boundary(schedule=schedule)
         for _ in range(2):
             b = dv.boundary(schedule=schedule)
@@ -629,7 +629,7 @@ def test_random_shapes_and_parameters(oracle, T, d, iters, eps, scale, family):
                                    eps=eps, rms_eps=eps, scale=scale, comb_family=family))
     dv = Dev(inp)
     o = oracle.boundary(inp)
-    for schedule in ("auto", "split", "invariant") + (("fused",) if d in FUSED_D else ()):
+    for schedule in ("auto", "split", "invariant", "stream") + (("fused",) if d in FUSED_D else ()):
         compare(dv.boundary(schedule=schedule), o, label=f"random {schedule}")
     compare(dv.pre(norm=True), oracle.pre(inp, use_norm=True), xn=False, label="random pre",
             fresh=(inp.X, inp.norm_w))
@@ -663,6 +663,8 @@ def distinct_inputs(T, d, seed):
     ("boundary", 8192 + 13, 1024, "fused"),
     ("boundary", 4696, 2048, "auto"),
     ("boundary", 300, 1024, "invariant"),
+    ("boundary", 32, 7168, "stream"),
+    ("boundary", 4096 + 70, 2048, "stream"),
     ("pre", 50, 7168, "split"),
     ("pre", 37, 2048, "fused"),
     ("pre", 8192 + 13, 1024, "fused"),
@@ -699,3 +701,33 @@ def test_distinct_scales_pre_mixes(oracle):
         assert err <= COEF_TOL, f"{k} abs {err:.3g}"
     check_fresh_layer_input(host_bits(li), pre.cpu().numpy(), o, inp.X, inp.norm_w,
                             label="distinct pre_mixes")
+
+
+def test_schedules_share_one_workspace(oracle):
+    """One workspace, zero-filled once, serves every schedule and batch size in
+    any order: the split schedules' records never touch the streaming
+    schedule's counters, which every streaming call leaves at zero (the error
+    count included)."""
+    d, Tmax = 1024, 300
+    inp = WL.make_inputs(WL.Config("share", d=d, T=Tmax, seed=123, scale=(0.2, 0.1, 0.5)))
+    full = Dev(inp)
+    ws = api.workspace(Tmax, d)
+    counters = 196864
+    for schedule, T in (("split", 300), ("stream", 300), ("invariant", 37), ("stream", 37),
+                        ("pre", 300), ("stream", 300), ("split", 129), ("stream", 129)):
+        say(f"shared workspace: {schedule} T={T}")
+        sub = prefix(inp, T)
+        if schedule == "pre":
+            api.pre(full.X[:T], full.wp, full.scale, full.base, full.norm_w, prm=full.prm(), ws=ws)
+        else:
+            r = api.boundary(full.x[:T], full.X[:T], full.post[:T], full.comb[:T], full.pre_lag[:T],
+                             full.wp, full.scale, full.base, full.norm_w,
+                             prm=full.prm(schedule=schedule), debug=True, ws=ws)
+            torch.cuda.synchronize()
+            nres, post, comb, li, pre, mixes, rstd = r
+            g = dict(xn=host_bits(nres), post=post.cpu().numpy().reshape(-1, 4),
+                     comb=comb.cpu().numpy(), layer_input=host_bits(li), pre=pre.cpu().numpy(),
+                     mixes=mixes.cpu().numpy(), rstd=rstd.cpu().numpy())
+            compare(g, oracle.boundary(sub), label=f"shared {schedule} T={T}")
+        torch.cuda.synchronize()
+        assert not ws[:counters].any().item(), f"counters not zero after {schedule} T={T}"

@@ -37,6 +37,7 @@ def same(a, b):
     ("auto", 7168, 32, 9),           # the decode split
     ("invariant", 2048, 200, 50),    # finest split: the most records per token
     ("fused", 2048, 40, 17),         # no records: the scratch is not touched
+    ("stream", 2048, 700, 65),       # queue and tile counters at the start of the scratch
 ])
 def test_noalloc_matches_workspace_entry_point(schedule, d, T1, T2):
     print(f"[noalloc] schedule={schedule} d={d} T={T1} then T={T2}", flush=True)
@@ -60,7 +61,7 @@ def test_noalloc_matches_workspace_entry_point(schedule, d, T1, T2):
 
 
 def test_noalloc_refuses_beyond_its_scratch():
-    T, d = 4096, 8192
+    T, d = 8192, 16384
     x = torch.zeros(T, d, dtype=torch.bfloat16, device="cuda")
     X = torch.zeros(T, 4, d, dtype=torch.bfloat16, device="cuda")
     post, pre = torch.zeros(T, 4, device="cuda"), torch.zeros(T, 4, device="cuda")
