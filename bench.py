@@ -32,31 +32,42 @@ sys.path.insert(0, ROOT)
 METRIC = "mHC boundary tokens/s at d=7168 (decode T=32, prefill T=8192); % HBM roofline"
 HBM_PEAK_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
-TRAFFIC_PROFILE = os.path.join(PROFILES, "k_fused_w4_prefill_traffic.txt")
-KERNEL_SOURCES = [os.path.join(ROOT, "mhc_hyper_connection_boundary_amd", "csrc", f)
-                  for f in ("mhc_fused.hip", "mhc_device.h")]
+# The sources whose text decides each boundary kernel's memory traffic (the
+# names are those mhc_boundary_kernels reports).
+KERNEL_FILES = {
+    "k_fused_w4": ("mhc_fused.hip", "mhc_device.h"),
+    "k_fused": ("mhc_fused.hip", "mhc_device.h"),
+    "k_stream": ("mhc_stream.hip", "mhc_device.h"),
+    "k_partial+k_finish": ("mhc_kernels.hip", "mhc_device.h"),
+}
 COPY_BYTES = 1 << 30
 
 
-def kernel_sources_sha256() -> str:
+def traffic_profile_path(kernel: str) -> str:
+    return os.path.join(PROFILES, f"{kernel.replace('+', '_')}_prefill_traffic.txt")
+
+
+def kernel_sources_sha256(kernel: str) -> str:
     import hashlib
 
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(f, "rb") as fh:
+    for f in KERNEL_FILES[kernel]:
+        with open(os.path.join(ROOT, "mhc_hyper_connection_boundary_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def recorded_traffic():
-    """HBM bytes per call of the fused kernel from the committed counter
-    summary, if it was taken on the current kernel sources (else None)."""
+def recorded_traffic(kernel: str):
+    """HBM bytes per call of the kernel(s) from the committed counter summary,
+    if it was taken on the current kernel sources (else None)."""
+    if kernel not in KERNEL_FILES:
+        return None
     try:
-        with open(TRAFFIC_PROFILE) as f:
+        with open(traffic_profile_path(kernel)) as f:
             kv = dict(l.split(":", 1) for l in f if ":" in l and not l.startswith(" "))
     except OSError:
         return None
-    if kv.get("sources_sha256", "").strip() != kernel_sources_sha256():
+    if kv.get("sources_sha256", "").strip() != kernel_sources_sha256(kernel):
         return None
     return float(kv["traffic_bytes_per_call"])
 
@@ -373,8 +384,23 @@ def cpu_baseline(inp, budget_s=10.0):
         if dt >= budget_s:
             break
     return dict(value=tokens / dt, unit="tokens/s", cores=O.max_threads(), kind="oracle",
+                cpu=cpu_model(), logical_cpus=os.cpu_count(),
                 sample=f"{passes} pass(es) over the prefill batch (T={inp.T}, d={inp.d}), "
                        f"{dt:.1f} s wall")
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (first processor in /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+
+    return platform.processor() or "unknown"
 
 
 def copy_calibration():
@@ -404,20 +430,26 @@ def _counter_median(directory, counter, kernel_substr):
     return vals[len(vals) // 2], len(vals)
 
 
-def write_traffic_profile(prof_dir):
+def write_traffic_profile(prof_dir, kernel, schedule):
     """Summarises four rocprofv3 --pmc runs (see the command list written into
-    the summary) into profiles/k_fused_w4_prefill_traffic.txt."""
-    f_k, nf = _counter_median(os.path.join(prof_dir, "fetch_boundary"), "FETCH_SIZE", "k_fused_w4")
-    w_k, nw = _counter_median(os.path.join(prof_dir, "write_boundary"), "WRITE_SIZE", "k_fused_w4")
+    the summary) into profiles/<kernel>_prefill_traffic.txt.  For a schedule of
+    two kernels the per-call figure adds the two kernels' medians."""
+    f_k = w_k = 0.0
+    for name in kernel.split("+"):
+        fk, nf = _counter_median(os.path.join(prof_dir, "fetch_boundary"), "FETCH_SIZE", name)
+        wk, nw = _counter_median(os.path.join(prof_dir, "write_boundary"), "WRITE_SIZE", name)
+        f_k += fk
+        w_k += wk
     f_c, _ = _counter_median(os.path.join(prof_dir, "fetch_copy"), "FETCH_SIZE", "copyBuffer")
     w_c, _ = _counter_median(os.path.join(prof_dir, "write_copy"), "WRITE_SIZE", "copyBuffer")
     f_scale = COPY_BYTES / (f_c * 1024)
     w_scale = COPY_BYTES / (w_c * 1024)
     traffic = f_k * 1024 * f_scale + w_k * 1024 * w_scale
     T, d = 8192, 7168
+    sched = f" --schedule {schedule}" if schedule != "auto" else ""
     lines = [
-        "k_fused_w4<28> prefill (d=7168, T=8192): HBM traffic per launch from rocprofv3 counters",
-        f"sources_sha256: {kernel_sources_sha256()}",
+        f"{kernel} prefill (d=7168, T=8192): HBM traffic per call from rocprofv3 counters",
+        f"sources_sha256: {kernel_sources_sha256(kernel)}",
         f"fetch_size_kib_per_dispatch: {f_k:.1f}",
         f"write_size_kib_per_dispatch: {w_k:.1f}",
         f"dispatches: {nf} / {nw}",
@@ -431,14 +463,14 @@ def write_traffic_profile(prof_dir):
         f"algorithmic_bytes_per_call: {algorithmic_bytes(T, d)}",
         f"traffic_over_algorithmic: {traffic / algorithmic_bytes(T, d):.3f}",
         "commands (from the repository root, TMPDIR=/tmp):",
-        "  rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/fetch_boundary -o run -- python bench.py --steps 5 --warmup 2 --no-decode --no-cpu-baseline --no-entry-points --no-configs",
-        "  rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/write_boundary -o run -- python bench.py --steps 5 --warmup 2 --no-decode --no-cpu-baseline --no-entry-points --no-configs",
+        f"  rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/fetch_boundary -o run -- python bench.py --steps 5 --warmup 2 --no-decode --no-cpu-baseline --no-entry-points --no-configs{sched}",
+        f"  rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/write_boundary -o run -- python bench.py --steps 5 --warmup 2 --no-decode --no-cpu-baseline --no-entry-points --no-configs{sched}",
         "  rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/fetch_copy -o run -- python bench.py --copy-calibration",
         "  rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/write_copy -o run -- python bench.py --copy-calibration",
-        "  python bench.py --write-traffic-profile <dir>",
+        f"  python bench.py --write-traffic-profile <dir> --traffic-kernel {kernel}{sched}",
     ]
     os.makedirs(PROFILES, exist_ok=True)
-    with open(TRAFFIC_PROFILE, "w") as f:
+    with open(traffic_profile_path(kernel), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -450,7 +482,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--settle", type=float, default=0.3,
                     help="seconds of untimed prefill calls before the warmup steps")
-    ap.add_argument("--schedule", default="auto", choices=["auto", "split", "fused"])
+    ap.add_argument("--schedule", default="auto", choices=["auto", "split", "fused", "stream"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-configs", action="store_true",
@@ -463,9 +495,11 @@ def main():
                     help="time a plain 1 GiB device copy and exit")
     ap.add_argument("--write-traffic-profile", metavar="DIR",
                     help="summarise rocprofv3 counter runs under DIR into profiles/")
+    ap.add_argument("--traffic-kernel", default="k_fused_w4", choices=sorted(KERNEL_FILES),
+                    help="the kernel(s) the counter runs of --write-traffic-profile timed")
     a = ap.parse_args()
     if a.write_traffic_profile:
-        write_traffic_profile(a.write_traffic_profile)
+        write_traffic_profile(a.write_traffic_profile, a.traffic_kernel, a.schedule)
         return
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the boundary has "
@@ -490,14 +524,9 @@ def main():
     pct = percentiles_us(torch, w.call)
     b = algorithmic_bytes(T, d)
     gbs = b / (ms * 1e-3) / 1e9
-    # (on 256 compute units AUTO runs the 32-token fused kernel at this size)
-    fused = a.schedule == "fused" or (a.schedule == "auto" and T >= 3072)
-    if fused:
-        kernel = (f"k_fused_w4<{d // 256}>" if T >= 8192 else f"k_fused<{d // 512}>") + \
-            " (one launch per call)"
-    else:
-        kernel = "k_partial + k_finish"
-    traffic = recorded_traffic() if fused else None
+    # the kernels the library itself runs for this shape and schedule
+    kernel = w.api.boundary_kernels(T, d, a.schedule)
+    traffic = recorded_traffic(kernel)
     line = dict(
         metric=METRIC, value=T / (ms * 1e-3), unit="tokens/s", n_gpus=1, steps=a.steps,
         warmup=a.warmup, ms_per_step=ms, higher_is_better=True, scaling="weak",
@@ -506,7 +535,7 @@ def main():
                     schedule=a.schedule),
         roofline=dict(bound="hbm", achieved=gbs, peak=HBM_PEAK_GBS, unit="GB/s",
                       frac=gbs / HBM_PEAK_GBS, traffic=traffic, bytes_per_call=b,
-                      kernel=kernel),
+                      kernel=kernel, launches_per_call=len(kernel.split("+"))),
         us_per_call_percentiles=pct,
     )
     if not a.no_decode:

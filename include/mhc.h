@@ -264,8 +264,26 @@ mhc_status mhc_post(int tokens, int hidden, const uint16_t* x, const uint16_t* r
  * its producer) is to enqueue this on a stream forked from the caller's before
  * the producer of x, joined back before mhc_boundary, so the weight fetch
  * overlaps the producer instead of the boundary.  It writes nothing.
+ *
+ * NOT RECOMMENDED as a latency optimisation.  Measured in a HIP graph beside a
+ * 4 us producer, a decode call (32 tokens, hidden 7168) takes 27.7 us with the
+ * fork, prefetch and join against 12.1 us without; the most the prefetch can
+ * save is the cold-versus-warm weight fetch, about 1.2 us.  The join is a
+ * dependency between two streams of the graph, which the runtime resolves with
+ * a signal between hardware queues; that costs far more than the fetch it
+ * hides.  Callers get the better latency from the plain mhc_boundary call.
  * Errors: INVALID_ARGUMENT (NULL), UNSUPPORTED_SHAPE, MISALIGNED, DEVICE. */
 mhc_status mhc_prefetch_weight(const void* w_prepared, int hidden, void* stream);
+
+/* The kernels mhc_boundary launches for this batch size, width and schedule
+ * (an MHC_SCHEDULE_* value), as the library itself decides them: static text,
+ * "k_fused_w4" (32-token tiles, or fewer where AUTO balances the tiles over
+ * whole rounds of compute units), "k_fused" (16-token tiles),
+ * "k_partial+k_finish" (the split schedule: two launches) or "k_stream" (one
+ * persistent launch).  AUTO's choice depends on the current device's
+ * compute-unit count.  Returns "" where mhc_boundary would refuse the shape or
+ * the schedule, and for tokens <= 0 (nothing is launched).  Host only. */
+const char* mhc_boundary_kernels(int tokens, int hidden, int schedule);
 
 /* Static text for a status code (the refusal causes listed with mhc_status). */
 const char* mhc_status_string(mhc_status status);

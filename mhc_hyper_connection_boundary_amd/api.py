@@ -47,6 +47,8 @@ def lib() -> ctypes.CDLL:
         L.mhc_abi_version.argtypes = []
         L.mhc_status_string.restype = ctypes.c_char_p
         L.mhc_status_string.argtypes = [I]
+        L.mhc_boundary_kernels.restype = ctypes.c_char_p
+        L.mhc_boundary_kernels.argtypes = [I, I, I]
         L.mhc_prepared_weight_bytes.restype = Z
         L.mhc_prepared_weight_bytes.argtypes = [I]
         L.mhc_workspace_bytes.restype = Z
@@ -147,6 +149,12 @@ def _check_common(w_prepared, scale, base, norm_w, hidden, dev):
 
 def prepared_weight_bytes(hidden: int) -> int:
     return lib().mhc_prepared_weight_bytes(hidden)
+
+
+def boundary_kernels(tokens: int, hidden: int, schedule: str = "auto") -> str:
+    """The kernels mhc_boundary launches for this shape and schedule, as the
+    library decides them ("" where it would refuse or launch nothing)."""
+    return lib().mhc_boundary_kernels(int(tokens), int(hidden), SCHEDULES[schedule]).decode()
 
 
 def workspace_bytes(tokens: int, hidden: int) -> int:

@@ -358,6 +358,20 @@ const char* mhc_status_string(mhc_status s) {
     return "unknown status";
 }
 
+const char* mhc_boundary_kernels(int tokens, int hidden, int schedule) {
+    if (tokens <= 0 || tokens > MHC_MAX_TOKENS || !shape_ok(hidden) || schedule < MHC_SCHEDULE_AUTO ||
+        schedule > MHC_SCHEDULE_STREAM)
+        return "";
+    if (schedule == MHC_SCHEDULE_FUSED && !fused_supported(hidden)) return "";
+    switch (boundary_path(schedule, tokens, hidden).path) {
+        case BoundaryPath::Fused32: return "k_fused_w4";
+        case BoundaryPath::Fused16: return "k_fused";
+        case BoundaryPath::Stream: return "k_stream";
+        case BoundaryPath::Split: break;
+    }
+    return "k_partial+k_finish";
+}
+
 size_t mhc_prepared_weight_bytes(int hidden) {
     return shape_ok(hidden) ? (size_t)384 * hidden : 0;
 }

@@ -90,11 +90,17 @@ struct StreamArgs {
     Scalars p;
 };
 
-// Activations of one k-block for one lane: 8 hidden elements of the 4 streams
-// of X and of x, for token tc.
-struct ActS {
-    uint4 X[4];
-    uint4 x;
+// Activations of one step (two k-blocks, h = 0, 1) for one lane: 8 hidden
+// elements of the 4 streams of X and of x in each k-block.
+struct Act2 {
+    uint4 X[2][4];
+    uint4 x[2];
+};
+
+// The six weight fragments a thread stages for one step (named members: an
+// array here ends up in scratch memory).
+struct Frag6 {
+    uint4 f0, f1, f2, f3, f4, f5;
 };
 
 // The rows of one tile: X (4 per token), x, X' and the layer input, each a
@@ -116,40 +122,53 @@ __device__ __forceinline__ TileRows tile_rows(const StreamArgs& s, int b) {
     return r;
 }
 
-// Lane (n, g) of wave w: row 16w + n of the tile, 8 elements at column col.
-// X stream j sits j rows further (soffset j * row_bytes).
-template <bool NT>
-__device__ __forceinline__ void load_act_s(ActS& a, const TileRows& r, unsigned row, unsigned row_bytes,
-                                           unsigned col) {
+// Lane (n, g) of wave w: row 16w + n of the tile, 8 elements at column col
+// and at col + 32 (the other half of the same 128-byte line, loaded right
+// after it).  X stream j sits j rows further (soffset j * row_bytes).
+__device__ __forceinline__ void load_act2(Act2& a, const TileRows& r, unsigned row, unsigned row_bytes,
+                                          unsigned col) {
     const unsigned vX = row * 4 * row_bytes + col * 2, vx = row * row_bytes + col * 2;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-        a.X[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r.X, vX, j * row_bytes, NT ? 2 : 0));
-    a.x = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r.x, vx, 0, NT ? 2 : 0));
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            a.X[h][j] = __builtin_bit_cast(
+                uint4, __builtin_amdgcn_raw_buffer_load_b128(r.X, vX + h * kStep * 2, j * row_bytes, 0));
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+        a.x[h] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r.x, vx + h * kStep * 2, 0, 0));
 }
+
+// Device-coherent load of a float at byte offset off of a buffer resource
+// (0 past its end).  Unlike an atomic load, several can be in flight at once.
+__device__ __forceinline__ float ld_coh(__amdgpu_buffer_rsrc_t r, unsigned off) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kCoherent));
+}
+constexpr unsigned kOob = 0x40000000u;  // a buffer offset past every resource's end
 
 // Spin (thread 0) until *p is nonzero; false if the bound ran out.
 __device__ __forceinline__ bool wait_flag(const unsigned* p) {
     for (int n = 0; n < kSpinLimit; ++n) {
         if (ld_dev(p) != 0u) return true;
-        __builtin_amdgcn_s_sleep(2);
+        __builtin_amdgcn_s_sleep(20);  // about half a microsecond: few polls on the counters' lines
     }
     return false;
 }
 
-template <int KB, bool NORM, bool NT>
-__global__ __launch_bounds__(256) void k_stream(StreamArgs a) {
-    static_assert(KB >= 2 && KB <= 16, "k-blocks per item");
+template <int KB, bool NORM>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_stream(StreamArgs a) {
+    static_assert(KB % 2 == 0 && KB >= 6 && KB <= 16, "k-blocks per item");
+    constexpr int KS = KB / 2;                      // steps (pairs of k-blocks) per item
     constexpr int TT = kTileS;
     constexpr int kCoefTok = 3;                     // coefficient tokens handled at once
-    __shared__ uint4 frag[2][kFragsPerStep][64];    // a k-block's weight fragments, double buffered
+    constexpr unsigned kRec = kPart * 4;            // bytes per partial record
+    __shared__ uint4 frag[2][2 * kFragsPerStep][64];  // a step's weight fragments, double buffered
     __shared__ float cred[kCoefTok][8][26];
     __shared__ float ctot[kCoefTok][26];
-    __shared__ float srli[TT];
-    __shared__ float prev_s[TT][24];                // the next tile's post[4], comb[16], pre[4]
+    __shared__ float prev_s[2][TT][24];             // this and the next tile's post[4], comb[16], pre[4]
     __shared__ int s_next, s_last;
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
+    const int tid = threadIdx.x;
     const int S = a.slices, T = a.T, hidden = a.hidden;
     unsigned* const head = a.sync;
     unsigned* const exits = a.sync + 1;
@@ -158,29 +177,16 @@ __global__ __launch_bounds__(256) void k_stream(StreamArgs a) {
     unsigned* const flag = arrive + a.tiles;
     unsigned* const done = flag + a.tiles;
 
-    // Fragment words of k-block kb that this thread stages: fragments 3*wave .. 3*wave+2.
-    auto load_frag = [&](uint4 (&f)[3], int kb) {
-        const uint4* src = a.wprep + (size_t)kb * kFragsPerStep * 64 + lane;
-#pragma unroll
-        for (int k = 0; k < 3; ++k) f[k] = src[(3 * wave + k) * 64];
-    };
-    auto store_frag = [&](const uint4 (&f)[3], int buf) {
-#pragma unroll
-        for (int k = 0; k < 3; ++k) frag[buf][3 * wave + k][lane] = f[k];
-    };
-
     if (tid == 0) s_next = (int)add_dev(head, 1u);
     __syncthreads();
-    int q = s_next;
+    int q = __builtin_amdgcn_readfirstlane(s_next);
     __syncthreads();
     unsigned ticket = 0;  // (thread 0) the queue position of the item after q
-    if (tid == 0) ticket = add_dev(head, 1u);
 
-    // Pipeline state: activations and coefficients of the next partial k-block.
-    ActS cur;
-    PrevCoef c;
-    int buf = 0;
-    bool primed = false;  // cur / c / frag[buf] hold (q, k-block 0)
+    // Pipeline state: activations of the next partial step.
+    Act2 cur;
+    int buf = 0, pb = 0;
+    bool primed = false;  // cur / frag[buf] / prev_s[pb] hold (q, step 0)
     // (thread 0) the finisher counts of this item's and the previous item's
     // phase B: the tile and the value the done counter had.
     constexpr unsigned kNone = 0xffffffffu;
@@ -196,12 +202,59 @@ __global__ __launch_bounds__(256) void k_stream(StreamArgs a) {
     // (positions are compared as unsigned: whatever a counter holds, an item
     // outside [0, items) ends the loop and addresses nothing)
     while ((unsigned)q < (unsigned)a.items) {
+        // Lane indexes and everything derived from them are computed anew for
+        // each item: hoisted out of the loop they would hold registers
+        // throughout (and spill).
+        int tl = threadIdx.x;
+        asm volatile("" : "+v"(tl));
+        const int lane = tl & 63, n = lane & 15, g = lane >> 4;
+        const int wave = __builtin_amdgcn_readfirstlane(tl >> 6);
+        // Fragment words of step st (k-blocks 2 st, 2 st + 1: 24 fragments) that
+        // this thread stages: fragments 6*wave .. 6*wave+5.
+        auto load_frag = [&](int st) -> Frag6 {
+            const uint4* src = a.wprep + (size_t)st * 2 * kFragsPerStep * 64 + 6 * wave * 64 + lane;
+            return Frag6{src[0], src[64], src[128], src[192], src[256], src[320]};
+        };
+        auto store_frag = [&](const Frag6& f, int fbuf) {
+            uint4* dst = &frag[fbuf][6 * wave][lane];
+            dst[0] = f.f0;
+            dst[64] = f.f1;
+            dst[128] = f.f2;
+            dst[192] = f.f3;
+            dst[256] = f.f4;
+            dst[320] = f.f5;
+        };
+
+        // The previous-layer coefficients of the tile from token tok0 on go to
+        // prev_s: element e = tl + 256 k (k = 0, 1; e < 6 TT) is float4 e % 6 of
+        // token e / 6 (post, comb rows 0-3, pre).  The loads are unconditional
+        // (clamped indexes), so both are in flight together.
+        auto pc_load = [&](int k, int tok0) -> float4 {
+            const int e = min(tl + 256 * k, TT * 6 - 1);
+            const int tok = min(tok0 + e / 6, T - 1), part4 = e % 6;
+            const float* src = part4 == 0 ? a.post_prev + (size_t)tok * 4
+                             : part4 < 5 ? a.comb_prev + (size_t)tok * 16 + 4 * (part4 - 1)
+                                         : a.pre_lag + (size_t)tok * 4;
+            return *reinterpret_cast<const float4*>(src);
+        };
+        auto pc_store = [&](float4 v0, float4 v1, int pbuf) {
+            static_assert(256 < TT * 6 && TT * 6 <= 512, "two float4 per thread");
+            *reinterpret_cast<float4*>(&prev_s[pbuf][tl / 6][4 * (tl % 6)]) = v0;
+            const int e = tl + 256;
+            if (e < TT * 6) *reinterpret_cast<float4*>(&prev_s[pbuf][e / 6][4 * (e % 6)]) = v1;
+        };
+
         const int b = q / S, j = q - b * S;
         const bool has_partial = b < a.tiles;
         const int rt = b - a.lag;
         const bool has_rescale = rt >= 0 && rt < a.tiles;
         unsigned arrive_old = 0;
-        int qn = a.items;  // the next item (known from the second-to-last k-block on)
+        int qn = a.items;  // the next item (known in the last step)
+        // The next item is taken while this one runs: in its second step
+        // (it is needed in the last), or at once if it has no partial phase.  Taken any earlier, in particular before workgroups
+        // still starting up have taken their first items, it would hold back
+        // an item that another workgroup could run.
+        if (tid == 0 && !has_partial) ticket = add_dev(head, 1u);
 
         if (has_partial) {
             const unsigned row_bytes = (unsigned)hidden * 2, row = 16 * wave + n;
@@ -209,68 +262,83 @@ __global__ __launch_bounds__(256) void k_stream(StreamArgs a) {
             const bool valid = t < T;
             const TileRows rows = tile_rows(a, b);
             if (!primed) {
-                uint4 f[3];
-                load_frag(f, j * KB);
-                load_act_s<NT>(cur, rows, row, row_bytes, j * KB * kStep + g * 8);
-                load_prev(c, a.post_prev, a.comb_prev, a.pre_lag, valid ? (size_t)t : (size_t)(T - 1));
+                const Frag6 f = load_frag(j * KS);
+                const float4 pc0 = pc_load(0, b * TT), pc1 = pc_load(1, b * TT);
+                load_act2(cur, rows, row, row_bytes, j * KB * kStep + g * 8);
                 store_frag(f, buf);
+                pc_store(pc0, pc1, pb);
                 __syncthreads();
             }
             f32x4_t acc[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
             float ssq = 0.0f, ssq_li = 0.0f;
             TileRows rows_n = rows;
-            float4 pc_st[2];  // the next tile's previous-layer coefficients, on their way to LDS
+            float4 pcn0, pcn1;  // the next tile's previous-layer coefficients, on their way to LDS
             bool next_partial = false;
+            int jn = 0;         // the next item's slice
 #pragma unroll 1
-            for (int kb = 0; kb < KB; ++kb) {
-                const unsigned col = (j * KB + kb) * kStep + g * 8;
-                // The next k-block: (q, kb + 1), or the first one of the next
-                // item if that item has a partial phase.
-                bool have_next = kb + 1 < KB;
-                int next_kb = j * KB + kb + 1;
-                unsigned next_col = col + kStep;
-                if (kb + 1 == KB) {
-                    qn = s_next;
+            for (int st = 0; st < KS; ++st) {
+                const unsigned col = (j * KB + 2 * st) * kStep + g * 8;  // the step's first k-block
+                if (st == 1 && tid == 0) ticket = add_dev(head, 1u);
+                if (st + 1 == KS) {
+                    // The next item: its first step follows this item's last
+                    // one in the pipeline if it has a partial phase.
+                    qn = __builtin_amdgcn_readfirstlane(s_next);
                     next_partial = (unsigned)qn < (unsigned)a.items && qn / S < a.tiles;
-                    const int bn = next_partial ? qn / S : 0;
                     if (next_partial) {
-                        have_next = true;
-                        next_kb = (qn - bn * S) * KB;
-                        next_col = next_kb * kStep + g * 8;
+                        const int bn = qn / S;
+                        jn = qn - bn * S;
                         rows_n = tile_rows(a, bn);
-#pragma unroll
-                        for (int k = 0; k < 2; ++k) {
-                            const int e = tid + 256 * k;  // (token, float4) of the next tile
-                            const int tok = min(bn * TT + e / 6, T - 1), part4 = e % 6;
-                            const float* src = part4 == 0 ? a.post_prev + (size_t)tok * 4
-                                             : part4 < 5 ? a.comb_prev + (size_t)tok * 16 + 4 * (part4 - 1)
-                                                         : a.pre_lag + (size_t)tok * 4;
-                            if (e < TT * 6) pc_st[k] = *reinterpret_cast<const float4*>(src);
-                        }
+                        pcn0 = pc_load(0, bn * TT);
+                        pcn1 = pc_load(1, bn * TT);
                     }
                 }
-                uint4 fn[3];
-                ActS nxt;
-                if (have_next) {
-                    load_frag(fn, next_kb);
-                    load_act_s<NT>(nxt, kb + 1 < KB ? rows : rows_n, row, row_bytes, next_col);
+                // The next step's weight fragments and activations.
+                const bool have_next = st + 1 < KS || next_partial;
+                const int next_st = st + 1 < KS ? j * KS + st + 1 : jn * KS;  // (a step of the whole row)
+                // (the fragment loads are unconditional, so that they stay in registers)
+                const Frag6 fn = load_frag(have_next ? next_st : 0);
+                Act2 nxt;
+                if (have_next)
+                    load_act2(nxt, st + 1 < KS ? rows : rows_n, row, row_bytes, next_st * 2 * kStep + g * 8);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    // (the scheduler keeps the two k-blocks apart: interleaved,
+                    // they would need more registers than two waves per SIMD have)
+                    __builtin_amdgcn_sched_barrier(0);
+                    // this lane's token: post[4], comb[16], pre[4] (read for
+                    // each k-block: registers are scarcer than LDS bandwidth)
+                    PrevCoef c;
+                    const float* v = prev_s[pb][row];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) c.post[k] = v[k];
+#pragma unroll
+                    for (int k = 0; k < 16; ++k) c.comb[k] = v[4 + k];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) c.pre[k] = v[20 + k];
+                    uint4 Xn[4], li;
+                    update_collapse(cur.X[h], cur.x[h], c, Xn, li, ssq, ssq_li);
+                    const unsigned ch = col + h * kStep;
+                    const unsigned vX = row * 4 * row_bytes + ch * 2, vx = row * row_bytes + ch * 2;
+#pragma unroll
+                    for (int s2 = 0; s2 < 4; ++s2)
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, Xn[s2]), rows.Xo, vX,
+                                                               s2 * row_bytes, 0);
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, li), rows.li, vx, 0,
+                                                           NORM ? kCoherent : 0);
+                    // the projection, one stream's three A tiles at a time
+#pragma unroll
+                    for (int s2 = 0; s2 < 4; ++s2) {
+                        const bf16x8_t bx = __builtin_bit_cast(bf16x8_t, Xn[s2]);
+#pragma unroll
+                        for (int m = 0; m < 3; ++m)
+                            acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                __builtin_bit_cast(bf16x8_t, frag[buf][kFragsPerStep * h + 3 * s2 + m][lane]), bx,
+                                acc[m], 0, 0, 0);
+                    }
                 }
-                uint4 A[kFragsPerStep];
-#pragma unroll
-                for (int i = 0; i < kFragsPerStep; ++i) A[i] = frag[buf][i][lane];
-                uint4 Xn[4], li;
-                update_collapse(cur.X, cur.x, c, Xn, li, ssq, ssq_li);
-                const unsigned vX = row * 4 * row_bytes + col * 2, vx = row * row_bytes + col * 2;
-#pragma unroll
-                for (int s2 = 0; s2 < 4; ++s2)
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, Xn[s2]), rows.Xo, vX,
-                                                           s2 * row_bytes, NT ? 2 : 0);
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, li), rows.li, vx, 0,
-                                                       NORM ? kCoherent : 0);
-                mfma_step(A, Xn, acc);
                 if (have_next) store_frag(fn, buf ^ 1);
-                if (kb + 2 == KB) {
-                    if (tid == 0) s_next = (int)ticket;  // (the lookahead grab returned long ago)
+                if (st + 2 == KS) {
+                    if (tid == 0) s_next = (int)ticket;  // (the grab of step 1 returned long ago)
                 }
                 __syncthreads();
                 buf ^= 1;
@@ -297,31 +365,15 @@ __global__ __launch_bounds__(256) void k_stream(StreamArgs a) {
             }
             // Everything this thread wrote (records, li) has landed before the
             // tile counts this item in.  (This also waits for the next item's
-            // prefetch, which the next k-block needs first anyway.)
+            // first two k-blocks, requested one and two k-blocks ago.)
             __builtin_amdgcn_s_waitcnt(0);
             if (next_partial) {
-#pragma unroll
-                for (int k = 0; k < 2; ++k) {
-                    const int e = tid + 256 * k;
-                    if (e < TT * 6) *reinterpret_cast<float4*>(&prev_s[e / 6][4 * (e % 6)]) = pc_st[k];
-                }
+                pb ^= 1;
+                pc_store(pcn0, pcn1, pb);
             }
             __syncthreads();
             if (tid == 0) arrive_old = add_dev(arrive + b, 1u);
-            if (next_partial) {
-                // this lane's token of the next tile: post[4], comb[16], pre[4]
-                const float* v = prev_s[row];
-#pragma unroll
-                for (int k = 0; k < 4; ++k) c.post[k] = v[k];
-#pragma unroll
-                for (int k = 0; k < 16; ++k) c.comb[k] = v[4 + k];
-#pragma unroll
-                for (int k = 0; k < 4; ++k) c.pre[k] = v[20 + k];
-            }
         } else {
-            if (tid == 0) s_next = (int)ticket;
-            __syncthreads();
-            qn = s_next;
             primed = false;
         }
 
@@ -331,40 +383,117 @@ __global__ __launch_bounds__(256) void k_stream(StreamArgs a) {
                 if (!wait_flag(flag + rt)) add_dev(errors, 1u);
             }
             __syncthreads();
-            if (NORM && tid < TT) srli[tid] = rt * TT + tid < T ? ld_dev(a.rli + rt * TT + tid) : 0.0f;
-            __syncthreads();
-            // Coefficient tokens of this item: j, j + S, ... of the tile.
-            for (int k0 = j; k0 < TT; k0 += kCoefTok * S) {
-                // thread p = (token kk, group grp, value v): slices grp, grp + 8, ...
-                for (int p = tid; p < kCoefTok * 200; p += 256) {
-                    const int kk = p / 200, r = p % 200, grp = r / 25, v = r % 25;
-                    const int k = k0 + kk * S;
-                    const int tt = rt * TT + k;
-                    float sum = 0.0f;
-                    if (k < TT && tt < T) {
-                        const float* src = a.part + (size_t)tt * S * kPart + v;
-                        for (int sl = grp; sl < S; sl += 8) sum += ld_dev(src + (size_t)sl * kPart);
+            // The loads of the phase go out together: li of the slice with
+            // its rstd_li, then the records of the first coefficient round.
+            const int rows_r = min(TT, T - rt * TT);
+            // li of the slice for this wave's 16 tokens: 16 rows x 32*KB
+            // elements.  kLpr lanes cover a row's slice (16 bytes each), a
+            // load instruction covers kRpi rows.
+            constexpr int kLpr = KB * kStep / 8, kRpi = 64 / kLpr, kLoads = 16 / kRpi;
+            const int lcol = j * KB * kStep + (lane % kLpr) * 8;
+            uint4 lv[kLoads], nw;
+            float rl[kLoads];
+            if (NORM) {
+                const auto li_rs = rsrc(a.layer_input + (size_t)rt * TT * hidden, (unsigned)(rows_r * hidden * 2));
+                const auto rli_rs = rsrc(a.rli + (size_t)rt * TT, (unsigned)rows_r * 4);
+                nw = *reinterpret_cast<const uint4*>(a.norm_w + lcol);
+#pragma unroll
+                for (int i = 0; i < kLoads; ++i) {
+                    const int row = 16 * wave + kRpi * i + lane / kLpr;
+                    const unsigned off = (unsigned)((min(row, rows_r - 1) * hidden + lcol) * 2);
+                    lv[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(li_rs, off, 0, kCoherent));
+                    rl[i] = ld_coh(rli_rs, (unsigned)row * 4);
+                }
+            }
+            // Coefficient tokens of this item: j, j + S, ... of the tile, in
+            // rounds of kCoefTok (j < S <= TT: at least one round).  Thread
+            // p = tid + 256 it = (token kk, group grp, value v) adds slices grp,
+            // grp + 8, ... in order, four slices per load batch.
+            const auto rec_rs = rsrc(a.part + (size_t)rt * TT * S * kPart, (unsigned)rows_r * S * kRec);
+            // coefficient constants of this thread's place in a quad / DPP row
+            const CoefParams cpar = load_coef_params(a.scale, a.base, tl & 3);
+            const float bcomb16 = a.base[8 + (tl & 15)];
+            unsigned roff[3];
+            int rgrp[3];
+            float rval[3][4];
+            auto rec_site = [&](int k0, int it, unsigned& off, int& grp_out) {
+                const int p = tl + 256 * it, kk = p / 200, r = p - 200 * kk, grp = r / 25, v = r - 25 * grp;
+                const int k = k0 + kk * S;
+                grp_out = grp;
+                off = p < kCoefTok * 200 && k < rows_r ? ((unsigned)(k * S + grp) * kPart + v) * 4 : kOob;
+            };
+#pragma unroll
+            for (int it = 0; it < 3; ++it) {
+                rec_site(j, it, roff[it], rgrp[it]);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) rval[it][u] = ld_coh(rec_rs, roff[it] + (unsigned)(8 * u) * kRec);
+            }
+            if (NORM) {
+                // the normalised layer input of the slice
+#pragma unroll
+                for (int i = 0; i < kLoads; ++i) {
+                    const int row = 16 * wave + kRpi * i + lane / kLpr;
+                    if (row < rows_r) {
+                        const float r = rl[i];
+                        uint4 out;
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) {
+                            const uint32_t av = word(lv[i], k), bv = word(nw, k);
+                            set_word(out, k, pack_bf16((bf_lo(av) * r) * bf_lo(bv), (bf_hi(av) * r) * bf_hi(bv)));
+                        }
+                        *reinterpret_cast<uint4*>(a.layer_input + ((size_t)rt * TT + row) * hidden + lcol) = out;
                     }
-                    cred[kk][grp][v] = sum;
+                }
+            }
+            for (int k0 = j; k0 < TT; k0 += kCoefTok * S) {
+                if (k0 != j) {
+#pragma unroll
+                    for (int it = 0; it < 3; ++it) {
+                        rec_site(k0, it, roff[it], rgrp[it]);
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) rval[it][u] = ld_coh(rec_rs, roff[it] + (unsigned)(8 * u) * kRec);
+                    }
+                }
+                float sum[3] = {0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int it = 0; it < 3; ++it)
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        if (rgrp[it] + 8 * u < S) sum[it] += rval[it][u];
+                for (int s0 = 32; s0 < S; s0 += 32) {
+                    float val[3][4];
+#pragma unroll
+                    for (int it = 0; it < 3; ++it)
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) val[it][u] = ld_coh(rec_rs, roff[it] + (unsigned)(s0 + 8 * u) * kRec);
+#pragma unroll
+                    for (int it = 0; it < 3; ++it)
+#pragma unroll
+                        for (int u = 0; u < 4; ++u)
+                            if (rgrp[it] + s0 + 8 * u < S) sum[it] += val[it][u];
+                }
+#pragma unroll
+                for (int it = 0; it < 3; ++it) {
+                    const int p = tl + 256 * it, kk = p / 200, r = p - 200 * kk, grp = r / 25, v = r - 25 * grp;
+                    if (p < kCoefTok * 200) cred[kk][grp][v] = sum[it];
                 }
                 __syncthreads();
                 if (tid < kCoefTok * 25) {
-                    const int kk = tid / 25, v = tid % 25;
-                    float sum = 0.0f;
+                    const int kk = tl / 25, v = tl % 25;
+                    float s = 0.0f;
 #pragma unroll
-                    for (int grp = 0; grp < 8; ++grp) sum += cred[kk][grp][v];
-                    ctot[kk][v] = sum;
+                    for (int grp = 0; grp < 8; ++grp) s += cred[kk][grp][v];
+                    ctot[kk][v] = s;
                 }
                 __syncthreads();
                 if (tid < kCoefTok * 16) {
-                    const int kk = tid >> 4, l16 = tid & 15, i = tid & 3;
+                    const int kk = tl >> 4, l16 = tl & 15, i = tl & 3;
                     const int k = k0 + kk * S;
                     const int tt = rt * TT + k;
-                    const CoefParams cp = load_coef_params(a.scale, a.base, i);
                     TokenCoef o;
-                    pre_post(o, ctot[kk], i, hidden, cp, a.p);
-                    const float cv = comb16(ctot[kk], l16, o.rstd, cp.s2, a.base[8 + l16], a.p);
-                    if (k < TT && tt < T) {
+                    pre_post(o, ctot[kk], i, hidden, cpar, a.p);
+                    const float cv = comb16(ctot[kk], l16, o.rstd, cpar.s2, bcomb16, a.p);
+                    if (k < rows_r) {
                         a.comb_out[(size_t)tt * 16 + l16] = cv;
                         if (l16 < 4) {
                             a.pre_out[(size_t)tt * 4 + i] = o.pre;
@@ -378,38 +507,6 @@ __global__ __launch_bounds__(256) void k_stream(StreamArgs a) {
                 }
                 __syncthreads();
             }
-            if (NORM) {
-                // li of the slice for this wave's 16 tokens: 16 rows x 32*KB
-                // elements.  kLpr lanes cover a row's slice (16 bytes each), a
-                // load instruction covers kRpi rows.
-                constexpr int kLpr = KB * kStep / 8, kRpi = 64 / kLpr, kLoads = 16 / kRpi;
-                const int rows_r = min(TT, T - rt * TT);
-                const auto li_rs = rsrc(a.layer_input + (size_t)rt * TT * hidden, (unsigned)(rows_r * hidden * 2));
-                const int col = j * KB * kStep + (lane % kLpr) * 8;
-                const uint4 nw = *reinterpret_cast<const uint4*>(a.norm_w + col);
-                uint4 lv[kLoads];
-#pragma unroll
-                for (int i = 0; i < kLoads; ++i) {
-                    const int row = 16 * wave + kRpi * i + lane / kLpr;
-                    const unsigned off = (unsigned)((min(row, rows_r - 1) * hidden + col) * 2);
-                    lv[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(li_rs, off, 0, kCoherent));
-                }
-#pragma unroll
-                for (int i = 0; i < kLoads; ++i) {
-                    const int row = 16 * wave + kRpi * i + lane / kLpr;
-                    if (row < rows_r) {
-                        const float r = srli[row];
-                        uint4 out;
-#pragma unroll
-                        for (int k = 0; k < 4; ++k) {
-                            const uint32_t av = word(lv[i], k), bv = word(nw, k);
-                            set_word(out, k, pack_bf16((bf_lo(av) * r) * bf_lo(bv), (bf_hi(av) * r) * bf_hi(bv)));
-                        }
-                        *reinterpret_cast<uint4*>(a.layer_input + ((size_t)rt * TT + row) * hidden + col) = out;
-                    }
-                }
-            }
-            __syncthreads();
             if (tid == 0) {
                 // (its result is looked at one item later, when it has long returned)
                 this_done = add_dev(done + rt, 1u);
@@ -422,12 +519,27 @@ __global__ __launch_bounds__(256) void k_stream(StreamArgs a) {
             if (tid == 0) s_last = arrive_old == (unsigned)S - 1u;
             __syncthreads();
             if (s_last) {
-                if (NORM && tid < TT && b * TT + tid < T) {
-                    const size_t tt = (size_t)b * TT + tid;
-                    const float* src = a.part + tt * S * kPart + 25;
+                if (NORM) {
+                    // Four threads per token: thread (tok, part) adds slices
+                    // part, part + 4, ... in order, then the four sums are
+                    // added in order.  Rows past the batch read 0.
+                    const int tok = tl >> 2, part = tl & 3;
+                    const int rows_b = min(TT, T - b * TT);
+                    const auto rs = rsrc(a.part + (size_t)b * TT * S * kPart, (unsigned)rows_b * S * kRec);
+                    const unsigned off = ((unsigned)(tok * S + part) * kPart + 25) * 4;
                     float sum = 0.0f;
-                    for (int sl = 0; sl < S; ++sl) sum += ld_dev(src + (size_t)sl * kPart);
-                    st_dev(a.rli + tt, rsqrt_nr(sum * (1.0f / (float)hidden) + a.p.norm_eps));
+                    for (int s0 = 0; s0 < S; s0 += 32) {
+                        float v[8];
+#pragma unroll
+                        for (int u = 0; u < 8; ++u) v[u] = ld_coh(rs, off + (unsigned)(s0 + 4 * u) * kRec);
+#pragma unroll
+                        for (int u = 0; u < 8; ++u)
+                            if (part + s0 + 4 * u < S) sum += v[u];
+                    }
+                    const int q0 = lane & ~3;
+                    const float tot = ((__shfl(sum, q0) + __shfl(sum, q0 + 1)) + __shfl(sum, q0 + 2)) + __shfl(sum, q0 + 3);
+                    if (part == 0 && tok < rows_b)
+                        st_dev(a.rli + (size_t)b * TT + tok, rsqrt_nr(tot * (1.0f / (float)hidden) + a.p.norm_eps));
                 }
                 __builtin_amdgcn_s_waitcnt(0);
                 __syncthreads();
@@ -442,8 +554,12 @@ __global__ __launch_bounds__(256) void k_stream(StreamArgs a) {
             pending_done = this_done;
             this_rt = kNone;
         }
+        if (!has_partial) {
+            if (tid == 0) s_next = (int)ticket;
+            __syncthreads();
+            qn = __builtin_amdgcn_readfirstlane(s_next);
+        }
         q = qn;
-        if (tid == 0 && (unsigned)q < (unsigned)a.items) ticket = add_dev(head, 1u);
     }
     // Every workgroup ends here; the last one clears the queue.
     if (tid == 0) {
@@ -481,7 +597,7 @@ int stream_resident_workgroups() {
         int units = 0, per_unit = 0;
         const bool ok =
             hipDeviceGetAttribute(&units, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_unit, k_stream<kStreamKb, true, true>,
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_unit, k_stream<kStreamKb, true>,
                                                          256, 0) == hipSuccess;
         v = ok && units > 0 && per_unit > 0 ? units * per_unit : -1;
         cache[dev].store(v, std::memory_order_relaxed);
@@ -551,10 +667,10 @@ hipError_t launch_stream(const StreamPlan& plan, int T, int hidden, const uint16
     a.part = reinterpret_cast<float*>(ws + kCounterBytes + align256((size_t)T * 4));
     a.p = p;
     if (norm_w)
-        hipLaunchKernelGGL((k_stream<kStreamKb, true, true>), dim3(plan.grid), dim3(256), 0,
+        hipLaunchKernelGGL((k_stream<kStreamKb, true>), dim3(plan.grid), dim3(256), 0,
                            stream, a);
     else
-        hipLaunchKernelGGL((k_stream<kStreamKb, false, true>), dim3(plan.grid), dim3(256), 0,
+        hipLaunchKernelGGL((k_stream<kStreamKb, false>), dim3(plan.grid), dim3(256), 0,
                            stream, a);
     return hipGetLastError();
 }

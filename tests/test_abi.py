@@ -37,6 +37,23 @@ def test_exports_every_declared_symbol(L):
     assert L.mhc_status_string(3) == b"pointer not 16-byte aligned"
 
 
+def test_boundary_kernels_query(L):
+    """The kernel names follow the schedule; shapes mhc_boundary refuses, and
+    empty batches, name nothing.  (AUTO depends on the device, so only the
+    explicit schedules are pinned here.)"""
+    split, fused, invariant, stream = (api.SCHEDULES[k] for k in ("split", "fused", "invariant", "stream"))
+    assert L.mhc_boundary_kernels(8192, 7168, split) == b"k_partial+k_finish"
+    assert L.mhc_boundary_kernels(32, 7168, invariant) == b"k_partial+k_finish"
+    assert L.mhc_boundary_kernels(8192, 7168, stream) == b"k_stream"
+    assert L.mhc_boundary_kernels(8192, 7168, fused) == b"k_fused_w4"
+    assert L.mhc_boundary_kernels(100, 7168, fused) == b"k_fused"
+    assert L.mhc_boundary_kernels(0, 7168, split) == b""
+    assert L.mhc_boundary_kernels(32, 7000, split) == b""
+    assert L.mhc_boundary_kernels(32, 7168, 5) == b""
+    assert L.mhc_boundary_kernels(32, 7168, -1) == b""
+    assert api.boundary_kernels(8192, 7168, "stream") == "k_stream"
+
+
 COUNTERS = 196864   # the streaming schedule's counters: 4 * (3 + 3 * 2^20 / 64), rounded to 256
 
 

@@ -24,8 +24,10 @@ pytestmark = pytest.mark.gpu
 MIX_TOL = 2e-5
 COEF_TOL = 1e-5
 # Fraction of the fresh-pre layer input that must be bit-identical to the
-# oracle's (the rest lies within the derived bound of fresh_pre_bound).
-FRESH_EXACT_FLOOR = 0.9
+# oracle's (the rest lies within the derived bound of fresh_pre_bound).  The
+# lowest fraction measured over these cases is 0.9995 (the fused and split
+# pre at 7168 hidden); the floor sits just under it.
+FRESH_EXACT_FLOOR = 0.999
 
 
 def say(msg):
