@@ -204,6 +204,73 @@ def decode_numbers(steps, schedule):
                 roofline_frac_cold=b / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
 
 
+def decode_phases_run(schedule, reps=8):
+    """Cold decode calls (T=32, 64 rotating input sets) replayed from a HIP
+    graph, for a kernel trace: rocprofv3 --kernel-trace then gives each
+    kernel's duration and the gaps between the launches of a call."""
+    import torch
+
+    w = Workload("decode", schedule=schedule)
+    sets = [({k: v.clone() for k, v in w.t.items()}, w.wp.clone()) for _ in range(64)]
+    ms = graph_time(torch, [lambda t=t, wp=wp: w.call(t, wp) for t, wp in sets], reps)
+    return dict(workload="decode d=7168 T=32", schedule=schedule,
+                kernels=w.api.boundary_kernels(w.inp.T, w.inp.d, schedule),
+                timing="HIP graph replay, cold (64 rotating input sets)", us_per_call=ms * 1e3)
+
+
+def write_decode_profile(trace_dir, schedule):
+    """Summarises the kernel trace of --decode-phases into
+    profiles/boundary_decode_t32_phases.txt: per call, the duration of each
+    kernel and the idle time before it (from the previous kernel's end)."""
+    import csv
+    import glob
+
+    rows = []
+    for f in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]))
+    rows.sort()
+    names = ("k_partial", "k_finish", "k_stream", "k_fused")
+    short = lambda n: next((k for k in names if k in n), None)
+    seq = [(s, e, short(n)) for s, e, n in rows if short(n)]
+    # the last 64 * reps calls are the timed graph replays (after one capture run and one warm replay)
+    first = seq[0][2]
+    calls, cur = [], []
+    for s, e, n in seq:
+        if n == first and cur:
+            calls.append(cur)
+            cur = []
+        cur.append((s, e, n))
+    calls.append(cur)
+    calls = calls[-64 * 8:]
+    kinds = [n for _, _, n in calls[-1]]
+    med = lambda v: sorted(v)[len(v) // 2] / 1e3
+    lines = [f"mhc_boundary decode d=7168 T=32, schedule {schedule} ({' + '.join(kinds)}): "
+             "per-phase breakdown of cold graph-replayed calls from a rocprofv3 kernel trace, MI355X",
+             "commands (from the repository root, TMPDIR=/tmp):",
+             f"  rocprofv3 --kernel-trace --output-format csv -d <dir> -o run -- python bench.py --decode-phases --schedule {schedule}",
+             f"  python bench.py --write-decode-profile <dir> --schedule {schedule}",
+             f"calls summarised: {len(calls)} (the last 512 replayed calls; medians in us)"]
+    prev_end = None
+    for i, k in enumerate(kinds):
+        durs = [c[i][1] - c[i][0] for c in calls if len(c) == len(kinds)]
+        if i == 0:
+            gaps = [c2[0][0] - c1[-1][1] for c1, c2 in zip(calls, calls[1:])]
+            what = "idle before it (from the previous call's last kernel)"
+        else:
+            gaps = [c[i][0] - c[i - 1][1] for c in calls if len(c) == len(kinds)]
+            what = f"idle before it (from the end of {kinds[i - 1]})"
+        lines.append(f"  {k:10s} duration {med(durs):6.2f}   {what} {med(gaps):6.2f}")
+    span = [c[-1][1] - c[0][0] for c in calls if len(c) == len(kinds)]
+    period = [c2[0][0] - c1[0][0] for c1, c2 in zip(calls, calls[1:])]
+    lines.append(f"  first kernel start to last kernel end {med(span):6.2f}; call period {med(period):6.2f}")
+    os.makedirs(PROFILES, exist_ok=True)
+    out = os.path.join(PROFILES, f"boundary_decode_t32_{schedule}_phases.txt")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def percentiles_us(torch, fn, n=30):
     """Per-call HIP-event times of n back-to-back calls (µs): p10, median, p90."""
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -403,6 +470,47 @@ def cpu_model() -> str:
     return platform.processor() or "unknown"
 
 
+MOVER_MODES = {
+    0: "tile-major 32x256 items, 2 rows x 512 B per instruction, nontemporal",
+    1: "tile-major 32x256 items, 2 rows x 512 B per instruction, plain",
+    2: "streaming-schedule pattern: persistent, 64x256 items in 64-element steps, lockstep waves",
+}
+
+
+def mover_numbers(T=8192, d=7168, steps=10):
+    """The movers of libmhc_mover.so on the prefill shape: each reads X and x
+    and writes X' and a layer-input-sized buffer (the boundary's activation
+    bytes, 20*T*d) and computes nothing.  Their rate is the ceiling of an
+    HBM-bound kernel with that access pattern on this device."""
+    import ctypes
+
+    import torch
+
+    from mhc_hyper_connection_boundary_amd import build as B
+
+    L = ctypes.CDLL(B.MOVER_LIB)
+    L.mhc_mover_run.restype = ctypes.c_int
+    L.mhc_mover_run.argtypes = [ctypes.c_int, ctypes.c_int] + [ctypes.c_void_p] * 4 + [ctypes.c_int, ctypes.c_void_p]
+    dev = torch.device("cuda")
+    X = torch.ones(T, 4, d, dtype=torch.bfloat16, device=dev)
+    x = torch.ones(T, d, dtype=torch.bfloat16, device=dev)
+    Xo, lo = torch.empty_like(X), torch.empty_like(x)
+    moved = 2 * (X.numel() + x.numel()) * 2
+    st = torch.cuda.current_stream().cuda_stream
+    out = {}
+    for mode, what in MOVER_MODES.items():
+        run = lambda k: L.mhc_mover_run(T, d, X.data_ptr(), x.data_ptr(), Xo.data_ptr(), lo.data_ptr(), mode, st)
+        if run(0) != 0:
+            raise RuntimeError(f"mhc_mover_run mode {mode} refused the shape")
+        ms, _ = time_calls(torch, run, steps, 3)
+        out[f"mode {mode}"] = dict(pattern=what, us=ms * 1e3, gbs=moved / (ms * 1e-3) / 1e9,
+                                   frac=moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
+    del X, x, Xo, lo
+    torch.cuda.empty_cache()
+    return dict(workload=f"activation bytes of the prefill boundary (T={T}, d={d}): {moved} B per call",
+                **out)
+
+
 def copy_calibration():
     """A plain 1 GiB device copy: the device's practical streaming ceiling and the
     reference reading for the FETCH_SIZE / WRITE_SIZE counters."""
@@ -463,8 +571,8 @@ def write_traffic_profile(prof_dir, kernel, schedule):
         f"algorithmic_bytes_per_call: {algorithmic_bytes(T, d)}",
         f"traffic_over_algorithmic: {traffic / algorithmic_bytes(T, d):.3f}",
         "commands (from the repository root, TMPDIR=/tmp):",
-        f"  rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/fetch_boundary -o run -- python bench.py --steps 5 --warmup 2 --no-decode --no-cpu-baseline --no-entry-points --no-configs{sched}",
-        f"  rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/write_boundary -o run -- python bench.py --steps 5 --warmup 2 --no-decode --no-cpu-baseline --no-entry-points --no-configs{sched}",
+        f"  rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/fetch_boundary -o run -- python bench.py --steps 5 --warmup 2 --no-decode --no-cpu-baseline --no-entry-points --no-configs --no-mover{sched}",
+        f"  rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/write_boundary -o run -- python bench.py --steps 5 --warmup 2 --no-decode --no-cpu-baseline --no-entry-points --no-configs --no-mover{sched}",
         "  rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/fetch_copy -o run -- python bench.py --copy-calibration",
         "  rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/write_copy -o run -- python bench.py --copy-calibration",
         f"  python bench.py --write-traffic-profile <dir> --traffic-kernel {kernel}{sched}",
@@ -491,6 +599,13 @@ def main():
                     help="skip the mhc_pre / mhc_pre_mixes / mhc_post / invariant legs")
     ap.add_argument("--leg", metavar="NAME",
                     help="run only the entry-point legs whose name contains NAME and exit")
+    ap.add_argument("--decode-phases", action="store_true",
+                    help="cold graph-replayed decode calls for a kernel trace, then exit")
+    ap.add_argument("--write-decode-profile", metavar="DIR",
+                    help="summarise the kernel trace of --decode-phases under DIR into profiles/")
+    ap.add_argument("--mover", action="store_true",
+                    help="time the movers (the access-pattern ceilings) and exit")
+    ap.add_argument("--no-mover", action="store_true", help="leave the mover ceilings out of the line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain 1 GiB device copy and exit")
     ap.add_argument("--write-traffic-profile", metavar="DIR",
@@ -501,6 +616,9 @@ def main():
     if a.write_traffic_profile:
         write_traffic_profile(a.write_traffic_profile, a.traffic_kernel, a.schedule)
         return
+    if a.write_decode_profile:
+        write_decode_profile(a.write_decode_profile, a.schedule)
+        return
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the boundary has "
               "no cross-GPU step to measure", file=sys.stderr)
@@ -508,6 +626,12 @@ def main():
 
     if a.copy_calibration:
         print(json.dumps(copy_calibration()), flush=True)
+        return
+    if a.mover:
+        print(json.dumps(mover_numbers()), flush=True)
+        return
+    if a.decode_phases:
+        print(json.dumps(decode_phases_run(a.schedule)), flush=True)
         return
     if a.leg:
         print(json.dumps(entry_point_numbers(a.leg)), flush=True)
@@ -538,6 +662,9 @@ def main():
                       kernel=kernel, launches_per_call=len(kernel.split("+"))),
         us_per_call_percentiles=pct,
     )
+    if not a.no_mover:
+        print("[bench] movers (access-pattern ceilings)", file=sys.stderr, flush=True)
+        line["mover_ceiling"] = mover_numbers()
     if not a.no_decode:
         print("[bench] decode T=32", file=sys.stderr, flush=True)
         line["decode_t32"] = decode_numbers(200, a.schedule)

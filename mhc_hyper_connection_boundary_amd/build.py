@@ -16,6 +16,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmhc.so")
 SOURCES = ["mhc_api.hip", "mhc_kernels.hip", "mhc_fused.hip", "mhc_stream.hip"]
+# The movers (a measurement tool for bench.py; mhc_boundary never calls them).
+MOVER_LIB = os.path.join(PKG, "libmhc_mover.so")
+MOVER_SOURCE = "mhc_mover.hip"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 ARCH = ["--offload-arch=gfx950"]
@@ -49,8 +52,10 @@ def build(verbose: bool = False, resource_usage: bool = False) -> str:
             if resource_usage:
                 cmd.insert(1, "-Rpass-analysis=kernel-resource-usage")
             jobs.append((cmd, obj))
-        with ThreadPoolExecutor(max_workers=len(jobs)) as ex:
-            outs = list(ex.map(lambda j: _run(j[0], verbose), jobs))
+        mover_obj = os.path.join(tmp, "mhc_mover.o")
+        mover_cmd = [HIPCC, *ARCH, *FLAGS, "-c", os.path.join(CSRC, MOVER_SOURCE), "-o", mover_obj]
+        with ThreadPoolExecutor(max_workers=len(jobs) + 1) as ex:
+            outs = list(ex.map(lambda j: _run(j[0], verbose), jobs + [(mover_cmd, mover_obj)]))
         outs.append(_run([HIPCC, *ARCH, "-shared", "-fPIC", *(o for _, o in jobs),
                           "-o", LIB + ".tmp"], verbose))
         if verbose:
@@ -58,6 +63,8 @@ def build(verbose: bool = False, resource_usage: bool = False) -> str:
                 if m.strip():
                     print(m)
         os.replace(LIB + ".tmp", LIB)
+        outs.append(_run([HIPCC, *ARCH, "-shared", "-fPIC", mover_obj, "-o", MOVER_LIB + ".tmp"], verbose))
+        os.replace(MOVER_LIB + ".tmp", MOVER_LIB)
     return LIB
 
 
