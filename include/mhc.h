@@ -62,7 +62,7 @@ extern "C" {
 #define MHC_MIN_HIDDEN 256
 #define MHC_MAX_HIDDEN 16384
 /* Size of the device array that mhc_boundary_noalloc uses in place of a
- * workspace (16 MiB per GPU, held until the process ends). */
+ * workspace (64 MiB per GPU, held until the process ends). */
 #define MHC_NOALLOC_SCRATCH_BYTES (64u << 20)
 
 /* Status codes.  The refusals mirror the ones of mhc_shifted_post_pre_boundary
@@ -148,12 +148,25 @@ typedef struct {
 size_t mhc_prepared_weight_bytes(int hidden);
 
 /* Device workspace bytes that mhc_pre / mhc_boundary need for `tokens`
- * tokens of `hidden` under every schedule (partial sums of the split kernels:
- * 128 bytes per token per 128 elements of hidden, T * hidden bytes in all).
- * The vLLM page's kernel reduces a token's partial sums over its 16-CTA
- * cluster on chip (module description: fixed-order reductions; the kernel's
- * "totals in rank order"); the split schedules here pass them between
- * workgroups through this workspace instead. */
+ * tokens of `hidden` under every schedule.  The vLLM page's kernel reduces a
+ * token's partial sums over its 16-CTA cluster on chip (module description:
+ * fixed-order reductions; the kernel's "totals in rank order"); the split and
+ * streaming schedules here pass them between workgroups through this
+ * workspace instead.  Layout:
+ *   bytes [0, 196864)  the streaming schedule's counters (a queue head, then
+ *                      three 32-bit counters per 64-token tile, sized for
+ *                      MHC_MAX_TOKENS).  They must hold zeros before the
+ *                      workspace is first used with MHC_SCHEDULE_STREAM; every
+ *                      streaming call returns them to zero before it ends, and
+ *                      no other schedule writes them.  A workspace zero-filled
+ *                      once after allocation therefore serves every schedule
+ *                      and any number of calls (calls that share it must be
+ *                      ordered, e.g. on one stream).
+ *   the rest           partial records, rewritten by every call: the split
+ *                      schedules' 128 bytes per token per 128 elements of
+ *                      hidden (T * hidden bytes in all), or the streaming
+ *                      schedule's rstd_li (4 bytes per token, padded to 256)
+ *                      and 128 bytes per token per 256 elements of hidden. */
 size_t mhc_workspace_bytes(int tokens, int hidden);  /* 0 for tokens == 0 or an invalid shape */
 
 /* Round W to TF32, split it into BF16 high/low parts and write them in the
@@ -174,7 +187,8 @@ mhc_status mhc_prepare_weight(const float* w, int hidden, void* w_prepared, void
  *   layer_input [T, hidden] BF16                (written)
  *   pre, post   [T, 4] FP32; comb [T, 4, 4] FP32 (written; comb row i = source stream)
  *   mixes       [T, 24] FP32 or NULL; rstd [T] FP32 or NULL (debug outputs)
- *   workspace   >= mhc_workspace_bytes(T, hidden) bytes (scratch) */
+ *   workspace   >= mhc_workspace_bytes(T, hidden) bytes, zero-filled once
+ *               before its first use (layout at mhc_workspace_bytes) */
 mhc_status mhc_pre(int tokens, int hidden, const uint16_t* residual, const void* w_prepared,
                    const float* scale, const float* base, const uint16_t* norm_w,
                    const mhc_params* params, uint16_t* layer_input, float* pre, float* post,
@@ -204,19 +218,25 @@ mhc_status mhc_boundary(int tokens, int hidden, const uint16_t* x, const uint16_
 /* mhc_boundary for callers that cannot allocate device memory: code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
  * The same arguments, kernels and results as mhc_boundary (bit for bit), but
- * no workspace: the split schedules' partial records go to a device array of
+ * no workspace: what the workspace holds (the streaming schedule's counters,
+ * then the split or streaming schedule's partial records, in the layout
+ * described at mhc_workspace_bytes) goes to a device array of
  * MHC_NOALLOC_SCRATCH_BYTES inside the library (one per GPU, looked up on the
  * first call on each device and kept until the process ends).  The call itself
  * allocates nothing.
- *   Limit: batches whose schedule needs more record space than the array
- *   holds return MHC_ERR_SCRATCH_LIMIT with nothing enqueued.  The records take
- *   128 bytes per token per hidden slice of the split schedule; the fused
- *   kernels need none.  (INVARIANT: tokens * hidden bytes; at hidden 7168 AUTO
- *   fits every batch, since it runs the fused kernels from 3072 tokens.)
+ *   Limit: batches whose schedule needs more space than the array holds
+ *   return MHC_ERR_SCRATCH_LIMIT with nothing enqueued.  The space is the
+ *   192 KiB counters region plus 128 bytes per token per hidden slice of the
+ *   split schedule (INVARIANT: tokens * hidden bytes), or plus 4 + 128 *
+ *   (hidden / 256) bytes per token for STREAM; the fused kernels need none.
+ *   (At hidden 7168 AUTO fits every batch, since it runs the fused kernels
+ *   from 3072 tokens.)
  *   Sharing: every call on one GPU uses the same array, so calls that overlap
  *   in time on one GPU (concurrent streams) race and give wrong results;
- *   calls ordered on one stream are safe.  Each call overwrites what it needs,
- *   so nothing has to be cleared between calls.
+ *   calls ordered on one stream are safe.  The array starts zeroed, as the
+ *   counters require, and the streaming kernel leaves its counters at zero;
+ *   the records are overwritten by each call, so nothing has to be cleared
+ *   between calls.
  * Errors: those of mhc_boundary, with MHC_ERR_SCRATCH_LIMIT in place of
  * MHC_ERR_WORKSPACE. */
 mhc_status mhc_boundary_noalloc(int tokens, int hidden, const uint16_t* x,
