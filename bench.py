@@ -388,10 +388,10 @@ def entry_point_numbers(only=None):
             sets.append(st)
         return inp, sets
 
-    def pre_leg(T, d):
+    def pre_leg(T, d, schedule="auto"):
         nbytes = T * (10 * d + 96) + 384 * d + 108
         inp, sets = residual_sets(T, d, nbytes)
-        prm = api.params(**inp.params())
+        prm = api.params(**inp.params(), schedule=schedule)
         mk = lambda st: (lambda: api.pre(st["X"], st["wp"], st["scale"], st["base"], None,
                                          prm=prm, ws=st["ws"]))
         return nbytes, cold_graph_time(torch, mk, sets) * 1e3
@@ -422,6 +422,11 @@ def entry_point_numbers(only=None):
     for T, d, S in ((4096, 7168, 1), (4096, 4096, 1), (128, 7168, 1), (4096, 7168, 16)):
         legs.append((f"mhc_pre_mixes T={T} d={d} splits={S}", T, d,
                      lambda T=T, d=d, S=S: pre_mixes_leg(T, d, S), dict(splits=S)))
+    for T in (1, 32, 64):
+        # the single pass (X read once, one launch) beside the split schedule
+        for sched in ("onepass", "split"):
+            legs.append((f"mhc_pre {sched} T={T} d=7168", T, 7168,
+                         lambda T=T, sched=sched: pre_leg(T, 7168, sched), dict(schedule=sched)))
     for T in (8192, 32):
         legs.append((f"mhc_pre T={T} d=7168", T, 7168, lambda T=T: pre_leg(T, 7168), {}))
         legs.append((f"mhc_post T={T} d=7168", T, 7168, lambda T=T: post_leg(T, 7168), {}))

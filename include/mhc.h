@@ -113,9 +113,17 @@ typedef enum {
                                      tiles on 8 waves, or from 8192 tokens 32-token tiles on
                                      4 waves */
     MHC_SCHEDULE_INVARIANT = 3,   /* batch-invariant: split with an order fixed by hidden */
-    MHC_SCHEDULE_STREAM = 4       /* mhc_boundary: one persistent launch over a queue of
+    MHC_SCHEDULE_STREAM = 4,      /* mhc_boundary: one persistent launch over a queue of
                                      (64-token tile, 256-element slice) items in tile-major
                                      order; mhc_pre: SPLIT */
+    MHC_SCHEDULE_ONEPASS = 5      /* mhc_pre only: one launch that reads X once ([P]
+                                     "computing pre_mix early"), for 1 <= T <= 64 on a device
+                                     with at least hidden / 128 compute units (one workgroup
+                                     per 128 elements of hidden holds every token's slice of X
+                                     in registers; the workgroups wait on each other, so all
+                                     must be resident at once); UNSUPPORTED_SHAPE otherwise.
+                                     mhc_boundary refuses it (INVALID_ARGUMENT); mhc_pre_mixes
+                                     ignores the schedule. */
 } mhc_schedule;
 
 /* Runtime scalars (the pages pass them as kernel arguments). */

@@ -13,7 +13,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmhc.so")
 ABI_VERSION = 1
 
-SCHEDULES = {"auto": 0, "split": 1, "fused": 2, "invariant": 3, "stream": 4}
+SCHEDULES = {"auto": 0, "split": 1, "fused": 2, "invariant": 3, "stream": 4, "onepass": 5}
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape", 3: "misaligned",
           4: "aliasing", 5: "workspace", 6: "device", 7: "scratch limit"}
 

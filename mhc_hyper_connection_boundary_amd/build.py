@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmhc.so")
-SOURCES = ["mhc_api.hip", "mhc_kernels.hip", "mhc_fused.hip", "mhc_stream.hip"]
+SOURCES = ["mhc_api.hip", "mhc_kernels.hip", "mhc_fused.hip", "mhc_stream.hip", "mhc_pre_one.hip"]
 # The movers (a measurement tool for bench.py; mhc_boundary never calls them).
 MOVER_LIB = os.path.join(PKG, "libmhc_mover.so")
 MOVER_SOURCE = "mhc_mover.hip"

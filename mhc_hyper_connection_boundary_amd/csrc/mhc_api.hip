@@ -68,7 +68,7 @@ mhc_status check_params(const mhc_params* p) {
     if (!(p->rms_eps >= 0.f) || !(p->pre_eps >= 0.f) || !(p->sinkhorn_eps >= 0.f) ||
         !(p->norm_eps >= 0.f) || !(p->post_mult == p->post_mult))
         return MHC_ERR_INVALID_ARGUMENT;
-    if (p->schedule < MHC_SCHEDULE_AUTO || p->schedule > MHC_SCHEDULE_STREAM)
+    if (p->schedule < MHC_SCHEDULE_AUTO || p->schedule > MHC_SCHEDULE_ONEPASS)
         return MHC_ERR_INVALID_ARGUMENT;
     return MHC_OK;
 }
@@ -235,6 +235,7 @@ mhc_status check_boundary(int tokens, int hidden, const uint16_t* x, const uint1
                           float* post_out, float* comb_out, float* mixes, float* rstd) {
     mhc_status st = check_params(params);
     if (st != MHC_OK) return st;
+    if (params->schedule == MHC_SCHEDULE_ONEPASS) return MHC_ERR_INVALID_ARGUMENT;  // (mhc_pre only)
     if (tokens < 0) return MHC_ERR_INVALID_ARGUMENT;
     if (tokens > MHC_MAX_TOKENS || !shape_ok(hidden)) return MHC_ERR_UNSUPPORTED_SHAPE;
     if (params->schedule == MHC_SCHEDULE_FUSED && !fused_supported(hidden))
@@ -465,6 +466,9 @@ mhc_status mhc_pre(int tokens, int hidden, const uint16_t* residual, const void*
     if (tokens > MHC_MAX_TOKENS || !shape_ok(hidden)) return MHC_ERR_UNSUPPORTED_SHAPE;
     if (params->schedule == MHC_SCHEDULE_FUSED && !fused_supported(hidden))
         return MHC_ERR_UNSUPPORTED_SHAPE;
+    if (params->schedule == MHC_SCHEDULE_ONEPASS && tokens > 0 &&
+        !pre_one_supported(tokens, hidden, device_compute_units()))
+        return MHC_ERR_UNSUPPORTED_SHAPE;
     if (tokens == 0) return MHC_OK;
     if (!residual || !w_prepared || !scale || !base || !layer_input || !pre || !post || !comb)
         return MHC_ERR_INVALID_ARGUMENT;
@@ -489,6 +493,12 @@ mhc_status mhc_pre(int tokens, int hidden, const uint16_t* residual, const void*
         if (launch_fused_pre(tokens, hidden, residual, w_prepared, scale, base, norm_w, s,
                              layer_input, pre, post, comb, mixes, rstd, tokens >= kW4MinTokens,
                              hs) != hipSuccess)
+            return MHC_ERR_DEVICE;
+        return MHC_OK;
+    }
+    if (params->schedule == MHC_SCHEDULE_ONEPASS) {
+        if (launch_pre_one(tokens, hidden, residual, w_prepared, scale, base, norm_w, s, layer_input, pre,
+                           post, comb, mixes, rstd, workspace, hs) != hipSuccess)
             return MHC_ERR_DEVICE;
         return MHC_OK;
     }

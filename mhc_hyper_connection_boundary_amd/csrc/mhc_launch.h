@@ -124,6 +124,17 @@ struct StreamPlan {
 
 StreamPlan stream_plan(int T, int hidden);
 size_t stream_data_bytes(int T, int hidden);  // after the counters
+// Single-pass non-shifted pre (T <= 64, one workgroup per 128 elements of
+// hidden, all resident at once): whether it runs on a device with this many
+// compute units, the bytes of its records (after the counters region), and
+// the launch.
+bool pre_one_supported(int T, int hidden, int compute_units);
+size_t pre_one_data_bytes(int T, int hidden);
+hipError_t launch_pre_one(int T, int hidden, const uint16_t* X, const void* wprep, const float* scale,
+                          const float* base, const uint16_t* norm_w, const Scalars& p, uint16_t* layer_input,
+                          float* pre, float* post, float* comb, float* mixes, float* rstd, void* workspace,
+                          hipStream_t stream);
+
 hipError_t launch_stream(const StreamPlan& plan, int T, int hidden, const uint16_t* x,
                          const uint16_t* X, const float* post_prev, const float* comb_prev,
                          const float* pre_lag, const void* wprep, const float* scale,

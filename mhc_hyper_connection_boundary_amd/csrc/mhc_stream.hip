@@ -33,6 +33,7 @@
 // every launch, so the workspace must hold zeros before the first call only.
 #include <atomic>
 
+#include "mhc_coherent.h"
 #include "mhc_device.h"
 #include "mhc_launch.h"
 
@@ -41,30 +42,6 @@ namespace {
 
 constexpr int kWavesS = 4;
 constexpr int kTileS = kTile * kWavesS;  // 64 tokens per tile: one 16-token group per wave
-constexpr int kCoherent = 16;            // buffer cache-policy bit sc1: device-coherent access
-constexpr int kSpinLimit = 1 << 22;      // polls (with a short sleep) before a wait gives up
-
-// Buffer resource over `bytes` bytes from base: accesses past the end read 0
-// and write nothing.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, unsigned bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
-}
-
-__device__ __forceinline__ unsigned ld_dev(const unsigned* p) {
-    return __hip_atomic_load(const_cast<unsigned*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float ld_dev(const float* p) {
-    return __uint_as_float(ld_dev(reinterpret_cast<const unsigned*>(p)));
-}
-__device__ __forceinline__ void st_dev(unsigned* p, unsigned v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_dev(float* p, float v) {
-    st_dev(reinterpret_cast<unsigned*>(p), __float_as_uint(v));
-}
-__device__ __forceinline__ unsigned add_dev(unsigned* p, unsigned v) {
-    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 struct StreamArgs {
     int T, hidden, tiles, slices, lag, items;
@@ -139,21 +116,6 @@ __device__ __forceinline__ void load_act2(Act2& a, const TileRows& r, unsigned r
         a.x[h] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r.x, vx + h * kStep * 2, 0, 0));
 }
 
-// Device-coherent load of a float at byte offset off of a buffer resource
-// (0 past its end).  Unlike an atomic load, several can be in flight at once.
-__device__ __forceinline__ float ld_coh(__amdgpu_buffer_rsrc_t r, unsigned off) {
-    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kCoherent));
-}
-constexpr unsigned kOob = 0x40000000u;  // a buffer offset past every resource's end
-
-// Spin (thread 0) until *p is nonzero; false if the bound ran out.
-__device__ __forceinline__ bool wait_flag(const unsigned* p) {
-    for (int n = 0; n < kSpinLimit; ++n) {
-        if (ld_dev(p) != 0u) return true;
-        __builtin_amdgcn_s_sleep(20);  // about half a microsecond: few polls on the counters' lines
-    }
-    return false;
-}
 
 template <int KB, bool NORM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_stream(StreamArgs a) {

@@ -118,8 +118,10 @@ def test_boundary_refusals(L):
     assert call(L, b, prm=ctypes.byref(api.params(rms_eps=-1.0))) == INVALID
     assert call(L, b, prm=ctypes.byref(api.params(norm_eps=float("nan")))) == INVALID
     bad_schedule = api.params()
-    bad_schedule.schedule = 5
+    bad_schedule.schedule = 6
     assert call(L, b, prm=ctypes.byref(bad_schedule)) == INVALID
+    # the single-pass schedule belongs to mhc_pre; the boundary refuses it
+    assert call(L, b, prm=ctypes.byref(api.params(schedule="onepass"))) == INVALID
     assert call(L, b, d=1000) == SHAPE
     assert call(L, b, d=128) == SHAPE
     assert call(L, b, T=(1 << 20) + 1) == SHAPE
@@ -149,6 +151,10 @@ def test_pre_refusals(L):
     assert pre(li=a["residual"]) == ALIASING
     assert pre(ws=0) == WORKSPACE
     assert pre(prm=ctypes.byref(api.params(sinkhorn_iters=0))) == INVALID
+    # the single pass holds at most 64 tokens (one 16-token group per wave)
+    onepass = ctypes.byref(api.params(schedule="onepass"))
+    assert pre(T=65, prm=onepass) == SHAPE
+    assert pre(T=0, prm=onepass) == OK
 
 
 def test_prepare_weight_refusals(L):

@@ -421,6 +421,50 @@ def test_pre_fused_32_token_tiles(oracle, T, d):
     compare(g, o, xn=False, label=f"pre w4 T={T} d={d}", fresh=(inp.X, inp.norm_w))
 
 
+@pytest.mark.parametrize("T,d", [(1, 7168), (16, 256), (33, 1024), (7, 2048), (32, 7168),
+                                 (64, 7168), (64, 16384), (50, 4096)])
+def test_pre_onepass(oracle, T, d):
+    """The single-pass pre (one launch, X read once) against the oracle, with
+    distinct scales per coefficient group, with and without the norm; twice in
+    a row on one workspace (its barrier counters must be back at zero)."""
+    say(f"pre onepass T={T} d={d}")
+    inp = distinct_inputs(T, d, seed=3 * T + d)
+    dv = Dev(inp)
+    ws = api.workspace(T, d)
+    for norm in (True, False, True):
+        r = api.pre(dv.X, dv.wp, dv.scale, dv.base, dv.norm_w if norm else None,
+                    prm=dv.prm(schedule="onepass"), debug=True, ws=ws)
+        torch.cuda.synchronize()
+        li, pre, post, comb, mixes, rstd = r
+        g = dict(layer_input=host_bits(li), pre=pre.cpu().numpy(),
+                 post=post.cpu().numpy().reshape(-1, 4), comb=comb.cpu().numpy(),
+                 mixes=mixes.cpu().numpy(), rstd=rstd.cpu().numpy())
+        compare(g, oracle.pre(inp, use_norm=norm), xn=False, label=f"pre onepass T={T} d={d} norm={norm}",
+                fresh=(inp.X, inp.norm_w if norm else None))
+        assert not ws[:16].any().item(), "barrier counters not back at zero (or a wait ran out)"
+
+
+def test_pre_onepass_is_deterministic():
+    inp = distinct_inputs(40, 7168, seed=77)
+    dv = Dev(inp)
+    first = dv.pre(norm=True, schedule="onepass")
+    for _ in range(3):
+        again = dv.pre(norm=True, schedule="onepass")
+        for k in first:
+            assert np.array_equal(first[k], again[k]), f"run-to-run difference in {k}"
+
+
+def test_pre_onepass_refuses_large_batches():
+    inp = WL.make_inputs(WL.Config("po", d=1024, T=65, seed=2))
+    dv = Dev(inp)
+    with pytest.raises(api.MhcError) as e:
+        dv.pre(schedule="onepass")
+    assert e.value.status == 2
+    with pytest.raises(api.MhcError) as e:
+        dv.boundary(schedule="onepass")
+    assert e.value.status == 1
+
+
 def test_pre_fused_refuses_unsupported_width():
     inp = WL.make_inputs(WL.Config("pu", d=1280, T=4, seed=1))
     dv = Dev(inp)
@@ -716,11 +760,22 @@ def test_schedules_share_one_workspace(oracle):
     ws = api.workspace(Tmax, d)
     counters = 196864
     for schedule, T in (("split", 300), ("stream", 300), ("invariant", 37), ("stream", 37),
-                        ("pre", 300), ("stream", 300), ("split", 129), ("stream", 129)):
+                        ("pre", 300), ("stream", 300), ("onepass", 64), ("split", 129),
+                        ("onepass", 5), ("stream", 129)):
         say(f"shared workspace: {schedule} T={T}")
         sub = prefix(inp, T)
         if schedule == "pre":
             api.pre(full.X[:T], full.wp, full.scale, full.base, full.norm_w, prm=full.prm(), ws=ws)
+        elif schedule == "onepass":
+            r = api.pre(full.X[:T], full.wp, full.scale, full.base, full.norm_w,
+                        prm=full.prm(schedule="onepass"), debug=True, ws=ws)
+            torch.cuda.synchronize()
+            li, pre, post, comb, mixes, rstd = r
+            g = dict(layer_input=host_bits(li), pre=pre.cpu().numpy(),
+                     post=post.cpu().numpy().reshape(-1, 4), comb=comb.cpu().numpy(),
+                     mixes=mixes.cpu().numpy(), rstd=rstd.cpu().numpy())
+            compare(g, oracle.pre(sub, use_norm=True), xn=False, label=f"shared onepass T={T}",
+                    fresh=(sub.X, sub.norm_w))
         else:
             r = api.boundary(full.x[:T], full.X[:T], full.post[:T], full.comb[:T], full.pre_lag[:T],
                              full.wp, full.scale, full.base, full.norm_w,
