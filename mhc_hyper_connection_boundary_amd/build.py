@@ -16,6 +16,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmhc.so")
 SOURCES = ["mhc_api.hip", "mhc_kernels.hip", "mhc_fused.hip", "mhc_stream.hip", "mhc_pre_one.hip"]
+# The LDS-poison debug build: the same sources with -DMHC_LDS_POISON (every
+# kernel fills its LDS with NaN before use); the tests run it beside libmhc.so.
+POISON_LIB = os.path.join(PKG, "libmhc_lds_poison.so")
 # The movers (a measurement tool for bench.py; mhc_boundary never calls them).
 MOVER_LIB = os.path.join(PKG, "libmhc_mover.so")
 MOVER_SOURCE = "mhc_mover.hip"
@@ -52,10 +55,15 @@ def build(verbose: bool = False, resource_usage: bool = False) -> str:
             if resource_usage:
                 cmd.insert(1, "-Rpass-analysis=kernel-resource-usage")
             jobs.append((cmd, obj))
+        poison_jobs = []
+        for s in SOURCES:
+            obj = os.path.join(tmp, "poison_" + os.path.splitext(s)[0] + ".o")
+            poison_jobs.append(([HIPCC, *ARCH, *FLAGS, "-DMHC_LDS_POISON", "-I", os.path.join(ROOT, "include"),
+                                 "-c", os.path.join(CSRC, s), "-o", obj], obj))
         mover_obj = os.path.join(tmp, "mhc_mover.o")
         mover_cmd = [HIPCC, *ARCH, *FLAGS, "-c", os.path.join(CSRC, MOVER_SOURCE), "-o", mover_obj]
-        with ThreadPoolExecutor(max_workers=len(jobs) + 1) as ex:
-            outs = list(ex.map(lambda j: _run(j[0], verbose), jobs + [(mover_cmd, mover_obj)]))
+        with ThreadPoolExecutor(max_workers=min(16, 2 * len(jobs) + 1)) as ex:
+            outs = list(ex.map(lambda j: _run(j[0], verbose), jobs + poison_jobs + [(mover_cmd, mover_obj)]))
         outs.append(_run([HIPCC, *ARCH, "-shared", "-fPIC", *(o for _, o in jobs),
                           "-o", LIB + ".tmp"], verbose))
         if verbose:
@@ -65,6 +73,9 @@ def build(verbose: bool = False, resource_usage: bool = False) -> str:
         os.replace(LIB + ".tmp", LIB)
         outs.append(_run([HIPCC, *ARCH, "-shared", "-fPIC", mover_obj, "-o", MOVER_LIB + ".tmp"], verbose))
         os.replace(MOVER_LIB + ".tmp", MOVER_LIB)
+        outs.append(_run([HIPCC, *ARCH, "-shared", "-fPIC", *(o for _, o in poison_jobs),
+                          "-o", POISON_LIB + ".tmp"], verbose))
+        os.replace(POISON_LIB + ".tmp", POISON_LIB)
     return LIB
 
 

@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <cstdlib>
 
 #include "mhc.h"
 #include "mhc_device.h"
@@ -271,6 +272,25 @@ size_t boundary_scratch_bytes(int tokens, int hidden, int schedule) {
 }
 
 // Launches of a validated call; part receives the split schedules' records.
+// MHC_SYNC_DEBUG=1 in the environment (read once per process): every entry
+// point waits for the kernels it enqueued and reports a failed one as
+// MHC_ERR_DEVICE, so a fault is tied to the call that caused it.  A debugging
+// aid: it makes each call synchronous, and a stream under graph capture cannot
+// be waited on.
+bool sync_debug() {
+    static const bool on = [] {
+        const char* e = std::getenv("MHC_SYNC_DEBUG");
+        return e != nullptr && e[0] == '1' && e[1] == '\0';
+    }();
+    return on;
+}
+
+mhc_status finish_call(mhc_status st, hipStream_t stream) {
+    if (st != MHC_OK || !sync_debug()) return st;
+    if (hipStreamSynchronize(stream) != hipSuccess) return MHC_ERR_DEVICE;
+    return hipGetLastError() == hipSuccess ? MHC_OK : MHC_ERR_DEVICE;
+}
+
 mhc_status run_boundary(int tokens, int hidden, const uint16_t* x, const uint16_t* residual,
                         const float* post_prev, const float* comb_prev, const float* pre_lag,
                         const void* w_prepared, const float* scale, const float* base,
@@ -392,7 +412,7 @@ mhc_status mhc_prepare_weight(const float* w, int hidden, void* w_prepared, void
     if (overlap(out, in)) return MHC_ERR_ALIASING;
     if (launch_prepare_weight(w, hidden, w_prepared, (hipStream_t)stream) != hipSuccess)
         return MHC_ERR_DEVICE;
-    return MHC_OK;
+    return finish_call(MHC_OK, (hipStream_t)stream);
 }
 
 mhc_status mhc_pre_mixes(int tokens, int hidden, int splits, const uint16_t* residual,
@@ -421,7 +441,7 @@ mhc_status mhc_pre_mixes(int tokens, int hidden, int splits, const uint16_t* res
                          scalars(params), layer_input, pre, post, comb,
                          (hipStream_t)stream) != hipSuccess)
         return MHC_ERR_DEVICE;
-    return MHC_OK;
+    return finish_call(MHC_OK, (hipStream_t)stream);
 }
 
 mhc_status mhc_prefetch_weight(const void* w_prepared, int hidden, void* stream) {
@@ -430,7 +450,7 @@ mhc_status mhc_prefetch_weight(const void* w_prepared, int hidden, void* stream)
     if (!aligned(w_prepared)) return MHC_ERR_MISALIGNED;
     if (launch_prefetch_weight(w_prepared, hidden, (hipStream_t)stream) != hipSuccess)
         return MHC_ERR_DEVICE;
-    return MHC_OK;
+    return finish_call(MHC_OK, (hipStream_t)stream);
 }
 
 mhc_status mhc_post(int tokens, int hidden, const uint16_t* x, const uint16_t* residual,
@@ -452,7 +472,7 @@ mhc_status mhc_post(int tokens, int hidden, const uint16_t* x, const uint16_t* r
     if (launch_post(tokens, hidden, x, residual, post_prev, comb_prev, residual_out,
                     (hipStream_t)stream) != hipSuccess)
         return MHC_ERR_DEVICE;
-    return MHC_OK;
+    return finish_call(MHC_OK, (hipStream_t)stream);
 }
 
 mhc_status mhc_pre(int tokens, int hidden, const uint16_t* residual, const void* w_prepared,
@@ -494,13 +514,13 @@ mhc_status mhc_pre(int tokens, int hidden, const uint16_t* residual, const void*
                              layer_input, pre, post, comb, mixes, rstd, tokens >= kW4MinTokens,
                              hs) != hipSuccess)
             return MHC_ERR_DEVICE;
-        return MHC_OK;
+        return finish_call(MHC_OK, hs);
     }
     if (params->schedule == MHC_SCHEDULE_ONEPASS) {
         if (launch_pre_one(tokens, hidden, residual, w_prepared, scale, base, norm_w, s, layer_input, pre,
                            post, comb, mixes, rstd, workspace, hs) != hipSuccess)
             return MHC_ERR_DEVICE;
-        return MHC_OK;
+        return finish_call(MHC_OK, hs);
     }
     const SplitPlan plan =
         split_plan(tokens, hidden, params->schedule == MHC_SCHEDULE_INVARIANT, false);
@@ -512,7 +532,7 @@ mhc_status mhc_pre(int tokens, int hidden, const uint16_t* residual, const void*
     if (launch_pre_finish(plan, tokens, hidden, residual, part, scale, base, norm_w, s,
                           layer_input, pre, post, comb, mixes, rstd, hs) != hipSuccess)
         return MHC_ERR_DEVICE;
-    return MHC_OK;
+    return finish_call(MHC_OK, hs);
 }
 
 mhc_status mhc_boundary(int tokens, int hidden, const uint16_t* x, const uint16_t* residual,
@@ -538,9 +558,11 @@ mhc_status mhc_boundary(int tokens, int hidden, const uint16_t* x, const uint16_
                            {mixes, mixes ? T * 96 : 0}, {rstd, rstd ? T * 4 : 0}};
     if (any_alias(&ws, 1, others, 16)) return MHC_ERR_ALIASING;
     if (!workspace || workspace_bytes < need) return MHC_ERR_WORKSPACE;
-    return run_boundary(tokens, hidden, x, residual, post_prev, comb_prev, pre_lag, w_prepared,
-                        scale, base, norm_w, params, residual_out, layer_input, pre_out, post_out,
-                        comb_out, mixes, rstd, workspace, (hipStream_t)stream);
+    return finish_call(run_boundary(tokens, hidden, x, residual, post_prev, comb_prev, pre_lag,
+                                    w_prepared, scale, base, norm_w, params, residual_out,
+                                    layer_input, pre_out, post_out, comb_out, mixes, rstd, workspace,
+                                    (hipStream_t)stream),
+                       (hipStream_t)stream);
 }
 
 mhc_status mhc_boundary_noalloc(int tokens, int hidden, const uint16_t* x,
@@ -559,9 +581,11 @@ mhc_status mhc_boundary_noalloc(int tokens, int hidden, const uint16_t* x,
         return MHC_ERR_SCRATCH_LIMIT;
     void* ws = scratch_address();
     if (!ws) return MHC_ERR_DEVICE;
-    return run_boundary(tokens, hidden, x, residual, post_prev, comb_prev, pre_lag, w_prepared,
-                        scale, base, norm_w, params, residual_out, layer_input, pre_out, post_out,
-                        comb_out, mixes, rstd, ws, (hipStream_t)stream);
+    return finish_call(run_boundary(tokens, hidden, x, residual, post_prev, comb_prev, pre_lag,
+                                    w_prepared, scale, base, norm_w, params, residual_out,
+                                    layer_input, pre_out, post_out, comb_out, mixes, rstd, ws,
+                                    (hipStream_t)stream),
+                       (hipStream_t)stream);
 }
 
 }  // extern "C"

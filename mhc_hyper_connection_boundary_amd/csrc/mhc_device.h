@@ -30,6 +30,28 @@ struct Scalars {
     float norm_eps;
 };
 
+// ---- LDS-poison debug build ------------------------------------------------
+//
+// Built with -DMHC_LDS_POISON (libmhc_lds_poison.so), every kernel starts by
+// filling its workgroup's whole LDS allocation (the static arrays, plus
+// dyn_bytes of dynamic LDS) with all-ones words, a NaN as FP32, so a read of
+// LDS that the kernel never wrote turns its outputs into NaN instead of
+// reusing whatever an earlier workgroup left there.  In the product build the
+// macro is empty.
+#ifdef MHC_LDS_POISON
+__device__ __forceinline__ void poison_lds(unsigned dyn_bytes) {
+    const unsigned words = (__builtin_amdgcn_groupstaticsize() + dyn_bytes) / 4;
+    // (LDS address 0 from a run-time value: a literal 0 would be the null pointer)
+    __attribute__((address_space(3))) unsigned* lds =
+        (__attribute__((address_space(3))) unsigned*)(uintptr_t)__builtin_amdgcn_readfirstlane(0u);
+    for (unsigned i = threadIdx.x; i < words; i += blockDim.x) lds[i] = 0xffffffffu;
+    __syncthreads();
+}
+#define MHC_POISON_LDS(dyn_bytes) ::mhc::poison_lds(dyn_bytes)
+#else
+#define MHC_POISON_LDS(dyn_bytes) ((void)0)
+#endif
+
 // ---- BF16 <-> FP32 --------------------------------------------------------
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }

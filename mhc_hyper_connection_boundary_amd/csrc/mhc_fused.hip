@@ -248,6 +248,7 @@ __global__ __launch_bounds__(512) void k_fused(
     uint16_t* __restrict__ layer_input, float* __restrict__ pre_out,
     float* __restrict__ post_out, float* __restrict__ comb_out, float* __restrict__ mixes_out,
     float* __restrict__ rstd_out) {
+    MHC_POISON_LDS(0);
     using Shape = FusedShape<S>;
     constexpr int hidden = S * kWide * kWaves;
     __shared__ uint4 li_lds[Shape::kLiLds > 0 ? Shape::kLiLds : 1][kWaves][2][64];
@@ -411,6 +412,7 @@ __global__ __launch_bounds__(256) void k_fused_w4(
     uint16_t* __restrict__ layer_input, float* __restrict__ pre_out,
     float* __restrict__ post_out, float* __restrict__ comb_out, float* __restrict__ mixes_out,
     float* __restrict__ rstd_out) {
+    MHC_POISON_LDS(0);
     // 9 li steps in LDS: the cross-wave sums need no buffer per wave.
     using Shape = FusedW4Shape<S, 9>;
     constexpr int hidden = S * kWide * kWaves4;
@@ -662,6 +664,7 @@ __global__ __launch_bounds__(512) void k_fused_pre(
     const uint16_t* __restrict__ norm_w, Scalars p, uint16_t* __restrict__ layer_input,
     float* __restrict__ pre_out, float* __restrict__ post_out, float* __restrict__ comb_out,
     float* __restrict__ mixes_out, float* __restrict__ rstd_out) {
+    MHC_POISON_LDS(0);
     using Shape = FusedShape<S>;
     using PreShape = FusedPreShape<S>;
     constexpr int hidden = S * kWide * kWaves;
@@ -794,6 +797,7 @@ __global__ __launch_bounds__(256) void k_fused_pre_w4(
     const uint16_t* __restrict__ norm_w, Scalars p, uint16_t* __restrict__ layer_input,
     float* __restrict__ pre_out, float* __restrict__ post_out, float* __restrict__ comb_out,
     float* __restrict__ mixes_out, float* __restrict__ rstd_out) {
+    MHC_POISON_LDS(0);
     using Shape = FusedW4Shape<S, 9>;
     constexpr int hidden = S * kWide * kWaves4;
     __shared__ uint4 li_lds[Shape::kLiLds > 0 ? Shape::kLiLds : 1][kWaves4][2][2][64];

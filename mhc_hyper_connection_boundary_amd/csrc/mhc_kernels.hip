@@ -75,6 +75,7 @@ __global__ __launch_bounds__(256) void k_partial(
     const float* __restrict__ comb_prev, const float* __restrict__ pre_lag,
     const uint4* __restrict__ wprep, uint16_t* __restrict__ xn_out,
     uint16_t* __restrict__ li_out, float* __restrict__ part) {
+    MHC_POISON_LDS(0);
     constexpr int kTok = kTile * G;  // tokens of the workgroup
     __shared__ float red[4][kTok][24];
     __shared__ float sq[4][4][kTok][2];
@@ -210,6 +211,7 @@ template <int G, bool NT>
 __global__ __launch_bounds__(256) void k_partial_pre_wide(
     int T, int hidden, int steps_per_wave, int slices, const uint16_t* __restrict__ X,
     const uint4* __restrict__ wprep, float* __restrict__ part) {
+    MHC_POISON_LDS(0);
     constexpr int kTok = kTile * G;
     __shared__ float red[4][kTok][24];
     __shared__ float sq[4][4][kTok];
@@ -416,6 +418,7 @@ __global__ __launch_bounds__(256) void k_finish(
     uint16_t* __restrict__ layer_input, float* __restrict__ pre_out,
     float* __restrict__ post_out, float* __restrict__ comb_out, float* __restrict__ mixes_out,
     float* __restrict__ rstd_out) {
+    MHC_POISON_LDS(0);
     __shared__ float lsum[kTile][16];
     __shared__ float rli[kTile];
     __shared__ float cred[8][26];
@@ -546,6 +549,7 @@ __global__ __launch_bounds__(512) void k_pre_finish(
     const uint16_t* __restrict__ norm_w, Scalars p, uint16_t* __restrict__ layer_input,
     float* __restrict__ pre_out, float* __restrict__ post_out, float* __restrict__ comb_out,
     float* __restrict__ mixes_out, float* __restrict__ rstd_out) {
+    MHC_POISON_LDS(norm_w ? (unsigned)hidden * 2 + (unsigned)hidden / 8 * 4 : 0u);
     // With norm_w: li of the row, [hidden / 8] chunks, then the sum of squares
     // of each chunk, [hidden / 8] floats.
     extern __shared__ uint4 li_s[];

@@ -105,6 +105,7 @@ __device__ __forceinline__ float sum_group1(__amdgpu_buffer_rsrc_t rs, unsigned 
 
 template <bool NORM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_pre_one(PreOneArgs a) {
+    MHC_POISON_LDS(0);
     __shared__ float4 gsum[kOneMaxTokens][2][kGroups];   // group sums of the 8-float records
     __shared__ float tot8[kOneMaxTokens][kRec1];           // pre mixes 0-3, ssq, ssq_li
     __shared__ float pre_s[kOneMaxTokens][4];

@@ -119,6 +119,7 @@ __device__ __forceinline__ void load_act2(Act2& a, const TileRows& r, unsigned r
 
 template <int KB, bool NORM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_stream(StreamArgs a) {
+    MHC_POISON_LDS(0);
     static_assert(KB % 2 == 0 && KB >= 6 && KB <= 16, "k-blocks per item");
     constexpr int KS = KB / 2;                      // steps (pairs of k-blocks) per item
     constexpr int TT = kTileS;
