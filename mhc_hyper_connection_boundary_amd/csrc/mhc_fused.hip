@@ -84,7 +84,10 @@ __device__ __forceinline__ void load_act(Act& a, const uint16_t* __restrict__ Xr
 // holds row 8i + L/8 of the token group, bytes 16(L%8) of the step's 128-byte
 // run, so each load instruction reads 8 rows x 128 bytes; HBM serves such
 // runs faster than 16 rows x 64 bytes (a plain mover: 4.91 against
-// 4.60 TB/s).
+// 4.60 TB/s).  X and x are read once, with the nontemporal hint: the parked
+// layer input that the epilogue reads back keeps more of the last-level
+// cache (d=7168, T=8192: 295 -> 289-291 us; the same hint on the X' stores,
+// on the parked li or on the final layer-input stores measured slower).
 struct ActRows {
     uint4 X[2][4];  // [instruction][stream]
     uint4 x[2];
@@ -97,8 +100,8 @@ __device__ __forceinline__ void load_rows(ActRows& a, const uint16_t* __restrict
     for (int i = 0; i < 2; ++i) {
         const uint16_t* Xr = X + (size_t)tok[i] * (4 * kHidden) + hl;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) a.X[i][j] = load_stream(Xr + j * kHidden);
-        a.x[i] = load_stream(x + (size_t)tok[i] * kHidden + hl);
+        for (int j = 0; j < 4; ++j) a.X[i][j] = ld16<true>(Xr + j * kHidden);
+        a.x[i] = ld16<true>(x + (size_t)tok[i] * kHidden + hl);
     }
 }
 
