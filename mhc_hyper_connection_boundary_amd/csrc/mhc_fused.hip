@@ -69,15 +69,17 @@ __device__ __forceinline__ void store_stream(uint16_t* p, const uint4& v) {
     *reinterpret_cast<uint4*>(p) = v;
 }
 
+// (k_fused only.  X and x are read once, with the nontemporal hint: d=7168,
+// T=4096 172 -> 166 us, T=3072 154 -> 152 us.)
 __device__ __forceinline__ void load_act(Act& a, const uint16_t* __restrict__ Xrow,
                                          const uint16_t* __restrict__ xrow, int hidden, int h) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        a.X[0][j] = load_stream(Xrow + (size_t)j * hidden + h);
-        a.X[1][j] = load_stream(Xrow + (size_t)j * hidden + h + kStep);
+        a.X[0][j] = ld16<true>(Xrow + (size_t)j * hidden + h);
+        a.X[1][j] = ld16<true>(Xrow + (size_t)j * hidden + h + kStep);
     }
-    a.x[0] = load_stream(xrow + h);
-    a.x[1] = load_stream(xrow + h + kStep);
+    a.x[0] = ld16<true>(xrow + h);
+    a.x[1] = ld16<true>(xrow + h + kStep);
 }
 
 // Row-layout activations of one wave step: instruction i, stream j: lane L
