@@ -532,6 +532,12 @@ __global__ __launch_bounds__(256) void k_finish(
 
 // ---------------------------------------------------------------------------
 // Non-shifted pre, kernel 2: one workgroup (256 or 512 threads) per token.
+// It is the last reader of X and the only writer of the layer input.  When X
+// is at least 128 MiB (half the last-level cache) both streams carry the
+// nontemporal hint (NT), measured with norm: d=7168 T=8192 219 -> 188 us,
+// T=4096 114 -> 103, T=3072 89 -> 85, T=2341 (just over the threshold)
+// 68.0 -> 69.5; d=16384 T=1024 73 -> 69.  Below it the hint costs: T=2048
+// d=7168 57 -> 63 us, T=32 9.8 -> 10.3.
 // ---------------------------------------------------------------------------
 // Where the partial sums of the projection live: value v (24 mixes, then the
 // sum of squares) of token t in split q is
@@ -543,6 +549,7 @@ struct PartialLayout {
     int splits;
 };
 
+template <bool NT>
 __global__ __launch_bounds__(512) void k_pre_finish(
     int hidden, PartialLayout pl, const uint16_t* __restrict__ X,
     const float* __restrict__ scale, const float* __restrict__ base,
@@ -576,7 +583,7 @@ __global__ __launch_bounds__(512) void k_pre_finish(
         if (cidx < nch) {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                b[j] = *reinterpret_cast<const uint4*>(Xrow + (size_t)j * hidden + cidx * 8);
+                b[j] = ld16<NT>(Xrow + (size_t)j * hidden + cidx * 8);
         }
     };
     // Thread (group, v) of the first 200 sums splits group, group + 8, ... of
@@ -650,7 +657,7 @@ __global__ __launch_bounds__(512) void k_pre_finish(
             if (norm_w) {
                 li_s[cidx] = li;
                 chunk_ssq[cidx] = ssq_li;
-            } else *reinterpret_cast<uint4*>(layer_input + (size_t)t * hidden + cidx * 8) = li;
+            } else st16<NT>(layer_input + (size_t)t * hidden + cidx * 8, li);
         };
         for (int cidx = u0; cidx < nch; cidx += 2 * nc) {
             collapse(bufA, cidx);
@@ -683,7 +690,7 @@ __global__ __launch_bounds__(512) void k_pre_finish(
                     const uint32_t a = word(li, q), b = word(nw, q);
                     set_word(out, q, pack_bf16((bf_lo(a) * r) * bf_lo(b), (bf_hi(a) * r) * bf_hi(b)));
                 }
-                *reinterpret_cast<uint4*>(layer_input + (size_t)t * hidden + h) = out;
+                st16<NT>(layer_input + (size_t)t * hidden + h, out);
             }
         }
     }
@@ -904,8 +911,15 @@ static hipError_t launch_pre_finish_layout(int T, int hidden, const PartialLayou
     // one round trip; large batches: 192, more workgroups per CU.
     const size_t lds = norm_w ? (size_t)hidden * 2 + (size_t)hidden / 8 * sizeof(float) : 0;
     const int threads = T <= 512 ? 512 : 256;
-    hipLaunchKernelGGL(k_pre_finish, dim3(T), dim3(threads), lds, stream, hidden, pl, X, scale,
-                       base, norm_w, p, layer_input, pre_out, post_out, comb_out, mixes, rstd);
+    const bool nt = (size_t)T * 4 * (size_t)hidden * 2 >= ((size_t)128 << 20);
+    if (nt)
+        hipLaunchKernelGGL(k_pre_finish<true>, dim3(T), dim3(threads), lds, stream, hidden, pl, X,
+                           scale, base, norm_w, p, layer_input, pre_out, post_out, comb_out, mixes,
+                           rstd);
+    else
+        hipLaunchKernelGGL(k_pre_finish<false>, dim3(T), dim3(threads), lds, stream, hidden, pl, X,
+                           scale, base, norm_w, p, layer_input, pre_out, post_out, comb_out, mixes,
+                           rstd);
     return hipGetLastError();
 }
 

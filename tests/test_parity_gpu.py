@@ -401,6 +401,21 @@ def test_pre_schedules(oracle, T, d, schedule):
                 fresh=(inp.X, inp.norm_w if norm else None))
 
 
+@pytest.mark.parametrize("T", [2340, 2341])
+def test_pre_finish_hint_threshold(oracle, T):
+    """The pre's finishing kernel loads X and stores the layer input with the
+    nontemporal hint from 128 MiB of X on: at d=7168 from 2341 tokens.  Both
+    sides of the threshold, with and without norm, split schedule."""
+    d = 7168
+    say(f"pre finish hint threshold T={T} d={d}")
+    inp = WL.make_inputs(WL.Config("nt", d=d, T=T, seed=T))
+    dv = Dev(inp)
+    for norm in (True, False):
+        g = dv.pre(norm=norm, schedule="split")
+        compare(g, oracle.pre(inp, use_norm=norm), xn=False, label=f"pre T={T} norm={norm}",
+                fresh=(inp.X, inp.norm_w if norm else None))
+
+
 @pytest.mark.parametrize("name", ["prefill", "stress"])
 def test_pre_large(oracle, name):
     """The full-size launch (automatic schedule) against the oracle on every token."""
