@@ -120,6 +120,19 @@ __device__ __forceinline__ uint4 rows_to_mfma(const uint4& r0, const uint4& r1, 
     return o;
 }
 
+// The inverse move, for stores: row-layout register i (lane L: row 8i + L/8,
+// chunk c = L%8) takes lane 16(c%4) + 8i + L/8 of matrix-core block c/4.
+__device__ __forceinline__ uint4 mfma_to_rows(const uint4& m0, const uint4& m1, int idx, bool hi) {
+    uint4 o;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int v0 = __builtin_amdgcn_ds_bpermute(idx, (int)word(m0, k));
+        const int v1 = __builtin_amdgcn_ds_bpermute(idx, (int)word(m1, k));
+        set_word(o, k, (uint32_t)(hi ? v1 : v0));
+    }
+    return o;
+}
+
 __device__ __forceinline__ void load_frags(uint4 (&A)[kFragsPerStep], const uint4* __restrict__ wprep,
                                            int kblock, int lane) {
     const uint4* wp = wprep + (size_t)kblock * kFragsPerStep * 64 + lane;
@@ -238,6 +251,93 @@ struct LayerInputEpilogue {
                 put(q, h, ring_li[slot][q][0], ring_nw[slot][0], r[q]);
                 put(q, h + kStep, ring_li[slot][q][1], ring_nw[slot][1], r[q]);
             }
+            if (i + kDepth < kParkEnd) load_parked(i + kDepth);
+        }
+    }
+};
+
+// The same for the 4-wave kernels, whose li is kept in row layout: register
+// (q, i) of a lane holds row 16q + 8i + L/8 of the tile, chunk L%8 of the
+// step's 128-byte run, so every load and store of li and norm_w covers 8 rows
+// x 128 bytes and a lane needs one norm_w register per step instead of two.
+// Lanes on rows past the last token read the row of token T-1 and write
+// nothing, as above.
+template <class Shape, int kWavesN, int kMaxDepth, bool kNorm>
+struct LayerInputRows {
+    static constexpr int kParkEnd = Shape::kSteps - Shape::kLiReg;  // parked: [kLiLds, kParkEnd)
+    static constexpr int kParked = kParkEnd - Shape::kLiLds;
+    static constexpr int kDepth = kParked < kMaxDepth ? (kParked > 0 ? kParked : 1) : kMaxDepth;
+    static constexpr int kLds = Shape::kLiLds > 0 ? Shape::kLiLds : 1;
+    static constexpr int kReg = Shape::kLiReg > 0 ? Shape::kLiReg : 1;
+
+    const uint16_t* norm_w;
+    uint16_t* row[2][2];  // [group][instruction]
+    bool valid[2][2];
+    int wave, hl0;
+    uint4 ring_li[kDepth][2][2], ring_nw[kDepth];
+    uint4 lds_nw[kLds], keep_nw[kReg];
+
+    __device__ __forceinline__ int col(int i) const { return (i * kWavesN + wave) * kWide + hl0; }
+
+    __device__ __forceinline__ void load_parked(int i) {
+        const int slot = (i - Shape::kLiLds) % kDepth, c = col(i);
+        ring_nw[slot] = load_stream(norm_w + c);
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int k = 0; k < 2; ++k) ring_li[slot][q][k] = load_stream(row[q][k] + c);
+    }
+
+    __device__ __forceinline__ void prefetch() {
+        if constexpr (kNorm) {
+#pragma unroll
+            for (int i = 0; i < Shape::kLiLds; ++i) lds_nw[i] = load_stream(norm_w + col(i));
+#pragma unroll
+            for (int rr = 0; rr < Shape::kLiReg; ++rr) keep_nw[rr] = load_stream(norm_w + col(kParkEnd + rr));
+#pragma unroll
+            for (int i = Shape::kLiLds; i < kParkEnd && i < Shape::kLiLds + kDepth; ++i) load_parked(i);
+        }
+    }
+
+    __device__ __forceinline__ void put(int q, int k, int c, const uint4& li, const uint4& nw, float r) {
+        if (!valid[q][k]) return;
+        uint4 out = li;
+        if constexpr (kNorm) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t a = word(li, e), b = word(nw, e);
+                set_word(out, e, pack_bf16((bf_lo(a) * r) * bf_lo(b), (bf_hi(a) * r) * bf_hi(b)));
+            }
+        }
+        store_stream(row[q][k] + c, out);
+    }
+
+    // lds_li(i, q, k) and keep_li(rr, q, k): li register (q, k) of LDS step i
+    // and of register step rr; r[q][k]: rstd_li of that register's row.
+    template <class LdsLi, class KeepLi>
+    __device__ __forceinline__ void emit(const LdsLi& lds_li, const KeepLi& keep_li,
+                                         const float (&r)[2][2]) {
+#pragma unroll
+        for (int i = 0; i < Shape::kLiLds; ++i)
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int k = 0; k < 2; ++k) put(q, k, col(i), lds_li(i, q, k), lds_nw[i], r[q][k]);
+#pragma unroll
+        for (int rr = 0; rr < Shape::kLiReg; ++rr)
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int k = 0; k < 2; ++k)
+                    put(q, k, col(kParkEnd + rr), keep_li(rr, q, k), keep_nw[rr], r[q][k]);
+        if constexpr (!kNorm) return;  // without norm_w the parked li already is the layer input
+#pragma unroll
+        for (int i = Shape::kLiLds; i < kParkEnd; ++i) {
+            const int slot = (i - Shape::kLiLds) % kDepth;
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int k = 0; k < 2; ++k) put(q, k, col(i), ring_li[slot][q][k], ring_nw[slot], r[q][k]);
             if (i + kDepth < kParkEnd) load_parked(i + kDepth);
         }
     }
@@ -398,13 +498,13 @@ constexpr int kWaves4 = 4;
 constexpr int kTileW4 = 32;
 
 // S = hidden / (kWaves4 * kWide): steps per wave; li of the first (at most
-// LdsMax) steps waits in LDS, 16 KB each, and of the last (at most 2) in
+// LdsMax) steps waits in LDS, 16 KB each, and of the last (at most RegMax) in
 // registers.  More registers spill.
-template <int S, int LdsMax = 8>
+template <int S, int LdsMax = 8, int RegMax = 2>
 struct FusedW4Shape {
     static constexpr int kSteps = S;
     static constexpr int kLiLds = S < LdsMax ? S : LdsMax;  // first steps: li waits in LDS
-    static constexpr int kLiReg = S - kLiLds < 2 ? S - kLiLds : 2;  // last steps: in registers
+    static constexpr int kLiReg = S - kLiLds < RegMax ? S - kLiLds : RegMax;  // last: registers
 };                                                // (steps between: layer_input)
 
 template <int S, bool kNorm>  // kNorm: norm_w is given
@@ -418,8 +518,10 @@ __global__ __launch_bounds__(256) void k_fused_w4(
     float* __restrict__ post_out, float* __restrict__ comb_out, float* __restrict__ mixes_out,
     float* __restrict__ rstd_out) {
     MHC_POISON_LDS(0);
-    // 9 li steps in LDS: the cross-wave sums need no buffer per wave.
-    using Shape = FusedW4Shape<S, 9>;
+    // 9 li steps in LDS: the cross-wave sums need no buffer per wave.  One in
+    // registers: with two, the row-layout moves of the last steps spill (T=8192:
+    // 263 us with one, 284 with two).
+    using Shape = FusedW4Shape<S, 9, 1>;
     constexpr int hidden = S * kWide * kWaves4;
     __shared__ uint4 li_lds[Shape::kLiLds > 0 ? Shape::kLiLds : 1][kWaves4][2][2][64];
     __shared__ float tot[kTileW4][26];
@@ -435,20 +537,14 @@ __global__ __launch_bounds__(256) void k_fused_w4(
     const int t0 = tile * tile_tokens;
     const int t_end = min(t0 + tile_tokens, T);
     size_t tc[2];
-    bool valid[2];
     PrevCoef c[2];
-    uint16_t* li_row[2];
-    uint16_t* xn_row[2];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
         // A lane past the tile's last token works on that token, so it stores
         // the same bytes as the token's own lane: no branch needed.
         const int t = t0 + 16 * q + n;
-        valid[q] = t < t_end;
-        tc[q] = valid[q] ? (size_t)t : (size_t)(t_end - 1);
+        tc[q] = t < t_end ? (size_t)t : (size_t)(t_end - 1);
         load_prev(c[q], post_prev, comb_prev, pre_lag, tc[q]);
-        li_row[q] = layer_input + tc[q] * hidden;
-        xn_row[q] = xn_out + tc[q] * 4 * hidden;
     }
 
     f32x4_t acc[2][3];
@@ -474,14 +570,19 @@ __global__ __launch_bounds__(256) void k_fused_w4(
     const int hl0 = (lane & 7) * 8;
     const int pidx[2] = {(8 * (n & 7) + g) * 4, (8 * (n & 7) + 4 + g) * 4};
     const bool phi = n >= 8;
+    const int ridx[2] = {(16 * (lane & 3) + (lane >> 3)) * 4, (16 * (lane & 3) + 8 + (lane >> 3)) * 4};
+    const bool rhi = (lane & 7) >= 4;
+    const bool rows3 = t0 + 24 < t_end;  // rows 24..31 hold a token of the tile (uniform)
     ActRows cur[2];
 #pragma unroll
     for (int q = 0; q < 2; ++q) load_rows<hidden>(cur[q], X, x, tok[q], wave * kWide + hl0);
     // One wave step.  keep: li stays in the caller's registers (last steps);
     // otherwise it waits in LDS (first steps) or in the layer-input buffer.
+    // X' and li leave the matrix-core layout for row layout before they are
+    // stored: 8 rows x 128 bytes per store instead of 16 x 64 (T=8192: X'
+    // 289 -> 269 us, same bits).
     auto body = [&](int i, bool keep, uint4 (&li)[2][2]) {
         const int step = i * kWaves4 + wave;
-        const int h = step * kWide + g * 8;
         uint4 A0[kFragsPerStep], A1[kFragsPerStep];
         load_frags(A0, wprep, 2 * step, lane);
         load_frags(A1, wprep, 2 * step + 1, lane);
@@ -494,27 +595,36 @@ __global__ __launch_bounds__(256) void k_fused_w4(
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-            uint4 Xn[2][4];
+            uint4 Xn[2][4], lm[2];
 #pragma unroll
             for (int b = 0; b < 2; ++b) {
                 uint4 Xs[4], xs;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) Xs[j] = rows_to_mfma(cur[q].X[0][j], cur[q].X[1][j], pidx[b], phi);
                 xs = rows_to_mfma(cur[q].x[0], cur[q].x[1], pidx[b], phi);
-                update_collapse(Xs, xs, c[q], Xn[b], li[q][b], ssq[q], ssq_li[q]);
+                update_collapse(Xs, xs, c[q], Xn[b], lm[b], ssq[q], ssq_li[q]);
             }
+            const int hr = step * kWide + hl0;
 #pragma unroll
-            for (int s2 = 0; s2 < 4; ++s2) {
-                store_stream(xn_row[q] + (size_t)s2 * hidden + h, Xn[0][s2]);
-                store_stream(xn_row[q] + (size_t)s2 * hidden + h + kStep, Xn[1][s2]);
-            }
-            if (!keep) {
-                if (i < Shape::kLiLds) {
-                    li_lds[i][wave][q][0][lane] = li[q][0];
-                    li_lds[i][wave][q][1][lane] = li[q][1];
-                } else {
-                    store_stream(li_row[q] + h, li[q][0]);
-                    store_stream(li_row[q] + h + kStep, li[q][1]);
+            for (int k = 0; k < 2; ++k) {
+                // In tiles of at most 24 tokens, rows 24..31 all repeat the
+                // last token: their stores are skipped (a uniform branch).
+                // Eight copies of one line per store cost more than the whole
+                // row-layout gain (T=5120, 20-token tiles: 198 us skipped,
+                // 217 us stored).
+                const bool rows = q == 0 || k == 0 || rows3;
+                if (rows) {
+#pragma unroll
+                    for (int s2 = 0; s2 < 4; ++s2)
+                        store_stream(xn_out + (size_t)tok[q][k] * (4 * hidden) + (size_t)s2 * hidden + hr,
+                                     mfma_to_rows(Xn[0][s2], Xn[1][s2], ridx[k], rhi));
+                }
+                li[q][k] = mfma_to_rows(lm[0], lm[1], ridx[k], rhi);
+                if (!keep) {
+                    if (i < Shape::kLiLds)
+                        li_lds[i][wave][q][k][lane] = li[q][k];
+                    else if (rows)
+                        store_stream(layer_input + (size_t)tok[q][k] * hidden + hr, li[q][k]);
                 }
             }
             mfma_step(A0, Xn[0], acc[q]);
@@ -535,8 +645,19 @@ __global__ __launch_bounds__(256) void k_fused_w4(
     // that waiting for them does not wait for those.
     CoefParams cp;
     if (wave < 2) cp = load_coef_params(scale, base, lane & 3);
-    LayerInputEpilogue<Shape, kWaves4, 2, 5, kNorm> out{
-        norm_w, {li_row[0], li_row[1]}, {valid[0], valid[1]}, wave, g};
+    // The epilogue's rows come from an opaque copy of the thread index, so the
+    // compiler cannot compute them before the loop and keep them live through it.
+    int tl = (int)threadIdx.x;
+    asm volatile("" : "+v"(tl));
+    const int er = (tl & 63) >> 3;  // the lane's row within each 8-row instruction
+    auto erow = [&](int q, int k) {
+        const int t = t0 + 16 * q + 8 * k + er;
+        return layer_input + (size_t)(t < t_end ? t : t_end - 1) * hidden;
+    };
+    LayerInputRows<Shape, kWaves4, 5, kNorm> out{
+        norm_w, {{erow(0, 0), erow(0, 1)}, {erow(1, 0), erow(1, 1)}},
+        {{t0 + er < t_end, t0 + 8 + er < t_end}, {t0 + 16 + er < t_end, t0 + 24 + er < t_end}},
+        tl >> 6, (tl & 7) * 8};
     out.prefetch();
 
     // Partials of the 4 waves, added into tot one wave at a time from 0.0f,
@@ -595,9 +716,9 @@ __global__ __launch_bounds__(256) void k_fused_w4(
     }
 
     // Layer input for this wave's steps.
-    const float r[2] = {rli[n], rli[16 + n]};
-    out.emit([&](int i, int q, int b) { return li_lds[i][wave][q][b][lane]; },
-             [&](int rr, int q, int b) { return li_keep[rr][q][b]; }, r);
+    const float r[2][2] = {{rli[er], rli[8 + er]}, {rli[16 + er], rli[24 + er]}};
+    out.emit([&](int i, int q, int k) { return li_lds[i][wave][q][k][lane]; },
+             [&](int rr, int q, int k) { return li_keep[rr][q][k]; }, r);
 }
 
 template <int S>
@@ -636,6 +757,32 @@ __device__ __forceinline__ void load_x4(ActX& a, const uint16_t* __restrict__ Xr
         a.X[0][j] = load_stream(Xrow + (size_t)j * hidden + h);
         a.X[1][j] = load_stream(Xrow + (size_t)j * hidden + h + kStep);
     }
+}
+
+// Row-layout X of one wave step (the pre has no block output): as ActRows
+// without x.  Plain loads: the second pass reads X again.
+struct ActRowsX {
+    uint4 X[2][4];  // [instruction][stream]
+};
+
+template <int kHidden>
+__device__ __forceinline__ void load_rows_x(ActRowsX& a, const uint16_t* __restrict__ X,
+                                            const int (&tok)[2], int hl) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const uint16_t* Xr = X + (size_t)tok[i] * (4 * kHidden) + hl;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) a.X[i][j] = load_stream(Xr + j * kHidden);
+    }
+}
+
+// The matrix-core blocks of a row-layout step.
+__device__ __forceinline__ void rows_x_to_mfma(const ActRowsX& a, uint4 (&m)[2][4], const int (&pidx)[2],
+                                               bool phi) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) m[b][j] = rows_to_mfma(a.X[0][j], a.X[1][j], pidx[b], phi);
 }
 
 // li = bf16(FMA chain over j of pre[j] * X[j], from 0) for 8 elements; adds li^2.
@@ -820,17 +967,25 @@ __global__ __launch_bounds__(256) void k_fused_pre_w4(
     const int lane = threadIdx.x & 63;
     const int n = lane & 15;
     const int g = lane >> 4;
-    const uint16_t* Xrow[2];
-    uint16_t* li_row[2];
-    bool valid[2];
+    const int t0 = tile * kTileW4;
+    // Row layout as in k_fused_w4: lane L loads row 8i + L/8 of token group q
+    // (tokens past the last one clamped to it), 8 rows x 128 bytes per load;
+    // ds_bpermute moves the data into the matrix-core layout, where the sums
+    // and the collapse run on the same values in the same order as before, and
+    // li goes back to row layout for its stores.
+    int tok[2][2];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int t = tile * kTileW4 + 16 * q + n;
-        valid[q] = t < T;
-        const size_t tc = valid[q] ? (size_t)t : (size_t)(T - 1);
-        Xrow[q] = X + tc * 4 * hidden;
-        li_row[q] = layer_input + tc * hidden;
-    }
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int t = t0 + 16 * q + 8 * i + (lane >> 3);
+            tok[q][i] = t < T ? t : T - 1;
+        }
+    const int hl0 = (lane & 7) * 8;
+    const int pidx[2] = {(8 * (n & 7) + g) * 4, (8 * (n & 7) + 4 + g) * 4};
+    const bool phi = n >= 8;
+    const int ridx[2] = {(16 * (lane & 3) + (lane >> 3)) * 4, (16 * (lane & 3) + 8 + (lane >> 3)) * 4};
+    const bool rhi = (lane & 7) >= 4;
 
     // Pass 1: sums of squares and the projection.
     f32x4_t acc[2][3];
@@ -839,36 +994,38 @@ __global__ __launch_bounds__(256) void k_fused_pre_w4(
 #pragma unroll
         for (int m = 0; m < 3; ++m) acc[q][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float ssq[2] = {0.0f, 0.0f};
-    ActX cur[2];
+    ActRowsX cur[2];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) load_x4(cur[q], Xrow[q], hidden, wave * kWide + g * 8);
+    for (int q = 0; q < 2; ++q) load_rows_x<hidden>(cur[q], X, tok[q], wave * kWide + hl0);
 #pragma unroll 1
     for (int i = 0; i < S; ++i) {
         const int step = i * kWaves4 + wave;
-        const int h = step * kWide + g * 8;
         uint4 A0[kFragsPerStep], A1[kFragsPerStep];
         load_frags(A0, wprep, 2 * step, lane);
         load_frags(A1, wprep, 2 * step + 1, lane);
         __builtin_amdgcn_sched_barrier(0);
-        ActX nxt[2];
+        ActRowsX nxt[2];
         if (i + 1 < S) {
 #pragma unroll
-            for (int q = 0; q < 2; ++q) load_x4(nxt[q], Xrow[q], hidden, h + kWaves4 * kWide);
+            for (int q = 0; q < 2; ++q)
+                load_rows_x<hidden>(nxt[q], X, tok[q], step * kWide + hl0 + kWaves4 * kWide);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-            square_sum(cur[q].X[0], ssq[q]);
-            square_sum(cur[q].X[1], ssq[q]);
-            mfma_step(A0, cur[q].X[0], acc[q]);
-            mfma_step(A1, cur[q].X[1], acc[q]);
+            uint4 Xm[2][4];
+            rows_x_to_mfma(cur[q], Xm, pidx, phi);
+            square_sum(Xm[0], ssq[q]);
+            square_sum(Xm[1], ssq[q]);
+            mfma_step(A0, Xm[0], acc[q]);
+            mfma_step(A1, Xm[1], acc[q]);
         }
 #pragma unroll
         for (int q = 0; q < 2; ++q) cur[q] = nxt[q];
     }
     // Pass 2's first activations are requested before the reductions.
 #pragma unroll
-    for (int q = 0; q < 2; ++q) load_x4(cur[q], Xrow[q], hidden, wave * kWide + g * 8);
+    for (int q = 0; q < 2; ++q) load_rows_x<hidden>(cur[q], X, tok[q], wave * kWide + hl0);
     CoefParams cp;
     if (wave < 2) cp = load_coef_params(scale, base, lane & 3);
 #pragma unroll
@@ -904,7 +1061,7 @@ __global__ __launch_bounds__(256) void k_fused_pre_w4(
     __syncthreads();
     if (wave < 2) {  // the Sinkhorn of the 32 tokens, ahead of these waves' collapse
         comb_row(o, tot[ctn], ci, cp, p);
-        const int tt = tile * kTileW4 + ctn;
+        const int tt = t0 + ctn;
         if (tt < T) {
             pre_out[(size_t)tt * 4 + ci] = o.pre;
             post_out[(size_t)tt * 4 + ci] = o.post;
@@ -925,23 +1082,26 @@ __global__ __launch_bounds__(256) void k_fused_pre_w4(
     float ssq_li[2] = {0.0f, 0.0f};
     auto body = [&](int i, bool keep, uint4 (&li)[2][2]) {
         const int step = i * kWaves4 + wave;
-        const int h = step * kWide + g * 8;
-        ActX nxt[2];
+        const int hr = step * kWide + hl0;
+        ActRowsX nxt[2];
         if (i + 1 < S) {
 #pragma unroll
-            for (int q = 0; q < 2; ++q) load_x4(nxt[q], Xrow[q], hidden, h + kWaves4 * kWide);
+            for (int q = 0; q < 2; ++q) load_rows_x<hidden>(nxt[q], X, tok[q], hr + kWaves4 * kWide);
         }
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-            li[q][0] = collapse8(cur[q].X[0], pr[q], ssq_li[q]);
-            li[q][1] = collapse8(cur[q].X[1], pr[q], ssq_li[q]);
-            if (!keep) {
-                if (i < Shape::kLiLds) {
-                    li_lds[i][wave][q][0][lane] = li[q][0];
-                    li_lds[i][wave][q][1][lane] = li[q][1];
-                } else {
-                    store_stream(li_row[q] + h, li[q][0]);
-                    store_stream(li_row[q] + h + kStep, li[q][1]);
+            uint4 Xm[2][4], lm[2];
+            rows_x_to_mfma(cur[q], Xm, pidx, phi);
+            lm[0] = collapse8(Xm[0], pr[q], ssq_li[q]);
+            lm[1] = collapse8(Xm[1], pr[q], ssq_li[q]);
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                li[q][k] = mfma_to_rows(lm[0], lm[1], ridx[k], rhi);
+                if (!keep) {
+                    if (i < Shape::kLiLds)
+                        li_lds[i][wave][q][k][lane] = li[q][k];
+                    else
+                        store_stream(layer_input + (size_t)tok[q][k] * hidden + hr, li[q][k]);
                 }
             }
         }
@@ -956,8 +1116,17 @@ __global__ __launch_bounds__(256) void k_fused_pre_w4(
     uint4 li_keep[Shape::kLiReg > 0 ? Shape::kLiReg : 1][2][2];
 #pragma unroll
     for (int r = 0; r < Shape::kLiReg; ++r) body(S - Shape::kLiReg + r, true, li_keep[r]);
-    LayerInputEpilogue<Shape, kWaves4, 2, 5, kNorm> out{
-        norm_w, {li_row[0], li_row[1]}, {valid[0], valid[1]}, wave, g};
+    // The epilogue's rows come from an opaque copy of the thread index (see k_fused_w4).
+    int tl = (int)threadIdx.x;
+    asm volatile("" : "+v"(tl));
+    const int er = (tl & 63) >> 3;
+    auto erow = [&](int q, int k) {
+        const int t = t0 + 16 * q + 8 * k + er;
+        return layer_input + (size_t)(t < T ? t : T - 1) * hidden;
+    };
+    LayerInputRows<Shape, kWaves4, 5, kNorm> out{
+        norm_w, {{erow(0, 0), erow(0, 1)}, {erow(1, 0), erow(1, 1)}},
+        {{t0 + er < T, t0 + 8 + er < T}, {t0 + 16 + er < T, t0 + 24 + er < T}}, tl >> 6, (tl & 7) * 8};
     out.prefetch();
 
 #pragma unroll
@@ -972,9 +1141,9 @@ __global__ __launch_bounds__(256) void k_fused_pre_w4(
         rli[threadIdx.x] = rsqrt_nr(sum * (1.0f / (float)hidden) + p.norm_eps);
     }
     __syncthreads();
-    const float r[2] = {rli[n], rli[16 + n]};
-    out.emit([&](int i, int q, int b) { return li_lds[i][wave][q][b][lane]; },
-             [&](int rr, int q, int b) { return li_keep[rr][q][b]; }, r);
+    const float r[2][2] = {{rli[er], rli[8 + er]}, {rli[16 + er], rli[24 + er]}};
+    out.emit([&](int i, int q, int k) { return li_lds[i][wave][q][k][lane]; },
+             [&](int rr, int q, int k) { return li_keep[rr][q][k]; }, r);
 }
 
 template <int S>
