@@ -261,8 +261,10 @@ struct LayerInputEpilogue {
 // step's 128-byte run, so every load and store of li and norm_w covers 8 rows
 // x 128 bytes and a lane needs one norm_w register per step instead of two.
 // Lanes on rows past the last token read the row of token T-1 and write
-// nothing, as above.
-template <class Shape, int kWavesN, int kMaxDepth, bool kNorm>
+// nothing, as above.  The wave's i-th step covers step (i + rot) mod kSteps of
+// the row (the tile's rotation, see k_fused_w4); kNtOut puts the nontemporal
+// hint on the final layer-input stores.
+template <class Shape, int kWavesN, int kMaxDepth, bool kNorm, bool kNtOut>
 struct LayerInputRows {
     static constexpr int kParkEnd = Shape::kSteps - Shape::kLiReg;  // parked: [kLiLds, kParkEnd)
     static constexpr int kParked = kParkEnd - Shape::kLiLds;
@@ -273,11 +275,14 @@ struct LayerInputRows {
     const uint16_t* norm_w;
     uint16_t* row[2][2];  // [group][instruction]
     bool valid[2][2];
-    int wave, hl0;
+    int wave, hl0, rot;
     uint4 ring_li[kDepth][2][2], ring_nw[kDepth];
     uint4 lds_nw[kLds], keep_nw[kReg];
 
-    __device__ __forceinline__ int col(int i) const { return (i * kWavesN + wave) * kWide + hl0; }
+    __device__ __forceinline__ int col(int i) const {
+        const int a = i + rot >= Shape::kSteps ? i + rot - Shape::kSteps : i + rot;
+        return (a * kWavesN + wave) * kWide + hl0;
+    }
 
     __device__ __forceinline__ void load_parked(int i) {
         const int slot = (i - Shape::kLiLds) % kDepth, c = col(i);
@@ -309,7 +314,7 @@ struct LayerInputRows {
                 set_word(out, e, pack_bf16((bf_lo(a) * r) * bf_lo(b), (bf_hi(a) * r) * bf_hi(b)));
             }
         }
-        store_stream(row[q][k] + c, out);
+        st16<kNtOut>(row[q][k] + c, out);
     }
 
     // lds_li(i, q, k) and keep_li(rr, q, k): li register (q, k) of LDS step i
@@ -536,6 +541,21 @@ __global__ __launch_bounds__(256) void k_fused_w4(
     // fewer in the last tile.
     const int t0 = tile * tile_tokens;
     const int t_end = min(t0 + tile_tokens, T);
+    // Every CU runs its tile at about the same pace, so without a rotation all
+    // tiles read and write the same columns of their rows at the same time.
+    // Where the token stride (8 hidden bytes) is a multiple of 16 KiB, those
+    // addresses share their low bits and crowd into a few memory channels:
+    // there each tile starts its sweep at its own step, drawn from a
+    // multiplicative hash of the tile index (a rotation equal to the tile index
+    // itself correlates with the address bits and measured slower still).  The
+    // step order is fixed per tile, so each token's sums still have one order.
+    // Cold calls, T=8192 (us, lockstep -> rotated): d=2048 93 -> 80, d=4096
+    // 184 -> 148, d=6144 260 -> 220, d=8192 390 -> 284; stress d=4096 T=16384
+    // 350 -> 284.  At d=1024, 5120 and 7168 the rotation measured 1-9 us slower
+    // (the tiles of an XCD then stop sharing the weight fragments in its L2).
+    constexpr bool kRotate = S % 8 == 0;
+    const int rot = kRotate ? (int)((((unsigned)tile * 2654435761u) >> 12) % (unsigned)S) : 0;
+    auto astep = [&](int i) { return i + rot >= S ? i + rot - S : i + rot; };
     size_t tc[2];
     PrevCoef c[2];
 #pragma unroll
@@ -575,14 +595,14 @@ __global__ __launch_bounds__(256) void k_fused_w4(
     const bool rows3 = t0 + 24 < t_end;  // rows 24..31 hold a token of the tile (uniform)
     ActRows cur[2];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) load_rows<hidden>(cur[q], X, x, tok[q], wave * kWide + hl0);
+    for (int q = 0; q < 2; ++q) load_rows<hidden>(cur[q], X, x, tok[q], (astep(0) * kWaves4 + wave) * kWide + hl0);
     // One wave step.  keep: li stays in the caller's registers (last steps);
     // otherwise it waits in LDS (first steps) or in the layer-input buffer.
     // X' and li leave the matrix-core layout for row layout before they are
     // stored: 8 rows x 128 bytes per store instead of 16 x 64 (T=8192: X'
     // 289 -> 269 us, same bits).
     auto body = [&](int i, bool keep, uint4 (&li)[2][2]) {
-        const int step = i * kWaves4 + wave;
+        const int step = astep(i) * kWaves4 + wave;
         uint4 A0[kFragsPerStep], A1[kFragsPerStep];
         load_frags(A0, wprep, 2 * step, lane);
         load_frags(A1, wprep, 2 * step + 1, lane);
@@ -590,7 +610,8 @@ __global__ __launch_bounds__(256) void k_fused_w4(
         ActRows nxt[2];
         if (i + 1 < S) {
 #pragma unroll
-            for (int q = 0; q < 2; ++q) load_rows<hidden>(nxt[q], X, x, tok[q], step * kWide + hl0 + kWaves4 * kWide);
+            for (int q = 0; q < 2; ++q)
+                load_rows<hidden>(nxt[q], X, x, tok[q], (astep(i + 1) * kWaves4 + wave) * kWide + hl0);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -613,11 +634,11 @@ __global__ __launch_bounds__(256) void k_fused_w4(
                 // row-layout gain (T=5120, 20-token tiles: 198 us skipped,
                 // 217 us stored).
                 const bool rows = q == 0 || k == 0 || rows3;
-                if (rows) {
+                if (rows) {  // X' is not read again here: nontemporal (T=8192: 273 -> 251 us)
 #pragma unroll
                     for (int s2 = 0; s2 < 4; ++s2)
-                        store_stream(xn_out + (size_t)tok[q][k] * (4 * hidden) + (size_t)s2 * hidden + hr,
-                                     mfma_to_rows(Xn[0][s2], Xn[1][s2], ridx[k], rhi));
+                        st16<true>(xn_out + (size_t)tok[q][k] * (4 * hidden) + (size_t)s2 * hidden + hr,
+                                   mfma_to_rows(Xn[0][s2], Xn[1][s2], ridx[k], rhi));
                 }
                 li[q][k] = mfma_to_rows(lm[0], lm[1], ridx[k], rhi);
                 if (!keep) {
@@ -641,23 +662,28 @@ __global__ __launch_bounds__(256) void k_fused_w4(
     uint4 li_keep[Shape::kLiReg > 0 ? Shape::kLiReg : 1][2][2];
 #pragma unroll
     for (int r = 0; r < Shape::kLiReg; ++r) body(S - Shape::kLiReg + r, true, li_keep[r]);
+    // From here on the lane's indices come from an opaque copy of the thread
+    // index, so the compiler cannot compute them before the loop and keep them
+    // (spilled) through it: a reload from scratch would wait for every load the
+    // epilogue has in flight.
+    int tl = (int)threadIdx.x;
+    asm volatile("" : "+v"(tl));
+    const int lw = tl >> 6, ll = tl & 63, ln = ll & 15, lg = ll >> 4;
     // The coefficient parameters are requested before the epilogue's loads, so
     // that waiting for them does not wait for those.
     CoefParams cp;
-    if (wave < 2) cp = load_coef_params(scale, base, lane & 3);
-    // The epilogue's rows come from an opaque copy of the thread index, so the
-    // compiler cannot compute them before the loop and keep them live through it.
-    int tl = (int)threadIdx.x;
-    asm volatile("" : "+v"(tl));
-    const int er = (tl & 63) >> 3;  // the lane's row within each 8-row instruction
+    if (lw < 2) cp = load_coef_params(scale, base, ll & 3);
+    const int er = ll >> 3;  // the lane's row within each 8-row instruction
     auto erow = [&](int q, int k) {
         const int t = t0 + 16 * q + 8 * k + er;
         return layer_input + (size_t)(t < t_end ? t : t_end - 1) * hidden;
     };
-    LayerInputRows<Shape, kWaves4, 5, kNorm> out{
+    // The final layer-input stores carry the nontemporal hint (stress d=4096,
+    // T=16384: 355 -> 331 us; level at d=7168).
+    LayerInputRows<Shape, kWaves4, 5, kNorm, true> out{
         norm_w, {{erow(0, 0), erow(0, 1)}, {erow(1, 0), erow(1, 1)}},
         {{t0 + er < t_end, t0 + 8 + er < t_end}, {t0 + 16 + er < t_end, t0 + 24 + er < t_end}},
-        tl >> 6, (tl & 7) * 8};
+        lw, (ll & 7) * 8, rot};
     out.prefetch();
 
     // Partials of the 4 waves, added into tot one wave at a time from 0.0f,
@@ -666,24 +692,24 @@ __global__ __launch_bounds__(256) void k_fused_w4(
     // a wave gathers the four k-group values of its token.
 #pragma unroll
     for (int w = 0; w < kWaves4; ++w) {
-        if (wave == w) {
+        if (lw == w) {
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
-                const int tn = 16 * q + n;
+                const int tn = 16 * q + ln;
 #pragma unroll
                 for (int m = 0; m < 3; ++m)
 #pragma unroll
                     for (int j = 0; j < 2; ++j) {
-                        const int v = 8 * m + 2 * g + j;
+                        const int v = 8 * m + 2 * lg + j;
                         tot[tn][v] = (w == 0 ? 0.0f : tot[tn][v]) + mix_of(acc[q], m, j);
                     }
                 float part[2][4];
 #pragma unroll
                 for (int gg = 0; gg < 4; ++gg) {
-                    part[0][gg] = __shfl(ssq[q], n + 16 * gg);
-                    part[1][gg] = __shfl(ssq_li[q], n + 16 * gg);
+                    part[0][gg] = __shfl(ssq[q], ln + 16 * gg);
+                    part[1][gg] = __shfl(ssq_li[q], ln + 16 * gg);
                 }
-                if (g == 0) {
+                if (lg == 0) {
 #pragma unroll
                     for (int e = 0; e < 2; ++e) {
                         float t = w == 0 ? 0.0f : tot[tn][24 + e];
@@ -700,8 +726,8 @@ __global__ __launch_bounds__(256) void k_fused_w4(
         rli[threadIdx.x] = rsqrt_nr(tot[threadIdx.x][25] * (1.0f / (float)hidden) + p.norm_eps);
     __syncthreads();
 
-    if (wave < 2) {  // 32 tokens x 4 lanes: waves 0 and 1
-        const int tn = 16 * wave + (lane >> 2), ci = lane & 3;
+    if (lw < 2) {  // 32 tokens x 4 lanes: waves 0 and 1
+        const int tn = 16 * lw + (ll >> 2), ci = ll & 3;
         const int tt = t0 + tn;
         const TokenCoef o = coefficients(tot[tn], ci, hidden, cp, p);
         if (tt < t_end) {
@@ -717,7 +743,7 @@ __global__ __launch_bounds__(256) void k_fused_w4(
 
     // Layer input for this wave's steps.
     const float r[2][2] = {{rli[er], rli[8 + er]}, {rli[16 + er], rli[24 + er]}};
-    out.emit([&](int i, int q, int k) { return li_lds[i][wave][q][k][lane]; },
+    out.emit([&](int i, int q, int k) { return li_lds[i][lw][q][k][ll]; },
              [&](int rr, int q, int k) { return li_keep[rr][q][k]; }, r);
 }
 
@@ -1124,9 +1150,9 @@ __global__ __launch_bounds__(256) void k_fused_pre_w4(
         const int t = t0 + 16 * q + 8 * k + er;
         return layer_input + (size_t)(t < T ? t : T - 1) * hidden;
     };
-    LayerInputRows<Shape, kWaves4, 5, kNorm> out{
+    LayerInputRows<Shape, kWaves4, 5, kNorm, false> out{
         norm_w, {{erow(0, 0), erow(0, 1)}, {erow(1, 0), erow(1, 1)}},
-        {{t0 + er < T, t0 + 8 + er < T}, {t0 + 16 + er < T, t0 + 24 + er < T}}, tl >> 6, (tl & 7) * 8};
+        {{t0 + er < T, t0 + 8 + er < T}, {t0 + 16 + er < T, t0 + 24 + er < T}}, tl >> 6, (tl & 7) * 8, 0};
     out.prefetch();
 
 #pragma unroll
