@@ -37,11 +37,11 @@ namespace {
 constexpr int kWaves = 8;
 constexpr int kWide = 2 * kStep;  // hidden elements per wave step: two MFMA k-blocks
 
-template <int S>                  // S = hidden / (kWaves * kWide): steps per wave
+template <int S, int RegMax = 3>   // S = hidden / (kWaves * kWide): steps per wave
 struct FusedShape {
     static constexpr int kSteps = S;
     static constexpr int kLiLds = S < 8 ? S : 8;  // first steps: li waits in LDS (16 KB each)
-    static constexpr int kLiReg = S - kLiLds < 3 ? S - kLiLds : 3;  // last steps: in registers
+    static constexpr int kLiReg = S - kLiLds < RegMax ? S - kLiLds : RegMax;  // last: registers
 };                                                // (steps between: layer_input)
 
 template <int S>                  // the 8-wave pre keeps no li in registers
@@ -264,7 +264,7 @@ struct LayerInputEpilogue {
 // nothing, as above.  The wave's i-th step covers step (i + rot) mod kSteps of
 // the row (the tile's rotation, see k_fused_w4); kNtOut puts the nontemporal
 // hint on the final layer-input stores.
-template <class Shape, int kWavesN, int kMaxDepth, bool kNorm, bool kNtOut>
+template <class Shape, int kWavesN, int kGroups, int kMaxDepth, bool kNorm, bool kNtOut>
 struct LayerInputRows {
     static constexpr int kParkEnd = Shape::kSteps - Shape::kLiReg;  // parked: [kLiLds, kParkEnd)
     static constexpr int kParked = kParkEnd - Shape::kLiLds;
@@ -273,10 +273,10 @@ struct LayerInputRows {
     static constexpr int kReg = Shape::kLiReg > 0 ? Shape::kLiReg : 1;
 
     const uint16_t* norm_w;
-    uint16_t* row[2][2];  // [group][instruction]
-    bool valid[2][2];
+    uint16_t* row[kGroups][2];  // [group][instruction]
+    bool valid[kGroups][2];
     int wave, hl0, rot;
-    uint4 ring_li[kDepth][2][2], ring_nw[kDepth];
+    uint4 ring_li[kDepth][kGroups][2], ring_nw[kDepth];
     uint4 lds_nw[kLds], keep_nw[kReg];
 
     __device__ __forceinline__ int col(int i) const {
@@ -288,7 +288,7 @@ struct LayerInputRows {
         const int slot = (i - Shape::kLiLds) % kDepth, c = col(i);
         ring_nw[slot] = load_stream(norm_w + c);
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
+        for (int q = 0; q < kGroups; ++q)
 #pragma unroll
             for (int k = 0; k < 2; ++k) ring_li[slot][q][k] = load_stream(row[q][k] + c);
     }
@@ -321,17 +321,17 @@ struct LayerInputRows {
     // and of register step rr; r[q][k]: rstd_li of that register's row.
     template <class LdsLi, class KeepLi>
     __device__ __forceinline__ void emit(const LdsLi& lds_li, const KeepLi& keep_li,
-                                         const float (&r)[2][2]) {
+                                         const float (&r)[kGroups][2]) {
 #pragma unroll
         for (int i = 0; i < Shape::kLiLds; ++i)
 #pragma unroll
-            for (int q = 0; q < 2; ++q)
+            for (int q = 0; q < kGroups; ++q)
 #pragma unroll
                 for (int k = 0; k < 2; ++k) put(q, k, col(i), lds_li(i, q, k), lds_nw[i], r[q][k]);
 #pragma unroll
         for (int rr = 0; rr < Shape::kLiReg; ++rr)
 #pragma unroll
-            for (int q = 0; q < 2; ++q)
+            for (int q = 0; q < kGroups; ++q)
 #pragma unroll
                 for (int k = 0; k < 2; ++k)
                     put(q, k, col(kParkEnd + rr), keep_li(rr, q, k), keep_nw[rr], r[q][k]);
@@ -340,7 +340,7 @@ struct LayerInputRows {
         for (int i = Shape::kLiLds; i < kParkEnd; ++i) {
             const int slot = (i - Shape::kLiLds) % kDepth;
 #pragma unroll
-            for (int q = 0; q < 2; ++q)
+            for (int q = 0; q < kGroups; ++q)
 #pragma unroll
                 for (int k = 0; k < 2; ++k) put(q, k, col(i), ring_li[slot][q][k], ring_nw[slot], r[q][k]);
             if (i + kDepth < kParkEnd) load_parked(i + kDepth);
@@ -359,7 +359,7 @@ __global__ __launch_bounds__(512) void k_fused(
     float* __restrict__ post_out, float* __restrict__ comb_out, float* __restrict__ mixes_out,
     float* __restrict__ rstd_out) {
     MHC_POISON_LDS(0);
-    using Shape = FusedShape<S>;
+    using Shape = FusedShape<S, 1>;  // two or three li steps in registers spill (row-layout moves)
     constexpr int hidden = S * kWide * kWaves;
     __shared__ uint4 li_lds[Shape::kLiLds > 0 ? Shape::kLiLds : 1][kWaves][2][64];
     __shared__ float red[kWaves][kTile][24];
@@ -371,48 +371,74 @@ __global__ __launch_bounds__(512) void k_fused(
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int n = lane & 15;
-    const int g = lane >> 4;
-    const int t = tile * kTile + n;
-    const size_t tc = t < T ? (size_t)t : (size_t)(T - 1);
+    const int t0 = tile * kTile;
+    const int t_end = min(t0 + kTile, T);
+    const size_t tc = t0 + n < t_end ? (size_t)(t0 + n) : (size_t)(t_end - 1);
 
     PrevCoef c;
     load_prev(c, post_prev, comb_prev, pre_lag, tc);
-
-    const uint16_t* Xrow = X + tc * 4 * hidden;
-    const uint16_t* xrow = x + tc * hidden;
-    uint16_t* li_row = layer_input + tc * hidden;
 
     f32x4_t acc[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
     float ssq = 0.0f, ssq_li = 0.0f;
 
     // Wave w takes steps w, w + 8, ...: at any moment the 8 waves cover 512
-    // contiguous hidden elements of every row of the tile.
-    Act cur;
-    load_act(cur, Xrow, xrow, hidden, wave * kWide + g * 8);
+    // contiguous hidden elements of every row of the tile.  As in k_fused_w4
+    // the activations are loaded in row layout (lane L: row 8i + L/8, 8 rows x
+    // 128 bytes per load), moved into the matrix-core layout with ds_bpermute,
+    // and X' and li go back to row layout for their stores; where hidden is a
+    // multiple of 2048 (token stride a multiple of 16 KiB) each tile starts its
+    // sweep at its own step.
+    int tok[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int t = t0 + 8 * i + (lane >> 3);
+        tok[i] = t < t_end ? t : t_end - 1;
+    }
+    const int hl0 = (lane & 7) * 8;
+    const int pidx[2] = {(8 * (n & 7) + (lane >> 4)) * 4, (8 * (n & 7) + 4 + (lane >> 4)) * 4};
+    const bool phi = n >= 8;
+    const int ridx[2] = {(16 * (lane & 3) + (lane >> 3)) * 4, (16 * (lane & 3) + 8 + (lane >> 3)) * 4};
+    const bool rhi = (lane & 7) >= 4;
+    const bool row1 = t0 + 8 < t_end;  // rows 8..15 hold a token of the tile (uniform)
+    constexpr bool kRotate = hidden % 2048 == 0;
+    const int rot = kRotate ? (int)((((unsigned)tile * 2654435761u) >> 12) % (unsigned)S) : 0;
+    auto astep = [&](int i) { return i + rot >= S ? i + rot - S : i + rot; };
+    ActRows cur;
+    load_rows<hidden>(cur, X, x, tok, (astep(0) * kWaves + wave) * kWide + hl0);
     // One wave step.  keep: li stays in the caller's registers (last steps);
     // otherwise it waits in LDS (first steps) or in the layer-input buffer.
     auto body = [&](int i, bool keep, uint4 (&li)[2]) {
-        const int step = i * kWaves + wave;
-        const int h = step * kWide + g * 8;
-        Act nxt;
-        if (i + 1 < S) load_act(nxt, Xrow, xrow, hidden, h + kWaves * kWide);
-        uint4 Xn[2][4];
+        const int step = astep(i) * kWaves + wave;
+        const int hr = step * kWide + hl0;
+        ActRows nxt;
+        if (i + 1 < S) load_rows<hidden>(nxt, X, x, tok, (astep(i + 1) * kWaves + wave) * kWide + hl0);
+        uint4 Xn[2][4], lm[2];
 #pragma unroll
-        for (int b = 0; b < 2; ++b) update_collapse(cur.X[b], cur.x[b], c, Xn[b], li[b], ssq, ssq_li);
-        // A lane past the last token works on token T-1 (tc), so it stores
-        // the same bytes as that token's own lane: no branch needed.
+        for (int b = 0; b < 2; ++b) {
+            uint4 Xs[4], xs;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            store_stream(xn_out + (tc * 4 + s) * hidden + h, Xn[0][s]);
-            store_stream(xn_out + (tc * 4 + s) * hidden + h + kStep, Xn[1][s]);
+            for (int j = 0; j < 4; ++j) Xs[j] = rows_to_mfma(cur.X[0][j], cur.X[1][j], pidx[b], phi);
+            xs = rows_to_mfma(cur.x[0], cur.x[1], pidx[b], phi);
+            update_collapse(Xs, xs, c, Xn[b], lm[b], ssq, ssq_li);
         }
-        if (!keep) {
-            if (i < Shape::kLiLds) {
-                li_lds[i][wave][0][lane] = li[0];
-                li_lds[i][wave][1][lane] = li[1];
-            } else {
-                store_stream(li_row + h, li[0]);
-                store_stream(li_row + h + kStep, li[1]);
+        // A lane past the last token works on the tile's last token, so it
+        // stores the same bytes as that token's own lane; rows 8..15 of a tile
+        // of at most 8 tokens are skipped (a uniform branch).
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const bool rows = k == 0 || row1;
+            if (rows) {
+#pragma unroll
+                for (int s2 = 0; s2 < 4; ++s2)
+                    st16<true>(xn_out + (size_t)tok[k] * (4 * hidden) + (size_t)s2 * hidden + hr,
+                               mfma_to_rows(Xn[0][s2], Xn[1][s2], ridx[k], rhi));
+            }
+            li[k] = mfma_to_rows(lm[0], lm[1], ridx[k], rhi);
+            if (!keep) {
+                if (i < Shape::kLiLds)
+                    li_lds[i][wave][k][lane] = li[k];
+                else if (rows)
+                    store_stream(layer_input + (size_t)tok[k] * hidden + hr, li[k]);
             }
         }
         // The weight fragments (L2-resident) are fetched only now, so they hold
@@ -434,20 +460,30 @@ __global__ __launch_bounds__(512) void k_fused(
     uint4 li_keep[Shape::kLiReg > 0 ? Shape::kLiReg : 1][2];
 #pragma unroll
     for (int r = 0; r < Shape::kLiReg; ++r) body(S - Shape::kLiReg + r, true, li_keep[r]);
+    // From here on the lane's indices come from an opaque copy of the thread
+    // index (see k_fused_w4).
+    int tl = (int)threadIdx.x;
+    asm volatile("" : "+v"(tl));
+    const int lw = tl >> 6, ll = tl & 63, ln = ll & 15, lg = ll >> 4, er = ll >> 3;
     // The coefficient parameters are requested before the epilogue's loads, so
     // that waiting for them does not wait for those.
     CoefParams cp;
-    if (wave == 0) cp = load_coef_params(scale, base, lane & 3);
-    LayerInputEpilogue<Shape, kWaves, 1, 3, kNorm> out{norm_w, {li_row}, {t < T}, wave, g};
+    if (lw == 0) cp = load_coef_params(scale, base, ll & 3);
+    auto erow = [&](int k) {
+        const int t = t0 + 8 * k + er;
+        return layer_input + (size_t)(t < t_end ? t : t_end - 1) * hidden;
+    };
+    LayerInputRows<Shape, kWaves, 1, 3, kNorm, true> out{
+        norm_w, {{erow(0), erow(1)}}, {{t0 + er < t_end, t0 + 8 + er < t_end}}, lw, (ll & 7) * 8, rot};
     out.prefetch();
 
     // Partials of the 8 waves, combined in a fixed order.
 #pragma unroll
     for (int m = 0; m < 3; ++m)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) red[wave][n][8 * m + 2 * g + j] = mix_of(acc, m, j);
-    sq[wave][g][n][0] = ssq;
-    sq[wave][g][n][1] = ssq_li;
+        for (int j = 0; j < 2; ++j) red[lw][ln][8 * m + 2 * lg + j] = mix_of(acc, m, j);
+    sq[lw][lg][ln][0] = ssq;
+    sq[lw][lg][ln][1] = ssq_li;
     __syncthreads();
     if (threadIdx.x < kTile * 26) {
         const int tn = threadIdx.x / 26, v = threadIdx.x % 26;
@@ -466,9 +502,9 @@ __global__ __launch_bounds__(512) void k_fused(
     }
     __syncthreads();
 
-    if (wave == 0) {
-        const int tn = lane >> 2, i = lane & 3;
-        const int tt = tile * kTile + tn;
+    if (lw == 0) {
+        const int tn = ll >> 2, i = ll & 3;
+        const int tt = t0 + tn;
         const TokenCoef o = coefficients(tot[tn], i, hidden, cp, p);
         if (tt < T) {
             pre_out[(size_t)tt * 4 + i] = o.pre;
@@ -482,9 +518,9 @@ __global__ __launch_bounds__(512) void k_fused(
     }
 
     // Layer input for this wave's steps.
-    const float r[1] = {rli[n]};
-    out.emit([&](int i, int, int b) { return li_lds[i][wave][b][lane]; },
-             [&](int rr, int, int b) { return li_keep[rr][b]; }, r);
+    const float r[1][2] = {{rli[er], rli[8 + er]}};
+    out.emit([&](int i, int, int k) { return li_lds[i][lw][k][ll]; },
+             [&](int rr, int, int k) { return li_keep[rr][k]; }, r);
 }
 
 // ---------------------------------------------------------------------------
@@ -680,7 +716,7 @@ __global__ __launch_bounds__(256) void k_fused_w4(
     };
     // The final layer-input stores carry the nontemporal hint (stress d=4096,
     // T=16384: 355 -> 331 us; level at d=7168).
-    LayerInputRows<Shape, kWaves4, 5, kNorm, true> out{
+    LayerInputRows<Shape, kWaves4, 2, 5, kNorm, true> out{
         norm_w, {{erow(0, 0), erow(0, 1)}, {erow(1, 0), erow(1, 1)}},
         {{t0 + er < t_end, t0 + 8 + er < t_end}, {t0 + 16 + er < t_end, t0 + 24 + er < t_end}},
         lw, (ll & 7) * 8, rot};
@@ -1150,7 +1186,7 @@ __global__ __launch_bounds__(256) void k_fused_pre_w4(
         const int t = t0 + 16 * q + 8 * k + er;
         return layer_input + (size_t)(t < T ? t : T - 1) * hidden;
     };
-    LayerInputRows<Shape, kWaves4, 5, kNorm, false> out{
+    LayerInputRows<Shape, kWaves4, 2, 5, kNorm, false> out{
         norm_w, {{erow(0, 0), erow(0, 1)}, {erow(1, 0), erow(1, 1)}},
         {{t0 + er < T, t0 + 8 + er < T}, {t0 + 16 + er < T, t0 + 24 + er < T}}, tl >> 6, (tl & 7) * 8, 0};
     out.prefetch();
