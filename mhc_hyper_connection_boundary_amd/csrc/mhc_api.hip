@@ -18,7 +18,7 @@ namespace {
 
 constexpr long kTargetWaves = 2048;  // waves of k_partial work to aim for
 constexpr int kFinishTarget = 2048;  // k_finish workgroups to aim for
-constexpr int kFusedMinTokens = 3072; // automatic schedule: fused from this many tokens
+constexpr int kFusedMinTokens = 3072; // automatic schedule, compute units unknown: fused from here
 constexpr int kTwoGroupStepsShifted = 8;  // split boundary: two token groups per wave from here
 constexpr int kTwoGroupStepsPre = 4;      // split pre: two groups from here (fewer registers)
 constexpr int kFourGroupStepsPre = 16;    // split pre: four groups from here
@@ -31,6 +31,7 @@ constexpr int kStreamStepsPerWave = 2;    // streaming plan: 32-element steps pe
 constexpr int kStreamFinishWidth = 1024;  // streaming plan: hidden elements per finishing workgroup
 constexpr bool kStreamNontemporal = true; // streaming plan: nontemporal residual streams
 constexpr int kW4MinTileTokens = 18;  // automatic schedule: balanced 4-wave tiles of at least this
+constexpr int kW4MinTileTokens2 = 28; // ... and of at least this over two or more rounds
 constexpr int kW4MinTokens = 8192;    // fused schedule: 32-token tiles on 4 waves from here
 
 int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
@@ -76,22 +77,26 @@ mhc_status check_params(const mhc_params* p) {
 
 // Which kernels run mhc_boundary.  FUSED is honoured (the caller gets
 // UNSUPPORTED_SHAPE where the width has no fused kernel): 16-token tiles below
-// kW4MinTokens, 32-token tiles from there.  AUTO spreads the tokens evenly over
-// whole rounds of compute units (one workgroup each), since a partly filled
-// last round costs a whole round:
-//   4-wave tiles of the balanced size ceil(T / (rounds x units)) (at most 32)
-//   where that is at least kW4MinTileTokens;
-//   else 16-token tiles from kFusedMinTokens where they fill at least 7/8 of
-//   one round;
-//   the split schedule otherwise.
-// Measured cold at d=7168 (us): 32-token tiles or split before -> balanced
-// tiles: T=6144 274 -> 256, T=7168 298 -> 285, T=9216 419 -> 404, T=12288
-// 530 -> 486, T=14336 580 -> 548; T=8192 and 16384 unchanged.  18-token tiles
-// are level with the split in one round (T=4608: 215 against 212) and ahead of
-// it in two (T=9216), so they are the smallest taken.  Where the compute-unit
-// count is unknown, AUTO
-// falls back to 16-token tiles from kFusedMinTokens and 32-token tiles from
-// kW4MinTokens.
+// kW4MinTokens, 32-token tiles from there.  AUTO, from the compute-unit count
+// (one fused workgroup per CU):
+//   the split schedule while 16-token tiles would fill less than 5/8 of one
+//   round of CUs (T < 2560 on 256 CUs);
+//   from hidden 6144, 4-wave tiles of the balanced size ceil(T / (rounds x
+//   units)) (at most 32 tokens) where that is at least kW4MinTileTokens in one
+//   round, or at least kW4MinTileTokens2 in more;
+//   16-token tiles otherwise, over as many rounds as they take.
+// Measured cold (us; split / 16-token / balanced 4-wave tiles), d=7168:
+// T=2048 95 / 111 / 196, T=2560 125 / 114 / 197, T=4096 180 / 136 / 201,
+// T=4608 202 / 227 / 199, T=8192 345 / 264 / 253, T=9216 410 / 358 / 389,
+// T=12288 517 / 390 / 410, T=14336 598 / 496 / 458; d=6144 alike (one round:
+// T=6144 233 / 201 / 185; two: T=9216 359 / 287 / 347, T=14336 522 / 403 /
+// 393).  Up to hidden 5120 the 16-token tiles are ahead or level from 2560
+// tokens at every size measured (d=4096: T=4608 131 / 121 / 129, T=8192
+// 225 / 147 / 147, T=9216 233 / 187 / 243, T=16384 473 / 282 / 287; d=5120,
+// 2048 and 1024 alike): with fewer steps per row the 32-token tiles' halved
+// fragment loads save less than their longer chain of steps costs.  Where the
+// compute-unit count is unknown, AUTO falls back to 16-token tiles from
+// kFusedMinTokens and 32-token tiles from kW4MinTokens.
 enum class BoundaryPath { Split, Fused16, Fused32, Stream };
 struct BoundaryChoice {
     BoundaryPath path;
@@ -103,18 +108,22 @@ BoundaryChoice boundary_path(int schedule, int tokens, int hidden) {
     if (schedule == MHC_SCHEDULE_FUSED)
         return tokens >= kW4MinTokens ? BoundaryChoice{BoundaryPath::Fused32, 32}
                                       : BoundaryChoice{BoundaryPath::Fused16, 16};
-    if (schedule != MHC_SCHEDULE_AUTO || !fused_supported(hidden) || tokens < kFusedMinTokens)
-        return {BoundaryPath::Split, 0};
+    if (schedule != MHC_SCHEDULE_AUTO || !fused_supported(hidden)) return {BoundaryPath::Split, 0};
     const long units = device_compute_units();
-    if (units <= 0)
+    if (units <= 0) {
+        if (tokens < kFusedMinTokens) return {BoundaryPath::Split, 0};
         return tokens >= kW4MinTokens ? BoundaryChoice{BoundaryPath::Fused32, 32}
                                       : BoundaryChoice{BoundaryPath::Fused16, 16};
-    const long rounds = (ceil_div(tokens, 32) + units - 1) / units;
-    const int balanced = (int)ceil_div(tokens, (int)(rounds * units));
-    if (balanced >= kW4MinTileTokens) return {BoundaryPath::Fused32, balanced};
+    }
     const long tiles16 = ceil_div(tokens, 16);
-    if (tiles16 <= units && 8 * tiles16 >= 7 * units) return {BoundaryPath::Fused16, 16};
-    return {BoundaryPath::Split, 0};
+    if (8 * tiles16 < 5 * units) return {BoundaryPath::Split, 0};
+    if (hidden >= 6144) {
+        const long rounds = (ceil_div(tokens, 32) + units - 1) / units;
+        const int balanced = (int)ceil_div(tokens, (int)(rounds * units));
+        if (balanced >= (rounds == 1 ? kW4MinTileTokens : kW4MinTileTokens2))
+            return {BoundaryPath::Fused32, balanced};
+    }
+    return {BoundaryPath::Fused16, 16};
 }
 
 // The non-shifted pre reads X twice on either schedule, and its split runs

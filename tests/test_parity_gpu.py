@@ -231,21 +231,38 @@ def test_split_token_groups_ragged(oracle, kind, T, d):
                 fresh=(inp.X, inp.norm_w))
 
 
-@pytest.mark.parametrize("T,d", [(7168 + 7, 7168), (5120 + 3, 7168), (9216 + 3, 4096),
-                                 (4096 + 600, 2048)])
+@pytest.mark.parametrize("T,d", [(7168 + 7, 7168), (5120 + 3, 7168), (14336 + 5, 7168),
+                                 (9216 + 3, 7168), (9216 + 3, 4096), (4096 + 600, 2048)])
 def test_auto_balanced_tiles(oracle, T, d):
-    """AUTO spreads the tokens over whole rounds of compute units with 4-wave
-    tiles of ceil(T / (rounds x units)) tokens (29, 21, 19 and 19 tokens on
-    256 units; two rounds at 9219), or takes the split where such tiles would
-    be small.  Every token is checked."""
+    """From hidden 6144 AUTO takes 4-wave tiles of ceil(T / (rounds x units))
+    tokens where they are large enough (29 and 21 tokens in one round on 256
+    units, 29 over two rounds at 14341); otherwise, and at smaller widths, it
+    takes 16-token tiles over as many rounds as they need (9219 tokens: three
+    rounds).  Every token is checked."""
     import torch
     units = torch.cuda.get_device_properties(0).multi_processor_count
     rounds = -(-(-(-T // 32)) // units)
     tile = -(-T // (rounds * units))
-    say(f"auto T={T} d={d} (balanced tile {tile} tokens on {units} units)")
+    say(f"auto T={T} d={d} (balanced tile {tile} tokens on {units} units; "
+        f"AUTO runs {api.boundary_kernels(T, d)})")
     inp = WL.make_inputs(WL.Config("at", d=d, T=T, seed=T + d))
     g = Dev(inp).boundary(schedule="auto")
     compare(g, oracle.boundary(inp), label=f"auto T={T} d={d}")
+
+
+def test_auto_choices_on_256_units():
+    """AUTO's kernel choice at the sizes its rule was measured on (256 CUs)."""
+    import torch
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the measured choices are for 256 compute units")
+    split, f16, f32 = "k_partial+k_finish", "k_fused", "k_fused_w4"
+    for (T, d), want in {(2048, 7168): split, (2560, 7168): f16, (4096, 7168): f16,
+                         (4608, 7168): f32, (8192, 7168): f32, (9216, 7168): f16,
+                         (12288, 7168): f16, (14336, 7168): f32, (16384, 7168): f32,
+                         (6144, 6144): f32, (9216, 6144): f16, (2048, 4096): split,
+                         (2560, 4096): f16, (8192, 4096): f16, (16384, 4096): f16,
+                         (8192, 5120): f16, (32, 7168): split, (256, 7168): split}.items():
+        assert api.boundary_kernels(T, d) == want, (T, d)
 
 
 def test_fused_refuses_unsupported_width():
