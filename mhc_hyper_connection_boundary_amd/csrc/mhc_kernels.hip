@@ -737,6 +737,53 @@ __global__ __launch_bounds__(256) void k_post(int hidden, int chunks, const uint
     for (int s = 0; s < 4; ++s) *reinterpret_cast<uint4*>(xn_out + (t * 4 + s) * hidden + h) = Xn[s];
 }
 
+// Residual update alone, in the fastest pattern the movers measured: item =
+// (tile of 32 tokens, slice of 256 hidden elements), tile-major; wave w takes
+// tokens 8w..8w+7; instruction (p, j) covers stream j (4 = the block output)
+// of tokens 8w + 2p (lanes 0-31) and 8w + 2p + 1 (lanes 32-63), 2 rows x 512
+// contiguous bytes.  All 20 loads of a lane are issued before any arithmetic.
+// Tokens past T read the last token's rows and store nothing.  Taken from 128
+// MiB of X, with the nontemporal hint on every load and store (cold, us, the
+// kernel above -> this one: d=7168 T=8192 198 -> 192, d=4096 T=16384 212 ->
+// 197; plain loads and stores 202 at T=8192; at T=1000 it was slower, 25 -> 30).
+template <bool NT>
+__global__ __launch_bounds__(256) void k_post_rows(int T, int hidden, const uint16_t* __restrict__ x,
+                                                   const uint16_t* __restrict__ X,
+                                                   const float* __restrict__ post_prev,
+                                                   const float* __restrict__ comb_prev,
+                                                   uint16_t* __restrict__ xn_out) {
+    const int slices = hidden >> 8;
+    const int tile = blockIdx.x / slices, slice = blockIdx.x - tile * slices;
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int col = slice * 256 + (l & 31) * 8;
+    int tk[4];
+    bool ok[4];
+    uint4 v[4][5];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int t = tile * 32 + 8 * w + 2 * p + (l >> 5);
+        ok[p] = t < T;
+        tk[p] = ok[p] ? t : T - 1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[p][j] = ld16<NT>(X + ((size_t)tk[p] * 4 + j) * hidden + col);
+        v[p][4] = ld16<NT>(x + (size_t)tk[p] * hidden + col);
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        PrevCoef c;
+        load_prev(c, post_prev, comb_prev, post_prev, (size_t)tk[p]);  // (pre unused)
+        const uint4 Xv[4] = {v[p][0], v[p][1], v[p][2], v[p][3]};
+        uint4 Xn[4], li;
+        float ssq = 0.0f, ssq_li = 0.0f;
+        update_collapse(Xv, v[p][4], c, Xn, li, ssq, ssq_li);  // li and the sums are unused
+        if (ok[p]) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) st16<NT>(xn_out + ((size_t)tk[p] * 4 + s) * hidden + col, Xn[s]);
+        }
+    }
+}
+
+
 // ---------------------------------------------------------------------------
 // Weight prefetch: every thread reads four 16-byte words of the prepared weight
 // so that its lines are resident in the last-level cache (and the reading
@@ -777,6 +824,11 @@ hipError_t launch_prefetch_weight(const void* wprep, int hidden, hipStream_t str
 hipError_t launch_post(int T, int hidden, const uint16_t* x, const uint16_t* X,
                        const float* post_prev, const float* comb_prev, uint16_t* xn_out,
                        hipStream_t stream) {
+    if ((size_t)T * 4 * (size_t)hidden * 2 >= ((size_t)128 << 20)) {
+        hipLaunchKernelGGL((k_post_rows<true>), dim3((unsigned)((T + 31) / 32) * (unsigned)(hidden / 256)),
+                           dim3(256), 0, stream, T, hidden, x, X, post_prev, comb_prev, xn_out);
+        return hipGetLastError();
+    }
     const int chunks = (hidden / 8 + 255) / 256;
     hipLaunchKernelGGL(k_post, dim3((unsigned)T * (unsigned)chunks), dim3(256), 0, stream, hidden,
                        chunks, x, X, post_prev, comb_prev, xn_out);
