@@ -6,24 +6,29 @@
 //   k_fused_w4 / k_fused_pre_w4  4 waves, 32-token tiles (two token groups per
 //                                wave sharing each weight fragment; one wave per
 //                                SIMD, so a wave may hold 512 registers).
-// The host picks the shape whose tiles fill whole rounds of compute units.
+// The host picks the shape from the batch size, the width and the number of
+// compute units.
 //
 // A wave step covers 64 hidden elements of the tile (two 32-element MFMA
-// k-blocks); wave w takes steps w, w + waves, ...  Every lane reads both
-// 64-byte halves of each 128-byte line it touches back to back, and the waves
-// together sweep contiguous kilobytes of every row, so HBM sees long runs.
-// k_fused_w4 goes further: each of its load instructions reads whole 128-byte
-// runs of 8 rows, and ds_bpermute moves the data into the matrix-core layout.
-// While a wave computes step i (residual update, X' store, lagged collapse,
-// sums of squares) the activations of step i+1 are in flight; the weight
-// fragments of step i come from L2 and feed the matrix cores.
+// k-blocks); wave w takes steps w, w + waves, ..., so the waves together sweep
+// contiguous kilobytes of every row.  The boundary kernels and the 32-token
+// pre load and store in row layout: each instruction covers whole 128-byte
+// runs of 8 rows, and ds_bpermute moves the data into the matrix-core layout
+// for the arithmetic and back for the stores (k_fused_pre loads both 64-byte
+// halves of each line in the matrix-core layout).  While a wave computes step
+// i (residual update, X' store, lagged collapse, sums of squares) the
+// activations of step i+1 are in flight; the weight fragments of step i come
+// from L2 and feed the matrix cores.  Where the token stride is a multiple of
+// 16 KiB the boundary tiles start their sweeps at different steps, so that the
+// tiles, which all run at about the same pace, do not hit the same columns at
+// the same time.
 //
 // The BF16 li of the tile must wait for rstd_li, which depends on the whole
-// row: the first 8 or 9 steps of every wave park it in LDS, the last few in
-// registers, the steps between in the layer-input buffer itself, which the
-// epilogue reads back and overwrites with the normalised values.  After the
-// loop the waves' partials are combined in LDS in a fixed order; one quad per
-// token computes pre / post / Sinkhorn comb while the other waves already
+// row: the first 8 or 9 steps of every wave park it in LDS, the last one or
+// two in registers, the steps between in the layer-input buffer itself, which
+// the epilogue reads back and overwrites with the normalised values.  After
+// the loop the waves' partials are combined in LDS in a fixed order; one quad
+// per token computes pre / post / Sinkhorn comb while the other waves already
 // write the layer input.  Every CU finishes its tile at about the same time,
 // so nothing overlaps the epilogue: its loads (norm_w, the first parked steps)
 // are requested before the reductions, and several parked steps stay in
@@ -1048,6 +1053,11 @@ __global__ __launch_bounds__(256) void k_fused_pre_w4(
     const bool phi = n >= 8;
     const int ridx[2] = {(16 * (lane & 3) + (lane >> 3)) * 4, (16 * (lane & 3) + 8 + (lane >> 3)) * 4};
     const bool rhi = (lane & 7) >= 4;
+    // Rotated sweeps as in k_fused_w4 (cold, T=8192: d=4096 137 -> 132 us,
+    // d=8192 321 -> 283 us; both passes take the same step order).
+    constexpr bool kRotate = hidden % 2048 == 0;
+    const int rot = kRotate ? (int)((((unsigned)tile * 2654435761u) >> 12) % (unsigned)S) : 0;
+    auto astep = [&](int i) { return i + rot >= S ? i + rot - S : i + rot; };
 
     // Pass 1: sums of squares and the projection.
     f32x4_t acc[2][3];
@@ -1058,10 +1068,10 @@ __global__ __launch_bounds__(256) void k_fused_pre_w4(
     float ssq[2] = {0.0f, 0.0f};
     ActRowsX cur[2];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) load_rows_x<hidden>(cur[q], X, tok[q], wave * kWide + hl0);
+    for (int q = 0; q < 2; ++q) load_rows_x<hidden>(cur[q], X, tok[q], (astep(0) * kWaves4 + wave) * kWide + hl0);
 #pragma unroll 1
     for (int i = 0; i < S; ++i) {
-        const int step = i * kWaves4 + wave;
+        const int step = astep(i) * kWaves4 + wave;
         uint4 A0[kFragsPerStep], A1[kFragsPerStep];
         load_frags(A0, wprep, 2 * step, lane);
         load_frags(A1, wprep, 2 * step + 1, lane);
@@ -1070,7 +1080,7 @@ __global__ __launch_bounds__(256) void k_fused_pre_w4(
         if (i + 1 < S) {
 #pragma unroll
             for (int q = 0; q < 2; ++q)
-                load_rows_x<hidden>(nxt[q], X, tok[q], step * kWide + hl0 + kWaves4 * kWide);
+                load_rows_x<hidden>(nxt[q], X, tok[q], (astep(i + 1) * kWaves4 + wave) * kWide + hl0);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -1087,7 +1097,7 @@ __global__ __launch_bounds__(256) void k_fused_pre_w4(
     }
     // Pass 2's first activations are requested before the reductions.
 #pragma unroll
-    for (int q = 0; q < 2; ++q) load_rows_x<hidden>(cur[q], X, tok[q], wave * kWide + hl0);
+    for (int q = 0; q < 2; ++q) load_rows_x<hidden>(cur[q], X, tok[q], (astep(0) * kWaves4 + wave) * kWide + hl0);
     CoefParams cp;
     if (wave < 2) cp = load_coef_params(scale, base, lane & 3);
 #pragma unroll
@@ -1143,12 +1153,13 @@ __global__ __launch_bounds__(256) void k_fused_pre_w4(
         for (int j = 0; j < 4; ++j) pr[q][j] = pre_s[16 * q + n][j];
     float ssq_li[2] = {0.0f, 0.0f};
     auto body = [&](int i, bool keep, uint4 (&li)[2][2]) {
-        const int step = i * kWaves4 + wave;
+        const int step = astep(i) * kWaves4 + wave;
         const int hr = step * kWide + hl0;
         ActRowsX nxt[2];
         if (i + 1 < S) {
 #pragma unroll
-            for (int q = 0; q < 2; ++q) load_rows_x<hidden>(nxt[q], X, tok[q], hr + kWaves4 * kWide);
+            for (int q = 0; q < 2; ++q)
+                load_rows_x<hidden>(nxt[q], X, tok[q], (astep(i + 1) * kWaves4 + wave) * kWide + hl0);
         }
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
@@ -1188,7 +1199,7 @@ __global__ __launch_bounds__(256) void k_fused_pre_w4(
     };
     LayerInputRows<Shape, kWaves4, 2, 5, kNorm, false> out{
         norm_w, {{erow(0, 0), erow(0, 1)}, {erow(1, 0), erow(1, 1)}},
-        {{t0 + er < T, t0 + 8 + er < T}, {t0 + 16 + er < T, t0 + 24 + er < T}}, tl >> 6, (tl & 7) * 8, 0};
+        {{t0 + er < T, t0 + 8 + er < T}, {t0 + 16 + er < T, t0 + 24 + er < T}}, tl >> 6, (tl & 7) * 8, rot};
     out.prefetch();
 
 #pragma unroll

@@ -80,6 +80,7 @@ def cases():
         ("pre split, four groups (k_partial_pre_wide)", 2400, 7168, pre("split")),
         ("pre fused 16-token tiles (k_fused_pre)", 100, 1024, pre("fused")),
         ("pre fused 32-token tiles (k_fused_pre_w4)", 8192 + 3, 1024, pre("fused")),
+        ("pre fused 32-token tiles, rotated sweeps (k_fused_pre_w4)", 8192 + 3, 2048, pre("fused")),
         ("pre onepass (k_pre_one)", 40, 2048, pre("onepass")),
         ("pre_mixes (k_pre_finish)", 45, 1024, pre_mixes),
     ]

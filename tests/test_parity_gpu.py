@@ -199,12 +199,13 @@ def test_boundary_small_full(oracle, T, d, schedule):
 
 
 @pytest.mark.parametrize("T,d", [(8192 + 13, 1024), (8192 + 29, 2048), (8192 + 3, 5120),
-                                 (8192 + 7, 8192)])
+                                 (8192 + 1, 6144), (8192 + 7, 8192)])
 def test_boundary_fused_32_token_tiles(oracle, T, d):
     """From 8192 tokens the fused schedule runs 32-token tiles (two token
     groups per wave).  Ragged tails leave the second group, or both, partly
     past the last token.  From d=4096 some li steps wait in the output buffer
-    (10 at d=5120, 22 at d=8192, more than the 5 the epilogue keeps in flight)."""
+    (10 at d=5120, 22 at d=8192, more than the 5 the epilogue keeps in flight).
+    At d=2048, 6144 and 8192 each tile starts its sweep at its own step."""
     say(f"boundary 32-token tiles T={T} d={d}")
     inp = WL.make_inputs(WL.Config("w4", d=d, T=T, seed=T + d))
     g = Dev(inp).boundary(schedule="fused")
