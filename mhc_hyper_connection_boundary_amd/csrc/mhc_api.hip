@@ -200,12 +200,13 @@ SplitPlan split_plan(int T, int hidden, bool invariant, bool shifted) {
             }
         }
     }
-    // INVARIANT pre from 64 tiles: two token groups share each fragment load.
-    // A token's sums have the same order for any number of groups, so the
-    // bits still do not depend on T (d=7168, cold: T=2048 65.5 -> 62.6 us,
-    // T=8192 281 -> 265.5 us; the boundary's two-group kernel is slower at one
-    // step per wave and keeps one group).
-    if (invariant && !shifted && tiles >= 64) plan.groups = 2;
+    // INVARIANT from 64 tiles: two token groups share each fragment load. A
+    // token's sums have the same order for any number of groups, so the bits
+    // still do not depend on T (d=7168, cold: pre T=2048 65.5 -> 62.6 us,
+    // T=8192 281 -> 265.5 us; the boundary, once the one-step kernel let two
+    // of its two-group workgroups share a CU: T=1024 55.8 -> 53.7 us, T=8192
+    // 411 -> 406 us).
+    if (invariant && tiles >= 64) plan.groups = 2;
     plan.steps_per_wave = spw;
     plan.slices = ceil_div(nsteps, 4L * spw);
     // Finisher workgroups per tile: each rescales at least 256 elements of

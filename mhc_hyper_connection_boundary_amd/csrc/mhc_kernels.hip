@@ -66,9 +66,12 @@ __global__ __launch_bounds__(256) void k_prepare_weight(const float* __restrict_
 // Split schedule, kernel 1: partial sums over a run of hidden steps.  A wave
 // carries G groups of 16 tokens (tokens n, n + 16, ... of the workgroup's
 // tile in lane n) through every step and feeds all of them from one set of
-// weight fragments.  Each token's sums have the same order for any G.
+// weight fragments.  Each token's sums have the same order for any G.  ONE:
+// the plan gives every wave one step (decode, INVARIANT), so the next step's
+// buffers are not needed: 140 registers instead of 192 with one group, 224
+// instead of 303 with two (two workgroups per CU instead of one).
 // ---------------------------------------------------------------------------
-template <bool SHIFTED, int G, bool NT>
+template <bool SHIFTED, int G, bool NT, bool ONE>
 __global__ __launch_bounds__(256) void k_partial(
     int T, int hidden, int steps_per_wave, int slices, const uint16_t* __restrict__ x,
     const uint16_t* __restrict__ X, const float* __restrict__ post_prev,
@@ -133,7 +136,7 @@ __global__ __launch_bounds__(256) void k_partial(
 #pragma unroll
         for (int q = 0; q < G; ++q) load_x(Xv[q], xv[q], q, first + wave);
     }
-    for (int step = first + wave; step < last; step += 4) {
+    for (int step = first + wave; step < last; step += ONE ? last : 4) {
         const int h = step * kStep + g * 8;
         uint4 A[kFragsPerStep];
         const uint4* wp = wprep + (size_t)step * kFragsPerStep * 64 + lane;
@@ -141,7 +144,7 @@ __global__ __launch_bounds__(256) void k_partial(
         for (int i = 0; i < kFragsPerStep; ++i) A[i] = wp[i * 64];
         __builtin_amdgcn_sched_barrier(0);
         uint4 Xnx[G][4], xnx[G];
-        if (step + 4 < last) {
+        if (!ONE && step + 4 < last) {
 #pragma unroll
             for (int q = 0; q < G; ++q) load_x(Xnx[q], xnx[q], q, step + 4);
         }
@@ -842,10 +845,16 @@ static void launch_partial_g(bool shifted, const SplitPlan& plan, int T, int hid
                              uint16_t* xn_out, uint16_t* li_out, float* part, hipStream_t stream) {
     const dim3 grid((unsigned)((T + kTile * G - 1) / (kTile * G)) * (unsigned)plan.slices);
     if (shifted) {
-        if constexpr (G <= 2)  // (four groups would spill in the shifted kernel)
-            hipLaunchKernelGGL((k_partial<true, G, NT>), grid, dim3(256), 0, stream, T, hidden,
-                               plan.steps_per_wave, plan.slices, x, X, post_prev, comb_prev,
-                               pre_lag, w, xn_out, li_out, part);
+        if constexpr (G <= 2) {  // (four groups would spill in the shifted kernel)
+            if (plan.steps_per_wave == 1)
+                hipLaunchKernelGGL((k_partial<true, G, NT, true>), grid, dim3(256), 0, stream, T, hidden,
+                                   plan.steps_per_wave, plan.slices, x, X, post_prev, comb_prev,
+                                   pre_lag, w, xn_out, li_out, part);
+            else
+                hipLaunchKernelGGL((k_partial<true, G, NT, false>), grid, dim3(256), 0, stream, T, hidden,
+                                   plan.steps_per_wave, plan.slices, x, X, post_prev, comb_prev,
+                                   pre_lag, w, xn_out, li_out, part);
+        }
     } else {
         if constexpr (G == 4) {
             if (plan.steps_per_wave % 2 == 0) {
@@ -854,9 +863,14 @@ static void launch_partial_g(bool shifted, const SplitPlan& plan, int T, int hid
                 return;
             }
         }
-        hipLaunchKernelGGL((k_partial<false, G, NT>), grid, dim3(256), 0, stream, T, hidden,
-                           plan.steps_per_wave, plan.slices, nullptr, X, nullptr, nullptr,
-                           nullptr, w, nullptr, nullptr, part);
+        if (plan.steps_per_wave == 1)
+            hipLaunchKernelGGL((k_partial<false, G, NT, true>), grid, dim3(256), 0, stream, T, hidden,
+                               plan.steps_per_wave, plan.slices, nullptr, X, nullptr, nullptr,
+                               nullptr, w, nullptr, nullptr, part);
+        else
+            hipLaunchKernelGGL((k_partial<false, G, NT, false>), grid, dim3(256), 0, stream, T, hidden,
+                               plan.steps_per_wave, plan.slices, nullptr, X, nullptr, nullptr,
+                               nullptr, w, nullptr, nullptr, part);
     }
 }
 
@@ -930,11 +944,11 @@ int partial_resident_workgroups(bool shifted, int groups) {
         int per_unit = 0;
         hipError_t e;
         if (shifted)
-            e = groups == 2 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_unit, k_partial<true, 2, false>, 256, 0)
-                            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_unit, k_partial<true, 1, false>, 256, 0);
+            e = groups == 2 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_unit, k_partial<true, 2, false, false>, 256, 0)
+                            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_unit, k_partial<true, 1, false, false>, 256, 0);
         else
-            e = groups == 2 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_unit, k_partial<false, 2, false>, 256, 0)
-                            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_unit, k_partial<false, 1, false>, 256, 0);
+            e = groups == 2 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_unit, k_partial<false, 2, false, false>, 256, 0)
+                            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_unit, k_partial<false, 1, false, false>, 256, 0);
         v = (e == hipSuccess && units > 0 && per_unit > 0) ? units * per_unit : -1;
         slot.store(v, std::memory_order_relaxed);
     }
