@@ -102,12 +102,13 @@ typedef enum {
  * hidden 7168 on 256 compute units; mhc_pre: one workgroup per compute unit,
  * T <= 64), so small decode batches give the same bits under all three. */
 typedef enum {
-    MHC_SCHEDULE_AUTO = 0,        /* mhc_boundary: the fused kernels where they exist and
-                                     their tiles fill the device's compute units: 4-wave tiles
-                                     of ceil(T / (rounds x units)) <= 32 tokens (tokens spread
-                                     evenly over whole rounds) where that is at least 18, else
-                                     16-token tiles (from 3072 tokens) where they fill at least
-                                     7/8 of one round; else SPLIT.  mhc_pre: SPLIT */
+    MHC_SCHEDULE_AUTO = 0,        /* mhc_boundary, from the device's compute-unit count:
+                                     SPLIT while 16-token tiles would fill less than 5/8 of
+                                     one round of compute units (T < 2560 on 256); where the
+                                     fused kernels exist, from hidden 6144 4-wave tiles of
+                                     ceil(T / (rounds x units)) <= 32 tokens where that is at
+                                     least 18 in one round or 28 in more, else 16-token
+                                     tiles over as many rounds as they take.  mhc_pre: SPLIT */
     MHC_SCHEDULE_SPLIT = 1,       /* hidden split over many workgroups + finishing kernel */
     MHC_SCHEDULE_FUSED = 2,       /* one workgroup per token tile owns all of hidden: 16-token
                                      tiles on 8 waves, or from 8192 tokens 32-token tiles on
@@ -238,7 +239,8 @@ mhc_status mhc_boundary(int tokens, int hidden, const uint16_t* x, const uint16_
  *   split schedule (INVARIANT: tokens * hidden bytes), or plus 4 + 128 *
  *   (hidden / 256) bytes per token for STREAM; the fused kernels need none.
  *   (At hidden 7168 AUTO fits every batch, since it runs the fused kernels
- *   from 3072 tokens.)
+ *   from 2560 tokens on 256 compute units, from 3072 where the count is
+ *   unknown.)
  *   Sharing: every call on one GPU uses the same array, so calls that overlap
  *   in time on one GPU (concurrent streams) race and give wrong results;
  *   calls ordered on one stream are safe.  The array starts zeroed, as the
