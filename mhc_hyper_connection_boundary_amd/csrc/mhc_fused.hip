@@ -56,35 +56,12 @@ struct FusedPreShape {
     static constexpr int kLiReg = 0;
 };
 
-// Activations of one wave step.  Lane (n, g) holds, for token n, the 8 hidden
-// elements 64*step + 32*b + 8*g + [0, 8) of block b = 0, 1: the two 64-byte
-// halves of every 128-byte line of the step are read by the same lane group
-// with back-to-back loads, and block b is directly the B operand of MFMA
-// k-block 2*step + b.
-struct Act {
-    uint4 X[2][4];  // [block][stream]
-    uint4 x[2];
-};
-
 __device__ __forceinline__ uint4 load_stream(const uint16_t* p) {
     return *reinterpret_cast<const uint4*>(p);
 }
 
 __device__ __forceinline__ void store_stream(uint16_t* p, const uint4& v) {
     *reinterpret_cast<uint4*>(p) = v;
-}
-
-// (k_fused only.  X and x are read once, with the nontemporal hint: d=7168,
-// T=4096 172 -> 166 us, T=3072 154 -> 152 us.)
-__device__ __forceinline__ void load_act(Act& a, const uint16_t* __restrict__ Xrow,
-                                         const uint16_t* __restrict__ xrow, int hidden, int h) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        a.X[0][j] = ld16<true>(Xrow + (size_t)j * hidden + h);
-        a.X[1][j] = ld16<true>(Xrow + (size_t)j * hidden + h + kStep);
-    }
-    a.x[0] = ld16<true>(xrow + h);
-    a.x[1] = ld16<true>(xrow + h + kStep);
 }
 
 // Row-layout activations of one wave step: instruction i, stream j: lane L
@@ -806,13 +783,17 @@ hipError_t launch_w4_s(int T, int tile_tokens, const uint16_t* x, const uint16_t
 // ---------------------------------------------------------------------------
 // Non-shifted pre, fused: one 8-wave workgroup per 16-token tile.  Pass 1
 // streams the tile's X through the sums of squares and the projection (same
-// step order and lane map as k_fused, X' = X).  After the fixed-order
+// step order as k_fused, X' = X), loading it in the matrix-core layout
+// itself.  After the fixed-order
 // reduction wave 0 publishes pre, then runs the Sinkhorn; pass 2 reads the
 // tile's X again, which was read a few tens of microseconds earlier and is
 // normally still in the last-level cache, collapses it with the fresh pre,
 // and parks li as k_fused does (LDS for the first steps, then the
 // layer-input buffer) until rstd_li is known.
 // ---------------------------------------------------------------------------
+// Lane (n, g) holds, for token n, the 8 hidden elements 64*step + 32*b + 8*g
+// + [0, 8) of block b = 0, 1 (both 64-byte halves of every 128-byte line, read
+// back to back); block b is directly the B operand of MFMA k-block 2*step + b.
 struct ActX {
     uint4 X[2][4];  // [block][stream]
 };
