@@ -299,7 +299,8 @@ def config_numbers():
     sets = [({k: v.clone() for k, v in w.t.items()}, w.wp.clone()) for _ in range(_sets_for(b))]
     cold_ms = graph_time(torch, [lambda t=t, wp=wp: w.call(t, wp) for t, wp in sets] * 2, 4)
     out["decode wave limit d=7168 T=256"] = dict(
-        timing="HIP graph replay", us_per_call_hot=hot_ms * 1e3, us_per_call_cold=cold_ms * 1e3,
+        kernels=w.api.boundary_kernels(T, d), timing="HIP graph replay",
+        us_per_call_hot=hot_ms * 1e3, us_per_call_cold=cold_ms * 1e3,
         tokens_per_s_cold=T / (cold_ms * 1e-3), bytes_per_call=b,
         gbs_cold=b / (cold_ms * 1e-3) / 1e9, roofline_frac_cold=b / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
     del w, sets
@@ -310,7 +311,8 @@ def config_numbers():
     settle(torch, w.call, 0.1)
     ms, _ = time_calls(torch, lambda k: w.call(), 30, 5)
     out["stress d=4096 T=16384"] = dict(
-        timing="HIP events over 30 eager calls", us_per_call=ms * 1e3,
+        kernels=w.api.boundary_kernels(T, d), timing="HIP events over 30 eager calls",
+        us_per_call=ms * 1e3,
         us_per_call_percentiles=percentiles_us(torch, w.call), tokens_per_s=T / (ms * 1e-3),
         bytes_per_call=b, gbs=b / (ms * 1e-3) / 1e9, roofline_frac=b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
     del w
