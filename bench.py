@@ -481,6 +481,7 @@ MOVER_MODES = {
     0: "tile-major 32x256 items, 2 rows x 512 B per instruction, nontemporal",
     1: "tile-major 32x256 items, 2 rows x 512 B per instruction, plain",
     2: "streaming-schedule pattern: persistent, 64x256 items in 64-element steps, lockstep waves",
+    3: "tile-major 32x512 items, 1 row x 1024 B per instruction, nontemporal",
 }
 
 

@@ -16,6 +16,9 @@
 //           both 64-byte halves of a 128-byte line per row; the next step is
 //           requested before the current one is stored; a workgroup barrier
 //           per step
+//   mode 3  as mode 0 with items of 32 tokens x 512 elements: each load /
+//           store instruction covers 1 row x 1024 contiguous bytes;
+//           nontemporal (measured faster than mode 0)
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -44,31 +47,34 @@ struct MoverArgs {
     unsigned xbytes, sbytes;  // bytes of X (and X'), of x (and lo)
 };
 
-// Modes 0 and 1: item blockIdx.x = (tile of 32 tokens, slice of 256 elements).
-template <int AUX>
+// Modes 0, 1 and 3: item blockIdx.x = (tile of 32 tokens, slice of 256 or,
+// for one row per instruction, 512 elements).
+template <int AUX, int RPI>  // RPI: rows per load / store instruction (2 or 1)
 __global__ __launch_bounds__(256) void k_mover_rows(MoverArgs a) {
-    const int slices = a.hidden / 256;
+    constexpr int kRunBytes = 1024 / RPI;  // contiguous bytes of a row per instruction
+    constexpr int kInst = 40 / RPI;        // instructions per wave
+    const int slices = a.hidden * 2 / kRunBytes;
     const int tile = blockIdx.x / slices, slice = blockIdx.x - tile * slices;
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
     const unsigned row_bytes = (unsigned)a.hidden * 2;
     const auto rX = rsrc(a.X, a.xbytes), rx = rsrc(a.x, a.sbytes);
     const auto rXo = rsrc(a.Xo, a.xbytes), rlo = rsrc(a.lo, a.sbytes);
     // 160 rows per item: 128 of X (32 tokens x 4 streams), 32 of x; wave w
-    // takes rows 40w .. 40w + 39, instruction k rows 40w + 2k and 40w + 2k + 1.
-    u32x4_t v[20];
-    unsigned off[20];
+    // takes rows 40w .. 40w + 39, instruction k rows 40w + RPI*k .. + RPI - 1.
+    u32x4_t v[kInst];
+    unsigned off[kInst];
 #pragma unroll
-    for (int k = 0; k < 20; ++k) {
-        const int row = 40 * w + 2 * k + l / 32;
-        const unsigned col = (unsigned)slice * 512 + (l % 32) * 16;
+    for (int k = 0; k < kInst; ++k) {
+        const int row = 40 * w + RPI * k + l / (64 / RPI);
+        const unsigned col = (unsigned)slice * kRunBytes + (l % (64 / RPI)) * 16;
         off[k] = row < 128 ? ((unsigned)tile * 128 + row) * row_bytes + col
                            : ((unsigned)tile * 32 + row - 128) * row_bytes + col;
         v[k] = row < 128 ? __builtin_amdgcn_raw_buffer_load_b128(rX, off[k], 0, AUX)
                          : __builtin_amdgcn_raw_buffer_load_b128(rx, off[k], 0, AUX);
     }
 #pragma unroll
-    for (int k = 0; k < 20; ++k) {
-        const int row = 40 * w + 2 * k + l / 32;
+    for (int k = 0; k < kInst; ++k) {
+        const int row = 40 * w + RPI * k + l / (64 / RPI);
         if (row < 128)
             __builtin_amdgcn_raw_buffer_store_b128(touch(v[k]), rXo, off[k], 0, AUX);
         else
@@ -138,13 +144,15 @@ extern "C" {
 // `hidden` in mode 0, 1 or 2 (above).  X, Xo: tokens*4*hidden bf16 values;
 // x, lo: tokens*hidden; all device pointers, 16-byte aligned, caller-owned.
 // Returns 0 on success, 1 for arguments outside the movers' shapes (tokens a
-// positive multiple of 64, hidden a multiple of 256 in [256, 16384], X under
-// 4 GiB, non-null pointers, mode in 0..2), 2 if the launch failed.
+// positive multiple of 64, hidden a multiple of 256 in [256, 16384] (of 512
+// for mode 3), X under 4 GiB, non-null pointers, mode in 0..3), 2 if the
+// launch failed.
 int mhc_mover_run(int tokens, int hidden, const void* X, const void* x, void* Xo, void* lo, int mode,
                   void* stream) {
     if (tokens <= 0 || tokens % 64 != 0 || hidden < 256 || hidden > 16384 || hidden % 256 != 0)
         return 1;
-    if (!X || !x || !Xo || !lo || mode < 0 || mode > 2) return 1;
+    if (!X || !x || !Xo || !lo || mode < 0 || mode > 3) return 1;
+    if (mode == 3 && hidden % 512 != 0) return 1;
     const uint64_t xbytes = (uint64_t)tokens * 4 * hidden * 2;
     if (xbytes >= ((uint64_t)1 << 32)) return 1;
     MoverArgs a;
@@ -159,9 +167,11 @@ int mhc_mover_run(int tokens, int hidden, const void* X, const void* x, void* Xo
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const int items32 = (tokens / 32) * (hidden / 256);
     if (mode == 0) {
-        hipLaunchKernelGGL((k_mover_rows<2>), dim3(items32), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((k_mover_rows<2, 2>), dim3(items32), dim3(256), 0, s, a);
     } else if (mode == 1) {
-        hipLaunchKernelGGL((k_mover_rows<0>), dim3(items32), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((k_mover_rows<0, 2>), dim3(items32), dim3(256), 0, s, a);
+    } else if (mode == 3) {
+        hipLaunchKernelGGL((k_mover_rows<2, 1>), dim3((tokens / 32) * (hidden / 512)), dim3(256), 0, s, a);
     } else {
         int dev = 0, units = 0;
         if (hipGetDevice(&dev) != hipSuccess ||
