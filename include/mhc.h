@@ -105,10 +105,10 @@ typedef enum {
     MHC_SCHEDULE_AUTO = 0,        /* mhc_boundary, from the device's compute-unit count:
                                      SPLIT while 16-token tiles would fill less than 5/8 of
                                      one round of compute units (T < 2560 on 256); where the
-                                     fused kernels exist, from hidden 6144 4-wave tiles of
-                                     ceil(T / (rounds x units)) <= 32 tokens where that is at
-                                     least 18 in one round or 28 in more, else 16-token
-                                     tiles over as many rounds as they take.  mhc_pre: SPLIT */
+                                     fused kernels exist, 4-wave tiles of ceil(T / (rounds x
+                                     units)) <= 32 tokens where that is at least 18 in one
+                                     round or 28 in more, else 16-token tiles over as many
+                                     rounds as they take.  mhc_pre: SPLIT */
     MHC_SCHEDULE_SPLIT = 1,       /* hidden split over many workgroups + finishing kernel */
     MHC_SCHEDULE_FUSED = 2,       /* one workgroup per token tile owns all of hidden: 16-token
                                      tiles on 8 waves, or from 8192 tokens 32-token tiles on

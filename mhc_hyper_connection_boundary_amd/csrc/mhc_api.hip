@@ -81,20 +81,19 @@ mhc_status check_params(const mhc_params* p) {
 // (one fused workgroup per CU):
 //   the split schedule while 16-token tiles would fill less than 5/8 of one
 //   round of CUs (T < 2560 on 256 CUs);
-//   from hidden 6144, 4-wave tiles of the balanced size ceil(T / (rounds x
-//   units)) (at most 32 tokens) where that is at least kW4MinTileTokens in one
-//   round, or at least kW4MinTileTokens2 in more;
+//   4-wave tiles of the balanced size ceil(T / (rounds x units)) (at most 32
+//   tokens) where that is at least kW4MinTileTokens in one round, or at least
+//   kW4MinTileTokens2 in more;
 //   16-token tiles otherwise, over as many rounds as they take.
-// Measured cold (us; split / 16-token / balanced 4-wave tiles), d=7168:
-// T=2048 95 / 111 / 196, T=2560 125 / 114 / 197, T=4096 180 / 136 / 201,
-// T=4608 202 / 227 / 199, T=8192 345 / 264 / 253, T=9216 410 / 358 / 389,
-// T=12288 517 / 390 / 410, T=14336 598 / 496 / 458; d=6144 alike (one round:
-// T=6144 233 / 201 / 185; two: T=9216 359 / 287 / 347, T=14336 522 / 403 /
-// 393).  Up to hidden 5120 the 16-token tiles are ahead or level from 2560
-// tokens at every size measured (d=4096: T=4608 131 / 121 / 129, T=8192
-// 225 / 147 / 147, T=9216 233 / 187 / 243, T=16384 473 / 282 / 287; d=5120,
-// 2048 and 1024 alike): with fewer steps per row the 32-token tiles' halved
-// fragment loads save less than their longer chain of steps costs.  Where the
+// Measured cold (us; split / 16-token / balanced 4-wave tiles): d=7168 T=2560
+// 126 / 115 / 160, T=4096 180 / 137 / 173, T=4608 202 / 228 / 177, T=6144
+// 267 / 240 / 201, T=8192 348 / 268 / 247, T=9216 410 / 361 / 342, T=12288
+// 519 / 394 / 396, T=16384 694 / 524 / 513; d=4096 T=4096 125 / 77 / 102,
+// T=4608 131 / 122 / 101, T=8192 224 / 148 / 134, T=9216 235 / 189 / 192,
+// T=12288 346 / 216 / 215, T=16384 459 / 288 / 258; d=1024 T=4608 44 / 38 /
+// 36, T=8192 64 / 48 / 42, T=9216 80 / 57 / 68, T=16384 114 / 91 / 76;
+// d=2048, 5120, 6144 and 8192 alike.  Two rounds of 18- or 24-token tiles
+// are level with or behind the 16-token tiles except at d >= 7168.  Where the
 // compute-unit count is unknown, AUTO falls back to 16-token tiles from
 // kFusedMinTokens and 32-token tiles from kW4MinTokens.
 enum class BoundaryPath { Split, Fused16, Fused32, Stream };
@@ -117,12 +116,10 @@ BoundaryChoice boundary_path(int schedule, int tokens, int hidden) {
     }
     const long tiles16 = ceil_div(tokens, 16);
     if (8 * tiles16 < 5 * units) return {BoundaryPath::Split, 0};
-    if (hidden >= 6144) {
-        const long rounds = (ceil_div(tokens, 32) + units - 1) / units;
-        const int balanced = (int)ceil_div(tokens, (int)(rounds * units));
-        if (balanced >= (rounds == 1 ? kW4MinTileTokens : kW4MinTileTokens2))
-            return {BoundaryPath::Fused32, balanced};
-    }
+    const long rounds = (ceil_div(tokens, 32) + units - 1) / units;
+    const int balanced = (int)ceil_div(tokens, (int)(rounds * units));
+    if (balanced >= (rounds == 1 ? kW4MinTileTokens : kW4MinTileTokens2))
+        return {BoundaryPath::Fused32, balanced};
     return {BoundaryPath::Fused16, 16};
 }
 

@@ -3,28 +3,30 @@
 // leave the chip.  Two shapes:
 //   k_fused / k_fused_pre        8 waves, 16-token tiles (one token group per
 //                                wave; two waves per SIMD);
-//   k_fused_w4 / k_fused_pre_w4  4 waves, 32-token tiles (two token groups per
-//                                wave sharing each weight fragment; one wave per
+//   k_fused_w4 / k_fused_pre_w4  4 waves, 32-token tiles (two token groups
+//                                sharing each weight fragment; one wave per
 //                                SIMD, so a wave may hold 512 registers).
 // The host picks the shape from the batch size, the width and the number of
 // compute units.
 //
-// A wave step covers 64 hidden elements of the tile (two 32-element MFMA
+// A projection step of a wave covers 64 hidden elements (two 32-element MFMA
 // k-blocks); wave w takes steps w, w + waves, ..., so the waves together sweep
-// contiguous kilobytes of every row.  The boundary kernels and the 32-token
-// pre load and store in row layout: each instruction covers whole 128-byte
-// runs of 8 rows, and ds_bpermute moves the data into the matrix-core layout
-// for the arithmetic and back for the stores (k_fused_pre loads both 64-byte
-// halves of each line in the matrix-core layout).  While a wave computes step
-// i (residual update, X' store, lagged collapse, sums of squares) the
-// activations of step i+1 are in flight; the weight fragments of step i come
-// from L2 and feed the matrix cores.  Where the token stride is a multiple of
-// 16 KiB the boundary tiles start their sweeps at different steps, so that the
-// tiles, which all run at about the same pace, do not hit the same columns at
-// the same time.
+// contiguous kilobytes of every row.  k_fused and k_fused_pre_w4 load and
+// store in row layout, each instruction covering whole 128-byte runs of 8
+// rows, and ds_bpermute moves the data into the matrix-core layout for the
+// arithmetic and back for the stores (k_fused_pre loads both 64-byte halves
+// of each line in the matrix-core layout).  k_fused_w4 splits the rows over
+// its waves instead:
+// each of its instructions covers 512-byte runs of 2 rows, and X' reaches the
+// matrix-core layout through LDS.  While a wave computes step i (residual
+// update, X' store, lagged collapse, sums of squares) the activations of step
+// i+1 are in flight; the weight fragments of step i come from L2 and feed the
+// matrix cores.  Where the token stride is a multiple of 16 KiB the boundary
+// tiles start their sweeps at different steps, so that the tiles, which all
+// run at about the same pace, do not hit the same columns at the same time.
 //
 // The BF16 li of the tile must wait for rstd_li, which depends on the whole
-// row: the first 8 or 9 steps of every wave park it in LDS, the last one or
+// row: the first 5 to 9 steps of every wave park it in LDS, the last one or
 // two in registers, the steps between in the layer-input buffer itself, which
 // the epilogue reads back and overwrites with the normalised values.  After
 // the loop the waves' partials are combined in LDS in a fixed order; one quad
@@ -238,14 +240,16 @@ struct LayerInputEpilogue {
     }
 };
 
-// The same for the 4-wave kernels, whose li is kept in row layout: register
-// (q, i) of a lane holds row 16q + 8i + L/8 of the tile, chunk L%8 of the
-// step's 128-byte run, so every load and store of li and norm_w covers 8 rows
-// x 128 bytes and a lane needs one norm_w register per step instead of two.
-// Lanes on rows past the last token read the row of token T-1 and write
-// nothing, as above.  The wave's i-th step covers step (i + rot) mod kSteps of
-// the row (the tile's rotation, see k_fused_w4); kNtOut puts the nontemporal
-// hint on the final layer-input stores.
+// The same for the kernels whose li is kept in row layout.  Register (q, k)
+// of a lane holds one row of the tile (row[q][k]) and 8 elements at hl0 of
+// each step's run, so a lane needs one norm_w register per step: in k_fused
+// and k_fused_pre_w4 row 16q + 8k + L/8, chunk L%8 of the wave's 128-byte run
+// (8 rows x 128 bytes per instruction); in k_fused_w4 one of the wave's 8
+// tokens, chunk L%32 of the step's 512-byte run (wave index 0 here: the whole
+// run is the wave's).  Lanes on rows past the last token read the row of
+// token T-1 and write nothing, as above.  The wave's i-th step covers step
+// (i + rot) mod kSteps of the row (the tile's rotation, see k_fused_w4);
+// kNtOut puts the nontemporal hint on the final layer-input stores.
 template <class Shape, int kWavesN, int kGroups, int kMaxDepth, bool kNorm, bool kNtOut>
 struct LayerInputRows {
     static constexpr int kParkEnd = Shape::kSteps - Shape::kLiReg;  // parked: [kLiLds, kParkEnd)
@@ -364,12 +368,12 @@ __global__ __launch_bounds__(512) void k_fused(
     float ssq = 0.0f, ssq_li = 0.0f;
 
     // Wave w takes steps w, w + 8, ...: at any moment the 8 waves cover 512
-    // contiguous hidden elements of every row of the tile.  As in k_fused_w4
-    // the activations are loaded in row layout (lane L: row 8i + L/8, 8 rows x
-    // 128 bytes per load), moved into the matrix-core layout with ds_bpermute,
-    // and X' and li go back to row layout for their stores; where hidden is a
-    // multiple of 2048 (token stride a multiple of 16 KiB) each tile starts its
-    // sweep at its own step.
+    // contiguous hidden elements of every row of the tile.  The activations
+    // are loaded in row layout (lane L: row 8i + L/8, 8 rows x 128 bytes per
+    // load), moved into the matrix-core layout with ds_bpermute, and X' and li
+    // go back to row layout for their stores; where hidden is a multiple of
+    // 2048 (token stride a multiple of 16 KiB) each tile starts its sweep at
+    // its own step (the rotation of k_fused_w4).
     int tok[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -508,27 +512,72 @@ __global__ __launch_bounds__(512) void k_fused(
 // ---------------------------------------------------------------------------
 // Fused schedule on 4 waves per workgroup (one per SIMD) with 32-token tiles.
 // The weight fragments are the costly loads of the 8-wave kernel: one 1 KB
-// load per fragment per 16 tokens.  Here each wave carries two 16-token groups
-// (tokens n and n + 16 of the tile in lane n) through every 64-element step and
-// feeds both from one set of fragments, which halves the fragment loads per
-// token while keeping 128-byte row runs.  With one wave per SIMD a wave may
-// hold 512 registers (architectural plus accumulation registers), enough for
-// both groups' activations, their prefetch and the fragments.  Each step issues
+// load per fragment per 16 tokens.  Here each wave feeds two 16-token groups
+// (tokens n and n + 16 of the tile in lane n) from one set of fragments, which
+// halves the fragment loads per token.  With one wave per SIMD a wave may hold
+// 512 registers (architectural plus accumulation registers).  Each step issues
 // its fragments first and the next step's activations after them, so the
 // projection never waits on HBM (loads complete in issue order).
 // ---------------------------------------------------------------------------
 constexpr int kWaves4 = 4;
 constexpr int kTileW4 = 32;
 
-// S = hidden / (kWaves4 * kWide): steps per wave; li of the first (at most
-// LdsMax) steps waits in LDS, 16 KB each, and of the last (at most RegMax) in
-// registers.  More registers spill.
+// S = hidden / (kWaves4 * kWide): steps; li of the first (at most LdsMax)
+// steps waits in LDS, 16 KB each, and of the last (at most RegMax) in
+// registers.
 template <int S, int LdsMax = 8, int RegMax = 2>
 struct FusedW4Shape {
     static constexpr int kSteps = S;
     static constexpr int kLiLds = S < LdsMax ? S : LdsMax;  // first steps: li waits in LDS
     static constexpr int kLiReg = S - kLiLds < RegMax ? S - kLiLds : RegMax;  // last: registers
 };                                                // (steps between: layer_input)
+
+// ---------------------------------------------------------------------------
+// The 4-wave boundary.  The tile's rows are split over the waves for the
+// memory side and its columns for the projection.  Wave w owns tokens
+// 4w..4w+3 and 16+4w..16+4w+3 of the tile; at every step it loads, updates,
+// stores and collapses 256 contiguous hidden elements of each of their rows:
+// for p = 0..3, lane L holds token 4w + 16(p/2) + 2(p%2) + L/32 and 16-byte
+// chunk L%32 of the step's 512-byte run, so every load and store instruction
+// covers 2 rows x 512 bytes.  The update and the lagged collapse are
+// elementwise and run in this layout as they are; only the projection needs
+// the matrix-core layout.  X' therefore goes through LDS: for each half q of
+// the tile (tokens 16q..16q+15, registers p = 2q, 2q+1 of every wave) a 32 KB
+// stage ([token][stream][chunk], chunks XOR-swizzled by the token, so that
+// both the row-order writes and the matrix-core reads are free of bank
+// conflicts), from which each wave reads, after a barrier, the operands of its
+// 64 columns (step 4i + w of 64 elements: MFMA k-blocks 8i + 2w, 8i + 2w + 1)
+// for the 16 tokens.  The halves alternate, so the matrix-core work of one
+// half overlaps the update of the other, and each stage is rewritten only
+// after the barrier that follows its reads.  A wave owns the sums of squares
+// of its tokens whole (a butterfly over a token's 32 lanes), so rstd_li needs
+// no cross-wave step.  The stages leave room for 5 li steps in LDS; one more
+// stays in registers (more measured no faster: the peeled steps' code).
+// Against the previous design of this kernel (each wave on 64 columns of all
+// 32 rows, 8 rows x 128 bytes per instruction, moved with ds_bpermute; li in
+// LDS for 9 steps), cold, us: d=7168 T=8192 251 -> 244, T=5120 198 -> 183;
+// d=8192 T=8192 287 -> 267; d=4096 T=8192 148 -> 134, T=16384 278 -> 254;
+// d=1024 T=8192 49.5 -> 42.7; d=7168 T=16384 (two rounds) 499 -> 506.
+// ---------------------------------------------------------------------------
+constexpr int kRun = kWaves4 * kWide;  // hidden elements of a row per step (512 bytes)
+
+// Row-run activations of one step: [p][stream] and [p] (see above).
+struct ActRuns {
+    uint4 X[4][4];
+    uint4 x[4];
+};
+
+template <int kHidden>
+__device__ __forceinline__ void load_runs(ActRuns& a, const uint16_t* __restrict__ X,
+                                          const uint16_t* __restrict__ x, const int (&tok)[4], int h) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint16_t* Xr = X + (size_t)tok[q] * (4 * kHidden) + h;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) a.X[q][j] = ld16<true>(Xr + j * kHidden);
+        a.x[q] = ld16<true>(x + (size_t)tok[q] * kHidden + h);
+    }
+}
 
 template <int S, bool kNorm>  // kNorm: norm_w is given
 __global__ __launch_bounds__(256) void k_fused_w4(
@@ -541,22 +590,19 @@ __global__ __launch_bounds__(256) void k_fused_w4(
     float* __restrict__ post_out, float* __restrict__ comb_out, float* __restrict__ mixes_out,
     float* __restrict__ rstd_out) {
     MHC_POISON_LDS(0);
-    // 9 li steps in LDS: the cross-wave sums need no buffer per wave.  One in
-    // registers: with two, the row-layout moves of the last steps spill (T=8192:
-    // 263 us with one, 284 with two).
-    using Shape = FusedW4Shape<S, 9, 1>;
-    constexpr int hidden = S * kWide * kWaves4;
-    __shared__ uint4 li_lds[Shape::kLiLds > 0 ? Shape::kLiLds : 1][kWaves4][2][2][64];
-    __shared__ float tot[kTileW4][26];
-    __shared__ float rli[kTileW4];
+    using Shape = FusedW4Shape<S, 5, 1>;
+    constexpr int hidden = S * kRun;
+    __shared__ uint4 stage[2][16 * 4 * 32];  // X' of one step: [half][token][stream][chunk ^ token]
+    __shared__ uint4 li_lds[Shape::kLiLds > 0 ? Shape::kLiLds : 1][kWaves4][4][64];
+    __shared__ __align__(16) PrevCoef cf[kTileW4];
+    __shared__ float tot[kTileW4][25];  // 24 mixes, the sum of squares of X'
 
     const int tile = blockIdx.x;
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int n = lane & 15;
     const int g = lane >> 4;
-    // The tile holds tokens [t0, t_end): tile_tokens of them (at most 32),
-    // fewer in the last tile.
+    const int ch = lane & 31;  // the lane's chunk of the step's 512-byte run
     const int t0 = tile * tile_tokens;
     const int t_end = min(t0 + tile_tokens, T);
     // Every CU runs its tile at about the same pace, so without a rotation all
@@ -567,22 +613,34 @@ __global__ __launch_bounds__(256) void k_fused_w4(
     // multiplicative hash of the tile index (a rotation equal to the tile index
     // itself correlates with the address bits and measured slower still).  The
     // step order is fixed per tile, so each token's sums still have one order.
-    // Cold calls, T=8192 (us, lockstep -> rotated): d=2048 93 -> 80, d=4096
-    // 184 -> 148, d=6144 260 -> 220, d=8192 390 -> 284; stress d=4096 T=16384
-    // 350 -> 284.  At d=1024, 5120 and 7168 the rotation measured 1-9 us slower
-    // (the tiles of an XCD then stop sharing the weight fragments in its L2).
+    // Cold calls, T=8192 (us, lockstep -> rotated, measured on the previous
+    // design): d=2048 93 -> 80, d=4096 184 -> 148, d=6144 260 -> 220, d=8192
+    // 390 -> 284; stress d=4096 T=16384 350 -> 284.  At d=1024, 5120 and 7168
+    // the rotation measured 1-9 us slower (the tiles of an XCD then stop
+    // sharing the weight fragments in its L2).
     constexpr bool kRotate = S % 8 == 0;
     const int rot = kRotate ? (int)((((unsigned)tile * 2654435761u) >> 12) % (unsigned)S) : 0;
     auto astep = [&](int i) { return i + rot >= S ? i + rot - S : i + rot; };
-    size_t tc[2];
-    PrevCoef c[2];
+
+    // The previous layer's coefficients of the tile's tokens, into LDS (token
+    // rows past the tile's last token repeat it, as below).
+    if (threadIdx.x < kTileW4 * 6) {
+        const int tl = threadIdx.x / 6, k = threadIdx.x - 6 * (threadIdx.x / 6);
+        const size_t t = (size_t)min(t0 + tl, t_end - 1);
+        const float* src = k == 0 ? post_prev + t * 4 : k == 5 ? pre_lag + t * 4 : comb_prev + t * 16 + 4 * (k - 1);
+        reinterpret_cast<float4*>(&cf[tl])[k] = *reinterpret_cast<const float4*>(src);
+    }
+
+    // A lane past the tile's last token works on that token (its loads and its
+    // share of the stage) but stores nothing: the token's own lane may sit in
+    // another wave.
+    int tl[4], tok[4];
+    bool own[4];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        // A lane past the tile's last token works on that token, so it stores
-        // the same bytes as the token's own lane: no branch needed.
-        const int t = t0 + 16 * q + n;
-        tc[q] = t < t_end ? (size_t)t : (size_t)(t_end - 1);
-        load_prev(c[q], post_prev, comb_prev, pre_lag, tc[q]);
+    for (int q = 0; q < 4; ++q) {
+        tl[q] = 4 * wave + 16 * (q >> 1) + 2 * (q & 1) + (lane >> 5);
+        own[q] = t0 + tl[q] < t_end;
+        tok[q] = own[q] ? t0 + tl[q] : t_end - 1;
     }
 
     f32x4_t acc[2][3];
@@ -590,124 +648,113 @@ __global__ __launch_bounds__(256) void k_fused_w4(
     for (int q = 0; q < 2; ++q)
 #pragma unroll
         for (int m = 0; m < 3; ++m) acc[q][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float ssq[2] = {0.0f, 0.0f}, ssq_li[2] = {0.0f, 0.0f};
+    float ssq[4] = {0.0f, 0.0f, 0.0f, 0.0f}, ssq_li[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 
-    // Wave w takes steps w, w + 4, ...: the 4 waves cover 256 contiguous
-    // hidden elements of every row of the tile at a time.  The activations
-    // are loaded in row layout (8 rows x 128 bytes per instruction) and moved
-    // into the matrix-core layout with ds_bpermute just before use: lane L
-    // loads row 8i + L/8 (tokens clamped to the tile's last one, as above).
-    int tok[2][2];
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int t = t0 + 16 * q + 8 * i + (lane >> 3);
-            tok[q][i] = t < t_end ? t : t_end - 1;
-        }
-    const int hl0 = (lane & 7) * 8;
-    const int pidx[2] = {(8 * (n & 7) + g) * 4, (8 * (n & 7) + 4 + g) * 4};
-    const bool phi = n >= 8;
-    const int ridx[2] = {(16 * (lane & 3) + (lane >> 3)) * 4, (16 * (lane & 3) + 8 + (lane >> 3)) * 4};
-    const bool rhi = (lane & 7) >= 4;
-    const bool rows3 = t0 + 24 < t_end;  // rows 24..31 hold a token of the tile (uniform)
-    ActRows cur[2];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) load_rows<hidden>(cur[q], X, x, tok[q], (astep(0) * kWaves4 + wave) * kWide + hl0);
-    // One wave step.  keep: li stays in the caller's registers (last steps);
+    // One activation buffer: as soon as a half's update has read its rows,
+    // the same registers receive that half's rows of the next step, so the
+    // loads of the next step are in flight during the rest of this one with
+    // no second buffer and no register copy.
+    ActRuns cur;
+    load_runs<hidden>(cur, X, x, tok, astep(0) * kRun + 8 * ch);
+    __syncthreads();  // cf
+    // One step.  keep: li stays in the caller's registers (last step);
     // otherwise it waits in LDS (first steps) or in the layer-input buffer.
-    // X' and li leave the matrix-core layout for row layout before they are
-    // stored: 8 rows x 128 bytes per store instead of 16 x 64 (T=8192: X'
-    // 289 -> 269 us, same bits).
-    auto body = [&](int i, bool keep, uint4 (&li)[2][2]) {
-        const int step = astep(i) * kWaves4 + wave;
+    auto body = [&](int i, bool keep, uint4 (&li)[4]) {
+        const int step = astep(i) * kWaves4 + wave;  // the wave's 64 columns for the projection
+        const int h = astep(i) * kRun + 8 * ch;
+        const int hn = astep(i + 1 < S ? i + 1 : i) * kRun + 8 * ch;  // the next step's
         uint4 A0[kFragsPerStep], A1[kFragsPerStep];
         load_frags(A0, wprep, 2 * step, lane);
         load_frags(A1, wprep, 2 * step + 1, lane);
         __builtin_amdgcn_sched_barrier(0);
-        ActRows nxt[2];
-        if (i + 1 < S) {
 #pragma unroll
-            for (int q = 0; q < 2; ++q)
-                load_rows<hidden>(nxt[q], X, x, tok[q], (astep(i + 1) * kWaves4 + wave) * kWide + hl0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            uint4 Xn[2][4], lm[2];
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                uint4 Xs[4], xs;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) Xs[j] = rows_to_mfma(cur[q].X[0][j], cur[q].X[1][j], pidx[b], phi);
-                xs = rows_to_mfma(cur[q].x[0], cur[q].x[1], pidx[b], phi);
-                update_collapse(Xs, xs, c[q], Xn[b], lm[b], ssq[q], ssq_li[q]);
-            }
-            const int hr = step * kWide + hl0;
+        for (int hq = 0; hq < 2; ++hq) {
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
-                // In tiles of at most 24 tokens, rows 24..31 all repeat the
-                // last token: their stores are skipped (a uniform branch).
-                // Eight copies of one line per store cost more than the whole
-                // row-layout gain (T=5120, 20-token tiles: 198 us skipped,
-                // 217 us stored).
-                const bool rows = q == 0 || k == 0 || rows3;
-                if (rows) {  // X' is not read again here: nontemporal (T=8192: 273 -> 251 us)
+                const int q = 2 * hq + k, t16 = tl[q] - 16 * hq;
+                const PrevCoef c = cf[tl[q]];
+                uint4 Xn[4];
+                update_collapse(cur.X[q], cur.x[q], c, Xn, li[q], ssq[q], ssq_li[q]);
 #pragma unroll
-                    for (int s2 = 0; s2 < 4; ++s2)
-                        st16<true>(xn_out + (size_t)tok[q][k] * (4 * hidden) + (size_t)s2 * hidden + hr,
-                                   mfma_to_rows(Xn[0][s2], Xn[1][s2], ridx[k], rhi));
+                for (int s2 = 0; s2 < 4; ++s2) {
+                    if (own[q])  // X' is not read again here: nontemporal
+                        st16<true>(xn_out + (size_t)tok[q] * (4 * hidden) + (size_t)s2 * hidden + h, Xn[s2]);
+                    stage[hq][(t16 * 4 + s2) * 32 + (ch ^ t16)] = Xn[s2];
                 }
-                li[q][k] = mfma_to_rows(lm[0], lm[1], ridx[k], rhi);
                 if (!keep) {
                     if (i < Shape::kLiLds)
-                        li_lds[i][wave][q][k][lane] = li[q][k];
-                    else if (rows)
-                        store_stream(layer_input + (size_t)tok[q][k] * hidden + hr, li[q][k]);
+                        li_lds[i][wave][q][lane] = li[q];
+                    else if (own[q])
+                        store_stream(layer_input + (size_t)tok[q] * hidden + h, li[q]);
                 }
             }
-            mfma_step(A0, Xn[0], acc[q]);
-            mfma_step(A1, Xn[1], acc[q]);
-        }
+            if (i + 1 < S) {
 #pragma unroll
-        for (int q = 0; q < 2; ++q) cur[q] = nxt[q];
+                for (int k = 0; k < 2; ++k) {
+                    const int q = 2 * hq + k;
+                    const uint16_t* Xr = X + (size_t)tok[q] * (4 * hidden) + hn;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) cur.X[q][j] = ld16<true>(Xr + j * hidden);
+                    cur.x[q] = ld16<true>(x + (size_t)tok[q] * hidden + hn);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();
+            uint4 B[2][4];
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int s2 = 0; s2 < 4; ++s2) B[b][s2] = stage[hq][(n * 4 + s2) * 32 + ((8 * wave + 4 * b + g) ^ n)];
+            mfma_step(A0, B[0], acc[hq]);
+            mfma_step(A1, B[1], acc[hq]);
+        }
     };
 #pragma unroll 1
     for (int i = 0; i < S - Shape::kLiReg; ++i) {
-        uint4 li[2][2];
+        uint4 li[4];
         body(i, false, li);
     }
-    uint4 li_keep[Shape::kLiReg > 0 ? Shape::kLiReg : 1][2][2];
+    uint4 li_keep[Shape::kLiReg > 0 ? Shape::kLiReg : 1][4];
 #pragma unroll
     for (int r = 0; r < Shape::kLiReg; ++r) body(S - Shape::kLiReg + r, true, li_keep[r]);
     // From here on the lane's indices come from an opaque copy of the thread
     // index, so the compiler cannot compute them before the loop and keep them
     // (spilled) through it: a reload from scratch would wait for every load the
     // epilogue has in flight.
-    int tl = (int)threadIdx.x;
-    asm volatile("" : "+v"(tl));
-    const int lw = tl >> 6, ll = tl & 63, ln = ll & 15, lg = ll >> 4;
-    // The coefficient parameters are requested before the epilogue's loads, so
-    // that waiting for them does not wait for those.
+    int tx = (int)threadIdx.x;
+    asm volatile("" : "+v"(tx));
+    const int lw = tx >> 6, ll = tx & 63, ln = ll & 15, lg = ll >> 4, lh = ll >> 5;
     CoefParams cp;
     if (lw < 2) cp = load_coef_params(scale, base, ll & 3);
-    const int er = ll >> 3;  // the lane's row within each 8-row instruction
+    // Epilogue register (q, k) is the lane's token p = 2q + k.
+    auto etok = [&](int q, int k) { return 4 * lw + 16 * q + 2 * k + lh; };
     auto erow = [&](int q, int k) {
-        const int t = t0 + 16 * q + 8 * k + er;
+        const int t = t0 + etok(q, k);
         return layer_input + (size_t)(t < t_end ? t : t_end - 1) * hidden;
     };
-    // The final layer-input stores carry the nontemporal hint (stress d=4096,
-    // T=16384: 355 -> 331 us; level at d=7168).
+    auto evalid = [&](int q, int k) { return t0 + etok(q, k) < t_end; };
+    // The wave's columns are the whole 256 of each step (wave index 0 there).
     LayerInputRows<Shape, kWaves4, 2, 5, kNorm, true> out{
         norm_w, {{erow(0, 0), erow(0, 1)}, {erow(1, 0), erow(1, 1)}},
-        {{t0 + er < t_end, t0 + 8 + er < t_end}, {t0 + 16 + er < t_end, t0 + 24 + er < t_end}},
-        lw, (ll & 7) * 8, rot};
+        {{evalid(0, 0), evalid(0, 1)}, {evalid(1, 0), evalid(1, 1)}}, 0, (ll & 31) * 8, rot};
     out.prefetch();
 
-    // Partials of the 4 waves, added into tot one wave at a time from 0.0f,
-    // wave 0 first: each mix is ((w0 + w1) + w2) + w3, each sum of squares
-    // adds the k-groups 0..3 of wave 0, then of wave 1, ...  Lane group 0 of
-    // a wave gathers the four k-group values of its token.
+    // The wave's own tokens: sums of squares over their 32 lanes (butterfly,
+    // the same bits in every lane), rstd_li in registers, the X' sum into tot.
+    float rl[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        float a = ssq[q], b = ssq_li[q];
+#pragma unroll
+        for (int o = 16; o >= 1; o >>= 1) {
+            a += __shfl_xor(a, o);
+            b += __shfl_xor(b, o);
+        }
+        if ((ll & 31) == 0) tot[etok(q >> 1, q & 1)][24] = a;
+        rl[q] = rsqrt_nr(b * (1.0f / (float)hidden) + p.norm_eps);
+    }
+    // Mixes of the 4 waves, added into tot one wave at a time from 0.0f, wave
+    // 0 first: each mix is ((w0 + w1) + w2) + w3.
 #pragma unroll
     for (int w = 0; w < kWaves4; ++w) {
         if (lw == w) {
@@ -721,28 +768,10 @@ __global__ __launch_bounds__(256) void k_fused_w4(
                         const int v = 8 * m + 2 * lg + j;
                         tot[tn][v] = (w == 0 ? 0.0f : tot[tn][v]) + mix_of(acc[q], m, j);
                     }
-                float part[2][4];
-#pragma unroll
-                for (int gg = 0; gg < 4; ++gg) {
-                    part[0][gg] = __shfl(ssq[q], ln + 16 * gg);
-                    part[1][gg] = __shfl(ssq_li[q], ln + 16 * gg);
-                }
-                if (lg == 0) {
-#pragma unroll
-                    for (int e = 0; e < 2; ++e) {
-                        float t = w == 0 ? 0.0f : tot[tn][24 + e];
-#pragma unroll
-                        for (int gg = 0; gg < 4; ++gg) t += part[e][gg];
-                        tot[tn][24 + e] = t;
-                    }
-                }
             }
         }
         __syncthreads();
     }
-    if (threadIdx.x < kTileW4)
-        rli[threadIdx.x] = rsqrt_nr(tot[threadIdx.x][25] * (1.0f / (float)hidden) + p.norm_eps);
-    __syncthreads();
 
     if (lw < 2) {  // 32 tokens x 4 lanes: waves 0 and 1
         const int tn = 16 * lw + (ll >> 2), ci = ll & 3;
@@ -759,10 +788,10 @@ __global__ __launch_bounds__(256) void k_fused_w4(
         }
     }
 
-    // Layer input for this wave's steps.
-    const float r[2][2] = {{rli[er], rli[8 + er]}, {rli[16 + er], rli[24 + er]}};
-    out.emit([&](int i, int q, int k) { return li_lds[i][lw][q][k][ll]; },
-             [&](int rr, int q, int k) { return li_keep[rr][q][k]; }, r);
+    // Layer input of the wave's tokens.
+    const float r[2][2] = {{rl[0], rl[1]}, {rl[2], rl[3]}};
+    out.emit([&](int i, int q, int k) { return li_lds[i][lw][2 * q + k][ll]; },
+             [&](int rr, int q, int k) { return li_keep[rr][2 * q + k]; }, r);
 }
 
 template <int S>
@@ -1016,7 +1045,7 @@ __global__ __launch_bounds__(256) void k_fused_pre_w4(
     const int n = lane & 15;
     const int g = lane >> 4;
     const int t0 = tile * kTileW4;
-    // Row layout as in k_fused_w4: lane L loads row 8i + L/8 of token group q
+    // Row layout as in k_fused: lane L loads row 8i + L/8 of token group q
     // (tokens past the last one clamped to it), 8 rows x 128 bytes per load;
     // ds_bpermute moves the data into the matrix-core layout, where the sums
     // and the collapse run on the same values in the same order as before, and

@@ -75,6 +75,7 @@ def cases():
         ("boundary fused 32-token tiles (k_fused_w4)", 8192 + 7, 1024, boundary("fused")),
         ("boundary fused 32-token tiles, rotated sweeps (k_fused_w4)", 8192 + 7, 2048, boundary("fused")),
         ("boundary fused 16-token tiles, rotated sweeps (k_fused)", 700, 2048, boundary("fused")),
+        ("boundary auto 19-token tiles, rotated sweeps (k_fused_w4)", 4096 + 600, 2048, boundary("auto")),
         ("boundary stream (k_stream)", 200, 2048, boundary("stream")),
         ("pre split (k_partial, k_pre_finish)", 50, 4096, pre("split")),
         ("pre split, four groups (k_partial_pre_wide)", 2400, 7168, pre("split")),

@@ -235,11 +235,10 @@ def test_split_token_groups_ragged(oracle, kind, T, d):
 @pytest.mark.parametrize("T,d", [(7168 + 7, 7168), (5120 + 3, 7168), (14336 + 5, 7168),
                                  (9216 + 3, 7168), (9216 + 3, 4096), (4096 + 600, 2048)])
 def test_auto_balanced_tiles(oracle, T, d):
-    """From hidden 6144 AUTO takes 4-wave tiles of ceil(T / (rounds x units))
-    tokens where they are large enough (29 and 21 tokens in one round on 256
-    units, 29 over two rounds at 14341); otherwise, and at smaller widths, it
-    takes 16-token tiles over as many rounds as they need (9219 tokens: three
-    rounds).  Every token is checked."""
+    """AUTO takes 4-wave tiles of ceil(T / (rounds x units)) tokens where they
+    are large enough (29, 21 and 19 tokens in one round on 256 units, 29 over
+    two rounds at 14341); otherwise it takes 16-token tiles over as many rounds
+    as they need (9219 tokens: three rounds).  Every token is checked."""
     import torch
     units = torch.cuda.get_device_properties(0).multi_processor_count
     rounds = -(-(-(-T // 32)) // units)
@@ -261,8 +260,10 @@ def test_auto_choices_on_256_units():
                          (4608, 7168): f32, (8192, 7168): f32, (9216, 7168): f16,
                          (12288, 7168): f16, (14336, 7168): f32, (16384, 7168): f32,
                          (6144, 6144): f32, (9216, 6144): f16, (2048, 4096): split,
-                         (2560, 4096): f16, (8192, 4096): f16, (16384, 4096): f16,
-                         (8192, 5120): f16, (32, 7168): split, (256, 7168): split}.items():
+                         (2560, 4096): f16, (4096, 4096): f16, (4608, 4096): f32,
+                         (8192, 4096): f32, (9216, 4096): f16, (12288, 4096): f16,
+                         (16384, 4096): f32, (8192, 5120): f32, (8192, 1024): f32,
+                         (4096, 1024): f16, (32, 7168): split, (256, 7168): split}.items():
         assert api.boundary_kernels(T, d) == want, (T, d)
 
 
