@@ -177,7 +177,7 @@ SplitPlan split_plan(int T, int hidden, bool invariant, bool shifted) {
         // filling every resident slot.
         plan.groups = spw >= (shifted ? kTwoGroupStepsShifted : kTwoGroupStepsPre) ? 2 : 1;
         if (!shifted && spw >= kFourGroupStepsPre) plan.groups = 4;
-        const long resident = shifted ? partial_resident_workgroups(shifted, plan.groups)
+        const long resident = shifted ? partial_resident_workgroups(plan.groups)
                                       : device_compute_units();
         if (resident > 0) {
             const long group_tiles = ceil_div(T, kTile * plan.groups);

@@ -2,13 +2,18 @@
 //
 // Split schedule (any token count):
 //   k_partial   one workgroup = 4 waves on a tile of one, two or four 16-token
-//               groups and a contiguous run of hidden steps (the groups share
-//               each weight-fragment load; how many is the split plan's
-//               choice).  Each wave streams its steps: 16-byte
-//               loads of X and x, residual update, lagged collapse, stores of
-//               X' and li, sums of squares, and the projection on the matrix
-//               cores.  The 4 waves' partials are combined in LDS in a fixed
-//               order and written as one record per (token, slice).
+//               groups and 4 adjacent 32-element steps of hidden, one per wave
+//               (the groups share each weight-fragment load; how many is the
+//               split plan's choice): 16-byte loads of X and x, residual
+//               update, lagged collapse, stores of X' and li, sums of squares,
+//               and the projection on the matrix cores.  The 4 waves' partials
+//               are combined in LDS in a fixed order and written as one record
+//               per (token, slice).  Plans of one step per wave: decode sizes
+//               and INVARIANT.
+//   k_partial_rows  the same records for plans of more steps per wave, with
+//               the tile's rows split over the waves for the loads and stores
+//               (4 rows x 256 bytes per instruction) and X' handed to the
+//               matrix cores through LDS.
 //   k_partial_pre_wide  the non-shifted pre's four-group form with 64-element
 //               wave steps (both 64-byte halves of each 128-byte line per
 //               lane), for plans with an even number of 32-element steps.
@@ -63,17 +68,18 @@ __global__ __launch_bounds__(256) void k_prepare_weight(const float* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// Split schedule, kernel 1: partial sums over a run of hidden steps.  A wave
-// carries G groups of 16 tokens (tokens n, n + 16, ... of the workgroup's
-// tile in lane n) through every step and feeds all of them from one set of
-// weight fragments.  Each token's sums have the same order for any G.  ONE:
-// the plan gives every wave one step (decode, INVARIANT), so the next step's
-// buffers are not needed: 140 registers instead of 192 with one group, 224
-// instead of 303 with two (two workgroups per CU instead of one).
+// Split schedule, kernel 1 for plans of one step per wave (decode sizes,
+// INVARIANT at every size): partial sums over one 32-element step of each
+// wave, 4 adjacent steps per workgroup (k_partial_rows takes plans of more).
+// A wave carries G groups of 16 tokens (tokens n, n + 16, ... of the
+// workgroup's tile in lane n) through its step and feeds all of them from one
+// set of weight fragments.  Each token's sums have the same order for any G.
+// With one step no next-step buffers are needed: 140 registers with one group,
+// 224 with two (two workgroups per CU).
 // ---------------------------------------------------------------------------
-template <bool SHIFTED, int G, bool NT, bool ONE>
+template <bool SHIFTED, int G, bool NT>
 __global__ __launch_bounds__(256) void k_partial(
-    int T, int hidden, int steps_per_wave, int slices, const uint16_t* __restrict__ x,
+    int T, int hidden, int slices, const uint16_t* __restrict__ x,
     const uint16_t* __restrict__ X, const float* __restrict__ post_prev,
     const float* __restrict__ comb_prev, const float* __restrict__ pre_lag,
     const uint4* __restrict__ wprep, uint16_t* __restrict__ xn_out,
@@ -104,12 +110,11 @@ __global__ __launch_bounds__(256) void k_partial(
         xrow[q] = SHIFTED ? x + tc[q] * hidden : nullptr;
     }
 
-    // The slice covers steps [slice*4*spw, (slice+1)*4*spw); its 4 waves take
-    // them interleaved (wave w: first + w, first + 4 + w, ...) so the waves read
-    // adjacent pieces of each row at the same time.
+    // The slice covers steps [4 slice, 4 slice + 4); wave w takes step
+    // 4 slice + w, so the waves read adjacent pieces of each row.
     const int nsteps = hidden / kStep;
-    const int first = slice * 4 * steps_per_wave;
-    const int last = min(first + 4 * steps_per_wave, nsteps);
+    const int first = slice * 4;
+    const int last = min(first + 4, nsteps);
 
     f32x4_t acc[G][3];
     float ssq[G], ssq_li[G];
@@ -121,9 +126,6 @@ __global__ __launch_bounds__(256) void k_partial(
         ssq_li[q] = 0.0f;
     }
 
-    // Step k's weight fragments are requested first, then step k+1's
-    // activations (prefetch), so the projection never waits on HBM: loads
-    // complete in issue order.
     auto load_x = [&](uint4 (&Xv)[4], uint4& xv, int q, int step) {
         const int h = step * kStep + g * 8;
 #pragma unroll
@@ -131,24 +133,16 @@ __global__ __launch_bounds__(256) void k_partial(
         xv = make_uint4(0, 0, 0, 0);
         if (SHIFTED) xv = ld16<NT>(xrow[q] + h);
     };
-    uint4 Xv[G][4], xv[G];
-    if (first + wave < last) {
+    const int step = first + wave;
+    if (step < last) {
+        uint4 Xv[G][4], xv[G];
 #pragma unroll
-        for (int q = 0; q < G; ++q) load_x(Xv[q], xv[q], q, first + wave);
-    }
-    for (int step = first + wave; step < last; step += ONE ? last : 4) {
+        for (int q = 0; q < G; ++q) load_x(Xv[q], xv[q], q, step);
         const int h = step * kStep + g * 8;
         uint4 A[kFragsPerStep];
         const uint4* wp = wprep + (size_t)step * kFragsPerStep * 64 + lane;
 #pragma unroll
         for (int i = 0; i < kFragsPerStep; ++i) A[i] = wp[i * 64];
-        __builtin_amdgcn_sched_barrier(0);
-        uint4 Xnx[G][4], xnx[G];
-        if (!ONE && step + 4 < last) {
-#pragma unroll
-            for (int q = 0; q < G; ++q) load_x(Xnx[q], xnx[q], q, step + 4);
-        }
-        __builtin_amdgcn_sched_barrier(0);
 
 #pragma unroll
         for (int q = 0; q < G; ++q) {
@@ -167,12 +161,6 @@ __global__ __launch_bounds__(256) void k_partial(
                 square_sum(Xv[q], ssq[q]);
             }
             mfma_step(A, Xn, acc[q]);
-        }
-#pragma unroll
-        for (int q = 0; q < G; ++q) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) Xv[q][j] = Xnx[q][j];
-            xv[q] = xnx[q];
         }
     }
 
@@ -197,6 +185,168 @@ __global__ __launch_bounds__(256) void k_partial(
             for (int w = 0; w < 4; ++w)
                 for (int q = 0; q < 4; ++q) sum += sq[w][q][tn][v - 24];
         }
+        const int tt = tile * kTok + tn;
+        if (tt < T) part[((size_t)tt * slices + slice) * kPart + v] = sum;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Split schedule, kernel 1 for plans of two or more steps per wave: the
+// records of k_partial (SHIFTED: the boundary; otherwise the non-shifted pre,
+// which only reads X), with the tile's rows split over the waves for the
+// memory side.  A workgroup step covers the 4 k-blocks (128
+// hidden elements) that the 4 waves of k_partial take side by side: wave w
+// loads, updates, stores and collapses tokens 16r + 4w .. 16r + 4w + 3 of the
+// tile (r < G), lane L on token 16r + 4w + L/16 and 16-byte chunk L%16 of the
+// step's 256-byte run, so each load and store instruction covers 4 rows x 256
+// bytes (a plain mover: 5.37 TB/s, against 4.60 for the 16 rows x 64 bytes
+// of the matrix-core layout).  X' goes to a double-buffered LDS stage
+// ([group][token][stream][chunk], chunks XOR-swizzled by the token: no bank
+// conflicts either way), from which wave w reads k-block w of the step for
+// the projection after one barrier; the buffer a step writes was last read
+// before the previous step's barrier.  The projection sees the operands,
+// fragments and order of k_partial, so the mixes of every record are
+// bit-identical to it; a token's sums of squares belong to one wave (a
+// butterfly over its 16 lanes) and add in another order.
+// ---------------------------------------------------------------------------
+template <bool SHIFTED, int G, bool NT>
+__global__ __launch_bounds__(256) void k_partial_rows(
+    int T, int hidden, int steps_per_wave, int slices, const uint16_t* __restrict__ x,
+    const uint16_t* __restrict__ X, const float* __restrict__ post_prev,
+    const float* __restrict__ comb_prev, const float* __restrict__ pre_lag,
+    const uint4* __restrict__ wprep, uint16_t* __restrict__ xn_out,
+    uint16_t* __restrict__ li_out, float* __restrict__ part) {
+    MHC_POISON_LDS(0);
+    constexpr int kTok = kTile * G;  // tokens of the workgroup
+    __shared__ uint4 stage[2][G][16 * 4 * 16];
+    __shared__ float red[4][kTok][24];
+    __shared__ float sqo[kTok][2];
+
+    const int tile = blockIdx.x / slices;  // (tile-major grid)
+    const int slice = blockIdx.x - tile * slices;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 15;
+    const int g = lane >> 4;
+    const int ch = lane & 15;                 // the lane's chunk of the step's run
+    const int t4 = 4 * wave + (lane >> 4);   // the lane's token within each group
+    // A lane past the last token works on token T-1 and stores nothing.
+    bool own[G];
+    size_t tok[G];
+    PrevCoef c[G];
+#pragma unroll
+    for (int r = 0; r < G; ++r) {
+        const int t = tile * kTok + 16 * r + t4;
+        own[r] = t < T;
+        tok[r] = own[r] ? (size_t)t : (size_t)(T - 1);
+        if (SHIFTED) load_prev(c[r], post_prev, comb_prev, pre_lag, tok[r]);
+    }
+
+    // The slice covers k-blocks [first, last), a whole number of workgroup
+    // steps (hidden is a multiple of 256).
+    const int nsteps = hidden / kStep;
+    const int first = slice * 4 * steps_per_wave;
+    const int last = min(first + 4 * steps_per_wave, nsteps);
+    const int wsteps = (last - first) / 4;
+
+    f32x4_t acc[G][3];
+    float ssq[G], ssq_li[G];
+#pragma unroll
+    for (int q = 0; q < G; ++q) {
+#pragma unroll
+        for (int m = 0; m < 3; ++m) acc[q][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        ssq[q] = 0.0f;
+        ssq_li[q] = 0.0f;
+    }
+
+    // Step j's weight fragments are requested first, then step j+1's
+    // activations, as in k_partial.
+    auto load_step = [&](uint4 (&Xv)[G][4], uint4 (&xv)[G], int j) {
+        const int h = (first + 4 * j) * kStep + 8 * ch;
+#pragma unroll
+        for (int r = 0; r < G; ++r) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) Xv[r][s] = ld16<NT>(X + (tok[r] * 4 + s) * hidden + h);
+            xv[r] = make_uint4(0, 0, 0, 0);
+            if (SHIFTED) xv[r] = ld16<NT>(x + tok[r] * hidden + h);
+        }
+    };
+    uint4 Xv[G][4], xv[G];
+    load_step(Xv, xv, 0);
+    for (int j = 0; j < wsteps; ++j) {
+        uint4 A[kFragsPerStep];
+        const uint4* wp = wprep + (size_t)(first + 4 * j + wave) * kFragsPerStep * 64 + lane;
+#pragma unroll
+        for (int i = 0; i < kFragsPerStep; ++i) A[i] = wp[i * 64];
+        __builtin_amdgcn_sched_barrier(0);
+        uint4 Xnx[G][4], xnx[G];
+        if (j + 1 < wsteps) load_step(Xnx, xnx, j + 1);
+        __builtin_amdgcn_sched_barrier(0);
+
+        const int h = (first + 4 * j) * kStep + 8 * ch;
+        uint4* st = &stage[j & 1][0][0];
+#pragma unroll
+        for (int r = 0; r < G; ++r) {
+            uint4 Xn[4];
+            if (SHIFTED) {
+                uint4 li;
+                update_collapse(Xv[r], xv[r], c[r], Xn, li, ssq[r], ssq_li[r]);
+                if (own[r]) {
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) st16<NT>(xn_out + (tok[r] * 4 + s) * hidden + h, Xn[s]);
+                    *reinterpret_cast<uint4*>(li_out + tok[r] * hidden + h) = li;
+                }
+            } else {
+#pragma unroll
+                for (int s = 0; s < 4; ++s) Xn[s] = Xv[r][s];
+                square_sum(Xv[r], ssq[r]);
+            }
+#pragma unroll
+            for (int s = 0; s < 4; ++s) st[r * 1024 + (t4 * 4 + s) * 16 + (ch ^ t4)] = Xn[s];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < G; ++q) {
+            uint4 B[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) B[s] = st[q * 1024 + (n * 4 + s) * 16 + ((4 * wave + g) ^ n)];
+            mfma_step(A, B, acc[q]);
+        }
+#pragma unroll
+        for (int r = 0; r < G; ++r) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) Xv[r][s] = Xnx[r][s];
+            xv[r] = xnx[r];
+        }
+    }
+
+    // Mixes: the 4 waves in a fixed order, as in k_partial.  Sums of squares:
+    // the owning wave's 16 lanes of each token (every lane ends with the same
+    // bits).
+#pragma unroll
+    for (int q = 0; q < G; ++q)
+#pragma unroll
+        for (int m = 0; m < 3; ++m)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) red[wave][16 * q + n][8 * m + 2 * g + j] = mix_of(acc[q], m, j);
+#pragma unroll
+    for (int r = 0; r < G; ++r) {
+        float a = ssq[r], b = ssq_li[r];
+#pragma unroll
+        for (int o = 8; o >= 1; o >>= 1) {
+            a += __shfl_xor(a, o);
+            b += __shfl_xor(b, o);
+        }
+        if (ch == 0) {
+            sqo[16 * r + t4][0] = a;
+            sqo[16 * r + t4][1] = b;
+        }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < kTok * 26; i += blockDim.x) {
+        const int tn = i / 26, v = i % 26;
+        const float sum = v < 24 ? ((red[0][tn][v] + red[1][tn][v]) + red[2][tn][v]) + red[3][tn][v]
+                                 : sqo[tn][v - 24];
         const int tt = tile * kTok + tn;
         if (tt < T) part[((size_t)tt * slices + slice) * kPart + v] = sum;
     }
@@ -845,32 +995,37 @@ static void launch_partial_g(bool shifted, const SplitPlan& plan, int T, int hid
                              uint16_t* xn_out, uint16_t* li_out, float* part, hipStream_t stream) {
     const dim3 grid((unsigned)((T + kTile * G - 1) / (kTile * G)) * (unsigned)plan.slices);
     if (shifted) {
-        if constexpr (G <= 2) {  // (four groups would spill in the shifted kernel)
+        if constexpr (G <= 2) {  // (four groups would spill in the shifted kernels)
             if (plan.steps_per_wave == 1)
-                hipLaunchKernelGGL((k_partial<true, G, NT, true>), grid, dim3(256), 0, stream, T, hidden,
-                                   plan.steps_per_wave, plan.slices, x, X, post_prev, comb_prev,
-                                   pre_lag, w, xn_out, li_out, part);
+                hipLaunchKernelGGL((k_partial<true, G, NT>), grid, dim3(256), 0, stream, T, hidden,
+                                   plan.slices, x, X, post_prev, comb_prev, pre_lag, w, xn_out,
+                                   li_out, part);
             else
-                hipLaunchKernelGGL((k_partial<true, G, NT, false>), grid, dim3(256), 0, stream, T, hidden,
+                hipLaunchKernelGGL((k_partial_rows<true, G, NT>), grid, dim3(256), 0, stream, T, hidden,
                                    plan.steps_per_wave, plan.slices, x, X, post_prev, comb_prev,
                                    pre_lag, w, xn_out, li_out, part);
         }
     } else {
-        if constexpr (G == 4) {
+        // Four groups keep the 64-element-step kernel (T=8192: 185.7 us against
+        // 188.4 for the row-split kernel; T=4096 104.3 against 101.5); one or
+        // two groups over several steps take the row-split kernel (T=2048
+        // 60.1 -> 56.7, T=1024 34.7 -> 33.7, T=256 16.2 -> 15.8 us, cold).
+        if (plan.steps_per_wave == 1) {
+            hipLaunchKernelGGL((k_partial<false, G, NT>), grid, dim3(256), 0, stream, T, hidden,
+                               plan.slices, nullptr, X, nullptr, nullptr, nullptr, w, nullptr,
+                               nullptr, part);
+            return;
+        }
+        if constexpr (G == 4) {  // (the plan gives four groups an even number of steps)
             if (plan.steps_per_wave % 2 == 0) {
                 hipLaunchKernelGGL((k_partial_pre_wide<G, NT>), grid, dim3(256), 0, stream, T,
                                    hidden, plan.steps_per_wave, plan.slices, X, w, part);
                 return;
             }
         }
-        if (plan.steps_per_wave == 1)
-            hipLaunchKernelGGL((k_partial<false, G, NT, true>), grid, dim3(256), 0, stream, T, hidden,
-                               plan.steps_per_wave, plan.slices, nullptr, X, nullptr, nullptr,
-                               nullptr, w, nullptr, nullptr, part);
-        else
-            hipLaunchKernelGGL((k_partial<false, G, NT, false>), grid, dim3(256), 0, stream, T, hidden,
-                               plan.steps_per_wave, plan.slices, nullptr, X, nullptr, nullptr,
-                               nullptr, w, nullptr, nullptr, part);
+        hipLaunchKernelGGL((k_partial_rows<false, G, NT>), grid, dim3(256), 0, stream, T, hidden,
+                           plan.steps_per_wave, plan.slices, nullptr, X, nullptr, nullptr, nullptr,
+                           w, nullptr, nullptr, part);
     }
 }
 
@@ -933,22 +1088,18 @@ int device_compute_units() {
     return v > 0 ? v : 0;
 }
 
-int partial_resident_workgroups(bool shifted, int groups) {
-    static std::atomic<int> cache[kMaxDevices][2][2];  // 0: not asked yet; -1: unknown
+int partial_resident_workgroups(int groups) {
+    static std::atomic<int> cache[kMaxDevices][2];  // 0: not asked yet; -1: unknown
     const int dev = current_device();
     if (dev < 0) return 0;
-    std::atomic<int>& slot = cache[dev][shifted ? 1 : 0][groups == 2 ? 1 : 0];
+    std::atomic<int>& slot = cache[dev][groups == 2 ? 1 : 0];
     int v = slot.load(std::memory_order_relaxed);
     if (v == 0) {
         const int units = query_compute_units(dev);
         int per_unit = 0;
         hipError_t e;
-        if (shifted)
-            e = groups == 2 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_unit, k_partial<true, 2, false, false>, 256, 0)
-                            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_unit, k_partial<true, 1, false, false>, 256, 0);
-        else
-            e = groups == 2 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_unit, k_partial<false, 2, false, false>, 256, 0)
-                            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_unit, k_partial<false, 1, false, false>, 256, 0);
+        e = groups == 2 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_unit, k_partial_rows<true, 2, false>, 256, 0)
+                        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_unit, k_partial_rows<true, 1, false>, 256, 0);
         v = (e == hipSuccess && units > 0 && per_unit > 0) ? units * per_unit : -1;
         slot.store(v, std::memory_order_relaxed);
     }

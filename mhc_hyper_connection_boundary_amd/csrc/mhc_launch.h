@@ -31,10 +31,10 @@ struct SplitPlan {
 
 SplitPlan split_plan(int T, int hidden, bool invariant, bool shifted);
 
-// Workgroups of the partial kernel (shifted or not, 1 or 2 token groups) the
-// current device holds at once: compute units times resident workgroups per
-// unit.  0 if the runtime cannot say.
-int partial_resident_workgroups(bool shifted, int groups);
+// Workgroups of the boundary's multi-step partial kernel (1 or 2 token groups)
+// the current device holds at once: compute units times resident workgroups
+// per unit.  0 if the runtime cannot say.
+int partial_resident_workgroups(int groups);
 
 // Compute units of the current device; 0 if the runtime cannot say.
 int device_compute_units();
