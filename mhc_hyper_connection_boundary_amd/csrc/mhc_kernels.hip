@@ -2,18 +2,14 @@
 //
 // Split schedule (any token count):
 //   k_partial   one workgroup = 4 waves on a tile of one, two or four 16-token
-//               groups and 4 adjacent 32-element steps of hidden, one per wave
-//               (the groups share each weight-fragment load; how many is the
-//               split plan's choice): 16-byte loads of X and x, residual
-//               update, lagged collapse, stores of X' and li, sums of squares,
-//               and the projection on the matrix cores.  The 4 waves' partials
-//               are combined in LDS in a fixed order and written as one record
-//               per (token, slice).  Plans of one step per wave: decode sizes
-//               and INVARIANT.
-//   k_partial_rows  the same records for plans of more steps per wave, with
-//               the tile's rows split over the waves for the loads and stores
-//               (4 rows x 256 bytes per instruction) and X' handed to the
-//               matrix cores through LDS.
+//               groups and a slice of hidden, in steps of 128 elements of every
+//               row: the rows are split over the waves for the 16-byte loads
+//               of X and x, the residual update, the lagged collapse and the
+//               stores of X' and li (4 rows x 256 bytes per instruction); X'
+//               reaches the matrix cores through LDS, where each wave projects
+//               one 32-element k-block of the step for every group from one
+//               set of weight fragments.  The waves' partials are combined in
+//               a fixed order and written as one record per (token, slice).
 //   k_partial_pre_wide  the non-shifted pre's four-group form with 64-element
 //               wave steps (both 64-byte halves of each 128-byte line per
 //               lane), for plans with an even number of 32-element steps.
@@ -68,149 +64,33 @@ __global__ __launch_bounds__(256) void k_prepare_weight(const float* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// Split schedule, kernel 1 for plans of one step per wave (decode sizes,
-// INVARIANT at every size): partial sums over one 32-element step of each
-// wave, 4 adjacent steps per workgroup (k_partial_rows takes plans of more).
-// A wave carries G groups of 16 tokens (tokens n, n + 16, ... of the
-// workgroup's tile in lane n) through its step and feeds all of them from one
-// set of weight fragments.  Each token's sums have the same order for any G.
-// With one step no next-step buffers are needed: 140 registers with one group,
-// 224 with two (two workgroups per CU).
+// Split schedule, kernel 1: partial sums of a tile of 16G tokens over a slice
+// of hidden (SHIFTED: the boundary; otherwise the non-shifted pre, which only
+// reads X), one record per (token, slice).  A workgroup step covers 4
+// k-blocks (128 hidden elements) of every row of the tile; the slice holds
+// steps_per_wave of them (ONE: exactly one, so no next-step buffers: the
+// plans of decode sizes and of INVARIANT, at 136 registers with one group and
+// 216 with two instead of 196 and 306).  Wave w loads, updates, stores and
+// collapses tokens 16r + 4w .. 16r + 4w + 3 of the tile (r < G), lane L on
+// token 16r + 4w + L/16 and 16-byte chunk L%16 of the step's 256-byte run, so
+// each load and store instruction covers 4 rows x 256 bytes (a plain mover:
+// 5.37 TB/s, against 4.60 for the 16 rows x 64 bytes of the matrix-core
+// layout).  X' goes to a double-buffered LDS stage ([group][token][stream]
+// [chunk], chunks XOR-swizzled by the token: no bank conflicts either way),
+// from which wave w reads k-block w of the step for the projection after one
+// barrier; the buffer a step writes was last read before the previous step's
+// barrier.  Wave w projects k-blocks first + w, first + 4 + w, ... of its
+// slice for all G groups from one set of weight fragments per k-block.  A
+// token's sums of squares belong to one wave (a butterfly over its 16 lanes),
+// the same order for every G and every position in the tile, so INVARIANT's
+// bits do not depend on the batch.  Against the earlier form of this kernel,
+// which loaded in the matrix-core layout (16 rows x 64 bytes per instruction),
+// cold, d=7168, us: boundary T=32 10.95 -> 10.51, T=128 15.2 -> 14.3, T=512
+// 31.7 -> 28.5, T=1024 51.7 -> 44.7, T=2048 88.8 -> 79.3; INVARIANT T=1024
+// 61.1 -> 51.1, T=8192 419 -> 353; pre T=32 9.87 -> 9.62, T=2048 60.1 -> 56.7.
 // ---------------------------------------------------------------------------
-template <bool SHIFTED, int G, bool NT>
+template <bool SHIFTED, int G, bool NT, bool ONE>
 __global__ __launch_bounds__(256) void k_partial(
-    int T, int hidden, int slices, const uint16_t* __restrict__ x,
-    const uint16_t* __restrict__ X, const float* __restrict__ post_prev,
-    const float* __restrict__ comb_prev, const float* __restrict__ pre_lag,
-    const uint4* __restrict__ wprep, uint16_t* __restrict__ xn_out,
-    uint16_t* __restrict__ li_out, float* __restrict__ part) {
-    MHC_POISON_LDS(0);
-    constexpr int kTok = kTile * G;  // tokens of the workgroup
-    __shared__ float red[4][kTok][24];
-    __shared__ float sq[4][4][kTok][2];
-
-    const int tile = blockIdx.x / slices;  // (tile-major grid)
-    const int slice = blockIdx.x - tile * slices;
-    const int wave = threadIdx.x >> 6;
-    const int lane = threadIdx.x & 63;
-    const int n = lane & 15;
-    const int g = lane >> 4;
-    bool valid[G];
-    size_t tc[G];
-    PrevCoef c[G];
-    const uint16_t* Xrow[G];
-    const uint16_t* xrow[G];
-#pragma unroll
-    for (int q = 0; q < G; ++q) {
-        const int t = tile * kTok + 16 * q + n;
-        valid[q] = t < T;
-        tc[q] = valid[q] ? (size_t)t : (size_t)(T - 1);
-        if (SHIFTED) load_prev(c[q], post_prev, comb_prev, pre_lag, tc[q]);
-        Xrow[q] = X + tc[q] * 4 * hidden;
-        xrow[q] = SHIFTED ? x + tc[q] * hidden : nullptr;
-    }
-
-    // The slice covers steps [4 slice, 4 slice + 4); wave w takes step
-    // 4 slice + w, so the waves read adjacent pieces of each row.
-    const int nsteps = hidden / kStep;
-    const int first = slice * 4;
-    const int last = min(first + 4, nsteps);
-
-    f32x4_t acc[G][3];
-    float ssq[G], ssq_li[G];
-#pragma unroll
-    for (int q = 0; q < G; ++q) {
-#pragma unroll
-        for (int m = 0; m < 3; ++m) acc[q][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        ssq[q] = 0.0f;
-        ssq_li[q] = 0.0f;
-    }
-
-    auto load_x = [&](uint4 (&Xv)[4], uint4& xv, int q, int step) {
-        const int h = step * kStep + g * 8;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) Xv[j] = ld16<NT>(Xrow[q] + (size_t)j * hidden + h);
-        xv = make_uint4(0, 0, 0, 0);
-        if (SHIFTED) xv = ld16<NT>(xrow[q] + h);
-    };
-    const int step = first + wave;
-    if (step < last) {
-        uint4 Xv[G][4], xv[G];
-#pragma unroll
-        for (int q = 0; q < G; ++q) load_x(Xv[q], xv[q], q, step);
-        const int h = step * kStep + g * 8;
-        uint4 A[kFragsPerStep];
-        const uint4* wp = wprep + (size_t)step * kFragsPerStep * 64 + lane;
-#pragma unroll
-        for (int i = 0; i < kFragsPerStep; ++i) A[i] = wp[i * 64];
-
-#pragma unroll
-        for (int q = 0; q < G; ++q) {
-            uint4 Xn[4];
-            if (SHIFTED) {
-                uint4 li;
-                update_collapse(Xv[q], xv[q], c[q], Xn, li, ssq[q], ssq_li[q]);
-                if (valid[q]) {
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) st16<NT>(xn_out + (tc[q] * 4 + s) * hidden + h, Xn[s]);
-                    *reinterpret_cast<uint4*>(li_out + tc[q] * hidden + h) = li;
-                }
-            } else {
-#pragma unroll
-                for (int s = 0; s < 4; ++s) Xn[s] = Xv[q][s];
-                square_sum(Xv[q], ssq[q]);
-            }
-            mfma_step(A, Xn, acc[q]);
-        }
-    }
-
-    // Combine the 4 waves in a fixed order: waves ascending, lane groups ascending.
-#pragma unroll
-    for (int q = 0; q < G; ++q) {
-#pragma unroll
-        for (int m = 0; m < 3; ++m)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) red[wave][16 * q + n][8 * m + 2 * g + j] = mix_of(acc[q], m, j);
-        sq[wave][g][16 * q + n][0] = ssq[q];
-        sq[wave][g][16 * q + n][1] = ssq_li[q];
-    }
-    __syncthreads();
-    for (int i = threadIdx.x; i < kTok * 26; i += blockDim.x) {
-        const int tn = i / 26, v = i % 26;
-        float sum;
-        if (v < 24) {
-            sum = ((red[0][tn][v] + red[1][tn][v]) + red[2][tn][v]) + red[3][tn][v];
-        } else {
-            sum = 0.0f;
-            for (int w = 0; w < 4; ++w)
-                for (int q = 0; q < 4; ++q) sum += sq[w][q][tn][v - 24];
-        }
-        const int tt = tile * kTok + tn;
-        if (tt < T) part[((size_t)tt * slices + slice) * kPart + v] = sum;
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Split schedule, kernel 1 for plans of two or more steps per wave: the
-// records of k_partial (SHIFTED: the boundary; otherwise the non-shifted pre,
-// which only reads X), with the tile's rows split over the waves for the
-// memory side.  A workgroup step covers the 4 k-blocks (128
-// hidden elements) that the 4 waves of k_partial take side by side: wave w
-// loads, updates, stores and collapses tokens 16r + 4w .. 16r + 4w + 3 of the
-// tile (r < G), lane L on token 16r + 4w + L/16 and 16-byte chunk L%16 of the
-// step's 256-byte run, so each load and store instruction covers 4 rows x 256
-// bytes (a plain mover: 5.37 TB/s, against 4.60 for the 16 rows x 64 bytes
-// of the matrix-core layout).  X' goes to a double-buffered LDS stage
-// ([group][token][stream][chunk], chunks XOR-swizzled by the token: no bank
-// conflicts either way), from which wave w reads k-block w of the step for
-// the projection after one barrier; the buffer a step writes was last read
-// before the previous step's barrier.  The projection sees the operands,
-// fragments and order of k_partial, so the mixes of every record are
-// bit-identical to it; a token's sums of squares belong to one wave (a
-// butterfly over its 16 lanes) and add in another order.
-// ---------------------------------------------------------------------------
-template <bool SHIFTED, int G, bool NT>
-__global__ __launch_bounds__(256) void k_partial_rows(
     int T, int hidden, int steps_per_wave, int slices, const uint16_t* __restrict__ x,
     const uint16_t* __restrict__ X, const float* __restrict__ post_prev,
     const float* __restrict__ comb_prev, const float* __restrict__ pre_lag,
@@ -247,7 +127,7 @@ __global__ __launch_bounds__(256) void k_partial_rows(
     const int nsteps = hidden / kStep;
     const int first = slice * 4 * steps_per_wave;
     const int last = min(first + 4 * steps_per_wave, nsteps);
-    const int wsteps = (last - first) / 4;
+    const int wsteps = ONE ? 1 : (last - first) / 4;
 
     f32x4_t acc[G][3];
     float ssq[G], ssq_li[G];
@@ -260,7 +140,8 @@ __global__ __launch_bounds__(256) void k_partial_rows(
     }
 
     // Step j's weight fragments are requested first, then step j+1's
-    // activations, as in k_partial.
+    // activations: loads complete in issue order, so the projection never
+    // waits on HBM.
     auto load_step = [&](uint4 (&Xv)[G][4], uint4 (&xv)[G], int j) {
         const int h = (first + 4 * j) * kStep + 8 * ch;
 #pragma unroll
@@ -280,7 +161,7 @@ __global__ __launch_bounds__(256) void k_partial_rows(
         for (int i = 0; i < kFragsPerStep; ++i) A[i] = wp[i * 64];
         __builtin_amdgcn_sched_barrier(0);
         uint4 Xnx[G][4], xnx[G];
-        if (j + 1 < wsteps) load_step(Xnx, xnx, j + 1);
+        if (!ONE && j + 1 < wsteps) load_step(Xnx, xnx, j + 1);
         __builtin_amdgcn_sched_barrier(0);
 
         const int h = (first + 4 * j) * kStep + 8 * ch;
@@ -320,9 +201,8 @@ __global__ __launch_bounds__(256) void k_partial_rows(
         }
     }
 
-    // Mixes: the 4 waves in a fixed order, as in k_partial.  Sums of squares:
-    // the owning wave's 16 lanes of each token (every lane ends with the same
-    // bits).
+    // Mixes: the 4 waves in a fixed order.  Sums of squares: the owning
+    // wave's 16 lanes of each token (every lane ends with the same bits).
 #pragma unroll
     for (int q = 0; q < G; ++q)
 #pragma unroll
@@ -356,10 +236,9 @@ __global__ __launch_bounds__(256) void k_partial_rows(
 // k-blocks per step, every lane reading both 64-byte halves of each 128-byte
 // line it touches, as in the fused kernels.  Launched for four token groups
 // and an even number of 32-element steps per wave (the slice then holds
-// whole 64-element steps); the records are the same as k_partial's, the order
-// of each lane's sums within the slice differs.  (With two groups it would
-// need 306 registers, one workgroup per CU instead of two, and measured
-// slower.)
+// whole 64-element steps); its records hold the sums of k_partial's, in
+// another order within the slice.  (With two groups it would need 306
+// registers, one workgroup per CU instead of two, and measured slower.)
 template <int G, bool NT>
 __global__ __launch_bounds__(256) void k_partial_pre_wide(
     int T, int hidden, int steps_per_wave, int slices, const uint16_t* __restrict__ X,
@@ -994,39 +873,38 @@ static void launch_partial_g(bool shifted, const SplitPlan& plan, int T, int hid
                              const float* comb_prev, const float* pre_lag, const uint4* w,
                              uint16_t* xn_out, uint16_t* li_out, float* part, hipStream_t stream) {
     const dim3 grid((unsigned)((T + kTile * G - 1) / (kTile * G)) * (unsigned)plan.slices);
+    const bool one = plan.steps_per_wave == 1;
     if (shifted) {
-        if constexpr (G <= 2) {  // (four groups would spill in the shifted kernels)
-            if (plan.steps_per_wave == 1)
-                hipLaunchKernelGGL((k_partial<true, G, NT>), grid, dim3(256), 0, stream, T, hidden,
-                                   plan.slices, x, X, post_prev, comb_prev, pre_lag, w, xn_out,
-                                   li_out, part);
+        if constexpr (G <= 2) {  // (four groups would spill in the shifted kernel)
+            if (one)
+                hipLaunchKernelGGL((k_partial<true, G, NT, true>), grid, dim3(256), 0, stream, T,
+                                   hidden, plan.steps_per_wave, plan.slices, x, X, post_prev,
+                                   comb_prev, pre_lag, w, xn_out, li_out, part);
             else
-                hipLaunchKernelGGL((k_partial_rows<true, G, NT>), grid, dim3(256), 0, stream, T, hidden,
-                                   plan.steps_per_wave, plan.slices, x, X, post_prev, comb_prev,
-                                   pre_lag, w, xn_out, li_out, part);
+                hipLaunchKernelGGL((k_partial<true, G, NT, false>), grid, dim3(256), 0, stream, T,
+                                   hidden, plan.steps_per_wave, plan.slices, x, X, post_prev,
+                                   comb_prev, pre_lag, w, xn_out, li_out, part);
         }
-    } else {
-        // Four groups keep the 64-element-step kernel (T=8192: 185.7 us against
-        // 188.4 for the row-split kernel; T=4096 104.3 against 101.5); one or
-        // two groups over several steps take the row-split kernel (T=2048
-        // 60.1 -> 56.7, T=1024 34.7 -> 33.7, T=256 16.2 -> 15.8 us, cold).
-        if (plan.steps_per_wave == 1) {
-            hipLaunchKernelGGL((k_partial<false, G, NT>), grid, dim3(256), 0, stream, T, hidden,
-                               plan.slices, nullptr, X, nullptr, nullptr, nullptr, w, nullptr,
-                               nullptr, part);
-            return;
-        }
-        if constexpr (G == 4) {  // (the plan gives four groups an even number of steps)
-            if (plan.steps_per_wave % 2 == 0) {
-                hipLaunchKernelGGL((k_partial_pre_wide<G, NT>), grid, dim3(256), 0, stream, T,
-                                   hidden, plan.steps_per_wave, plan.slices, X, w, part);
-                return;
-            }
-        }
-        hipLaunchKernelGGL((k_partial_rows<false, G, NT>), grid, dim3(256), 0, stream, T, hidden,
+        return;
+    }
+    if (one) {
+        hipLaunchKernelGGL((k_partial<false, G, NT, true>), grid, dim3(256), 0, stream, T, hidden,
                            plan.steps_per_wave, plan.slices, nullptr, X, nullptr, nullptr, nullptr,
                            w, nullptr, nullptr, part);
+        return;
     }
+    // Four groups over several steps keep the 64-element-step kernel (T=8192:
+    // 185.7 us against 188.4 with k_partial; T=4096 104.3 against 101.5).
+    if constexpr (G == 4) {  // (the plan gives four groups an even number of steps)
+        if (plan.steps_per_wave % 2 == 0) {
+            hipLaunchKernelGGL((k_partial_pre_wide<G, NT>), grid, dim3(256), 0, stream, T, hidden,
+                               plan.steps_per_wave, plan.slices, X, w, part);
+            return;
+        }
+    }
+    hipLaunchKernelGGL((k_partial<false, G, NT, false>), grid, dim3(256), 0, stream, T, hidden,
+                       plan.steps_per_wave, plan.slices, nullptr, X, nullptr, nullptr, nullptr, w,
+                       nullptr, nullptr, part);
 }
 
 template <int G>
@@ -1098,8 +976,8 @@ int partial_resident_workgroups(int groups) {
         const int units = query_compute_units(dev);
         int per_unit = 0;
         hipError_t e;
-        e = groups == 2 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_unit, k_partial_rows<true, 2, false>, 256, 0)
-                        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_unit, k_partial_rows<true, 1, false>, 256, 0);
+        e = groups == 2 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_unit, k_partial<true, 2, false, false>, 256, 0)
+                        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_unit, k_partial<true, 1, false, false>, 256, 0);
         v = (e == hipSuccess && units > 0 && per_unit > 0) ? units * per_unit : -1;
         slot.store(v, std::memory_order_relaxed);
     }

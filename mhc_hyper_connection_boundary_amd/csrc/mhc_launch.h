@@ -17,7 +17,8 @@ struct Scalars;
 // bytes).
 //   k_partial: slice q of a tile covers hidden steps
 //              [4q * steps_per_wave, 4(q + 1) * steps_per_wave) of 32 elements,
-//              interleaved over its 4 waves.
+//              4 at a time; wave w projects steps 4q * steps_per_wave + w,
+//              + 4, ...
 //   k_finish:  workgroup q of a 16-token tile rescales hidden
 //              [q * finish_width, (q + 1) * finish_width).
 struct SplitPlan {

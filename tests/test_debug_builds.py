@@ -70,6 +70,7 @@ def cases():
 
     return [
         ("boundary split (k_partial, k_finish)", 37, 1024, boundary("split")),
+        ("boundary split, several steps per wave (k_partial, k_finish)", 2000, 7168, boundary("split")),
         ("boundary invariant", 33, 2048, boundary("invariant")),
         ("boundary fused 16-token tiles (k_fused)", 300, 1024, boundary("fused")),
         ("boundary fused 32-token tiles (k_fused_w4)", 8192 + 7, 1024, boundary("fused")),
@@ -78,6 +79,7 @@ def cases():
         ("boundary auto 19-token tiles, rotated sweeps (k_fused_w4)", 4096 + 600, 2048, boundary("auto")),
         ("boundary stream (k_stream)", 200, 2048, boundary("stream")),
         ("pre split (k_partial, k_pre_finish)", 50, 4096, pre("split")),
+        ("pre split, several steps per wave (k_partial, k_pre_finish)", 1000, 4096, pre("split")),
         ("pre split, four groups (k_partial_pre_wide)", 2400, 7168, pre("split")),
         ("pre fused 16-token tiles (k_fused_pre)", 100, 1024, pre("fused")),
         ("pre fused 32-token tiles (k_fused_pre_w4)", 8192 + 3, 1024, pre("fused")),
