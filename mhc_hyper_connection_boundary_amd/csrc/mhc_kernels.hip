@@ -769,31 +769,38 @@ __global__ __launch_bounds__(256) void k_post(int hidden, int chunks, const uint
     for (int s = 0; s < 4; ++s) *reinterpret_cast<uint4*>(xn_out + (t * 4 + s) * hidden + h) = Xn[s];
 }
 
-// Residual update alone, in the fastest pattern the movers measured: item =
-// (tile of 32 tokens, slice of 256 hidden elements), tile-major; wave w takes
-// tokens 8w..8w+7; instruction (p, j) covers stream j (4 = the block output)
-// of tokens 8w + 2p (lanes 0-31) and 8w + 2p + 1 (lanes 32-63), 2 rows x 512
-// contiguous bytes.  All 20 loads of a lane are issued before any arithmetic.
-// Tokens past T read the last token's rows and store nothing.  Taken from 128
-// MiB of X, with the nontemporal hint on every load and store (cold, us, the
-// kernel above -> this one: d=7168 T=8192 198 -> 192, d=4096 T=16384 212 ->
-// 197; plain loads and stores 202 at T=8192; at T=1000 it was slower, 25 -> 30).
-template <bool NT>
+// Residual update alone, in the movers' fastest patterns: item = (tile of
+// tokens, slice of RUN hidden elements), tile-major, 16 tokens per item for
+// RUN = 512 and 32 for RUN = 256.  Wave w takes 4 tokens
+// (RUN = 512: tokens 4w..4w+3, each instruction 1 row x 1024 contiguous
+// bytes) or 8 (RUN = 256: tokens 8w..8w+7, instruction p covering tokens
+// 8w + 2p and 8w + 2p + 1, 2 rows x 512 bytes); stream j = 4 is the block
+// output.  All 20 loads of a lane are issued before any arithmetic.  Tokens
+// past T read the last token's rows and store nothing.  Taken from 128 MiB of
+// X, with the nontemporal hint on every load and store (cold, us, the kernel
+// above -> RUN = 256: d=7168 T=8192 198 -> 192, d=4096 T=16384 212 -> 197;
+// plain loads and stores 202 at T=8192; at T=1000 it was slower, 25 -> 30).
+// RUN = 512 where hidden is a multiple of 512 but not of 2048 (d=7168 T=8192
+// 192.4 -> 182.1, T=4096 99.1 -> 95.6); where the token stride is a multiple
+// of 16 KiB it measured slower (d=4096 T=16384 197 -> 204).
+template <bool NT, int RUN>
 __global__ __launch_bounds__(256) void k_post_rows(int T, int hidden, const uint16_t* __restrict__ x,
                                                    const uint16_t* __restrict__ X,
                                                    const float* __restrict__ post_prev,
                                                    const float* __restrict__ comb_prev,
                                                    uint16_t* __restrict__ xn_out) {
-    const int slices = hidden >> 8;
+    static_assert(RUN == 256 || RUN == 512, "runs of 256 or 512 elements");
+    constexpr int kTok = RUN == 512 ? 16 : 32;  // tokens of an item
+    const int slices = hidden / RUN;
     const int tile = blockIdx.x / slices, slice = blockIdx.x - tile * slices;
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-    const int col = slice * 256 + (l & 31) * 8;
+    const int col = slice * RUN + (RUN == 512 ? l : (l & 31)) * 8;
     int tk[4];
     bool ok[4];
     uint4 v[4][5];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-        const int t = tile * 32 + 8 * w + 2 * p + (l >> 5);
+        const int t = RUN == 512 ? tile * kTok + 4 * w + p : tile * kTok + 8 * w + 2 * p + (l >> 5);
         ok[p] = t < T;
         tk[p] = ok[p] ? t : T - 1;
 #pragma unroll
@@ -857,8 +864,12 @@ hipError_t launch_post(int T, int hidden, const uint16_t* x, const uint16_t* X,
                        const float* post_prev, const float* comb_prev, uint16_t* xn_out,
                        hipStream_t stream) {
     if ((size_t)T * 4 * (size_t)hidden * 2 >= ((size_t)128 << 20)) {
-        hipLaunchKernelGGL((k_post_rows<true>), dim3((unsigned)((T + 31) / 32) * (unsigned)(hidden / 256)),
-                           dim3(256), 0, stream, T, hidden, x, X, post_prev, comb_prev, xn_out);
+        if (hidden % 512 == 0 && hidden % 2048 != 0)
+            hipLaunchKernelGGL((k_post_rows<true, 512>), dim3((unsigned)((T + 15) / 16) * (unsigned)(hidden / 512)),
+                               dim3(256), 0, stream, T, hidden, x, X, post_prev, comb_prev, xn_out);
+        else
+            hipLaunchKernelGGL((k_post_rows<true, 256>), dim3((unsigned)((T + 31) / 32) * (unsigned)(hidden / 256)),
+                               dim3(256), 0, stream, T, hidden, x, X, post_prev, comb_prev, xn_out);
         return hipGetLastError();
     }
     const int chunks = (hidden / 8 + 255) / 256;

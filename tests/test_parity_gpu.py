@@ -526,11 +526,13 @@ def test_determinism_decode(schedule):
             assert np.array_equal(a[k], b[k]), k
 
 
-@pytest.mark.parametrize("T,d", [(1, 256), (37, 1024), (300, 7168), (2341, 7168), (8197, 4096)])
+@pytest.mark.parametrize("T,d", [(1, 256), (37, 1024), (300, 7168), (2341, 7168), (4101, 5120),
+                                 (8197, 4096)])
 def test_post_matches_boundary_residual(oracle, T, d):
     """The standalone residual update gives the oracle's X' bit for bit (from 128
-    MiB of X it runs in 32-token tiles; 2341 and 8197 tokens end in ragged
-    tiles)."""
+    MiB of X it runs in tiles of 16 tokens x 512 elements, or 32 x 256 where the
+    token stride is a multiple of 16 KiB; 2341, 4101 and 8197 tokens end in
+    ragged tiles)."""
     say(f"post T={T} d={d}")
     inp = WL.make_inputs(WL.Config("post", d=d, T=T, seed=T + d))
     dv = Dev(inp)
