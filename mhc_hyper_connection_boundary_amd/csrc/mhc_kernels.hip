@@ -98,7 +98,8 @@ __global__ __launch_bounds__(256) void k_partial(
     uint16_t* __restrict__ li_out, float* __restrict__ part) {
     MHC_POISON_LDS(0);
     constexpr int kTok = kTile * G;  // tokens of the workgroup
-    __shared__ uint4 stage[2][G][16 * 4 * 16];
+    constexpr int kGroupStage = kTile * 4 * 16;  // one group's X' of a step: [token][stream][chunk]
+    __shared__ uint4 stage[2][G][kGroupStage];
     __shared__ float red[4][kTok][24];
     __shared__ float sqo[kTok][2];
 
@@ -183,14 +184,14 @@ __global__ __launch_bounds__(256) void k_partial(
                 square_sum(Xv[r], ssq[r]);
             }
 #pragma unroll
-            for (int s = 0; s < 4; ++s) st[r * 1024 + (t4 * 4 + s) * 16 + (ch ^ t4)] = Xn[s];
+            for (int s = 0; s < 4; ++s) st[r * kGroupStage + (t4 * 4 + s) * 16 + (ch ^ t4)] = Xn[s];
         }
         __syncthreads();
 #pragma unroll
         for (int q = 0; q < G; ++q) {
             uint4 B[4];
 #pragma unroll
-            for (int s = 0; s < 4; ++s) B[s] = st[q * 1024 + (n * 4 + s) * 16 + ((4 * wave + g) ^ n)];
+            for (int s = 0; s < 4; ++s) B[s] = st[q * kGroupStage + (n * 4 + s) * 16 + ((4 * wave + g) ^ n)];
             mfma_step(A, B, acc[q]);
         }
 #pragma unroll
