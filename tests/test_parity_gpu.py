@@ -719,6 +719,40 @@ def test_random_shapes_and_parameters(oracle, T, d, iters, eps, scale, family):
             fresh=(inp.X, inp.norm_w))
 
 
+def _random_large_cases(n, seed):
+    """Batch sizes drawn from the ranges where AUTO (on 256 compute units) runs
+    4-wave tiles in one round (4608-8192 tokens), 16-token tiles (2560-4607)
+    and 4-wave tiles over two rounds (14336-16384, widths up to 4096)."""
+    rng = np.random.default_rng(seed)
+    ranges = ((4608, 8192), (2560, 4607), (14336, 16384))
+    cases = []
+    for k in range(n):
+        lo, hi = ranges[k % 3]
+        d = int(rng.choice([w for w in sorted(FUSED_D) if lo < 14336 or w <= 4096]))
+        T = int(rng.integers(lo, hi + 1))
+        iters = int(rng.integers(1, 30))
+        scale = tuple(float(v) for v in rng.uniform(0.005, 0.8, 3))
+        cases.append((T, d, iters, scale, "mixture" if k % 2 else "routed"))
+    return cases
+
+
+@pytest.mark.parametrize("T,d,iters,scale,family", _random_large_cases(5, seed=87))
+def test_random_large_batches(oracle, T, d, iters, scale, family):
+    """Seeded batch sizes where AUTO runs the fused kernels (its tile shape then
+    depends on T and the width), every token compared, beside the fused and
+    split schedules and the pre."""
+    say(f"random large T={T} d={d} iters={iters} scale={scale} {family} "
+        f"({api.boundary_kernels(T, d)})")
+    inp = WL.make_inputs(WL.Config("rndL", d=d, T=T, seed=T * 7 + d, sinkhorn_iters=iters,
+                                   scale=scale, comb_family=family))
+    dv = Dev(inp)
+    o = oracle.boundary(inp)
+    for schedule in ("auto", "fused", "split"):
+        compare(dv.boundary(schedule=schedule), o, label=f"random large {schedule}")
+    compare(dv.pre(norm=True), oracle.pre(inp, use_norm=True), xn=False, label="random large pre",
+            fresh=(inp.X, inp.norm_w))
+
+
 # Per-group scales far apart, a strongly routed comb_prev and comb bases far from
 # symmetric: a scale applied to the wrong group of coefficients, a comb logit read
 # transposed or a mix row sent to the wrong coefficient fails these cases.  Every
