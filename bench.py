@@ -34,9 +34,9 @@ HBM_PEAK_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 # The sources whose text decides each boundary kernel's memory traffic (the
 # names are those mhc_boundary_kernels reports).
-KERNEL_FILES = {
-    "k_fused_w4": ("mhc_fused.hip", "mhc_device.h"),
-    "k_fused": ("mhc_fused.hip", "mhc_device.h"),
+KERNEL_FILES = {  # (build.py: the fused kernels' compiler flags)
+    "k_fused_w4": ("mhc_fused.hip", "mhc_device.h", "../build.py"),
+    "k_fused": ("mhc_fused.hip", "mhc_device.h", "../build.py"),
     "k_stream": ("mhc_stream.hip", "mhc_device.h"),
     "k_partial+k_finish": ("mhc_kernels.hip", "mhc_device.h"),
 }
@@ -566,6 +566,7 @@ def write_traffic_profile(prof_dir, kernel, schedule):
     lines = [
         f"{kernel} prefill (d=7168, T=8192): HBM traffic per call from rocprofv3 counters",
         f"sources_sha256: {kernel_sources_sha256(kernel)}",
+        f"sources_hashed: {' '.join(KERNEL_FILES[kernel])} (under the package's csrc/)",
         f"fetch_size_kib_per_dispatch: {f_k:.1f}",
         f"write_size_kib_per_dispatch: {w_k:.1f}",
         f"dispatches: {nf} / {nw}",

@@ -23,6 +23,11 @@ POISON_LIB = os.path.join(PKG, "libmhc_lds_poison.so")
 MOVER_LIB = os.path.join(PKG, "libmhc_mover.so")
 MOVER_SOURCE = "mhc_mover.hip"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+# Second compilations of a source, each with its own defines and flags: the
+# 16-token fused boundary kernel at hidden 7168 under LLVM's max-ilp machine
+# scheduler (mhc_fused.hip holds the measurements).
+EXTRA_UNITS = [("mhc_fused.hip", "mhc_fused_maxilp",
+                ["-DMHC_FUSED_MAXILP", "-mllvm", "-amdgpu-sched-strategy=max-ilp"])]
 
 ARCH = ["--offload-arch=gfx950"]
 FLAGS = [
@@ -47,18 +52,19 @@ def _run(cmd: list[str], verbose: bool) -> str:
 
 def build(verbose: bool = False, resource_usage: bool = False) -> str:
     with tempfile.TemporaryDirectory(prefix="mhc_build_") as tmp:
+        units = [(s, os.path.splitext(s)[0], []) for s in SOURCES] + EXTRA_UNITS
         jobs = []
-        for s in SOURCES:
-            obj = os.path.join(tmp, os.path.splitext(s)[0] + ".o")
-            cmd = [HIPCC, *ARCH, *FLAGS, "-I", os.path.join(ROOT, "include"),
+        for s, name, extra in units:
+            obj = os.path.join(tmp, name + ".o")
+            cmd = [HIPCC, *ARCH, *FLAGS, *extra, "-I", os.path.join(ROOT, "include"),
                    "-c", os.path.join(CSRC, s), "-o", obj]
             if resource_usage:
                 cmd.insert(1, "-Rpass-analysis=kernel-resource-usage")
             jobs.append((cmd, obj))
         poison_jobs = []
-        for s in SOURCES:
-            obj = os.path.join(tmp, "poison_" + os.path.splitext(s)[0] + ".o")
-            poison_jobs.append(([HIPCC, *ARCH, *FLAGS, "-DMHC_LDS_POISON", "-I", os.path.join(ROOT, "include"),
+        for s, name, extra in units:
+            obj = os.path.join(tmp, "poison_" + name + ".o")
+            poison_jobs.append(([HIPCC, *ARCH, *FLAGS, *extra, "-DMHC_LDS_POISON", "-I", os.path.join(ROOT, "include"),
                                  "-c", os.path.join(CSRC, s), "-o", obj], obj))
         mover_obj = os.path.join(tmp, "mhc_mover.o")
         mover_cmd = [HIPCC, *ARCH, *FLAGS, "-c", os.path.join(CSRC, MOVER_SOURCE), "-o", mover_obj]

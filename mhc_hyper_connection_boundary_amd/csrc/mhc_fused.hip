@@ -1270,6 +1270,36 @@ hipError_t launch_s(int T, const uint16_t* x, const uint16_t* X, const float* po
 
 }  // namespace
 
+// The 16-token boundary kernel at hidden 7168 comes from a second compilation
+// of this file with LLVM's max-ilp machine scheduler (MHC_FUSED_MAXILP): the
+// same arithmetic in the same order, so the same bits.  Cold, d=7168, us,
+// default scheduler -> max-ilp (two runs): T=2560 115 -> 111.6 / 113.0,
+// T=4096 135 -> 130.8 / 134.8, T=9216 358 -> 340.5 / 338.8, T=12288 392 -> 378
+// / 378.7.  The 4-wave kernel at 7168 measured level with it (T=5120-8192 and
+// 16384 within 1%), and at hidden 4096, 5120 and 6144 the 16-token kernel
+// measured 1-5% slower, so those keep the default scheduler.
+hipError_t launch_fused_7168(int T, const uint16_t* x, const uint16_t* X, const float* post_prev,
+                             const float* comb_prev, const float* pre_lag, const void* wprep,
+                             const float* scale, const float* base, const uint16_t* norm_w,
+                             const Scalars& p, uint16_t* xn_out, uint16_t* layer_input,
+                             float* pre_out, float* post_out, float* comb_out, float* mixes,
+                             float* rstd, hipStream_t stream);
+
+#ifdef MHC_FUSED_MAXILP
+
+hipError_t launch_fused_7168(int T, const uint16_t* x, const uint16_t* X, const float* post_prev,
+                             const float* comb_prev, const float* pre_lag, const void* wprep,
+                             const float* scale, const float* base, const uint16_t* norm_w,
+                             const Scalars& p, uint16_t* xn_out, uint16_t* layer_input,
+                             float* pre_out, float* post_out, float* comb_out, float* mixes,
+                             float* rstd, hipStream_t stream) {
+    return launch_s<7168 / 512>(T, x, X, post_prev, comb_prev, pre_lag, wprep, scale, base, norm_w,
+                                p, xn_out, layer_input, pre_out, post_out, comb_out, mixes, rstd,
+                                stream);
+}
+
+#else  // the default scheduler: every other kernel and width, and the dispatch
+
 bool fused_supported(int hidden) {
     switch (hidden) {
         case 1024: case 2048: case 4096: case 5120: case 6144: case 7168: case 8192:
@@ -1296,7 +1326,10 @@ hipError_t launch_fused(int T, int hidden, const uint16_t* x, const uint16_t* X,
         MHC_FUSED_CASE(4096)
         MHC_FUSED_CASE(5120)
         MHC_FUSED_CASE(6144)
-        MHC_FUSED_CASE(7168)
+        case 7168:
+            return launch_fused_7168(T, x, X, post_prev, comb_prev, pre_lag, wprep, scale, base,
+                                     norm_w, p, xn_out, layer_input, pre_out, post_out, comb_out,
+                                     mixes, rstd, stream);
         MHC_FUSED_CASE(8192)
         default:
             return hipErrorInvalidValue;
@@ -1357,5 +1390,7 @@ hipError_t launch_fused_pre(int T, int hidden, const uint16_t* X, const void* wp
     }
 #undef MHC_FUSED_PRE_CASE
 }
+
+#endif  // MHC_FUSED_MAXILP
 
 }  // namespace mhc
