@@ -23,11 +23,13 @@ POISON_LIB = os.path.join(PKG, "libmhc_lds_poison.so")
 MOVER_LIB = os.path.join(PKG, "libmhc_mover.so")
 MOVER_SOURCE = "mhc_mover.hip"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-# Second compilations of a source, each with its own defines and flags: the
-# 16-token fused boundary kernel at hidden 7168 under LLVM's max-ilp machine
-# scheduler (mhc_fused.hip holds the measurements).
+# Further compilations of a source, each with its own defines and flags: the
+# fused boundary kernels at hidden 7168 under other LLVM machine schedulers
+# (mhc_fused.hip holds the measurements).
 EXTRA_UNITS = [("mhc_fused.hip", "mhc_fused_maxilp",
-                ["-DMHC_FUSED_MAXILP", "-mllvm", "-amdgpu-sched-strategy=max-ilp"])]
+                ["-DMHC_FUSED_MAXILP", "-mllvm", "-amdgpu-sched-strategy=max-ilp"]),
+               ("mhc_fused.hip", "mhc_fused_maxclause",
+                ["-DMHC_FUSED_MAXCLAUSE", "-mllvm", "-amdgpu-sched-strategy=max-memory-clause"])]
 
 ARCH = ["--offload-arch=gfx950"]
 FLAGS = [

@@ -1270,22 +1270,46 @@ hipError_t launch_s(int T, const uint16_t* x, const uint16_t* X, const float* po
 
 }  // namespace
 
-// The 16-token boundary kernel at hidden 7168 comes from a second compilation
-// of this file with LLVM's max-ilp machine scheduler (MHC_FUSED_MAXILP): the
-// same arithmetic in the same order, so the same bits.  Cold, d=7168, us,
-// default scheduler -> max-ilp (two runs): T=2560 115 -> 111.6 / 113.0,
-// T=4096 135 -> 130.8 / 134.8, T=9216 358 -> 340.5 / 338.8, T=12288 392 -> 378
-// / 378.7.  The 4-wave kernel at 7168 measured level with it (T=5120-8192 and
-// 16384 within 1%), and at hidden 4096, 5120 and 6144 the 16-token kernel
-// measured 1-5% slower, so those keep the default scheduler.
+// The boundary kernels at hidden 7168 come from further compilations of this
+// file, each under another of LLVM's machine schedulers: the 16-token kernel
+// under max-ilp (MHC_FUSED_MAXILP), the 4-wave kernel under max-memory-clause
+// (MHC_FUSED_MAXCLAUSE).  The same arithmetic in the same order, so the same
+// bits.  Cold, d=7168, us, default scheduler -> the unit's: 16-token tiles
+// (two runs) T=2560 115 -> 111.6 / 113.0, T=4096 135 -> 130.8 / 134.8, T=9216
+// 358 -> 340.5 / 338.8, T=12288 392 -> 378 / 378.7; 4-wave tiles T=4608 173.2
+// -> 167.5, T=5120 183.6 -> 177.5, T=8192 244.5 -> 243.3, T=6144 and 16384
+// level.  The 4-wave kernel measured level under max-ilp; the 16-token kernel
+// measured 1-8% slower under max-ilp at hidden 4096, 5120, 6144 and 8192, so
+// the other widths keep the default scheduler.
 hipError_t launch_fused_7168(int T, const uint16_t* x, const uint16_t* X, const float* post_prev,
                              const float* comb_prev, const float* pre_lag, const void* wprep,
                              const float* scale, const float* base, const uint16_t* norm_w,
                              const Scalars& p, uint16_t* xn_out, uint16_t* layer_input,
                              float* pre_out, float* post_out, float* comb_out, float* mixes,
                              float* rstd, hipStream_t stream);
+hipError_t launch_fused_w4_7168(int T, int tile_tokens, const uint16_t* x, const uint16_t* X,
+                                const float* post_prev, const float* comb_prev,
+                                const float* pre_lag, const void* wprep, const float* scale,
+                                const float* base, const uint16_t* norm_w, const Scalars& p,
+                                uint16_t* xn_out, uint16_t* layer_input, float* pre_out,
+                                float* post_out, float* comb_out, float* mixes, float* rstd,
+                                hipStream_t stream);
 
-#ifdef MHC_FUSED_MAXILP
+#if defined(MHC_FUSED_MAXCLAUSE)
+
+hipError_t launch_fused_w4_7168(int T, int tile_tokens, const uint16_t* x, const uint16_t* X,
+                                const float* post_prev, const float* comb_prev,
+                                const float* pre_lag, const void* wprep, const float* scale,
+                                const float* base, const uint16_t* norm_w, const Scalars& p,
+                                uint16_t* xn_out, uint16_t* layer_input, float* pre_out,
+                                float* post_out, float* comb_out, float* mixes, float* rstd,
+                                hipStream_t stream) {
+    return launch_w4_s<7168 / 256>(T, tile_tokens, x, X, post_prev, comb_prev, pre_lag, wprep,
+                                   scale, base, norm_w, p, xn_out, layer_input, pre_out, post_out,
+                                   comb_out, mixes, rstd, stream);
+}
+
+#elif defined(MHC_FUSED_MAXILP)
 
 hipError_t launch_fused_7168(int T, const uint16_t* x, const uint16_t* X, const float* post_prev,
                              const float* comb_prev, const float* pre_lag, const void* wprep,
@@ -1356,7 +1380,10 @@ hipError_t launch_fused_w4(int T, int tile_tokens, int hidden, const uint16_t* x
         MHC_W4_CASE(4096)
         MHC_W4_CASE(5120)
         MHC_W4_CASE(6144)
-        MHC_W4_CASE(7168)
+        case 7168:
+            return launch_fused_w4_7168(T, tile_tokens, x, X, post_prev, comb_prev, pre_lag, wprep,
+                                        scale, base, norm_w, p, xn_out, layer_input, pre_out,
+                                        post_out, comb_out, mixes, rstd, stream);
         MHC_W4_CASE(8192)
         default:
             return hipErrorInvalidValue;
@@ -1391,6 +1418,6 @@ hipError_t launch_fused_pre(int T, int hidden, const uint16_t* X, const void* wp
 #undef MHC_FUSED_PRE_CASE
 }
 
-#endif  // MHC_FUSED_MAXILP
+#endif  // the scheduler units
 
 }  // namespace mhc
